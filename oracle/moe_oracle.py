@@ -1,0 +1,248 @@
+"""Plain CPU oracle for the DeepSeekMoE layer forward, in float64.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import or call this
+module: only the tests, the smoke check and the bench's CPU-baseline leg do.
+It shares no code with the HIP library and takes plain numpy arrays.
+
+What it computes, and where the pages define it (page titles as printed):
+
+* "DeepSeek-V2 ... walkthrough" (page 1), section on the DeepSeekMoE
+  architecture: the FFN output of token t is its input u_t plus the outputs of
+  N_s always-active shared experts plus the gate-weighted outputs of the K_r
+  routed experts with the highest token-to-expert affinity s_i,t. The same
+  page's MoEGate code fixes the router: an fp32 linear map of the token to E
+  logits, softmax scores, then greedy top-K or group-limited greedy top-K
+  (per-group maximum, keep the best topk_group groups, top-K inside them).
+  Its MoE code fuses the shared experts into one SwiGLU of hidden
+  hidden_dim * n_shared_experts.
+* "DeepSeekMoE + MLA" notes (page 3), section 2.1: p = softmax(W_gate x) and
+  y = sum over the top-K of p_i E_i(x), gates not renormalised; section 5 and
+  the architecture article (page 2, section 3.3): a SwiGLU expert without
+  biases, down(SiLU(gate x) * up x).
+* "DeepSeek-V3 basics" (page 5), section 1.2: a per-expert bias is added to
+  the affinity only to choose the top-K; the gate value comes from the
+  original affinity.
+* "Transformer block" article (page 4), data-flow section: the scores may come
+  from softmax "or another activation" (sigmoid is used for the V3 shapes).
+
+Readings where the pages are silent or garbled (the formula images are
+missing from the extracted pages):
+
+* groups are contiguous runs of E/G experts (the view(n, n_group, -1) of the
+  MoEGate code); the group score is the maximum of score + bias over the group;
+* experts outside the kept groups are excluded outright (never selected);
+* ties go to the lower group index and to the lower expert index; selected
+  indices are listed by descending selection score, then ascending index;
+* softmax is taken over all E logits before any masking;
+* gates: g_k = s[idx_k]; if normalised, g_k /= sum_k s[idx_k]; then g_k *= rsf;
+* the output includes the residual u_t when add_residual is set.
+
+Every routine below is pinned by tests in tests/test_oracle_pins.py (brute
+force on tiny inputs, closed forms, reductions to a dense FFN or to the dense
+softmax mixture, library decoders for the storage formats).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------
+# storage formats: exact decoders
+# ----------------------------------------------------------------------------
+
+
+def decode_bf16(bits) -> np.ndarray:
+    """bfloat16 bit patterns (uint16/int16) -> float64: the upper half of a
+    float32, so widening by 16 zero bits is exact."""
+    b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):  # NaN codes stay NaN
+        return b.view(np.float32).astype(np.float64)
+
+
+def decode_f32(values) -> np.ndarray:
+    return np.asarray(values, dtype=np.float32).astype(np.float64)
+
+
+def decode_e4m3(bits) -> np.ndarray:
+    """OCP FP8 E4M3 codes -> float64, from the format's definition: 1 sign bit,
+    4 exponent bits with bias 7, 3 mantissa bits; exponent 0 is subnormal
+    (m/8 * 2^-6); S.1111.111 is NaN; no infinities; largest finite 448."""
+    c = np.asarray(bits).astype(np.int64) & 0xFF
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    ex = (c >> 3) & 0xF
+    man = (c & 0x7).astype(np.float64)
+    normal = (1.0 + man / 8.0) * np.exp2(ex.astype(np.float64) - 7.0)
+    sub = (man / 8.0) * 2.0 ** -6
+    v = sign * np.where(ex == 0, sub, normal)
+    return np.where((c & 0x7F) == 0x7F, np.nan, v)
+
+
+def dequant_e4m3_blocks(codes, scale, block: int = 128) -> np.ndarray:
+    """w[r, c] = e4m3(codes[r, c]) * scale[r // block, c // block]."""
+    q = decode_e4m3(codes)
+    s = np.asarray(scale, dtype=np.float32).astype(np.float64)
+    s_full = np.repeat(np.repeat(s, block, axis=-2), block, axis=-1)
+    return q * s_full
+
+
+# ----------------------------------------------------------------------------
+# parameters
+# ----------------------------------------------------------------------------
+
+
+@dataclass(frozen=True)
+class RouterParams:
+    E: int  # routed experts
+    K: int  # experts per token
+    G: int = 1  # groups (1: greedy)
+    kg: int = 1  # groups kept
+    score_fn: str = "softmax"  # "softmax" | "sigmoid"
+    norm: bool = False
+    rsf: float = 1.0
+
+
+# ----------------------------------------------------------------------------
+# router
+# ----------------------------------------------------------------------------
+
+
+def router_logits(u: np.ndarray, gate_w: np.ndarray) -> np.ndarray:
+    """l[t, e] = sum_d u[t, d] * gate_w[e, d] (the MoEGate linear map, here in
+    float64)."""
+    return np.asarray(u, np.float64) @ np.asarray(gate_w, np.float64).T
+
+
+def affinity(logits: np.ndarray, score_fn: str) -> np.ndarray:
+    """s = softmax over all E experts, or the element-wise sigmoid."""
+    if score_fn == "softmax":
+        z = logits - logits.max(axis=1, keepdims=True)
+        ez = np.exp(z)
+        return ez / ez.sum(axis=1, keepdims=True)
+    if score_fn == "sigmoid":
+        with np.errstate(over="ignore"):
+            return 1.0 / (1.0 + np.exp(-logits))
+    raise ValueError(score_fn)
+
+
+def select_experts(z: np.ndarray, G: int, kg: int, K: int):
+    """Group-limited greedy top-K on selection scores z [T, E].
+
+    Returns (idx [T, K] int64, gap_k [T], gap_g [T], kept_groups [T, kg]).
+    gap_k is z_(K) - z_(K+1) over the candidate experts; gap_g is
+    m_(kg) - m_(kg+1) over the group maxima (inf where no (K+1)-th exists).
+    """
+    T, E = z.shape
+    rows = np.arange(T)
+    allowed = np.ones((T, E), dtype=bool)
+    gap_g = np.full(T, np.inf)
+    kept = np.zeros((T, 0), dtype=np.int64)
+    if G > 1:
+        m = z.reshape(T, G, E // G).max(axis=2)
+        gorder = np.argsort(-m, axis=1, kind="stable")  # descending, lower group first on ties
+        kept = gorder[:, :kg]
+        gmask = np.zeros((T, G), dtype=bool)
+        gmask[rows[:, None], kept] = True
+        allowed = np.repeat(gmask, E // G, axis=1)
+        if kg < G:
+            gap_g = m[rows, gorder[:, kg - 1]] - m[rows, gorder[:, kg]]
+    zc = np.where(allowed, z, -np.inf)
+    order = np.argsort(-zc, axis=1, kind="stable")  # descending, lower expert first on ties
+    idx = order[:, :K]
+    n_cand = int(allowed[0].sum()) if T else 0
+    gap_k = np.full(T, np.inf)
+    if n_cand > K:
+        gap_k = zc[rows, order[:, K - 1]] - zc[rows, order[:, K]]
+    return idx, gap_k, gap_g, kept
+
+
+def gate_values(s: np.ndarray, idx: np.ndarray, norm: bool, rsf: float) -> np.ndarray:
+    """g_k = s[idx_k] from the unbiased affinity; optional renormalisation over
+    the K chosen experts; then the routed scaling factor."""
+    g = np.take_along_axis(s, idx, axis=1)
+    if norm:
+        g = g / g.sum(axis=1, keepdims=True)
+    return g * rsf
+
+
+def expert_counts(idx: np.ndarray, E: int) -> np.ndarray:
+    """c[e] = number of (token, slot) pairs routed to expert e."""
+    c = np.zeros(E, dtype=np.int64)
+    for e in idx.reshape(-1):
+        c[e] += 1
+    return c
+
+
+def route(u: np.ndarray, gate_w: np.ndarray, sel_bias, p: RouterParams) -> dict:
+    logits = router_logits(u, gate_w)
+    s = affinity(logits, p.score_fn)
+    z = s if sel_bias is None else s + np.asarray(sel_bias, np.float64)[None, :]
+    idx, gap_k, gap_g, kept = select_experts(z, p.G, p.kg, p.K)
+    return dict(logits=logits, scores=s, z=z, idx=idx, gate=gate_values(s, idx, p.norm, p.rsf),
+                counts=expert_counts(idx, p.E),
+                gap_k=gap_k, gap_g=gap_g, kept_groups=kept)
+
+
+# ----------------------------------------------------------------------------
+# experts
+# ----------------------------------------------------------------------------
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z) = z / (1 + exp(-z))."""
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+def swiglu_ffn(u: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """FFN(u) = W_down (SiLU(W_gate u) * (W_up u)) for rows u [n, D]; weights in
+    nn.Linear layout: w_gate, w_up [h, D], w_down [D, h]."""
+    return (silu(u @ w_gate.T) * (u @ w_up.T)) @ w_down.T
+
+
+def split_gate_up(gate_up: np.ndarray):
+    """[2h, D] -> (W_gate = rows 0..h-1, W_up = rows h..2h-1)."""
+    h = gate_up.shape[0] // 2
+    return gate_up[:h], gate_up[h:]
+
+
+def layer_forward(p: RouterParams, u: np.ndarray, gate_w: np.ndarray, sel_bias, routed_expert,
+                  shared_expert=None, add_residual: bool = True, tokens=None, routing: dict | None = None):
+    """out_t = [u_t] + FFN_shared(u_t) + sum_k g_{t,k} FFN_{idx_{t,k}}(u_t).
+
+    routed_expert(e) -> (w_gate, w_up, w_down) float64 for routed expert e;
+    shared_expert() -> the same for the fused shared expert, or None.
+    Routing is computed for every token (counts need all of them); the
+    output only for `tokens` (default: all), in that order.
+    Returns (out [len(tokens), D], routing dict).
+    """
+    u = np.asarray(u, np.float64)
+    if routing is None:
+        routing = route(u, gate_w, sel_bias, p)
+    T = u.shape[0]
+    tokens = np.arange(T) if tokens is None else np.asarray(tokens)
+    ut = u[tokens]
+    idx = routing["idx"][tokens]
+    gate = routing["gate"][tokens]
+    n, D = ut.shape
+    # Y[i, k] = FFN_{idx[i, k]}(u_{tokens[i]}); each expert's weights are decoded once
+    Y = np.zeros((n, p.K, D))
+    for e in np.unique(idx):
+        ii, kk = np.nonzero(idx == e)
+        Y[ii, kk] = swiglu_ffn(ut[ii], *routed_expert(int(e)))
+    out = np.zeros((n, D))
+    if add_residual:
+        out += ut
+    if shared_expert is not None:
+        sw = shared_expert()
+        if sw is not None:
+            out += swiglu_ffn(ut, *sw)
+    for k in range(p.K):
+        out += gate[:, k:k + 1] * Y[:, k]
+    return out, routing
+
+
+def near_tie_tokens(routing: dict, window: float = 1e-6) -> np.ndarray:
+    """Tokens whose K/K+1 or group-boundary selection-score gap is within the window."""
+    return np.nonzero((routing["gap_k"] < window) | (routing["gap_g"] < window))[0]

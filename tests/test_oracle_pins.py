@@ -1,0 +1,392 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: brute force
+over subsets on tiny inputs, closed forms, special cases that reduce to a
+dense FFN or to the dense softmax mixture, and library decoders for the
+storage formats. A dropped term, a wrong sign or index, or a transposed
+operand in the oracle fails at least one of them (test_pins_catch_planted_bugs
+plants such mistakes in a copy of the oracle and checks that they are caught).
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+
+RNG = np.random.default_rng(1234)
+
+
+# ----------------------------------------------------------------------------
+# storage formats
+# ----------------------------------------------------------------------------
+
+
+def test_bf16_decode_all_codes_match_torch():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = O.decode_bf16(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_e4m3_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = O.decode_e4m3(codes)
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # format facts: largest finite 448, smallest subnormal 2^-9
+    assert np.nanmax(got) == 448.0 and got[1] == 2.0 ** -9
+
+
+def test_e4m3_block_dequant_uses_the_right_block():
+    codes = np.full((256, 384), 0x38, dtype=np.uint8)  # e4m3 1.0
+    scale = np.arange(6, dtype=np.float32).reshape(2, 3) + 1.0
+    w = O.dequant_e4m3_blocks(codes, scale)
+    for i in range(2):
+        for j in range(3):
+            assert np.all(w[128 * i:128 * (i + 1), 128 * j:128 * (j + 1)] == scale[i, j])
+
+
+# ----------------------------------------------------------------------------
+# router
+# ----------------------------------------------------------------------------
+
+
+def test_logits_brute_force():
+    u = RNG.standard_normal((5, 7))
+    w = RNG.standard_normal((3, 7))
+    got = O.router_logits(u, w)
+    for t in range(5):
+        for e in range(3):
+            acc = 0.0
+            for d in range(7):
+                acc += u[t, d] * w[e, d]
+            assert abs(got[t, e] - acc) < 1e-12
+
+
+def test_softmax_rows_sum_to_one_and_match_torch():
+    l = RNG.standard_normal((64, 12)) * 3
+    s = O.affinity(l, "softmax")
+    assert np.allclose(s.sum(1), 1.0, atol=1e-12, rtol=0)
+    ref = torch.softmax(torch.from_numpy(l), dim=-1).numpy()
+    assert np.allclose(s, ref, atol=1e-15, rtol=1e-13)
+    # shift invariance and monotonicity
+    assert np.allclose(O.affinity(l + 5.0, "softmax"), s, atol=1e-15)
+    assert np.array_equal(np.argsort(l, axis=1), np.argsort(s, axis=1))
+
+
+def test_sigmoid_closed_forms():
+    l = np.array([[0.0, math.log(3.0), -math.log(3.0), 800.0, -800.0]])
+    s = O.affinity(l, "sigmoid")
+    assert s[0, 0] == 0.5
+    assert abs(s[0, 1] - 0.75) < 1e-15 and abs(s[0, 2] - 0.25) < 1e-15
+    assert s[0, 3] == 1.0 and s[0, 4] == 0.0
+
+
+def _brute_select(z_row, G, kg, K):
+    """Exhaustive search: the kept groups are the kg-subset with the largest sum
+    of group maxima (lexicographically smallest index tuple among equals); the
+    experts are the K-subset of their members with the largest sum of z (same
+    tie rule)."""
+    E = len(z_row)
+    gs = E // G
+    members = list(range(E))
+    if G > 1:
+        m = [max(z_row[j * gs:(j + 1) * gs]) for j in range(G)]
+        best = None
+        for S in itertools.combinations(range(G), kg):
+            key = (sum(m[j] for j in S), tuple(-j for j in S))
+            if best is None or key > best[0]:
+                best = (key, S)
+        members = [e for j in best[1] for e in range(j * gs, (j + 1) * gs)]
+    best = None
+    for S in itertools.combinations(members, K):
+        key = (sum(z_row[e] for e in S), tuple(-e for e in sorted(S)))
+        if best is None or key > best[0]:
+            best = (key, S)
+    return set(best[1])
+
+
+@pytest.mark.parametrize("E,G,kg,K", [(8, 1, 1, 3), (8, 4, 2, 3), (12, 3, 2, 4), (12, 4, 4, 2),
+                                      (16, 4, 1, 4), (9, 3, 2, 6), (6, 1, 1, 6)])
+def test_selection_matches_brute_force(E, G, kg, K):
+    # values on a coarse grid so that exact ties happen often
+    for trial in range(60):
+        z = RNG.integers(0, 6, size=(1, E)).astype(np.float64) / 4.0
+        if trial % 3 == 0:
+            z = RNG.standard_normal((1, E))
+        idx, _, _, _ = O.select_experts(z, G, kg, K)
+        assert set(idx[0].tolist()) == _brute_select(list(z[0]), G, kg, K)
+        # canonical order: descending z, then ascending index
+        order = sorted(idx[0].tolist(), key=lambda e: (-z[0, e], e))
+        assert idx[0].tolist() == order
+
+
+def test_all_groups_kept_and_single_group_are_greedy():
+    z = RNG.standard_normal((200, 16))
+    greedy = O.select_experts(z, 1, 1, 4)[0]
+    assert np.array_equal(O.select_experts(z, 4, 4, 4)[0], greedy)
+    assert np.array_equal(O.select_experts(z, 8, 8, 4)[0], greedy)
+    # greedy: the K largest, verified by a full sort
+    for t in range(200):
+        assert set(greedy[t]) == set(np.argsort(-z[t], kind="stable")[:4])
+
+
+def test_all_ties_pick_lowest_groups_and_indices():
+    p = O.RouterParams(E=16, K=3, G=4, kg=2, score_fn="softmax")
+    r = O.route(np.zeros((3, 8)), RNG.standard_normal((16, 8)), None, p)
+    assert np.all(r["idx"] == [0, 1, 2])
+    assert np.all(r["kept_groups"] == [0, 1])
+    assert np.allclose(r["gate"], 1.0 / 16)
+
+
+def test_large_bias_forces_an_expert_and_constant_bias_is_inert():
+    T, D, E = 50, 16, 16
+    u = RNG.standard_normal((T, D))
+    w = RNG.standard_normal((E, D)) * 0.3
+    p = O.RouterParams(E=E, K=4, G=4, kg=2, score_fn="sigmoid", norm=True, rsf=2.5)
+    b = RNG.standard_normal(E) * 0.01
+    r0 = O.route(u, w, b, p)
+    b2 = b.copy()
+    b2[11] = 10.0
+    r1 = O.route(u, w, b2, p)
+    assert np.all(np.any(r1["idx"] == 11, axis=1))
+    assert r1["counts"][11] == T
+    r2 = O.route(u, w, b + 3.0, p)
+    assert np.array_equal(r2["idx"], r0["idx"])
+    assert np.allclose(r2["gate"], r0["gate"], rtol=0, atol=1e-15)
+
+
+def test_never_outside_kept_groups():
+    T, E, G, kg = 300, 32, 8, 3
+    z = RNG.standard_normal((T, E))
+    idx, _, _, kept = O.select_experts(z, G, kg, 5)
+    assert np.all(np.isin(idx // (E // G), kept).reshape(T, -1).all(axis=1))
+    # the kept groups hold the kg largest group maxima
+    m = z.reshape(T, G, -1).max(2)
+    for t in range(T):
+        assert set(kept[t]) == set(np.argsort(-m[t], kind="stable")[:kg])
+
+
+def test_exclusion_differs_from_zero_fill_when_scores_are_negative():
+    # z <= 0 everywhere (negative bias): an excluded expert must still never win
+    z = np.array([[-0.5, -0.4, -0.1, -0.2, -0.9, -0.8, -0.7, -0.6]])
+    idx, _, _, kept = O.select_experts(z, 4, 1, 2)
+    assert kept[0].tolist() == [1]  # group {2,3} has the largest max (-0.1)
+    assert set(idx[0].tolist()) == {2, 3}
+
+
+def test_gates_normalised_sum_to_rsf_and_come_from_unbiased_scores():
+    T, D, E = 40, 8, 12
+    u = RNG.standard_normal((T, D))
+    w = RNG.standard_normal((E, D))
+    for fn in ("softmax", "sigmoid"):
+        p = O.RouterParams(E=E, K=4, G=3, kg=2, score_fn=fn, norm=True, rsf=2.5)
+        b = RNG.standard_normal(E) * 0.05
+        r = O.route(u, w, b, p)
+        assert np.allclose(r["gate"].sum(1), 2.5, atol=1e-12, rtol=0)
+        # recompute from the unbiased scores on the chosen set
+        s = r["scores"]
+        for t in range(T):
+            sel = s[t, r["idx"][t]]
+            assert np.allclose(r["gate"][t], 2.5 * sel / sel.sum(), atol=1e-15)
+        pn = O.RouterParams(E=E, K=4, G=3, kg=2, score_fn=fn, norm=False, rsf=16.0)
+        rn = O.route(u, w, b, pn)
+        assert np.array_equal(rn["idx"], r["idx"])
+        assert np.allclose(rn["gate"], 16.0 * np.take_along_axis(s, r["idx"], 1), atol=1e-14)
+
+
+def test_counts_sum_and_bincount():
+    z = RNG.standard_normal((500, 20))
+    idx = O.select_experts(z, 4, 2, 3)[0]
+    c = O.expert_counts(idx, 20)
+    assert c.sum() == 500 * 3
+    assert np.array_equal(c, np.bincount(idx.ravel(), minlength=20))
+
+
+def test_gaps_measure_the_selection_boundary():
+    z = np.array([[0.9, 0.5, 0.5 + 1e-9, 0.1]])
+    idx, gap_k, gap_g, _ = O.select_experts(z, 1, 1, 2)
+    assert set(idx[0]) == {0, 2}
+    assert abs(gap_k[0] - 1e-9) < 1e-15 and gap_g[0] == np.inf
+    z = np.array([[0.9, 0.1, 0.3, 0.3, 0.2, 0.25]])
+    idx, gap_k, gap_g, kept = O.select_experts(z, 3, 2, 2)
+    assert kept[0].tolist() == [0, 1] and abs(gap_g[0] - 0.05) < 1e-15
+
+
+# ----------------------------------------------------------------------------
+# experts
+# ----------------------------------------------------------------------------
+
+
+def test_silu_closed_forms():
+    z = np.array([0.0, 1.0, -1.0, 50.0, -50.0, -800.0])
+    s = O.silu(z)
+    assert s[0] == 0.0
+    assert abs(s[1] - 1.0 / (1.0 + math.exp(-1.0))) < 1e-16
+    assert abs(s[2] + math.exp(-1.0) / (1.0 + math.exp(-1.0))) < 1e-16
+    assert abs(s[3] - 50.0) < 1e-12 and abs(s[4]) < 1e-19 and s[5] == 0.0
+
+
+def test_swiglu_worked_example():
+    # D=3, h=2, worked by hand: gate = [1, -2], up = [4, 0.5]
+    u = np.array([[1.0, 2.0, -1.0]])
+    w_gate = np.array([[1.0, 0.0, 0.0], [0.0, -1.0, 0.0]])
+    w_up = np.array([[0.0, 2.0, 0.0], [0.0, 0.0, -0.5]])
+    w_down = np.array([[1.0, 0.0], [0.0, 1.0], [2.0, -3.0]])
+    s1 = 1.0 / (1.0 + math.exp(-1.0))
+    s2 = -2.0 / (1.0 + math.exp(2.0))
+    h = np.array([s1 * 4.0, s2 * 0.5])
+    expect = np.array([h[0], h[1], 2 * h[0] - 3 * h[1]])
+    got = O.swiglu_ffn(u, w_gate, w_up, w_down)[0]
+    assert np.allclose(got, expect, atol=1e-15, rtol=0)
+
+
+def test_fine_grained_split_identity():
+    """An FFN of hidden m*h equals the sum of its m slices taken as experts."""
+    D, h, m = 16, 8, 4
+    u = RNG.standard_normal((10, D))
+    Wg = RNG.standard_normal((m * h, D))
+    Wu = RNG.standard_normal((m * h, D))
+    Wd = RNG.standard_normal((D, m * h))
+    dense = O.swiglu_ffn(u, Wg, Wu, Wd)
+    parts = sum(O.swiglu_ffn(u, Wg[i * h:(i + 1) * h], Wu[i * h:(i + 1) * h], Wd[:, i * h:(i + 1) * h])
+                for i in range(m))
+    assert np.allclose(dense, parts, atol=1e-12)
+
+
+def _rand_experts(E, D, h, scale=0.3):
+    return [(RNG.standard_normal((h, D)) * scale, RNG.standard_normal((h, D)) * scale,
+             RNG.standard_normal((D, h)) * scale) for _ in range(E)]
+
+
+def test_shared_fusion_identity():
+    """Two shared experts of hidden h equal one fused shared expert of hidden 2h."""
+    D, h, E = 12, 6, 6
+    u = RNG.standard_normal((20, D))
+    gw = RNG.standard_normal((E, D))
+    p = O.RouterParams(E=E, K=2)
+    ex = _rand_experts(E, D, h)
+    s1, s2 = _rand_experts(2, D, h)
+    fused = (np.vstack([s1[0], s2[0]]), np.vstack([s1[1], s2[1]]), np.hstack([s1[2], s2[2]]))
+    out_f, r = O.layer_forward(p, u, gw, None, lambda e: ex[e], lambda: fused)
+    out_0, _ = O.layer_forward(p, u, gw, None, lambda e: ex[e], None)
+    assert np.allclose(out_f - out_0, O.swiglu_ffn(u, *s1) + O.swiglu_ffn(u, *s2), atol=1e-12)
+
+
+def test_identical_experts_reduce_to_dense_ffn():
+    D, h, E = 16, 8, 16
+    u = RNG.standard_normal((30, D))
+    gw = RNG.standard_normal((E, D))
+    ex = _rand_experts(1, D, h)[0]
+    p = O.RouterParams(E=E, K=4, G=4, kg=2, score_fn="sigmoid", norm=True, rsf=2.5)
+    b = RNG.standard_normal(E) * 0.01
+    out, _ = O.layer_forward(p, u, gw, b, lambda e: ex, None, add_residual=False)
+    assert np.allclose(out, 2.5 * O.swiglu_ffn(u, *ex), atol=1e-12)
+
+
+def test_all_experts_softmax_is_the_dense_mixture():
+    """K = E, one group, softmax, rsf 1: out = sum_e p_e FFN_e(u) (the dense
+    einsum gate fusion of the architecture article, section 3.3)."""
+    D, h, E = 8, 4, 6
+    u = RNG.standard_normal((12, D))
+    gw = RNG.standard_normal((E, D))
+    ex = _rand_experts(E, D, h)
+    p = O.RouterParams(E=E, K=E)
+    out, _ = O.layer_forward(p, u, gw, None, lambda e: ex[e], None, add_residual=False)
+    ut = torch.from_numpy(u)
+    probs = torch.softmax(ut @ torch.from_numpy(gw).T, dim=-1)
+    outs = torch.stack([torch.nn.functional.linear(
+        torch.nn.functional.silu(torch.nn.functional.linear(ut, torch.from_numpy(g))) *
+        torch.nn.functional.linear(ut, torch.from_numpy(up)), torch.from_numpy(dn)) for g, up, dn in ex], dim=1)
+    dense = torch.einsum("ted,te->td", outs, probs).numpy()
+    assert np.allclose(out, dense, atol=1e-12)
+
+
+def test_top1_moe_without_shared_or_residual():
+    D, h, E = 8, 4, 5
+    u = RNG.standard_normal((25, D))
+    gw = RNG.standard_normal((E, D))
+    ex = _rand_experts(E, D, h)
+    p = O.RouterParams(E=E, K=1)
+    out, r = O.layer_forward(p, u, gw, None, lambda e: ex[e], None, add_residual=False)
+    l = u @ gw.T
+    for t in range(25):
+        e = int(np.argmax(l[t]))
+        pmax = np.exp(l[t, e]) / np.exp(l[t]).sum()
+        assert np.allclose(out[t], pmax * O.swiglu_ffn(u[t:t + 1], *ex[e])[0], atol=1e-12)
+
+
+def test_residual_term_and_token_subset():
+    D, h, E = 8, 4, 8
+    u = RNG.standard_normal((20, D))
+    gw = RNG.standard_normal((E, D))
+    ex = _rand_experts(E, D, h)
+    sh = _rand_experts(1, D, 2 * h)[0]
+    p = O.RouterParams(E=E, K=3, G=2, kg=1)
+    o1, _ = O.layer_forward(p, u, gw, None, lambda e: ex[e], lambda: sh, add_residual=True)
+    o0, _ = O.layer_forward(p, u, gw, None, lambda e: ex[e], lambda: sh, add_residual=False)
+    assert np.allclose(o1 - o0, u, atol=1e-14)
+    tok = np.array([7, 3, 19])
+    os_, _ = O.layer_forward(p, u, gw, None, lambda e: ex[e], lambda: sh, tokens=tok)
+    assert np.allclose(os_, o1[tok], atol=1e-14)
+
+
+def test_permutation_equivariance():
+    D, h, E = 8, 4, 8
+    u = RNG.standard_normal((30, D))
+    gw = RNG.standard_normal((E, D))
+    ex = _rand_experts(E, D, h)
+    p = O.RouterParams(E=E, K=3)
+    out, r = O.layer_forward(p, u, gw, None, lambda e: ex[e], None)
+    tp = RNG.permutation(30)
+    out_t, _ = O.layer_forward(p, u[tp], gw, None, lambda e: ex[e], None)
+    assert np.allclose(out_t, out[tp], atol=1e-13)
+    ep = RNG.permutation(E)  # expert j of the new layer is expert ep[j] of the old
+    out_e, r_e = O.layer_forward(p, u, gw[ep], None, lambda e: ex[ep[e]], None)
+    assert np.allclose(out_e, out, atol=1e-13)
+    assert np.array_equal(np.sort(ep[r_e["idx"]], 1), np.sort(r["idx"], 1))
+
+
+# ----------------------------------------------------------------------------
+# the pins must catch plausible mistakes
+# ----------------------------------------------------------------------------
+
+
+def test_pins_catch_planted_bugs(monkeypatch):
+    """Plant typical mistakes in the oracle (on the CPU) and check that the
+    pins above fail for each of them."""
+    D, h, E = 16, 8, 16
+    u = RNG.standard_normal((30, D))
+    gw = RNG.standard_normal((E, D))
+    ex = _rand_experts(1, D, h)[0]
+    good = O.swiglu_ffn
+
+    def swapped(uu, g, up, dn):  # gate and up exchanged
+        return good(uu, up, g, dn)
+    monkeypatch.setattr(O, "swiglu_ffn", swapped)
+    with pytest.raises(AssertionError):
+        test_swiglu_worked_example()
+    monkeypatch.setattr(O, "swiglu_ffn", good)
+
+    good_gate = O.gate_values
+    monkeypatch.setattr(O, "gate_values", lambda s, idx, norm, rsf: np.take_along_axis(s, idx, 1) * rsf)
+    p = O.RouterParams(E=E, K=4, G=4, kg=2, score_fn="sigmoid", norm=True, rsf=2.5)
+    out, _ = O.layer_forward(p, u, gw, None, lambda e: ex, None, add_residual=False)
+    assert not np.allclose(out, 2.5 * good(u, *ex), atol=1e-12)  # dropped renormalisation caught
+    monkeypatch.setattr(O, "gate_values", good_gate)
+
+    good_sel = O.select_experts
+
+    def ascending(z, G, kg, K):  # sign error in the selection
+        return good_sel(-z, G, kg, K)
+    monkeypatch.setattr(O, "select_experts", ascending)
+    with pytest.raises(AssertionError):
+        test_top1_moe_without_shared_or_residual()
+    monkeypatch.setattr(O, "select_experts", good_sel)
