@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Throughput of the DeepSeekMoE layer forward on one MI355X.
+
+One step = one moe_layer_forward (router, dispatch, gate/up GEMM, down GEMM,
+shared expert, combine) over one batch of seeded synthetic inputs already
+resident in HBM. Default workload: the DeepSeek-V3-shaped prefill layer
+(T=16384, D=7168, 256 routed experts of hidden 2048 in 8 groups keep 4,
+top-8 sigmoid routing with selection bias, 1 shared expert), bf16.
+Reported: routed tokens/s, % of bf16 MFMA peak, the dominant kernel's
+roofline, the fp8 decode-shaped layer's HBM GB/s, and the CPU oracle's rate
+on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed tokens/s per MoE layer (V3-shape T=16384) + %MFMA peak; decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def mfma_flops(cfg, T=None):
+    T = cfg.T if T is None else T
+    return 2.0 * T * (cfg.K * 3 * cfg.D * cfg.H + 3 * cfg.D * cfg.Hs)
+
+
+def gateup_flops(cfg):
+    return 2.0 * cfg.T * (cfg.K * 2 * cfg.D * cfg.H + 2 * cfg.D * cfg.Hs)
+
+
+def run_prefill(args, torch, M, MI):
+    cfg = MI.CONFIGS[args.config]
+    log(f"generating {cfg.name} inputs on the GPU")
+    inp = MI.make_layer(cfg, "cuda")
+    layer = M.MoELayer.from_config(cfg)
+    out = torch.empty((cfg.T, cfg.D), dtype=torch.float32, device="cuda")
+    counts = torch.empty((cfg.E,), dtype=torch.int32, device="cuda")
+
+    def step():
+        layer.forward(inp.x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared, out=out, expert_counts=counts)
+
+    for i in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+    layer.set_stage_timing(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stages, calls = layer.stage_times()
+    layer.set_stage_timing(False)
+    ms = (t1 - t0) * 1e3 / args.steps
+    stage_avg = {k: v / max(calls, 1) for k, v in stages.items()}
+    log(f"{args.steps} steps: {ms:.3f} ms/step; stages {stage_avg}")
+    g1_ms = stage_avg["gate_up_gemm"]
+    g1_tflops = gateup_flops(cfg) / (g1_ms * 1e-3) / 1e12
+    res = dict(cfg=cfg, inp=inp, ms=ms, stages=stage_avg, counts=counts.cpu().tolist(),
+               mfma_frac=mfma_flops(cfg) / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+               roofline=dict(bound="mfma", achieved=round(g1_tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                             frac=round(g1_tflops / PEAK_BF16_TFLOPS, 4), traffic=None,
+                             kernel="grouped_gemm_bf16_kernel<0> (gate/up + SwiGLU)",
+                             per_launch_flop=gateup_flops(cfg), avg_ms=round(g1_ms, 4)))
+    del layer, out
+    return res
+
+
+def decode_bytes(cfg, n_touched):
+    E, D, H, Hs = cfg.E, cfg.D, cfg.H, cfg.Hs
+    per_expert = 3 * H * D + 4 * ((2 * H // 128) * (D // 128) + (D // 128) * (H // 128))
+    shared = 3 * Hs * D + 4 * ((2 * Hs // 128) * (D // 128) + (D // 128) * (Hs // 128))
+    gate_up = n_touched * (2 * H * D + 4 * (2 * H // 128) * (D // 128)) + 2 * Hs * D + 4 * (2 * Hs // 128) * (D // 128)
+    total = n_touched * per_expert + shared + E * D * 4 + E * 4 + cfg.T * D * 2 + cfg.T * D * 4
+    return total, gate_up
+
+
+def run_decode(args, torch, M, MI):
+    cfg = MI.CONFIGS[args.decode_config]
+    log(f"generating {cfg.name} inputs on the GPU")
+    inp = MI.make_layer(cfg, "cuda")
+    layer = M.MoELayer.from_config(cfg)
+    out = torch.empty((cfg.T, cfg.D), dtype=torch.float32, device="cuda")
+    counts = torch.empty((cfg.E,), dtype=torch.int32, device="cuda")
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB > 256 MiB MALL
+
+    def step():
+        layer.forward(inp.x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared, out=out, expert_counts=counts)
+
+    for i in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    layer.set_stage_timing(True)
+    times = []
+    for i in range(args.steps):
+        flush.fill_(float(i))  # evict the weights from the last-level cache between steps
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    stages, calls = layer.stage_times()
+    layer.set_stage_timing(False)
+    stage_avg = {k: v / max(calls, 1) for k, v in stages.items()}
+    n_touched = int((counts > 0).sum())
+    total, gu = decode_bytes(cfg, n_touched)
+    ms = sorted(times)[len(times) // 2]
+    log(f"decode: median {ms:.4f} ms, touched {n_touched}, stages {stage_avg}")
+    g1 = stage_avg["gate_up_gemm"]
+    del layer, inp, flush
+    torch.cuda.empty_cache()
+    return dict(workload=cfg.name, T=cfg.T, ms_median=round(ms, 4), ms_min=round(min(times), 4),
+                experts_touched=n_touched, algorithmic_bytes=total, hbm_gbs=round(total / (ms * 1e-3) / 1e9, 1),
+                hbm_frac=round(total / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                stages_ms={k: round(v, 4) for k, v in stage_avg.items()},
+                roofline=dict(bound="hbm", kernel="stream_gemm_kernel<fp8, gate/up + SwiGLU>",
+                              achieved=round(gu / (g1 * 1e-3) / 1e9, 1), peak=PEAK_HBM_GBS, unit="GB/s",
+                              frac=round(gu / (g1 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), per_launch_bytes=gu,
+                              avg_ms=round(g1, 4)))
+
+
+def cpu_baseline(res, n_sample):
+    """The CPU oracle, as it stands, on the first n_sample tokens of the same
+    workload (routing and output of those tokens)."""
+    import numpy as np
+
+    from oracle import adapter as A
+    from oracle import moe_oracle as O
+    cfg, inp = res["cfg"], res["inp"]
+    tokens = np.arange(n_sample)
+    # inputs handed over before the clock starts
+    x = A.decode_tensor(inp.x[:n_sample])
+    gw = A.decode_tensor(inp.gate_w)
+    bias = None if inp.sel_bias is None else A.decode_tensor(inp.sel_bias)
+    t0 = time.perf_counter()
+    out, R = O.layer_forward(A.router_params(cfg), x, gw, bias, A.routed_expert_fn(inp.experts),
+                             A.shared_expert_fn(inp.shared), add_residual=cfg.add_residual)
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    return dict(value=round(n_sample / dt, 4), unit="routed tokens/s", cores=int(cores), kind="oracle",
+                sample=f"first {n_sample} tokens of {cfg.name} (routing + shared + {cfg.K} routed expert FFNs "
+                       f"each, float64, expert weights decoded per touched expert); {dt:.1f} s",
+                seconds=round(dt, 2), touched_experts=int(len(np.unique(R['idx']))))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="v3_prefill")
+    ap.add_argument("--decode-config", default="v3_decode_fp8")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=16)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this layer forward is built and timed on a single MI355X "
+              "(--gpus 1). Expert-parallel sharding over several GPUs is a design, not a built path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_layer_38_amd as M
+    import moe_inputs as MI
+    M.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+
+    res = run_prefill(args, torch, M, MI)
+    cfg = res["cfg"]
+    line = {
+        "metric": METRIC,
+        "value": round(cfg.T / (res["ms"] * 1e-3), 1),
+        "unit": "routed tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "D": cfg.D, "E": cfg.E, "H": cfg.H, "G": cfg.G,
+                   "topk_group": cfg.kg, "K": cfg.K, "Hs": cfg.Hs, "score": cfg.score_fn,
+                   "weights": cfg.weight, "parallelism": "single GPU"},
+        "mfma_frac": round(res["mfma_frac"], 4),
+        "stages_ms": {k: round(v, 4) for k, v in res["stages"].items()},
+        "roofline": res["roofline"],
+    }
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on {args.cpu_sample} tokens")
+        line["cpu_baseline"] = cpu_baseline(res, args.cpu_sample)
+    del res
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        line["decode"] = run_decode(args, torch, M, MI)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,165 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) DeepSeekMoE layer forward.
+ *
+ * The layer (DeepSeek-V2 walkthrough page, DeepSeekMoE architecture section and
+ * its MoEGate / MoE code; DeepSeek-V3 basics page, section 1.2):
+ *
+ *   h'_t = [u_t] + FFN_shared(u_t) + sum_{k<K} g_{t,k} * FFN_{idx_{t,k}}(u_t)
+ *   FFN(u) = W_down (SiLU(W_gate u) * (W_up u)),   SiLU(z) = z / (1 + e^-z)
+ *
+ * Router: logits l = x * gate_w^T in fp32; scores s = softmax(l) or sigmoid(l);
+ * selection scores z = s + sel_bias (bias used only to choose experts); groups
+ * are contiguous runs of E/G experts scored by max z; the best topk_group groups
+ * are kept (ties: lower group), the other experts are excluded; the K largest z
+ * among the kept experts are chosen (ties: lower index). Gates g = s[idx]
+ * (unbiased), renormalised over the K if norm_topk, then times
+ * routed_scaling_factor.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller, row-major,
+ *    except the moe_params / moe_weights structs, which are host memory read
+ *    during the call only. A moe_cfg is owned by the library.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream). Work is
+ *    enqueued asynchronously on it; no entry point synchronises the host.
+ *  - Arguments are validated on the host before anything is launched; an
+ *    invalid call returns an error status and launches nothing.
+ *  - A moe_cfg holds one workspace: calls on one cfg must be ordered (same
+ *    stream, or externally synchronised). Use one cfg per concurrent stream.
+ *  - Status: 0 = OK, negative = error (moe_status_string names it).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* bad pointer, size or parameter combination */
+  MOE_ERR_UNSUPPORTED = -2, /* valid layer, but a shape/dtype this build does not run */
+  MOE_ERR_OOM = -3,         /* workspace allocation failed */
+  MOE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
+
+/* Which expert-GEMM kernels run. AUTO picks by token count. */
+typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GROUPED = 1, MOE_PATH_STREAM = 2 } moe_path;
+
+typedef struct {
+  int dim;            /* D: model dim (row length of x and out) */
+  int n_routed;       /* E: routed experts, 1..512 */
+  int hidden;         /* H: hidden size of each routed expert */
+  int shared_hidden;  /* Hs: hidden of the fused shared expert (N_s shared experts
+                         of hidden h fused as one of hidden N_s*h); 0 = none */
+  int top_k;          /* K: routed experts per token, 1..16 */
+  int n_group;        /* G: expert groups, E % G == 0; 1 = greedy */
+  int topk_group;     /* groups kept per token, 1..G; K <= topk_group*E/G */
+  int score_fn;       /* moe_score_fn */
+  int norm_topk;      /* 1: g /= sum of the K chosen scores */
+  float routed_scaling_factor;
+  int act_dtype;      /* x dtype: MOE_F32 or MOE_BF16 */
+  int weight_dtype;   /* expert weights: MOE_F32 (with F32 x), MOE_BF16 or
+                         MOE_FP8_E4M3 (with BF16 x) */
+  int out_dtype;      /* MOE_F32 or MOE_BF16 */
+  int add_residual;   /* 1: out includes x (h'_t = u_t + ...) */
+  int max_tokens;     /* largest T any call on this cfg may pass */
+  int path;           /* moe_path */
+} moe_params;
+
+/* Expert weights in nn.Linear layout [out, in], row-major, dtype weight_dtype.
+ * Routed set (E experts):   gate_up [E][2H][D] (rows 0..H-1 = W_gate,
+ *                           rows H..2H-1 = W_up), down [E][D][H].
+ * Shared expert:            gate_up [2Hs][D], down [D][Hs].
+ * FP8_E4M3 only: one fp32 scale per 128x128 block, w = e4m3(q) * scale:
+ *   gate_up_scale [E][2H/128][D/128] (shared: [2Hs/128][D/128]),
+ *   down_scale    [E][D/128][H/128]  (shared: [D/128][Hs/128]).
+ * For F32 / BF16 weights the scale pointers are ignored. */
+typedef struct {
+  const void* gate_up;
+  const void* down;
+  const float* gate_up_scale;
+  const float* down_scale;
+} moe_weights;
+
+typedef struct moe_cfg moe_cfg;
+
+/* Validates *p and allocates the workspace for up to p->max_tokens tokens on
+ * the current HIP device. Returns MOE_ERR_INVALID_ARG for an invalid layer
+ * (E % G != 0, topk_group > G, K > topk_group*E/G, ...), MOE_ERR_UNSUPPORTED
+ * for a dtype/shape this build does not run (bf16/fp8 weights need D, H, Hs
+ * multiples of 128; f32 needs D % 32 == 0), MOE_ERR_OOM if the workspace does
+ * not fit. On success *out owns the workspace until moe_cfg_destroy. */
+moe_status moe_cfg_create(const moe_params* p, moe_cfg** out);
+
+/* Frees the workspace (synchronises the device first). NULL is a no-op. */
+moe_status moe_cfg_destroy(moe_cfg* cfg);
+
+/* Bytes of device workspace the cfg holds. */
+size_t moe_cfg_workspace_bytes(const moe_cfg* cfg);
+
+/* The layer forward (page-1 MoE forward with the V3 bias rule).
+ *   x           [T][D]  act_dtype
+ *   gate_w      [E][D]  fp32 router weight
+ *   sel_bias    [E]     fp32 selection-only bias, or NULL (= 0)
+ *   expert_w    routed weights (see moe_weights), required
+ *   shared_w    shared expert weights; required iff shared_hidden > 0
+ *               (pass NULL to skip the shared expert only when Hs == 0)
+ *   out         [T][D]  out_dtype; written in full
+ *   expert_counts [E] int32 tokens routed to each expert, or NULL; overwritten
+ * 0 <= T <= max_tokens. T == 0 only zeroes expert_counts. */
+moe_status moe_layer_forward(moe_cfg* cfg, const void* x, int T, const float* gate_w,
+                             const float* sel_bias, const moe_weights* expert_w,
+                             const moe_weights* shared_w, void* out, int32_t* expert_counts,
+                             void* stream);
+
+/* The router alone (the MoEGate forward plus the selection bias):
+ *   topk_idx [T][K] int32, listed by descending z then ascending index
+ *   topk_gate [T][K] fp32 gate values in the same order
+ *   expert_counts [E] int32 or NULL. */
+moe_status moe_router_forward(moe_cfg* cfg, const void* x, int T, const float* gate_w,
+                              const float* sel_bias, int32_t* topk_idx, float* topk_gate,
+                              int32_t* expert_counts, void* stream);
+
+/* Dispatch alone, from a given routing (the page-1 MoE code's
+ * repeat_interleave + per-expert mask gather, done as histogram + prefix scan
+ * + permutation):
+ *   topk_idx    [T][K] int32 in [0, E)   (input; entries outside [0, E)
+ *               are skipped and leave their slot_row entry unwritten)
+ *   offsets     [E+1]  int32: rows of expert e are offsets[e] .. offsets[e+1]-1
+ *   row_token   [T*K]  int32: token of each expert-contiguous row
+ *   slot_row    [T*K]  int32: row that holds (t, k), at index t*K + k
+ * Rows of one expert may come in any order (the kernels that consume them do
+ * not depend on it); offsets, and the set of tokens of each expert, are
+ * unique. */
+moe_status moe_dispatch_forward(moe_cfg* cfg, const int32_t* topk_idx, int T, int32_t* offsets,
+                                int32_t* row_token, int32_t* slot_row, void* stream);
+
+/* Stage timing (observability): when enabled, moe_layer_forward records HIP
+ * events on its stream around each stage -- 0 router, 1 dispatch, 2 gate/up
+ * GEMM, 3 down GEMM, 4 combine -- for up to MOE_TIMING_CALLS calls.
+ * moe_cfg_stage_times waits for the last recorded call, writes the summed
+ * milliseconds of each stage to ms[MOE_NUM_STAGES] and the number of timed
+ * calls to *calls, and starts a new window. Enabling creates the events
+ * (host-side HIP calls); timing does not synchronise the host inside
+ * forward. */
+#define MOE_NUM_STAGES 5
+#define MOE_TIMING_CALLS 256
+moe_status moe_cfg_set_stage_timing(moe_cfg* cfg, int enable);
+moe_status moe_cfg_stage_times(moe_cfg* cfg, double* ms, int* calls);
+
+/* HIP error code behind the last MOE_ERR_HIP on this cfg (0 if none). */
+int moe_cfg_last_hip_error(const moe_cfg* cfg);
+
+const char* moe_status_string(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,230 @@
+"""ctypes binding of libmoe_mi355x.so (include/moe.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the layer runs in the library's kernels.
+Loading fails loudly if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe.h")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_OOM, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
+MOE_PATH_AUTO, MOE_PATH_GROUPED, MOE_PATH_STREAM = 0, 1, 2
+
+_DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+_TORCH_OF = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_FP8_E4M3: torch.uint8}
+
+
+class MoeParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("dim", "n_routed", "hidden", "shared_hidden", "top_k", "n_group",
+                                             "topk_group", "score_fn", "norm_topk")] + \
+               [("routed_scaling_factor", ctypes.c_float)] + \
+               [(n, ctypes.c_int) for n in ("act_dtype", "weight_dtype", "out_dtype", "add_residual",
+                                             "max_tokens", "path")]
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [("gate_up", ctypes.c_void_p), ("down", ctypes.c_void_p),
+                ("gate_up_scale", ctypes.c_void_p), ("down_scale", ctypes.c_void_p)]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, what: str, hip_error: int = 0):
+        self.status = status
+        msg = f"{what}: {status_string(status)} ({status})"
+        if hip_error:
+            msg += f", HIP error {hip_error}"
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """The built HIP library; raises if it is missing (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m mixture_experts_layer_38_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
+    lib.moe_cfg_create.argtypes = [ctypes.POINTER(MoeParams), ctypes.POINTER(vp)]
+    lib.moe_cfg_destroy.argtypes = [vp]
+    lib.moe_cfg_workspace_bytes.argtypes = [vp]
+    lib.moe_cfg_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_cfg_last_hip_error.argtypes = [vp]
+    lib.moe_layer_forward.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.POINTER(MoeWeights),
+                                      ctypes.POINTER(MoeWeights), vp, vp, vp]
+    lib.moe_router_forward.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp]
+    lib.moe_dispatch_forward.argtypes = [vp, vp, ctypes.c_int, vp, vp, vp, vp]
+    lib.moe_cfg_set_stage_timing.argtypes = [vp, ctypes.c_int]
+    lib.moe_cfg_stage_times.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    for f in ("moe_cfg_create", "moe_cfg_destroy", "moe_layer_forward", "moe_router_forward",
+              "moe_dispatch_forward", "moe_cfg_last_hip_error", "moe_cfg_set_stage_timing",
+              "moe_cfg_stage_times"):
+        getattr(lib, f).restype = ctypes.c_int
+    del i32p
+    _lib = lib
+    return lib
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions include/moe.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return load_library().moe_status_string(status).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_params(*, dim, n_routed, hidden, shared_hidden, top_k, n_group=1, topk_group=1,
+                score_fn="softmax", norm_topk=False, routed_scaling_factor=1.0, act="bf16", weight="bf16",
+                out="f32", add_residual=True, max_tokens, path="auto") -> MoeParams:
+    return MoeParams(dim=dim, n_routed=n_routed, hidden=hidden, shared_hidden=shared_hidden, top_k=top_k,
+                     n_group=n_group, topk_group=topk_group,
+                     score_fn={"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}.get(score_fn, score_fn),
+                     norm_topk=int(bool(norm_topk)), routed_scaling_factor=float(routed_scaling_factor),
+                     act_dtype=_DTYPE_CODE.get(act, act), weight_dtype=_DTYPE_CODE.get(weight, weight),
+                     out_dtype=_DTYPE_CODE.get(out, out), add_residual=int(bool(add_residual)),
+                     max_tokens=max_tokens,
+                     path={"auto": MOE_PATH_AUTO, "grouped": MOE_PATH_GROUPED, "stream": MOE_PATH_STREAM}.get(path, path))
+
+
+def create_cfg(params: MoeParams) -> tuple[int, ctypes.c_void_p]:
+    """(status, handle) of moe_cfg_create; no exception, for validation tests."""
+    h = ctypes.c_void_p()
+    st = load_library().moe_cfg_create(ctypes.byref(params), ctypes.byref(h))
+    return st, h
+
+
+def _weights(w) -> MoeWeights | None:
+    if w is None:
+        return None
+    return MoeWeights(w.gate_up.data_ptr(), w.down.data_ptr(),
+                      None if getattr(w, "gate_up_scale", None) is None else w.gate_up_scale.data_ptr(),
+                      None if getattr(w, "down_scale", None) is None else w.down_scale.data_ptr())
+
+
+class MoELayer:
+    """One cfg (validated parameters + device workspace) of the layer forward."""
+
+    def __init__(self, params: MoeParams):
+        self.lib = load_library()
+        self.params = params
+        st, h = create_cfg(params)
+        if st != MOE_OK:
+            raise MoEError(st, "moe_cfg_create")
+        self.handle = h
+
+    @classmethod
+    def from_config(cls, cfg, max_tokens=None, path="auto", **overrides):
+        """From an object with the fields of a layer description (T, D, E, H,
+        G, kg, K, score_fn, norm, rsf, Hs, act, weight, out, add_residual)."""
+        kw = dict(dim=cfg.D, n_routed=cfg.E, hidden=cfg.H, shared_hidden=cfg.Hs, top_k=cfg.K, n_group=cfg.G,
+                  topk_group=cfg.kg, score_fn=cfg.score_fn, norm_topk=cfg.norm, routed_scaling_factor=cfg.rsf,
+                  act=cfg.act, weight=cfg.weight, out=cfg.out, add_residual=cfg.add_residual,
+                  max_tokens=cfg.T if max_tokens is None else max_tokens, path=path)
+        kw.update(overrides)
+        return cls(make_params(**kw))
+
+    def close(self):
+        if getattr(self, "handle", None) is not None and self.handle.value:
+            self.lib.moe_cfg_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(self.lib.moe_cfg_workspace_bytes(self.handle))
+
+    STAGES = ("router", "dispatch", "gate_up_gemm", "down_gemm", "combine")
+
+    def set_stage_timing(self, enable: bool):
+        self._check(self.lib.moe_cfg_set_stage_timing(self.handle, int(bool(enable))), "moe_cfg_set_stage_timing")
+
+    def stage_times(self) -> tuple[dict, int]:
+        """({stage: summed ms}, timed calls) since the last read; waits for the last call."""
+        ms = (ctypes.c_double * len(self.STAGES))()
+        calls = ctypes.c_int()
+        self._check(self.lib.moe_cfg_stage_times(self.handle, ms, ctypes.byref(calls)), "moe_cfg_stage_times")
+        return dict(zip(self.STAGES, list(ms))), calls.value
+
+    def _check(self, st, what):
+        if st != MOE_OK:
+            raise MoEError(st, what, self.lib.moe_cfg_last_hip_error(self.handle))
+
+    def _check_x(self, x):
+        p = self.params
+        want = _TORCH_OF[p.act_dtype]
+        if x.dtype != want or not x.is_cuda or not x.is_contiguous() or x.dim() != 2 or x.shape[1] != p.dim:
+            raise ValueError(f"x must be a contiguous cuda {want} tensor [T, {p.dim}]")
+
+    def forward(self, x, gate_w, sel_bias, experts, shared, out=None, expert_counts=None, stream=None):
+        """out [T, D] (out dtype) and, if given, expert_counts [E] int32 are written."""
+        p = self.params
+        self._check_x(x)
+        T = x.shape[0]
+        if out is None:
+            out = torch.empty((T, p.dim), dtype=_TORCH_OF[p.out_dtype], device=x.device)
+        ew, sw = _weights(experts), _weights(shared)
+        st = self.lib.moe_layer_forward(self.handle, _ptr(x), T, _ptr(gate_w), _ptr(sel_bias),
+                                        ctypes.byref(ew), None if sw is None else ctypes.byref(sw), _ptr(out),
+                                        _ptr(expert_counts), _stream_handle(stream))
+        self._check(st, "moe_layer_forward")
+        return out
+
+    def router(self, x, gate_w, sel_bias, stream=None):
+        """(topk_idx [T, K] int32, topk_gate [T, K] fp32, expert_counts [E] int32)."""
+        p = self.params
+        self._check_x(x)
+        T = x.shape[0]
+        idx = torch.empty((T, p.top_k), dtype=torch.int32, device=x.device)
+        gate = torch.empty((T, p.top_k), dtype=torch.float32, device=x.device)
+        counts = torch.empty((p.n_routed,), dtype=torch.int32, device=x.device)
+        st = self.lib.moe_router_forward(self.handle, _ptr(x), T, _ptr(gate_w), _ptr(sel_bias), _ptr(idx),
+                                         _ptr(gate), _ptr(counts), _stream_handle(stream))
+        self._check(st, "moe_router_forward")
+        return idx, gate, counts
+
+    def dispatch(self, topk_idx, stream=None):
+        """(offsets [E+1], row_token [T*K], slot_row [T*K]), all int32."""
+        p = self.params
+        T = topk_idx.shape[0]
+        dev = topk_idx.device
+        offsets = torch.empty((p.n_routed + 1,), dtype=torch.int32, device=dev)
+        row_token = torch.empty((max(T * p.top_k, 1),), dtype=torch.int32, device=dev)
+        slot_row = torch.empty((max(T * p.top_k, 1),), dtype=torch.int32, device=dev)
+        st = self.lib.moe_dispatch_forward(self.handle, _ptr(topk_idx.contiguous()), T, _ptr(offsets),
+                                           _ptr(row_token), _ptr(slot_row), _stream_handle(stream))
+        self._check(st, "moe_dispatch_forward")
+        return offsets, row_token[:T * p.top_k], slot_row[:T * p.top_k]

@@ -1,0 +1,394 @@
+// C ABI: parameter validation, workspace, and the launch sequence of the
+// layer forward on one stream (router -> dispatch -> gate/up GEMM -> down GEMM
+// -> combine). Nothing here waits for the device.
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+
+#include "moe_internal.hpp"
+
+struct moe_cfg {
+  moe_params p;
+  int device;
+  int num_cus;
+  size_t ws_bytes;
+  char* ws;
+  float* logits;
+  int32_t* idx;
+  float* gate;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* cursor;
+  int32_t* pre1;
+  int32_t* pre2;
+  int32_t* row_token;
+  float* row_gate;
+  int32_t* slot_row;
+  void* h_routed;
+  void* h_shared;
+  void* y_routed;
+  void* y_shared;
+  int last_hip_error;
+  // stage timing
+  bool timing;
+  int timed_calls;
+  hipEvent_t* events;  // [MOE_TIMING_CALLS][MOE_NUM_STAGES + 1]
+};
+
+namespace {
+
+using namespace moe;
+
+moe_status validate(const moe_params* p) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  if (p->dim <= 0 || p->n_routed <= 0 || p->hidden <= 0 || p->shared_hidden < 0) return MOE_ERR_INVALID_ARG;
+  if (p->n_routed > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (p->top_k <= 0 || p->top_k > kMaxTopK) return MOE_ERR_INVALID_ARG;
+  if (p->n_group <= 0 || p->n_group > kMaxGroups || p->n_routed % p->n_group != 0) return MOE_ERR_INVALID_ARG;
+  if (p->topk_group <= 0 || p->topk_group > p->n_group) return MOE_ERR_INVALID_ARG;
+  if ((long)p->top_k > (long)p->topk_group * (p->n_routed / p->n_group)) return MOE_ERR_INVALID_ARG;
+  if (p->score_fn != MOE_SCORE_SOFTMAX && p->score_fn != MOE_SCORE_SIGMOID) return MOE_ERR_INVALID_ARG;
+  if (p->act_dtype != MOE_F32 && p->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (p->weight_dtype < MOE_F32 || p->weight_dtype > MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+  if (p->out_dtype != MOE_F32 && p->out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (p->max_tokens < 0) return MOE_ERR_INVALID_ARG;
+  if (p->path < MOE_PATH_AUTO || p->path > MOE_PATH_STREAM) return MOE_ERR_INVALID_ARG;
+  if (!(p->routed_scaling_factor == p->routed_scaling_factor)) return MOE_ERR_INVALID_ARG;  // NaN
+  // dtype combinations this build runs
+  const bool f32 = p->act_dtype == MOE_F32 && p->weight_dtype == MOE_F32;
+  const bool bf = p->act_dtype == MOE_BF16 && p->weight_dtype == MOE_BF16;
+  const bool fp8 = p->act_dtype == MOE_BF16 && p->weight_dtype == MOE_FP8_E4M3;
+  if (!(f32 || bf || fp8)) return MOE_ERR_UNSUPPORTED;
+  if (p->dim % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!f32 && (p->dim % 128 || p->hidden % 128 || p->shared_hidden % 128)) return MOE_ERR_UNSUPPORTED;
+  if (fp8 && p->path == MOE_PATH_GROUPED) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+enum class Path { kF32, kGrouped, kStream };
+
+Path choose_path(const moe_params& p, int T) {
+  if (p.weight_dtype == MOE_F32) return Path::kF32;
+  if (p.weight_dtype == MOE_FP8_E4M3) return Path::kStream;
+  if (p.path == MOE_PATH_GROUPED) return Path::kGrouped;
+  if (p.path == MOE_PATH_STREAM) return Path::kStream;
+  return T > 256 ? Path::kGrouped : Path::kStream;
+}
+
+moe_status hip_fail(moe_cfg* c, hipError_t e) {
+  c->last_hip_error = (int)e;
+  return MOE_ERR_HIP;
+}
+
+bool on_cfg_device(const moe_cfg* c) {
+  int d = -1;
+  return hipGetDevice(&d) == hipSuccess && d == c->device;
+}
+
+// the dispatch tables (item prefixes) for the chosen GEMM path
+void fill_dispatch_geometry(const moe_params& p, Path path, int T, DispatchArgs* d) {
+  d->shared_rows = p.shared_hidden > 0 ? T : 0;
+  if (path == Path::kGrouped) {
+    d->bm = kGB_BM;
+    d->n1_routed = p.hidden / kG1_BNH;
+    d->n1_shared = p.shared_hidden / kG1_BNH;
+    d->n2_routed = d->n2_shared = p.dim / kG2_BN;
+  } else if (path == Path::kStream) {
+    d->bm = kST_BM;
+    d->n1_routed = p.hidden / kST_N1;
+    d->n1_shared = p.shared_hidden / kST_N1;
+    d->n2_routed = d->n2_shared = p.dim / kST_N2;
+  } else {
+    d->bm = 1;
+    d->n1_routed = d->n1_shared = d->n2_routed = d->n2_shared = 0;
+  }
+}
+
+// records the boundary event `stage` (0 .. MOE_NUM_STAGES) of the current timed call
+void mark(moe_cfg* c, int stage, hipStream_t s) {
+  if (!c->timing || c->timed_calls >= MOE_TIMING_CALLS) return;
+  (void)hipEventRecord(c->events[c->timed_calls * (MOE_NUM_STAGES + 1) + stage], s);
+  if (stage == MOE_NUM_STAGES) c->timed_calls++;
+}
+
+void destroy_events(moe_cfg* c) {
+  if (!c->events) return;
+  for (int i = 0; i < MOE_TIMING_CALLS * (MOE_NUM_STAGES + 1); ++i) (void)hipEventDestroy(c->events[i]);
+  free(c->events);
+  c->events = nullptr;
+}
+
+__global__ void zero_counts_kernel(int32_t* p, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_ERR_OOM: return "out of device memory";
+    case MOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+moe_status moe_cfg_create(const moe_params* p, moe_cfg** out) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  *out = nullptr;
+  moe_status st = validate(p);
+  if (st != MOE_OK) return st;
+  moe_cfg* c = new (std::nothrow) moe_cfg;
+  if (!c) return MOE_ERR_OOM;
+  memset(c, 0, sizeof(*c));
+  c->p = *p;
+  if (hipGetDevice(&c->device) != hipSuccess) { delete c; return MOE_ERR_HIP; }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, c->device) != hipSuccess) { delete c; return MOE_ERR_HIP; }
+  c->num_cus = prop.multiProcessorCount;
+
+  const size_t Tm = (size_t)p->max_tokens, E = p->n_routed, K = p->top_k, D = p->dim;
+  const size_t H = p->hidden, Hs = p->shared_hidden;
+  const size_t act = (p->weight_dtype == MOE_F32) ? 4 : 2;  // h and y element size
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + std::max<size_t>(bytes, 1)); return o; };
+  const size_t o_logits = take(Tm * E * 4), o_idx = take(Tm * K * 4), o_gate = take(Tm * K * 4);
+  const size_t o_counts = take(E * 4), o_offsets = take((E + 1) * 4), o_cursor = take(E * 4);
+  const size_t o_pre1 = take((E + 2) * 4), o_pre2 = take((E + 2) * 4);
+  const size_t o_rt = take(Tm * K * 4), o_rg = take(Tm * K * 4), o_sr = take(Tm * K * 4);
+  const size_t o_hr = take(Tm * K * H * act), o_hs = take(Tm * Hs * act);
+  const size_t o_yr = take(Tm * K * D * act), o_ys = take(Tm * D * act);
+  c->ws_bytes = off;
+  if (hipMalloc((void**)&c->ws, c->ws_bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    delete c;
+    return MOE_ERR_OOM;
+  }
+  c->logits = (float*)(c->ws + o_logits);
+  c->idx = (int32_t*)(c->ws + o_idx);
+  c->gate = (float*)(c->ws + o_gate);
+  c->counts = (int32_t*)(c->ws + o_counts);
+  c->offsets = (int32_t*)(c->ws + o_offsets);
+  c->cursor = (int32_t*)(c->ws + o_cursor);
+  c->pre1 = (int32_t*)(c->ws + o_pre1);
+  c->pre2 = (int32_t*)(c->ws + o_pre2);
+  c->row_token = (int32_t*)(c->ws + o_rt);
+  c->row_gate = (float*)(c->ws + o_rg);
+  c->slot_row = (int32_t*)(c->ws + o_sr);
+  c->h_routed = c->ws + o_hr;
+  c->h_shared = c->ws + o_hs;
+  c->y_routed = c->ws + o_yr;
+  c->y_shared = c->ws + o_ys;
+  *out = c;
+  return MOE_OK;
+}
+
+moe_status moe_cfg_destroy(moe_cfg* cfg) {
+  if (!cfg) return MOE_OK;
+  int prev = -1;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(cfg->device);
+  (void)hipDeviceSynchronize();
+  destroy_events(cfg);
+  hipError_t e = hipFree(cfg->ws);
+  if (prev >= 0) (void)hipSetDevice(prev);
+  delete cfg;
+  return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+size_t moe_cfg_workspace_bytes(const moe_cfg* cfg) { return cfg ? cfg->ws_bytes : 0; }
+
+int moe_cfg_last_hip_error(const moe_cfg* cfg) { return cfg ? cfg->last_hip_error : 0; }
+
+moe_status moe_cfg_set_stage_timing(moe_cfg* c, int enable) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (enable && !c->events) {
+    const int n = MOE_TIMING_CALLS * (MOE_NUM_STAGES + 1);
+    c->events = (hipEvent_t*)calloc(n, sizeof(hipEvent_t));
+    if (!c->events) return MOE_ERR_OOM;
+    for (int i = 0; i < n; ++i) {
+      hipError_t e = hipEventCreate(&c->events[i]);
+      if (e != hipSuccess) {
+        for (int j = 0; j < i; ++j) (void)hipEventDestroy(c->events[j]);
+        free(c->events);
+        c->events = nullptr;
+        return hip_fail(c, e);
+      }
+    }
+  }
+  c->timing = enable != 0 && c->events != nullptr;
+  c->timed_calls = 0;
+  return MOE_OK;
+}
+
+moe_status moe_cfg_stage_times(moe_cfg* c, double* ms, int* calls) {
+  if (!c || !ms) return MOE_ERR_INVALID_ARG;
+  for (int k = 0; k < MOE_NUM_STAGES; ++k) ms[k] = 0.0;
+  const int n = c->timed_calls;
+  if (calls) *calls = n;
+  if (n == 0) return MOE_OK;
+  hipError_t e = hipEventSynchronize(c->events[(n - 1) * (MOE_NUM_STAGES + 1) + MOE_NUM_STAGES]);
+  if (e != hipSuccess) return hip_fail(c, e);
+  for (int i = 0; i < n; ++i) {
+    for (int k = 0; k < MOE_NUM_STAGES; ++k) {
+      float t = 0.f;
+      e = hipEventElapsedTime(&t, c->events[i * (MOE_NUM_STAGES + 1) + k], c->events[i * (MOE_NUM_STAGES + 1) + k + 1]);
+      if (e != hipSuccess) return hip_fail(c, e);
+      ms[k] += t;
+    }
+  }
+  c->timed_calls = 0;
+  return MOE_OK;
+}
+
+moe_status moe_router_forward(moe_cfg* c, const void* x, int T, const float* gate_w, const float* sel_bias,
+                              int32_t* topk_idx, float* topk_gate, int32_t* expert_counts, void* stream) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || T > c->p.max_tokens) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !gate_w || !topk_idx || !topk_gate)) return MOE_ERR_INVALID_ARG;
+  if (!on_cfg_device(c)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* counts = expert_counts ? expert_counts : c->counts;
+  if (T == 0) {
+    hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(256), 0, s, counts, c->p.n_routed);
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? MOE_OK : hip_fail(c, e);
+  }
+  RouterArgs r{};
+  r.x = x; r.gate_w = gate_w; r.bias = sel_bias; r.logits = c->logits;
+  r.idx = topk_idx; r.gate = topk_gate; r.counts = counts;
+  r.T = T; r.D = c->p.dim; r.E = c->p.n_routed; r.G = c->p.n_group; r.kg = c->p.topk_group; r.K = c->p.top_k;
+  r.act_bf16 = c->p.act_dtype == MOE_BF16; r.score_fn = c->p.score_fn; r.norm = c->p.norm_topk;
+  r.rsf = c->p.routed_scaling_factor;
+  hipError_t e = launch_router(r, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(c, e);
+}
+
+moe_status moe_dispatch_forward(moe_cfg* c, const int32_t* topk_idx, int T, int32_t* offsets,
+                                int32_t* row_token, int32_t* slot_row, void* stream) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || T > c->p.max_tokens) return MOE_ERR_INVALID_ARG;
+  if (!offsets || (T > 0 && (!topk_idx || !row_token || !slot_row))) return MOE_ERR_INVALID_ARG;
+  if (!on_cfg_device(c)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = launch_histogram(topk_idx, c->counts, T * c->p.top_k, c->p.n_routed, s);
+  if (e != hipSuccess) return hip_fail(c, e);
+  DispatchArgs d{};
+  d.idx = topk_idx; d.gate = nullptr; d.counts = c->counts; d.counts_out = nullptr;
+  d.offsets = offsets; d.cursor = c->cursor; d.row_token = row_token; d.row_gate = nullptr;
+  d.slot_row = slot_row; d.pre1 = c->pre1; d.pre2 = c->pre2;
+  d.T = T; d.K = c->p.top_k; d.E = c->p.n_routed;
+  fill_dispatch_geometry(c->p, choose_path(c->p, T), T, &d);
+  e = launch_dispatch(d, s);
+  return e == hipSuccess ? MOE_OK : hip_fail(c, e);
+}
+
+moe_status moe_layer_forward(moe_cfg* c, const void* x, int T, const float* gate_w, const float* sel_bias,
+                             const moe_weights* expert_w, const moe_weights* shared_w, void* out,
+                             int32_t* expert_counts, void* stream) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  const moe_params& p = c->p;
+  if (T < 0 || T > p.max_tokens) return MOE_ERR_INVALID_ARG;
+  if (!on_cfg_device(c)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) {
+    if (expert_counts) {
+      hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(256), 0, s, expert_counts, p.n_routed);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return hip_fail(c, e);
+    }
+    return MOE_OK;
+  }
+  if (!x || !gate_w || !out || !expert_w || !expert_w->gate_up || !expert_w->down) return MOE_ERR_INVALID_ARG;
+  const bool fp8 = p.weight_dtype == MOE_FP8_E4M3;
+  if (fp8 && (!expert_w->gate_up_scale || !expert_w->down_scale)) return MOE_ERR_INVALID_ARG;
+  const bool has_shared = p.shared_hidden > 0;
+  if (has_shared) {
+    if (!shared_w || !shared_w->gate_up || !shared_w->down) return MOE_ERR_INVALID_ARG;
+    if (fp8 && (!shared_w->gate_up_scale || !shared_w->down_scale)) return MOE_ERR_INVALID_ARG;
+  }
+
+  const Path path = choose_path(p, T);
+  hipError_t e;
+
+  // 1. router
+  mark(c, 0, s);
+  RouterArgs r{};
+  r.x = x; r.gate_w = gate_w; r.bias = sel_bias; r.logits = c->logits;
+  r.idx = c->idx; r.gate = c->gate; r.counts = c->counts;
+  r.T = T; r.D = p.dim; r.E = p.n_routed; r.G = p.n_group; r.kg = p.topk_group; r.K = p.top_k;
+  r.act_bf16 = p.act_dtype == MOE_BF16; r.score_fn = p.score_fn; r.norm = p.norm_topk;
+  r.rsf = p.routed_scaling_factor;
+  if ((e = launch_router(r, s)) != hipSuccess) return hip_fail(c, e);
+  mark(c, 1, s);
+
+  // 2. dispatch
+  DispatchArgs d{};
+  d.idx = c->idx; d.gate = c->gate; d.counts = c->counts; d.counts_out = expert_counts;
+  d.offsets = c->offsets; d.cursor = c->cursor; d.row_token = c->row_token; d.row_gate = c->row_gate;
+  d.slot_row = c->slot_row; d.pre1 = c->pre1; d.pre2 = c->pre2;
+  d.T = T; d.K = p.top_k; d.E = p.n_routed;
+  fill_dispatch_geometry(p, path, T, &d);
+  if ((e = launch_dispatch(d, s)) != hipSuccess) return hip_fail(c, e);
+  mark(c, 2, s);
+
+  // 3./4. expert GEMMs
+  const int TK = T * p.top_k;
+  ExpertGemmArgs g{};
+  g.offsets = c->offsets; g.row_token = c->row_token; g.row_gate = c->row_gate;
+  g.E = p.n_routed; g.T = has_shared ? T : 0; g.D = p.dim; g.H = p.hidden; g.Hs = p.shared_hidden;
+  ExpertGemmArgs g1 = g, g2 = g;
+  g1.pre = c->pre1;
+  g1.a = x; g1.w = expert_w->gate_up; g1.w_scale = expert_w->gate_up_scale;
+  g1.w_shared = has_shared ? shared_w->gate_up : nullptr;
+  g1.w_shared_scale = has_shared ? shared_w->gate_up_scale : nullptr;
+  g1.c = c->h_routed; g1.c_shared = c->h_shared;
+  g2.pre = c->pre2;
+  g2.a = c->h_routed; g2.a_shared = c->h_shared; g2.w = expert_w->down; g2.w_scale = expert_w->down_scale;
+  g2.w_shared = has_shared ? shared_w->down : nullptr;
+  g2.w_shared_scale = has_shared ? shared_w->down_scale : nullptr;
+  g2.c = c->y_routed; g2.c_shared = c->y_shared;
+
+  if (path == Path::kF32) {
+    if ((e = launch_simple_gateup_f32(g1, TK, s)) != hipSuccess) return hip_fail(c, e);
+    mark(c, 3, s);
+    if ((e = launch_simple_down_f32(g2, TK, s)) != hipSuccess) return hip_fail(c, e);
+  } else {
+    // upper bounds on the item counts the dispatch can produce
+    const long mblk = (long)(TK + d.bm - 1) / d.bm + p.n_routed;
+    const long mblk_s = has_shared ? (T + d.bm - 1) / d.bm : 0;
+    g1.max_items = (int)(mblk * d.n1_routed + mblk_s * d.n1_shared);
+    g2.max_items = (int)(mblk * d.n2_routed + mblk_s * d.n2_shared);
+    if (path == Path::kGrouped) {
+      if ((e = launch_grouped_gateup_bf16(g1, s)) != hipSuccess) return hip_fail(c, e);
+      mark(c, 3, s);
+      if ((e = launch_grouped_down_bf16(g2, s)) != hipSuccess) return hip_fail(c, e);
+    } else {
+      const int cap = c->num_cus * 16;
+      if ((e = launch_stream_gateup(g1, fp8, std::min(g1.max_items, cap), s)) != hipSuccess) return hip_fail(c, e);
+      mark(c, 3, s);
+      if ((e = launch_stream_down(g2, fp8, std::min(g2.max_items, cap), s)) != hipSuccess) return hip_fail(c, e);
+    }
+  }
+
+  // 5. combine
+  mark(c, 4, s);
+  CombineArgs cb{};
+  cb.x = x; cb.y_routed = c->y_routed; cb.y_shared = has_shared ? c->y_shared : nullptr;
+  cb.slot_row = c->slot_row; cb.out = out; cb.T = T; cb.D = p.dim; cb.K = p.top_k;
+  cb.act_bf16 = p.act_dtype == MOE_BF16; cb.y_bf16 = p.weight_dtype != MOE_F32;
+  cb.out_bf16 = p.out_dtype == MOE_BF16; cb.add_residual = p.add_residual;
+  if ((e = launch_combine(cb, s)) != hipSuccess) return hip_fail(c, e);
+  mark(c, 5, s);
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,167 @@
+// Internal declarations shared by the kernel translation units and the C ABI.
+// Device helpers here are written for gfx950 (CDNA4): 64-lane wavefronts,
+// MFMA builtins, raw 16-bit bf16 storage.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr int kWave = 64;
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 16;
+constexpr int kMaxGroups = 64;
+
+// Tile geometry of the grouped bf16 MFMA GEMMs (prefill path).
+constexpr int kGB_BM = 256;   // rows (tokens) per tile
+constexpr int kG1_BNH = 64;   // hidden columns per gate/up tile (64 gate + 64 up rows of W)
+constexpr int kG2_BN = 128;   // output columns per down tile
+constexpr int kGB_BK = 64;    // K step
+// Weight-streaming path (small token counts): rows per pass and columns per wave item.
+constexpr int kST_BM = 64;
+constexpr int kST_N1 = 8;     // hidden columns per gate/up item (8 gate + 8 up rows)
+constexpr int kST_N2 = 16;    // output columns per down item
+constexpr int kST_KC = 128;   // K chunk (one fp8 scale block)
+
+// ---------------------------------------------------------------------------
+// scalar helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// round-to-nearest-even float32 -> bfloat16 (finite inputs)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// SiLU(z) = z / (1 + 2^(-z*log2(e))), on the hardware exp2 and reciprocal.
+__device__ __forceinline__ float silu_fast(float z) {
+  float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+__device__ __forceinline__ uint32_t ordered_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o, kWave);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// problem p in [0, E]: routed expert p (< E) or the shared expert (== E).
+// Largest p with pre[p] <= i, for a non-decreasing pre[0..E+1].
+__device__ __forceinline__ int find_problem(const int32_t* pre, int E, int i) {
+  int lo = 0, hi = E;  // answer in [0, E]
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------------------
+// kernel launchers (one translation unit each)
+// ---------------------------------------------------------------------------
+
+struct RouterArgs {
+  const void* x;
+  const float* gate_w;
+  const float* bias;
+  float* logits;
+  int32_t* idx;
+  float* gate;
+  int32_t* counts;
+  int T, D, E, G, kg, K;
+  int act_bf16;
+  int score_fn;
+  int norm;
+  float rsf;
+};
+hipError_t launch_router(const RouterArgs& a, hipStream_t s);
+
+struct DispatchArgs {
+  const int32_t* idx;     // [T*K]
+  const float* gate;      // [T*K] or null
+  int32_t* counts;        // [E] (input: histogram)
+  int32_t* counts_out;    // [E] user copy or null
+  int32_t* offsets;       // [E+1]
+  int32_t* cursor;        // [E]
+  int32_t* row_token;     // [T*K]
+  float* row_gate;        // [T*K] or null
+  int32_t* slot_row;      // [T*K]
+  int32_t* pre1;          // [E+2] item prefix, gate/up GEMM
+  int32_t* pre2;          // [E+2] item prefix, down GEMM
+  int T, K, E;
+  int shared_rows;        // rows of the shared problem (T, or 0 without shared expert)
+  int bm;                 // rows per item
+  int n1_routed, n1_shared;  // column items per row block, gate/up GEMM
+  int n2_routed, n2_shared;  // column items per row block, down GEMM
+};
+hipError_t launch_histogram(const int32_t* idx, int32_t* counts, int n, int E, hipStream_t s);
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s);
+
+struct ExpertGemmArgs {
+  // geometry
+  const int32_t* offsets;   // [E+1]
+  const int32_t* row_token; // [T*K]
+  const float* row_gate;    // [T*K]
+  const int32_t* pre;       // [E+2] item prefix of this GEMM
+  int E, T, D, H, Hs;
+  int max_items;            // grid upper bound (items)
+  // operands
+  const void* a;            // GEMM1: x [T][D]; GEMM2: h routed [T*K][H]
+  const void* a_shared;     // GEMM2: h shared [T][Hs]
+  const void* w;            // routed weights (gate_up or down)
+  const void* w_shared;
+  const float* w_scale;     // fp8 only
+  const float* w_shared_scale;
+  void* c;                  // GEMM1: h routed; GEMM2: y routed
+  void* c_shared;           // GEMM1: h shared; GEMM2: y shared
+};
+hipError_t launch_grouped_gateup_bf16(const ExpertGemmArgs& a, hipStream_t s);
+hipError_t launch_grouped_down_bf16(const ExpertGemmArgs& a, hipStream_t s);
+hipError_t launch_stream_gateup(const ExpertGemmArgs& a, int fp8, int n_waves, hipStream_t s);
+hipError_t launch_stream_down(const ExpertGemmArgs& a, int fp8, int n_waves, hipStream_t s);
+hipError_t launch_simple_gateup_f32(const ExpertGemmArgs& a, int TK, hipStream_t s);
+hipError_t launch_simple_down_f32(const ExpertGemmArgs& a, int TK, hipStream_t s);
+
+struct CombineArgs {
+  const void* x;            // residual source, act dtype
+  const void* y_routed;     // [T*K][D]
+  const void* y_shared;     // [T][D] or null
+  const int32_t* slot_row;  // [T*K]
+  void* out;
+  int T, D, K;
+  int act_bf16, y_bf16, out_bf16;
+  int add_residual;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+}  // namespace moe

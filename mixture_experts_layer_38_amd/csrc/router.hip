@@ -1,0 +1,234 @@
+// Router: fp32 logits on fp32 MFMA, then per-token scoring and group-limited
+// top-K selection in wavefront registers.
+//
+// Follows the MoEGate forward of the DeepSeek-V2 walkthrough page (fp32 linear
+// map, softmax, greedy or group-limited greedy top-K) and the selection-only
+// bias of the DeepSeek-V3 basics page (section 1.2): the bias shifts the scores
+// used to choose groups and experts; gates come from the unbiased scores.
+#include "moe_internal.hpp"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// logits[t][e] = sum_d x[t][d] * gate_w[e][d], fp32 accumulation.
+// Tile: 64 tokens x 64 experts per workgroup, 4 waves of 16 tokens x 64 experts.
+// v_mfma_f32_16x16x4_f32: lane l supplies A[row l%16][k l/16] and
+// B[k l/16][col l%16]. Each lane reads 4 consecutive k from LDS and feeds them
+// to 4 successive MFMAs (a consistent permutation of k in A and B leaves the
+// dot products unchanged).
+// ---------------------------------------------------------------------------
+template <bool kBf16X>
+__global__ __launch_bounds__(256) void router_logits_kernel(const void* __restrict__ xv,
+                                                            const float* __restrict__ w,
+                                                            float* __restrict__ logits,
+                                                            int32_t* __restrict__ counts, int T,
+                                                            int D, int E) {
+  constexpr int BT = 64, BE = 64, BK = 32, LD = BK + 4;
+  __shared__ __attribute__((aligned(16))) float sA[BT * LD];
+  __shared__ __attribute__((aligned(16))) float sB[BE * LD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * BT, e0 = blockIdx.y * BE;
+  if (blockIdx.x == 0 && blockIdx.y == 0)
+    for (int e = tid; e < E; e += 256) counts[e] = 0;  // histogram of the select kernel
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int lr = tid >> 2, lc = (tid & 3) * 8;  // loader: row, 8 columns
+  const int rr = lane & 15, q = lane >> 4;
+  for (int k0 = 0; k0 < D; k0 += BK) {
+    float va[8], vb[8];
+    const int t = t0 + lr;
+    if (t < T) {
+      if (kBf16X) {
+        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xv) +
+                                                         (size_t)t * D + k0 + lc);
+        const uint32_t p[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          va[2 * i] = __uint_as_float(p[i] << 16);
+          va[2 * i + 1] = __uint_as_float(p[i] & 0xFFFF0000u);
+        }
+      } else {
+        const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(xv) +
+                                                            (size_t)t * D + k0 + lc);
+        const float4 a = src[0], b = src[1];
+        va[0] = a.x; va[1] = a.y; va[2] = a.z; va[3] = a.w;
+        va[4] = b.x; va[5] = b.y; va[6] = b.z; va[7] = b.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) va[i] = 0.f;
+    }
+    const int e = e0 + lr;
+    if (e < E) {
+      const float4* src = reinterpret_cast<const float4*>(w + (size_t)e * D + k0 + lc);
+      const float4 a = src[0], b = src[1];
+      vb[0] = a.x; vb[1] = a.y; vb[2] = a.z; vb[3] = a.w;
+      vb[4] = b.x; vb[5] = b.y; vb[6] = b.z; vb[7] = b.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vb[i] = 0.f;
+    }
+    float4* da = reinterpret_cast<float4*>(&sA[lr * LD + lc]);
+    da[0] = make_float4(va[0], va[1], va[2], va[3]);
+    da[1] = make_float4(va[4], va[5], va[6], va[7]);
+    float4* db = reinterpret_cast<float4*>(&sB[lr * LD + lc]);
+    db[0] = make_float4(vb[0], vb[1], vb[2], vb[3]);
+    db[1] = make_float4(vb[4], vb[5], vb[6], vb[7]);
+    __syncthreads();
+#pragma unroll
+    for (int kc = 0; kc < BK; kc += 16) {
+      const float4 a = *reinterpret_cast<const float4*>(&sA[(16 * wave + rr) * LD + kc + 4 * q]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 b = *reinterpret_cast<const float4*>(&sB[(16 * j + rr) * LD + kc + 4 * q]);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc[j], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+  // D layout of the 16x16 MFMA: element i of lane l is row 4*(l/16)+i, column l%16
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = e0 + 16 * j + rr;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 16 * wave + 4 * q + i;
+      if (t < T && e < E) logits[(size_t)t * E + e] = acc[j][i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-token scoring and selection; one wave per token, expert e = lane + 64*j.
+// ---------------------------------------------------------------------------
+constexpr int kVPL = kMaxExperts / kWave;  // values per lane
+
+__global__ __launch_bounds__(256) void router_select_kernel(RouterArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.T) return;
+  const int E = a.E;
+  const float* lrow = a.logits + (size_t)t * E;
+  float s[kVPL], z[kVPL];
+  float lmax = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < kVPL; ++j) {
+    const int e = lane + kWave * j;
+    s[j] = (e < E) ? lrow[e] : -INFINITY;
+    lmax = fmaxf(lmax, s[j]);
+  }
+  if (a.score_fn == MOE_SCORE_SOFTMAX) {
+    lmax = wave_max_f32(lmax);
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < kVPL; ++j) {
+      const int e = lane + kWave * j;
+      s[j] = (e < E) ? expf(s[j] - lmax) : 0.f;
+      sum += s[j];
+    }
+    sum = wave_sum_f32(sum);
+    const float inv = 1.0f / sum;
+#pragma unroll
+    for (int j = 0; j < kVPL; ++j) s[j] *= inv;
+  } else {
+#pragma unroll
+    for (int j = 0; j < kVPL; ++j) s[j] = 1.0f / (1.0f + expf(-s[j]));
+  }
+#pragma unroll
+  for (int j = 0; j < kVPL; ++j) {
+    const int e = lane + kWave * j;
+    z[j] = s[j] + ((a.bias != nullptr && e < E) ? a.bias[e] : 0.f);
+  }
+
+  // allowed[j]: expert lane+64j may be chosen
+  uint32_t allowed = 0;
+#pragma unroll
+  for (int j = 0; j < kVPL; ++j)
+    if (lane + kWave * j < E) allowed |= 1u << j;
+
+  if (a.G > 1) {
+    const int gs = E / a.G;
+    // group maxima: lane g ends up holding max z over group g
+    float gmax = -INFINITY;
+    for (int g = 0; g < a.G; ++g) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kVPL; ++j) {
+        const int e = lane + kWave * j;
+        if (e < E && e / gs == g) m = fmaxf(m, z[j]);
+      }
+      m = wave_max_f32(m);
+      if (lane == g) gmax = m;
+    }
+    // keep the kg best groups (ties: lower group index)
+    uint64_t kept = 0;
+    uint64_t key = (lane < a.G) ? (((uint64_t)ordered_key(gmax) << 32) | (uint32_t)(~lane)) : 0;
+    for (int r = 0; r < a.kg; ++r) {
+      const uint64_t best = wave_max_u64(key);
+      const int g = (int)(~(uint32_t)best) & (kMaxGroups - 1);
+      kept |= 1ull << g;
+      if (lane == g) key = 0;
+    }
+#pragma unroll
+    for (int j = 0; j < kVPL; ++j) {
+      const int e = lane + kWave * j;
+      if (e < E && !((kept >> (e / gs)) & 1ull)) allowed &= ~(1u << j);
+    }
+  }
+
+  int my_e = -1;
+  float my_s = 0.f, sum_sel = 0.f;
+  for (int k = 0; k < a.K; ++k) {
+    uint64_t key = 0;
+#pragma unroll
+    for (int j = 0; j < kVPL; ++j) {
+      if ((allowed >> j) & 1u) {
+        const int e = lane + kWave * j;
+        const uint64_t kk = ((uint64_t)ordered_key(z[j]) << 32) | (uint32_t)(~e);
+        key = kk > key ? kk : key;
+      }
+    }
+    const uint64_t best = wave_max_u64(key);
+    int e = (int)(~(uint32_t)best);
+    e = (e < 0 || e >= E) ? 0 : e;  // unreachable: K <= candidate experts
+    const int jw = e >> 6;
+    float mine = 0.f;
+#pragma unroll
+    for (int j = 0; j < kVPL; ++j)
+      if (j == jw) mine = s[j];
+    const float se = __shfl(mine, e & 63, kWave);
+    if ((e & 63) == lane) allowed &= ~(1u << jw);
+    sum_sel += se;
+    if (lane == k) { my_e = e; my_s = se; }
+  }
+  if (lane < a.K) {
+    float g = my_s;
+    if (a.norm) g = g / sum_sel;
+    g *= a.rsf;
+    a.idx[(size_t)t * a.K + lane] = my_e;
+    a.gate[(size_t)t * a.K + lane] = g;
+    atomicAdd(&a.counts[my_e], 1);
+  }
+}
+
+hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
+  dim3 g1((a.T + 63) / 64, (a.E + 63) / 64);
+  if (a.act_bf16)
+    hipLaunchKernelGGL(router_logits_kernel<true>, g1, dim3(256), 0, s, a.x, a.gate_w, a.logits,
+                       a.counts, a.T, a.D, a.E);
+  else
+    hipLaunchKernelGGL(router_logits_kernel<false>, g1, dim3(256), 0, s, a.x, a.gate_w, a.logits,
+                       a.counts, a.T, a.D, a.E);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(router_select_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

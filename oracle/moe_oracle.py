@@ -79,12 +79,21 @@ def decode_e4m3(bits) -> np.ndarray:
     return np.where((c & 0x7F) == 0x7F, np.nan, v)
 
 
+_E4M3_TABLE = None
+
+
 def dequant_e4m3_blocks(codes, scale, block: int = 128) -> np.ndarray:
-    """w[r, c] = e4m3(codes[r, c]) * scale[r // block, c // block]."""
-    q = decode_e4m3(codes)
+    """w[r, c] = e4m3(codes[r, c]) * scale[r // block, c // block] (the codes
+    are decoded through a 256-entry table of decode_e4m3)."""
+    global _E4M3_TABLE
+    if _E4M3_TABLE is None:
+        _E4M3_TABLE = decode_e4m3(np.arange(256))
+    c = np.asarray(codes)
+    q = _E4M3_TABLE[c.astype(np.intp)]
     s = np.asarray(scale, dtype=np.float32).astype(np.float64)
-    s_full = np.repeat(np.repeat(s, block, axis=-2), block, axis=-1)
-    return q * s_full
+    *lead, R, C = q.shape
+    qb = q.reshape(*lead, R // block, block, C // block, block)
+    return (qb * s[..., :, None, :, None]).reshape(q.shape)
 
 
 # ----------------------------------------------------------------------------

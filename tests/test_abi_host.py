@@ -1,0 +1,73 @@
+"""Host-side checks of the C ABI: the library loads, exports every function the
+header declares, and rejects invalid layers before touching any device."""
+import ctypes
+
+import pytest
+
+import mixture_experts_layer_38_amd as M
+
+
+def _params(**kw):
+    base = dict(dim=1024, n_routed=64, hidden=512, shared_hidden=1024, top_k=6, n_group=8, topk_group=3,
+                score_fn="softmax", act="bf16", weight="bf16", max_tokens=4096)
+    base.update(kw)
+    return M.make_params(**base)
+
+
+def test_library_exports_every_declared_function():
+    lib = M.load_library()
+    names = M.declared_functions()
+    assert {"moe_cfg_create", "moe_layer_forward", "moe_router_forward", "moe_dispatch_forward",
+            "moe_cfg_destroy", "moe_status_string"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    assert M.status_string(M.MOE_OK) == "ok"
+    assert "invalid" in M.status_string(M.MOE_ERR_INVALID_ARG)
+    assert "unsupported" in M.status_string(M.MOE_ERR_UNSUPPORTED)
+    assert M.status_string(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("kw", [
+    dict(n_routed=63),                       # E % G != 0
+    dict(topk_group=9),                      # kg > G
+    dict(top_k=25),                          # K > max
+    dict(top_k=9, topk_group=1),             # K > kg * E / G (8 experts per group)
+    dict(n_group=0),
+    dict(dim=0),
+    dict(max_tokens=-1),
+    dict(score_fn=7),
+    dict(out=2),                             # fp8 output
+    dict(path=9),
+])
+def test_invalid_layers_rejected(kw):
+    st, h = M.create_cfg(_params(**kw))
+    assert st == M.MOE_ERR_INVALID_ARG and not h.value
+
+
+@pytest.mark.parametrize("kw", [
+    dict(act="f32", weight="bf16"),          # mixed dtypes
+    dict(act="bf16", weight="f32"),
+    dict(dim=1000),                          # D % 32
+    dict(hidden=500),                        # bf16 needs H % 128
+    dict(shared_hidden=1000),
+    dict(weight="fp8", path="grouped"),      # fp8 runs on the streaming kernels only
+    dict(n_routed=1024, n_group=8),          # E > 512
+])
+def test_unsupported_layers_rejected(kw):
+    st, h = M.create_cfg(_params(**kw))
+    assert st == M.MOE_ERR_UNSUPPORTED and not h.value
+
+
+def test_null_arguments_rejected():
+    lib = M.load_library()
+    h = ctypes.c_void_p()
+    assert lib.moe_cfg_create(None, ctypes.byref(h)) == M.MOE_ERR_INVALID_ARG
+    p = _params()
+    assert lib.moe_cfg_create(ctypes.byref(p), None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_forward(None, None, 0, None, None, None, None, None, None, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_router_forward(None, None, 0, None, None, None, None, None, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch_forward(None, None, 0, None, None, None, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_cfg_destroy(None) == M.MOE_OK

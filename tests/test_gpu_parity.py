@@ -1,0 +1,245 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle.
+
+Sizes: small layers that span several tiles with ragged tails (both expert
+GEMM paths), every workload at its full size (routing on all tokens; outputs
+on all tokens where the oracle finishes in seconds, else on a seeded token
+sample), and the edge cases (no tokens, one token, the maximum token count,
+repeat-run bit identity, bf16 output, routed-only runs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_38_amd as M
+import moe_inputs as MI
+from oracle import adapter as A
+from tests.parity import TOL, check_routing, layer_error, near_tie_mask
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _run_layer(inp, path="auto", with_shared=True, add_residual=None, out_dtype=None, T=None):
+    cfg = inp.cfg
+    over = {}
+    if not with_shared:
+        over["shared_hidden"] = 0
+    if add_residual is not None:
+        over["add_residual"] = add_residual
+    if out_dtype is not None:
+        over["out"] = out_dtype
+    layer = M.MoELayer.from_config(cfg, path=path, **over)
+    counts = torch.full((cfg.E,), -1, dtype=torch.int32, device=DEV)
+    x = inp.x if T is None else inp.x[:T]
+    out = layer.forward(x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared if with_shared else None,
+                        expert_counts=counts)
+    torch.cuda.synchronize()
+    return out, counts, layer
+
+
+def _sample(T, n, seed=7):
+    if n >= T:
+        return np.arange(T)
+    return np.sort(np.random.default_rng(seed).choice(T, size=n, replace=False))
+
+
+def _check_layer(inp, tokens=None, path="auto", routed_only=True):
+    cfg = inp.cfg
+    R = A.route_inputs(inp)
+    tokens = np.arange(cfg.T) if tokens is None else tokens
+    near = near_tie_mask(R)[tokens]
+    x64 = A.decode_tensor(inp.x)[tokens]
+    out, counts, layer = _run_layer(inp, path=path)
+    idx, gate, rc = layer.router(inp.x, inp.gate_w, inp.sel_bias)
+    torch.cuda.synchronize()
+    info = check_routing(idx, gate, rc, R, cfg.E, cfg.G, cfg.kg)
+    assert torch.equal(counts, rc)
+    ref, _ = A.run_layer(inp, tokens=tokens, routing=R)
+    err = layer_error(out[torch.as_tensor(tokens, device=DEV)], ref, x64, cfg.add_residual, exclude=near)
+    tol = TOL[cfg.weight]
+    print(f"{cfg.name} path={path}: routing {info}, full layer err {err}")
+    assert err["max"] <= tol, err
+    if routed_only:
+        out_r, _, _ = _run_layer(inp, path=path, with_shared=False, add_residual=False)
+        ref_r, _ = A.run_layer(inp, tokens=tokens, routing=R, with_shared=False, add_residual=False)
+        err_r = layer_error(out_r[torch.as_tensor(tokens, device=DEV)], ref_r, x64, False, exclude=near)
+        print(f"{cfg.name} path={path}: routed-only err {err_r}")
+        assert err_r["max"] <= tol, err_r
+    return info, err
+
+
+# ---------------------------------------------------------------------------
+# small layers: several tiles, ragged tails
+# ---------------------------------------------------------------------------
+
+SMALL_BF16 = MI.LayerConfig("small_bf16", T=300, D=256, E=16, H=128, G=4, kg=2, K=3, score_fn="softmax",
+                            bias="none", norm=False, rsf=1.0, Hs=256, act="bf16", weight="bf16")
+SMALL_SIG = MI.LayerConfig("small_sigmoid", T=517, D=384, E=32, H=256, G=8, kg=4, K=6, score_fn="sigmoid",
+                           bias="normal", norm=True, rsf=2.5, Hs=128, act="bf16", weight="bf16", bias_std=0.05)
+SMALL_FP8 = MI.LayerConfig("small_fp8", T=77, D=256, E=16, H=256, G=4, kg=2, K=4, score_fn="sigmoid",
+                           bias="normal", norm=True, rsf=2.5, Hs=256, act="bf16", weight="fp8", bias_std=0.05)
+SMALL_F32 = MI.LayerConfig("small_f32", T=129, D=96, E=10, H=48, G=2, kg=1, K=3, score_fn="softmax",
+                           bias="none", norm=False, rsf=1.5, Hs=40, act="f32", weight="f32")
+
+
+def test_generator_is_device_agnostic():
+    k = MI.stream_key(0, MI.TID_GATE_UP)
+    a = MI.uniform_pm(k, 12345, (300, 128), 0.03, "cpu")
+    b = MI.uniform_pm(k, 12345, (300, 128), 0.03, DEV).cpu()
+    assert torch.equal(a, b)
+
+
+def test_router_small_all_score_functions():
+    for cfg in (SMALL_BF16, SMALL_SIG, SMALL_F32, MI.CONFIGS["tiny_f32"]):
+        inp = MI.make_layer(cfg, DEV)
+        layer = M.MoELayer.from_config(cfg)
+        idx, gate, counts = layer.router(inp.x, inp.gate_w, inp.sel_bias)
+        torch.cuda.synchronize()
+        info = check_routing(idx, gate, counts, A.route_inputs(inp), cfg.E, cfg.G, cfg.kg)
+        # canonical order: descending selection score
+        R = A.route_inputs(inp)
+        zsel = np.take_along_axis(R["z"], idx.cpu().numpy().astype(np.int64), 1)
+        assert np.all(np.diff(zsel, axis=1) <= 2e-6)
+        print(cfg.name, info)
+
+
+def test_router_forced_expert_and_all_ties():
+    cfg = SMALL_SIG
+    inp = MI.make_layer(cfg, DEV)
+    layer = M.MoELayer.from_config(cfg)
+    b = torch.zeros(cfg.E, device=DEV)
+    b[13] = 10.0
+    idx, gate, counts = layer.router(inp.x, inp.gate_w, b)
+    torch.cuda.synchronize()
+    assert int(counts[13]) == cfg.T
+    assert bool((idx == 13).any(dim=1).all())
+    # x = 0: every score equal -> lowest groups, lowest indices
+    x0 = torch.zeros_like(inp.x)
+    idx, gate, counts = layer.router(x0, inp.gate_w, None)
+    torch.cuda.synchronize()
+    assert torch.equal(idx.cpu(), torch.arange(cfg.K, dtype=torch.int32).expand(cfg.T, cfg.K))
+    assert torch.allclose(gate.cpu(), torch.full((cfg.T, cfg.K), cfg.rsf / cfg.K))
+
+
+def test_dispatch_is_a_valid_permutation():
+    cfg = SMALL_SIG
+    layer = M.MoELayer.from_config(cfg)
+    rng = np.random.default_rng(3)
+    for T in (1, 77, 517):
+        idx = np.stack([rng.choice(cfg.E, size=cfg.K, replace=False) for _ in range(T)]).astype(np.int32)
+        off, row_token, slot_row = layer.dispatch(torch.from_numpy(idx).to(DEV))
+        torch.cuda.synchronize()
+        off, row_token, slot_row = off.cpu().numpy(), row_token.cpu().numpy(), slot_row.cpu().numpy()
+        cnt = np.bincount(idx.ravel(), minlength=cfg.E)
+        assert np.array_equal(off, np.concatenate([[0], np.cumsum(cnt)]))
+        for e in range(cfg.E):
+            seg = row_token[off[e]:off[e + 1]]
+            assert np.array_equal(np.sort(seg), np.nonzero((idx == e).any(axis=1))[0])
+        for t in range(T):
+            for k in range(cfg.K):
+                r = slot_row[t * cfg.K + k]
+                e = idx[t, k]
+                assert off[e] <= r < off[e + 1] and row_token[r] == t
+
+
+@pytest.mark.parametrize("cfg,path", [(SMALL_F32, "auto"), (MI.CONFIGS["tiny_f32"], "auto"),
+                                      (SMALL_BF16, "grouped"), (SMALL_BF16, "stream"),
+                                      (SMALL_SIG, "grouped"), (SMALL_SIG, "stream"), (SMALL_FP8, "stream")],
+                         ids=lambda v: v if isinstance(v, str) else v.name)
+def test_layer_small(cfg, path):
+    inp = MI.make_layer(cfg, DEV)
+    _check_layer(inp, path=path)
+
+
+def test_layer_fp8_every_code():
+    """Expert weights drawn uniformly over all 254 finite e4m3 codes (tiny,
+    subnormal and large values alike), so any mis-decoded code shows up."""
+    cfg = SMALL_FP8
+    inp = MI.make_layer(cfg, DEV)
+    g = torch.Generator().manual_seed(5)
+
+    def every_code(t):
+        r = torch.randint(0, 254, t.shape, generator=g, dtype=torch.int32)
+        r = torch.where(r >= 0x7F, r + 1, r)  # skip 0x7F; 0xFF is never reached
+        t.copy_(r.to(torch.uint8).to(t.device))
+    for w in (inp.experts.gate_up, inp.experts.down, inp.shared.gate_up, inp.shared.down):
+        every_code(w)
+    _check_layer(inp, path="stream")
+
+
+def test_layer_edge_cases():
+    cfg = SMALL_SIG
+    inp = MI.make_layer(cfg, DEV)
+    layer = M.MoELayer.from_config(cfg)
+    # T = 0 zeroes the counts and writes nothing
+    counts = torch.full((cfg.E,), 7, dtype=torch.int32, device=DEV)
+    out = torch.full((1, cfg.D), 3.0, device=DEV)
+    layer.forward(inp.x[:0], inp.gate_w, inp.sel_bias, inp.experts, inp.shared, out=out[:0], expert_counts=counts)
+    torch.cuda.synchronize()
+    assert int(counts.abs().sum()) == 0 and bool((out == 3.0).all())
+    # T = 1 and T = max_tokens agree with the oracle on those tokens
+    R = A.route_inputs(inp)
+    for T in (1, cfg.T):
+        o = layer.forward(inp.x[:T].contiguous(), inp.gate_w, inp.sel_bias, inp.experts, inp.shared)
+        torch.cuda.synchronize()
+        ref, _ = A.run_layer(inp, tokens=np.arange(T), routing=R)
+        err = layer_error(o, ref, A.decode_tensor(inp.x)[:T], True, exclude=near_tie_mask(R)[:T])
+        assert err["max"] <= TOL["bf16"]
+    # T > max_tokens is rejected
+    with pytest.raises(M.MoEError):
+        big = torch.zeros((cfg.T + 1, cfg.D), dtype=torch.bfloat16, device=DEV)
+        layer.forward(big, inp.gate_w, inp.sel_bias, inp.experts, inp.shared)
+    # repeat runs are bit-identical (no float atomics anywhere)
+    o1 = layer.forward(inp.x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared)
+    o2 = layer.forward(inp.x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    # bf16 output is the fp32 output rounded
+    ob, _, _ = _run_layer(inp, out_dtype="bf16")
+    assert torch.equal(ob, o1.to(torch.bfloat16))
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size
+# ---------------------------------------------------------------------------
+
+
+@pytest.fixture(scope="module")
+def layers():
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            cache[name] = MI.make_layer(MI.CONFIGS[name], DEV)
+        return cache[name]
+    yield get
+    cache.clear()
+    torch.cuda.empty_cache()
+
+
+def test_layer_tiny_f32(layers):
+    _check_layer(layers("tiny_f32"))
+
+
+def test_layer_group_bf16(layers):
+    inp = layers("group_bf16")
+    _check_layer(inp, path="grouped")
+    _check_layer(inp, tokens=_sample(inp.cfg.T, 256), path="stream", routed_only=False)
+
+
+def test_layer_v2_prefill(layers):
+    inp = layers("v2_prefill")
+    _check_layer(inp, tokens=_sample(inp.cfg.T, 48))
+
+
+def test_layer_v3_prefill(layers):
+    inp = layers("v3_prefill")
+    _check_layer(inp, tokens=_sample(inp.cfg.T, 24), routed_only=False)
+
+
+def test_layer_v3_decode_fp8(layers):
+    inp = layers("v3_decode_fp8")
+    _check_layer(inp)
