@@ -4,23 +4,29 @@
 // One launch covers every problem: routed expert e (its rows are the
 // expert-contiguous rows offsets[e] .. offsets[e+1]-1 built by the dispatch)
 // and the shared expert (all T tokens, gate 1). Work items are 256-row x
-// N-column output tiles; the dispatch writes their per-problem prefix, and a
+// 256-column output tiles; the dispatch writes their per-problem prefix, and a
 // block finds its problem by binary search, so the host never learns the
 // per-expert row counts.
 //
 // Gate/up GEMM (fine-grained SwiGLU expert, DeepSeek-V2 walkthrough page MoE
-// code; architecture article section 3.3): a tile loads 64 W_gate rows and the
-// matching 64 W_up rows, so the SwiGLU h = SiLU(x W_gate^T) * (x W_up^T) is
-// formed in registers and only h (bf16) is written. Token rows are gathered
-// from x through the dispatch's row -> token map.
-// Down GEMM: Y[row] = g_row * (h[row] W_down^T), bf16, 128 output columns per
+// code; architecture article section 3.3): a tile loads 128 W_gate rows and the
+// matching 128 W_up rows, so h = SiLU(x W_gate^T) * (x W_up^T) is formed in
+// registers and only h (bf16) is written. Token rows are gathered from x
+// through the dispatch's row -> token map.
+// Down GEMM: Y[row] = g_row * (h[row] W_down^T), bf16, 256 output columns per
 // tile; the combine sums the K rows of each token in a fixed order.
 //
-// Tile 256 x 128 (gate/up: 256 rows x (64 gate + 64 up) columns), K step 64,
-// 4 waves as 2 x 2, each wave 128 x 64 on v_mfma_f32_32x32x16_bf16. Global
-// tiles are staged through LDS (rows padded to 144 bytes so that the 16-byte
-// fragment reads of 16 consecutive rows hit distinct banks); the next K step
-// is loaded into registers while the current one is multiplied.
+// Tile 256 x 256, K step 64, 4 waves as 2 x 2, each wave 128 x 128 as 4 x 4
+// blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane, held in
+// AGPRs). A wave's four 32-row blocks are interleaved with the other row-wave's
+// (blocks wm, wm+2, wm+4, wm+6), so a ragged last tile of an expert splits its
+// valid rows evenly; the tile body is instantiated per count of valid row
+// blocks, so blocks with no valid row cost no MFMA and the K loop stays
+// branch-free.
+// Both operands are staged through two LDS buffers (rows padded to 144 bytes so
+// that the 16-byte fragment reads of consecutive rows hit distinct banks): the
+// next K step is loaded into registers while the current one is multiplied,
+// then written to the other buffer; one barrier per K step.
 // Blocks are mapped so that consecutive tiles (which share weight columns or
 // token rows) land on the same XCD and its L2.
 #include "moe_internal.hpp"
@@ -28,14 +34,197 @@
 namespace moe {
 
 namespace {
-constexpr int BM = kGB_BM, BK = kGB_BK, LDSW = BK + 8;
+constexpr int BM = kGB_BM, BN = 256, BK = kGB_BK, LDW = BK + 8;
+constexpr int kRows = BM + BN;  // LDS rows per buffer: A then B
+
+struct Tile {
+  const uint16_t* a_rows;  // GEMM1: x; GEMM2: h of this problem (row 0 = row_base)
+  const int32_t* tok;      // GEMM1 routed: row -> token map at row_base; null = identity
+  const uint16_t* w;       // weights of this problem
+  uint16_t* c;             // output rows of this problem (row 0 = row_base)
+  const float* gate;       // GEMM2 routed: gates at row_base; null = 1
+  uint32_t a_bytes;        // extent of a_rows (buffer range)
+  uint32_t w_bytes;        // extent of w
+  int lda;                 // row length of a_rows
+  int ldc;                 // row length of c
+  int K;                   // reduction length
+  int Hp;                  // hidden of this problem
+  int D;
+  int m0, vrows, nt;
+};
+}  // namespace
+
+template <int kMode, int NRB>
+__device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows * LDW]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int c8 = tid & 7, r0 = tid >> 3;
+
+  // loader: 16 chunks of 16 bytes per thread per K step, rows r0 + 32*j of
+  // the 512 LDS rows (j < 8: A rows, j >= 8: B rows), read as buffer loads:
+  // a 32-bit byte offset per row in a VGPR, the K position in a scalar offset.
+  // Rows past the tile's valid rows (and columns past D) read a valid row
+  // instead: their results are never stored, so every load is unconditional.
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(t.a_rows), (short)0, t.a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(t.w), (short)0, t.w_bytes, 0x00020000);
+  uint32_t voff[16];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int m = r0 + 32 * j;
+    const int mm = t.m0 + (m < t.vrows ? m : 0);
+    const int row = (kMode == 0 && t.tok != nullptr) ? t.tok[mm] : mm;
+    voff[j] = ((uint32_t)row * (uint32_t)t.lda + c8 * 8) * 2u;
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int b = r0 + 32 * j;  // 0..255
+    int wrow = (kMode == 0) ? (b < 128 ? t.nt * 128 + b : t.Hp + t.nt * 128 + b - 128) : t.nt * BN + b;
+    if (kMode == 1 && wrow >= t.D) wrow = 0;
+    voff[8 + j] = ((uint32_t)wrow * (uint32_t)t.K + c8 * 8) * 2u;
+  }
+  auto gload = [&](int j, int k0) __attribute__((always_inline)) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(j < 8 ? ra : rb, voff[j], k0 * 2, 0));
+  };
+
+  f32x16 acc[NRB > 0 ? NRB : 1][4];
+#pragma unroll
+  for (int i = 0; i < NRB; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][c][e] = 0.f;
+
+  // LDS B rows of this wave's four 32-column blocks
+  int bcol[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    bcol[c] = (kMode == 0) ? ((c < 2) ? 64 * wn + 32 * c : 128 + 64 * wn + 32 * (c - 2)) : 128 * wn + 32 * c;
+  const int lr = lane & 31, lk = (lane >> 5) * 8;
+
+  uint4 pf[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) pf[j] = gload(j, 0);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) *reinterpret_cast<uint4*>(&smem[0][(r0 + 32 * j) * LDW + c8 * 8]) = pf[j];
+  __syncthreads();
+
+  // Fragments are double-buffered across the four 16-wide substeps of a K
+  // step: the LDS reads of substep kk+1 are issued before the MFMAs of
+  // substep kk, so their latency hides behind those MFMAs.
+  constexpr int NA = NRB > 0 ? NRB : 1;
+  bf16x8 fb[2][4], fa[2][NA];
+  auto read_frags = [&](const uint16_t* sbuf, int kk, int slot) __attribute__((always_inline)) {
+    const uint16_t* sA = sbuf;
+    const uint16_t* sB = sbuf + BM * LDW;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      fb[slot][c] = *reinterpret_cast<const bf16x8*>(&sB[(bcol[c] + lr) * LDW + kk + lk]);
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+      fa[slot][i] = *reinterpret_cast<const bf16x8*>(&sA[(32 * (wm + 2 * i) + lr) * LDW + kk + lk]);
+  };
+  auto mfmas = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][c], acc[i][c], 0, 0, 0);
+  };
+
+  // The next K step's tile, loaded into registers at the top of a step, is
+  // written to the other LDS buffer in two halves interleaved with the MFMAs
+  // of the last two substeps, so the LDS writes overlap the matrix work.
+  auto store_half = [&](int buf, int h) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 8 * h; j < 8 * h + 8; ++j)
+      *reinterpret_cast<uint4*>(&smem[buf][(r0 + 32 * j) * LDW + c8 * 8]) = pf[j];
+  };
+
+  const int nk = t.K / BK;
+  read_frags(smem[0], 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    // The last step reloads its own K slice and writes the idle buffer, so
+    // the step body has no branch (and the scheduler sees one region).
+    const int knext = (kt + 1 < nk ? kt + 1 : kt) * BK;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) pf[j] = gload(j, knext);
+    // substeps 0, 1: next fragments interleaved with the MFMAs
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      read_frags(smem[cur], 16 * (s + 1), (s + 1) & 1);
+      mfmas(s & 1);
+#pragma unroll
+      for (int q = 0; q < 4 + NRB; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4 * NRB, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // substep 2: last fragments, then the first half of the next tile
+    read_frags(smem[cur], 48, 1);
+    store_half(cur ^ 1, 0);
+    mfmas(0);
+#pragma unroll
+    for (int q = 0; q < 4 + NRB; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NRB, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // substep 3: second half of the next tile
+    store_half(cur ^ 1, 1);
+    mfmas(1);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NRB, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    read_frags(smem[cur ^ 1], 0, 0);
+  }
+
+  // D layout of the 32x32 MFMA: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
+  // column l%32.
+#pragma unroll
+  for (int i = 0; i < NRB; ++i) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int m = 32 * (wm + 2 * i) + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      if (m >= t.vrows) continue;
+      const int mr = t.m0 + m;
+      uint16_t* cp = t.c + (size_t)mr * t.ldc;
+      if (kMode == 0) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const float h = silu_fast(acc[i][c][e]) * acc[i][c + 2][e];
+          cp[t.nt * 128 + 64 * wn + 32 * c + lr] = f32_to_bf16(h);
+        }
+      } else {
+        const float g = t.gate ? t.gate[mr] : 1.0f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int col = t.nt * BN + 128 * wn + 32 * c + lr;
+          if (col < t.D) cp[col] = f32_to_bf16(g * acc[i][c][e]);
+        }
+      }
+    }
+  }
 }
 
 template <int kMode>  // 0: gate/up + SwiGLU, 1: down + gate scale
 __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(ExpertGemmArgs a) {
-  constexpr int BN = 128;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[BM * LDSW];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[BN * LDSW];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][kRows * LDW];
 
   const int total = a.pre[a.E + 1];
   const int chunk = (total + 7) >> 3;
@@ -49,112 +238,51 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
   const bool routed = p < a.E;
   const int rows = routed ? a.offsets[p + 1] - a.offsets[p] : a.T;
   const int row_base = routed ? a.offsets[p] : 0;
-  const int Hp = routed ? a.H : a.Hs;
-  const int ntn = (kMode == 0) ? Hp / kG1_BNH : a.D / kG2_BN;
+  Tile t;
+  t.Hp = routed ? a.H : a.Hs;
+  t.D = a.D;
+  const int ntn = (kMode == 0) ? t.Hp / kG1_BNH : (a.D + BN - 1) / BN;  // D % 128 == 0: last tile may be half
   const int local = tile - a.pre[p];
-  const int m0 = (local / ntn) * BM;
-  const int nt = local % ntn;
-  const int K = (kMode == 0) ? a.D : Hp;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int c8 = tid & 7, r0 = tid >> 3;
-
-  // global source rows of this thread's 8 A chunks and 4 B chunks
-  const uint16_t* ap[8];
-  bool av[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int m = m0 + r0 + 32 * j;
-    av[j] = m < rows;
-    const int mm = av[j] ? m : m0;
-    if (kMode == 0) {
-      const int tok = routed ? a.row_token[row_base + mm] : mm;
-      ap[j] = static_cast<const uint16_t*>(a.a) + (size_t)tok * a.D + c8 * 8;
-    } else {
-      ap[j] = routed ? static_cast<const uint16_t*>(a.a) + (size_t)(row_base + mm) * a.H + c8 * 8
-                     : static_cast<const uint16_t*>(a.a_shared) + (size_t)mm * a.Hs + c8 * 8;
-    }
-  }
-  const uint16_t* wbase = routed ? static_cast<const uint16_t*>(a.w) +
-                                       (size_t)p * ((kMode == 0) ? 2 * Hp : a.D) * K
-                                 : static_cast<const uint16_t*>(a.w_shared);
-  const uint16_t* bp[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int b = r0 + 32 * j;
-    const int wrow = (kMode == 0) ? (b < 64 ? nt * 64 + b : Hp + nt * 64 + b - 64) : nt * BN + b;
-    bp[j] = wbase + (size_t)wrow * K + c8 * 8;
+  t.m0 = (local / ntn) * BM;
+  t.nt = local % ntn;
+  t.K = (kMode == 0) ? a.D : t.Hp;
+  t.vrows = min(rows - t.m0, BM);
+  if (kMode == 0) {
+    t.a_rows = static_cast<const uint16_t*>(a.a);
+    t.lda = a.D;
+    t.tok = routed ? a.row_token + row_base : nullptr;
+    t.w = routed ? static_cast<const uint16_t*>(a.w) + (size_t)p * 2 * t.Hp * a.D
+                 : static_cast<const uint16_t*>(a.w_shared);
+    t.c = routed ? static_cast<uint16_t*>(a.c) + (size_t)row_base * a.H : static_cast<uint16_t*>(a.c_shared);
+    t.ldc = t.Hp;
+    t.gate = nullptr;
+    t.a_bytes = (uint32_t)((size_t)a.x_rows * a.D * 2);
+    t.w_bytes = (uint32_t)((size_t)2 * t.Hp * a.D * 2);
+  } else {
+    t.a_rows = routed ? static_cast<const uint16_t*>(a.a) + (size_t)row_base * a.H
+                      : static_cast<const uint16_t*>(a.a_shared);
+    t.lda = t.Hp;
+    t.tok = nullptr;
+    t.w = routed ? static_cast<const uint16_t*>(a.w) + (size_t)p * a.D * t.Hp
+                 : static_cast<const uint16_t*>(a.w_shared);
+    t.c = routed ? static_cast<uint16_t*>(a.c) + (size_t)row_base * a.D : static_cast<uint16_t*>(a.c_shared);
+    t.ldc = a.D;
+    t.gate = routed ? a.row_gate + row_base : nullptr;
+    t.a_bytes = (uint32_t)((size_t)rows * t.Hp * 2);
+    t.w_bytes = (uint32_t)((size_t)a.D * t.Hp * 2);
   }
 
-  uint4 ra[8], rb[4];
-  auto load = [&](int k0) {
+  // valid 32-row blocks of this wave: wm + 2*i for i < nrb
+  const int wm = (threadIdx.x >> 6) >> 1;
+  int nrb = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      ra[j] = av[j] ? *reinterpret_cast<const uint4*>(ap[j] + k0) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) rb[j] = *reinterpret_cast<const uint4*>(bp[j] + k0);
-  };
-
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][c][e] = 0.f;
-
-  // B-tile rows of this wave's two 32-column blocks
-  const int bb0 = (kMode == 0) ? 32 * wn : 64 * wn;
-  const int bb1 = (kMode == 0) ? 64 + 32 * wn : 64 * wn + 32;
-  const int lr = lane & 31, lk = (lane >> 5) * 8;
-
-  load(0);
-  for (int k0 = 0; k0 < K; k0 += BK) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(&sA[(r0 + 32 * j) * LDSW + c8 * 8]) = ra[j];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&sB[(r0 + 32 * j) * LDSW + c8 * 8]) = rb[j];
-    __syncthreads();
-    if (k0 + BK < K) load(k0 + BK);
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 fa[4], fb[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(&sA[(wm * 128 + 32 * i + lr) * LDSW + kk + lk]);
-      fb[0] = *reinterpret_cast<const bf16x8*>(&sB[(bb0 + lr) * LDSW + kk + lk]);
-      fb[1] = *reinterpret_cast<const bf16x8*>(&sB[(bb1 + lr) * LDSW + kk + lk]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[c], acc[i][c], 0, 0, 0);
-    }
-    __syncthreads();
-  }
-
-  // D layout of the 32x32 MFMA: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
-  // column l%32.
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int m = m0 + wm * 128 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      if (m >= rows) continue;
-      if (kMode == 0) {
-        const float h = silu_fast(acc[i][0][e]) * acc[i][1][e];
-        uint16_t* hp = routed ? static_cast<uint16_t*>(a.c) + (size_t)(row_base + m) * a.H
-                              : static_cast<uint16_t*>(a.c_shared) + (size_t)m * a.Hs;
-        hp[nt * 64 + 32 * wn + lr] = f32_to_bf16(h);
-      } else {
-        const float g = routed ? a.row_gate[row_base + m] : 1.0f;
-        uint16_t* yp = routed ? static_cast<uint16_t*>(a.c) + (size_t)(row_base + m) * a.D
-                              : static_cast<uint16_t*>(a.c_shared) + (size_t)m * a.D;
-        yp[nt * BN + 64 * wn + lr] = f32_to_bf16(g * acc[i][0][e]);
-        yp[nt * BN + 64 * wn + 32 + lr] = f32_to_bf16(g * acc[i][1][e]);
-      }
-    }
+  for (int i = 0; i < 4; ++i) nrb += (32 * (wm + 2 * i) < t.vrows) ? 1 : 0;
+  switch (nrb) {
+    case 4: tile_body<kMode, 4>(t, smem); break;
+    case 3: tile_body<kMode, 3>(t, smem); break;
+    case 2: tile_body<kMode, 2>(t, smem); break;
+    case 1: tile_body<kMode, 1>(t, smem); break;
+    default: tile_body<kMode, 0>(t, smem); break;
   }
 }
 

@@ -96,7 +96,7 @@ void fill_dispatch_geometry(const moe_params& p, Path path, int T, DispatchArgs*
     d->bm = kGB_BM;
     d->n1_routed = p.hidden / kG1_BNH;
     d->n1_shared = p.shared_hidden / kG1_BNH;
-    d->n2_routed = d->n2_shared = p.dim / kG2_BN;
+    d->n2_routed = d->n2_shared = (p.dim + kG2_BN - 1) / kG2_BN;
   } else if (path == Path::kStream) {
     d->bm = kST_BM;
     d->n1_routed = p.hidden / kST_N1;
@@ -345,6 +345,7 @@ moe_status moe_layer_forward(moe_cfg* c, const void* x, int T, const float* gate
   ExpertGemmArgs g{};
   g.offsets = c->offsets; g.row_token = c->row_token; g.row_gate = c->row_gate;
   g.E = p.n_routed; g.T = has_shared ? T : 0; g.D = p.dim; g.H = p.hidden; g.Hs = p.shared_hidden;
+  g.x_rows = T;
   ExpertGemmArgs g1 = g, g2 = g;
   g1.pre = c->pre1;
   g1.a = x; g1.w = expert_w->gate_up; g1.w_scale = expert_w->gate_up_scale;

@@ -21,8 +21,8 @@ constexpr int kMaxGroups = 64;
 
 // Tile geometry of the grouped bf16 MFMA GEMMs (prefill path).
 constexpr int kGB_BM = 256;   // rows (tokens) per tile
-constexpr int kG1_BNH = 64;   // hidden columns per gate/up tile (64 gate + 64 up rows of W)
-constexpr int kG2_BN = 128;   // output columns per down tile
+constexpr int kG1_BNH = 128;  // hidden columns per gate/up tile (128 gate + 128 up rows of W)
+constexpr int kG2_BN = 256;   // output columns per down tile
 constexpr int kGB_BK = 64;    // K step
 // Weight-streaming path (small token counts): rows per pass and columns per wave item.
 constexpr int kST_BM = 64;
@@ -134,6 +134,7 @@ struct ExpertGemmArgs {
   const float* row_gate;    // [T*K]
   const int32_t* pre;       // [E+2] item prefix of this GEMM
   int E, T, D, H, Hs;
+  int x_rows;               // rows of x (tokens of the call)
   int max_items;            // grid upper bound (items)
   // operands
   const void* a;            // GEMM1: x [T][D]; GEMM2: h routed [T*K][H]
