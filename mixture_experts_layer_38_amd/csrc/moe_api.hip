@@ -160,7 +160,9 @@ moe_status moe_cfg_create(const moe_params* p, moe_cfg** out) {
   const size_t act = (p->weight_dtype == MOE_F32) ? 4 : 2;  // h and y element size
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + std::max<size_t>(bytes, 1)); return o; };
-  const size_t o_logits = take(Tm * E * 4), o_idx = take(Tm * K * 4), o_gate = take(Tm * K * 4);
+  // partial-logit planes: router_splits(T) * T <= 32 * CUs + T for every T
+  const size_t lg = (size_t)32 * c->num_cus + Tm;
+  const size_t o_logits = take(lg * E * 4), o_idx = take(Tm * K * 4), o_gate = take(Tm * K * 4);
   const size_t o_counts = take(E * 4), o_offsets = take((E + 1) * 4), o_cursor = take(E * 4);
   const size_t o_pre1 = take((E + 2) * 4), o_pre2 = take((E + 2) * 4);
   const size_t o_rt = take(Tm * K * 4), o_rg = take(Tm * K * 4), o_sr = take(Tm * K * 4);
@@ -268,6 +270,7 @@ moe_status moe_router_forward(moe_cfg* c, const void* x, int T, const float* gat
   r.T = T; r.D = c->p.dim; r.E = c->p.n_routed; r.G = c->p.n_group; r.kg = c->p.topk_group; r.K = c->p.top_k;
   r.act_bf16 = c->p.act_dtype == MOE_BF16; r.score_fn = c->p.score_fn; r.norm = c->p.norm_topk;
   r.rsf = c->p.routed_scaling_factor;
+  r.num_cus = c->num_cus;
   hipError_t e = launch_router(r, s);
   return e == hipSuccess ? MOE_OK : hip_fail(c, e);
 }
@@ -327,6 +330,7 @@ moe_status moe_layer_forward(moe_cfg* c, const void* x, int T, const float* gate
   r.T = T; r.D = p.dim; r.E = p.n_routed; r.G = p.n_group; r.kg = p.topk_group; r.K = p.top_k;
   r.act_bf16 = p.act_dtype == MOE_BF16; r.score_fn = p.score_fn; r.norm = p.norm_topk;
   r.rsf = p.routed_scaling_factor;
+  r.num_cus = c->num_cus;
   if ((e = launch_router(r, s)) != hipSuccess) return hip_fail(c, e);
   mark(c, 1, s);
 
@@ -373,7 +377,7 @@ moe_status moe_layer_forward(moe_cfg* c, const void* x, int T, const float* gate
       mark(c, 3, s);
       if ((e = launch_grouped_down_bf16(g2, s)) != hipSuccess) return hip_fail(c, e);
     } else {
-      const int cap = c->num_cus * 16;
+      const int cap = c->num_cus * 2;  // persistent workgroups
       if ((e = launch_stream_gateup(g1, fp8, std::min(g1.max_items, cap), s)) != hipSuccess) return hip_fail(c, e);
       mark(c, 3, s);
       if ((e = launch_stream_down(g2, fp8, std::min(g2.max_items, cap), s)) != hipSuccess) return hip_fail(c, e);

@@ -24,10 +24,10 @@ constexpr int kGB_BM = 256;   // rows (tokens) per tile
 constexpr int kG1_BNH = 128;  // hidden columns per gate/up tile (128 gate + 128 up rows of W)
 constexpr int kG2_BN = 256;   // output columns per down tile
 constexpr int kGB_BK = 64;    // K step
-// Weight-streaming path (small token counts): rows per pass and columns per wave item.
-constexpr int kST_BM = 64;
-constexpr int kST_N1 = 8;     // hidden columns per gate/up item (8 gate + 8 up rows)
-constexpr int kST_N2 = 16;    // output columns per down item
+// Weight-streaming path (small token counts): token rows and columns per workgroup item.
+constexpr int kST_BM = 16;
+constexpr int kST_N1 = 32;    // hidden columns per gate/up item (32 gate + 32 up rows)
+constexpr int kST_N2 = 64;    // output columns per down item
 constexpr int kST_KC = 128;   // K chunk (one fp8 scale block)
 
 // ---------------------------------------------------------------------------
@@ -103,7 +103,11 @@ struct RouterArgs {
   int score_fn;
   int norm;
   float rsf;
+  int num_cus;
+  int splits;  // set by launch_router
 };
+// number of partial-logit planes launch_router uses for T tokens
+int router_splits(int T, int D, int E, int num_cus);
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);
 
 struct DispatchArgs {
@@ -148,8 +152,8 @@ struct ExpertGemmArgs {
 };
 hipError_t launch_grouped_gateup_bf16(const ExpertGemmArgs& a, hipStream_t s);
 hipError_t launch_grouped_down_bf16(const ExpertGemmArgs& a, hipStream_t s);
-hipError_t launch_stream_gateup(const ExpertGemmArgs& a, int fp8, int n_waves, hipStream_t s);
-hipError_t launch_stream_down(const ExpertGemmArgs& a, int fp8, int n_waves, hipStream_t s);
+hipError_t launch_stream_gateup(const ExpertGemmArgs& a, int fp8, int blocks, hipStream_t s);
+hipError_t launch_stream_down(const ExpertGemmArgs& a, int fp8, int blocks, hipStream_t s);
 hipError_t launch_simple_gateup_f32(const ExpertGemmArgs& a, int TK, hipStream_t s);
 hipError_t launch_simple_down_f32(const ExpertGemmArgs& a, int TK, hipStream_t s);
 

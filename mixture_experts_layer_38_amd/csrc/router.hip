@@ -17,19 +17,25 @@ namespace moe {
 // to 4 successive MFMAs (a consistent permutation of k in A and B leaves the
 // dot products unchanged).
 // ---------------------------------------------------------------------------
+// For few tokens the reduction over D is split across blockIdx.z (kc columns
+// each); every split writes its own partial logits plane, and the select
+// kernel adds the planes in a fixed order, so the result does not depend on
+// scheduling.
 template <bool kBf16X>
 __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restrict__ xv,
                                                             const float* __restrict__ w,
                                                             float* __restrict__ logits,
                                                             int32_t* __restrict__ counts, int T,
-                                                            int D, int E) {
+                                                            int D, int E, int kc) {
   constexpr int BT = 64, BE = 64, BK = 32, LD = BK + 4;
   __shared__ __attribute__((aligned(16))) float sA[BT * LD];
   __shared__ __attribute__((aligned(16))) float sB[BE * LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * BT, e0 = blockIdx.y * BE;
-  if (blockIdx.x == 0 && blockIdx.y == 0)
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
     for (int e = tid; e < E; e += 256) counts[e] = 0;  // histogram of the select kernel
+  const int kbeg = blockIdx.z * kc, kend = min(D, kbeg + kc);
+  logits += (size_t)blockIdx.z * T * E;
 
   f32x4 acc[4];
 #pragma unroll
@@ -37,7 +43,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
 
   const int lr = tid >> 2, lc = (tid & 3) * 8;  // loader: row, 8 columns
   const int rr = lane & 15, q = lane >> 4;
-  for (int k0 = 0; k0 < D; k0 += BK) {
+  for (int k0 = kbeg; k0 < kend; k0 += BK) {
     float va[8], vb[8];
     const int t = t0 + lr;
     if (t < T) {
@@ -217,16 +223,42 @@ __global__ __launch_bounds__(256) void router_select_kernel(RouterArgs a) {
   }
 }
 
-hipError_t launch_router(const RouterArgs& a, hipStream_t s) {
-  dim3 g1((a.T + 63) / 64, (a.E + 63) / 64);
+// plane 0 += planes 1 .. splits-1, in plane order (one thread per logit)
+__global__ __launch_bounds__(256) void reduce_planes_kernel(float* __restrict__ logits, int n, int splits) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float v = logits[i];
+  for (int sp = 1; sp < splits; ++sp) v += logits[(size_t)sp * n + i];
+  logits[i] = v;
+}
+
+int router_splits(int T, int D, int E, int num_cus) {
+  const int tiles = ((T + 63) / 64) * ((E + 63) / 64);
+  int sp = (num_cus / 2 + tiles - 1) / tiles;
+  sp = sp < 1 ? 1 : (sp > D / 32 ? D / 32 : sp);
+  const int kc = ((D / sp + 31) / 32) * 32;
+  return (D + kc - 1) / kc;
+}
+
+hipError_t launch_router(const RouterArgs& a0, hipStream_t s) {
+  RouterArgs a = a0;
+  const int sp0 = router_splits(a.T, a.D, a.E, a.num_cus);
+  const int kc = ((a.D / sp0 + 31) / 32) * 32;
+  a.splits = (a.D + kc - 1) / kc;
+  dim3 g1((a.T + 63) / 64, (a.E + 63) / 64, a.splits);
   if (a.act_bf16)
     hipLaunchKernelGGL(router_logits_kernel<true>, g1, dim3(256), 0, s, a.x, a.gate_w, a.logits,
-                       a.counts, a.T, a.D, a.E);
+                       a.counts, a.T, a.D, a.E, kc);
   else
     hipLaunchKernelGGL(router_logits_kernel<false>, g1, dim3(256), 0, s, a.x, a.gate_w, a.logits,
-                       a.counts, a.T, a.D, a.E);
+                       a.counts, a.T, a.D, a.E, kc);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (a.splits > 1) {
+    const int n = a.T * a.E;
+    hipLaunchKernelGGL(reduce_planes_kernel, dim3((n + 255) / 256), dim3(256), 0, s, a.logits, n, a.splits);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   hipLaunchKernelGGL(router_select_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -2,11 +2,14 @@
 // (OCP e4m3 with one fp32 scale per 128x128 block) weights, bf16 activations.
 //
 // With a few tokens per expert the layer is bound by reading each touched
-// expert's weights once from HBM. Each wave owns one work item -- 16 weight
-// rows of one problem (routed expert or the shared expert) over the whole K
-// extent, for up to 64 token rows -- and streams those rows straight from HBM
-// into MFMA operands without LDS: the weights are used by exactly one wave, and
-// the activation rows (at most 64 per item) stay in L2.
+// expert's weights once from HBM. A workgroup owns a sequence of work items:
+// one item is up to 16 token rows of one problem (routed expert or the shared
+// expert) against 64 of its weight rows over the whole K extent. Each of the
+// four waves streams its own 16 weight rows straight from HBM into MFMA
+// operands; the activation rows are shared by the four waves through a small
+// LDS ring. An expert with more than 16 rows in the call gets one item per 16
+// rows; those items are adjacent, so they run together and share the weight
+// lines through L2.
 //
 // v_mfma_f32_16x16x32_bf16: lane l supplies A[token l%16][8 k] and
 // B[8 k][weight row l%16] for k-group l/16. Within a 128-wide K chunk, lane
@@ -16,10 +19,20 @@
 // the 128-wide chunk is accumulated unscaled, then multiplied by its block
 // scale and added to the fp32 accumulator.
 //
-// Gate/up items pair 8 W_gate rows with the matching 8 W_up rows, so the SwiGLU
-// epilogue (h = SiLU(gate) * up, DeepSeek-V2 walkthrough page MoE code and the
-// SwiGLU expert of the architecture article, section 3.3) needs only a lane
-// swap. Down items write g * (h W_down^T) for 16 output columns.
+// Gate/up items: wave w takes 8 W_gate rows and the matching 8 W_up rows, so
+// the SwiGLU epilogue (h = SiLU(gate) * up, DeepSeek-V2 walkthrough page MoE
+// code and the SwiGLU expert of the architecture article, section 3.3) needs
+// only a lane swap. Down items write g * (h W_down^T) for 16 output columns
+// per wave.
+//
+// Latency: chunks are handled in groups of four. The weights and the
+// activations of group g+1 -- of this item, or the first group of the
+// workgroup's next item -- are requested before group g is multiplied; the
+// activations go through registers into the other half of the LDS ring, with
+// one barrier per group. The problem tables (item prefix, expert row offsets)
+// are cached in LDS, so finding an item's problem costs no global round trips.
+#include <type_traits>
+
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -40,147 +53,215 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
+namespace {
+
+constexpr int kU = 4;               // chunks per group
+constexpr int kALd = kST_KC + 8;    // LDS row length of an activation chunk (bf16), padded
+constexpr int kASlot = 16 * kALd;   // one chunk of 16 activation rows
+
+// One work item, as seen by one thread.
+struct Item {
+  const char* wptr;      // this lane's weight row at its k-group offset
+  const float* sptr;     // this lane's block-scale row (fp8)
+  const uint16_t* aptr;  // this thread's activation row (row tid/16, piece tid%16)
+  bool aval;             // that row is a valid row of the item
+  int nrows;             // valid rows (<= 16)
+  int nch;               // 128-wide K chunks
+  uint16_t* out;         // output row 0 of the item, at this wave's first column
+  const float* gate;     // gates from row 0 (routed down items), else null
+  int ldo;               // output row length
+};
+
+template <bool kFp8, int kMode>
+__device__ __forceinline__ Item setup_item(const ExpertGemmArgs& a, const int32_t* s_pre, const int32_t* s_off,
+                                           int item) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rr = lane & 15, q = lane >> 4;
+  Item it;
+  const int p = find_problem(s_pre, a.E, item);
+  const bool routed = p < a.E;
+  const int rows = routed ? s_off[p + 1] - s_off[p] : a.T;
+  const int row_base = routed ? s_off[p] : 0;
+  const int Hp = routed ? a.H : a.Hs;
+  const int ncols = (kMode == 0) ? Hp / kST_N1 : a.D / kST_N2;
+  const int local = item - s_pre[p];
+  const int m0 = (local / ncols) * kST_BM;
+  const int nb = local % ncols;
+  it.nrows = min(rows - m0, kST_BM);
+  const int K = (kMode == 0) ? a.D : Hp;
+  it.nch = K / kST_KC;
+  // this wave's weight rows: gate/up -> 8 gate + 8 up rows; down -> 16 rows
+  const int wcol = (kMode == 0) ? nb * kST_N1 + 8 * wave : nb * kST_N2 + 16 * wave;
+  const int wrows = (kMode == 0) ? 2 * Hp : a.D;
+  const int wrow = (kMode == 0) ? (rr < 8 ? wcol + rr : Hp + wcol + rr - 8) : wcol + rr;
+  const size_t welt = kFp8 ? 1 : 2;
+  const char* wbase = static_cast<const char*>(routed ? a.w : a.w_shared) +
+                      (routed ? (size_t)p * wrows * K * welt : 0);
+  it.wptr = wbase + (size_t)wrow * K * welt + (size_t)32 * q * welt;
+  it.sptr = nullptr;
+  if (kFp8) {
+    const int kb = K / kST_KC;
+    it.sptr = (routed ? a.w_scale + (size_t)p * (wrows / kST_KC) * kb : a.w_shared_scale) +
+              (size_t)(wrow / kST_KC) * kb;
+  }
+  // activations: thread tid loads row tid/16, 8 elements at (tid%16)*8 of each chunk
+  const int arow = tid >> 4;
+  it.aval = arow < it.nrows;
+  const int mm = m0 + (it.aval ? arow : 0);  // in-bounds row for masked threads
+  if (kMode == 0) {
+    const int tok = routed ? a.row_token[row_base + mm] : mm;
+    it.aptr = static_cast<const uint16_t*>(a.a) + (size_t)tok * a.D + (tid & 15) * 8;
+  } else {
+    it.aptr = routed ? static_cast<const uint16_t*>(a.a) + (size_t)(row_base + mm) * a.H + (tid & 15) * 8
+                     : static_cast<const uint16_t*>(a.a_shared) + (size_t)mm * a.Hs + (tid & 15) * 8;
+  }
+  if (kMode == 0) {
+    it.ldo = Hp;
+    it.out = (routed ? static_cast<uint16_t*>(a.c) + (size_t)(row_base + m0) * a.H
+                     : static_cast<uint16_t*>(a.c_shared) + (size_t)m0 * a.Hs) + wcol;
+    it.gate = nullptr;
+  } else {
+    it.ldo = a.D;
+    it.out = (routed ? static_cast<uint16_t*>(a.c) + (size_t)(row_base + m0) * a.D
+                     : static_cast<uint16_t*>(a.c_shared) + (size_t)m0 * a.D) + wcol;
+    it.gate = routed ? a.row_gate + row_base + m0 : nullptr;
+  }
+  return it;
+}
+
+}  // namespace
+
 template <bool kFp8, int kMode>  // kMode 0: gate/up + SwiGLU, 1: down + gate scale
 __global__ __launch_bounds__(256) void stream_gemm_kernel(ExpertGemmArgs a) {
-  const int lane = threadIdx.x & 63;
+  __shared__ int32_t s_pre[kMaxExperts + 2];
+  __shared__ int32_t s_off[kMaxExperts + 1];
+  __shared__ __attribute__((aligned(16))) uint16_t s_act[2 * kU * kASlot];  // two groups of chunks
+  for (int i = threadIdx.x; i < a.E + 2; i += 256) s_pre[i] = a.pre[i];
+  for (int i = threadIdx.x; i < a.E + 1; i += 256) s_off[i] = a.offsets[i];
+  __syncthreads();
+
+  const int tid = threadIdx.x, lane = tid & 63;
   const int rr = lane & 15, q = lane >> 4;
-  const int total = a.pre[a.E + 1];
-  const int n_waves = gridDim.x * 4;
-  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < total; item += n_waves) {
-    const int p = find_problem(a.pre, a.E, item);
-    const bool routed = p < a.E;
-    const int rows = routed ? a.offsets[p + 1] - a.offsets[p] : a.T;
-    const int row_base = routed ? a.offsets[p] : 0;
-    const int Hp = routed ? a.H : a.Hs;
-    const int ncols = (kMode == 0) ? Hp / kST_N1 : a.D / kST_N2;
-    const int local = item - a.pre[p];
-    const int m0 = (local / ncols) * kST_BM;
-    const int nb = local % ncols;
-    const int nrows = min(rows - m0, kST_BM);
-    const int K = (kMode == 0) ? a.D : Hp;
-    const int wrows = (kMode == 0) ? 2 * Hp : a.D;
+  const int total = s_pre[a.E + 1];
+  int item = blockIdx.x;
+  if (item >= total) return;  // uniform over the workgroup
 
-    // this lane's weight row
-    const int wrow = (kMode == 0) ? (rr < 8 ? nb * kST_N1 + rr : Hp + nb * kST_N1 + rr - 8)
-                                  : nb * kST_N2 + rr;
-    const size_t welt = kFp8 ? 1 : 2;
-    const char* wbase = static_cast<const char*>(routed ? a.w : a.w_shared) +
-                        (routed ? (size_t)p * wrows * K * welt : 0);
-    const char* wptr = wbase + (size_t)wrow * K * welt + (size_t)32 * q * welt;
-    const float* sptr = nullptr;
-    if (kFp8) {
-      const int kb = K / kST_KC;
-      sptr = (routed ? a.w_scale + (size_t)p * (wrows / kST_KC) * kb : a.w_shared_scale) +
-             (size_t)(wrow / kST_KC) * kb;
-    }
-    // activation rows for up to four 16-row blocks
-    const uint16_t* aptr[4];
-    bool aval[4];
+  constexpr int kWv = kFp8 ? 2 : 4;  // 16-byte weight loads per lane per chunk
+  constexpr size_t welt = kFp8 ? 1 : 2;
+  uint4 wv[2][kU][kWv];
+  float sc[2][kU];
+  uint4 pa[kU];  // this thread's activation pieces of the next group
+
+  auto load_group = [&](const Item& it, int g, uint4 (&w)[kU][kWv], float (&s)[kU]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      const int m = m0 + 16 * mb + rr;
-      aval[mb] = (16 * mb + rr) < nrows;
-      const int mm = aval[mb] ? m : m0;  // in-bounds row for masked lanes
-      if (kMode == 0) {
-        const int tok = routed ? a.row_token[row_base + mm] : mm;
-        aptr[mb] = static_cast<const uint16_t*>(a.a) + (size_t)tok * a.D + 32 * q;
-      } else {
-        aptr[mb] = routed ? static_cast<const uint16_t*>(a.a) + (size_t)(row_base + mm) * a.H + 32 * q
-                          : static_cast<const uint16_t*>(a.a_shared) + (size_t)mm * a.Hs + 32 * q;
-      }
-    }
-    const int nmb = (nrows + 15) >> 4;
-
-    f32x4 acc[4];
+    for (int u = 0; u < kU; ++u) {
+      const int c = min(g * kU + u, it.nch - 1);  // past the end: a valid chunk, unused
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < kWv; ++j)
+        w[u][j] = *reinterpret_cast<const uint4*>(it.wptr + (size_t)c * kST_KC * welt + 16 * j);
+      s[u] = kFp8 ? it.sptr[c] : 1.0f;
+      pa[u] = it.aval ? *reinterpret_cast<const uint4*>(it.aptr + (size_t)c * kST_KC) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  // activation pieces -> LDS ring half `set`
+  auto store_act = [&](int set) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      *reinterpret_cast<uint4*>(&s_act[(set * kU + u) * kASlot + (tid >> 4) * kALd + (tid & 15) * 8]) = pa[u];
+  };
 
-    constexpr int kWv = kFp8 ? 2 : 4;  // 16-byte weight loads per lane per chunk
-    auto chunk = [&](int kc, const uint4* wv) {
-      bf16x8 b[4];
+  Item cur = setup_item<kFp8, kMode>(a, s_pre, s_off, item);
+  load_group(cur, 0, wv[0], sc[0]);
+  store_act(0);
+  __syncthreads();
+  int aset = 0;  // ring half holding the current group's activations
+
+  while (true) {
+    const int ngr = (cur.nch + kU - 1) / kU;
+    const int next_item = item + gridDim.x;
+    const bool has_next = next_item < total;  // uniform over the workgroup
+    Item nxt = cur;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto chunk = [&](const uint4 (&w)[kWv], float scale, const uint16_t* sa) __attribute__((always_inline)) {
+      bf16x8 b[4], av[4];
+      const uint16_t* ap = sa + rr * kALd + 32 * q;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) av[j] = *reinterpret_cast<const bf16x8*>(ap + 8 * j);
       if (kFp8) {
-        b[0] = fp8x8_to_bf16(wv[0].x, wv[0].y);
-        b[1] = fp8x8_to_bf16(wv[0].z, wv[0].w);
-        b[2] = fp8x8_to_bf16(wv[1].x, wv[1].y);
-        b[3] = fp8x8_to_bf16(wv[1].z, wv[1].w);
+        b[0] = fp8x8_to_bf16(w[0].x, w[0].y);
+        b[1] = fp8x8_to_bf16(w[0].z, w[0].w);
+        b[2] = fp8x8_to_bf16(w[1].x, w[1].y);
+        b[3] = fp8x8_to_bf16(w[1].z, w[1].w);
+        f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j], b[j], t, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(t[i], scale, acc[i]);
       } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) b[j] = as_bf16x8(wv[j]);
-      }
-      const float scale = kFp8 ? sptr[kc / kST_KC] : 1.0f;
+        for (int j = 0; j < 4; ++j) b[j] = as_bf16x8(w[j]);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        if (mb < nmb) {
-          const uint4* ap = reinterpret_cast<const uint4*>(aptr[mb] + kc);
-          uint4 av[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) av[j] = aval[mb] ? ap[j] : make_uint4(0, 0, 0, 0);
-          if (kFp8) {
-            f32x4 t = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[j]), b[j], t, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mb][i] = fmaf(t[i], scale, acc[mb][i]);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              acc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(av[j]), b[j], acc[mb], 0, 0, 0);
-          }
-        }
+        for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[j], b[j], acc, 0, 0, 0);
       }
     };
-    // four chunks per step: all their weight loads are issued before any use,
-    // so each wave keeps 4 chunks of its rows in flight
-    constexpr int kU = 4;
-    int kc = 0;
-    for (; kc + kU * kST_KC <= K; kc += kU * kST_KC) {
-      uint4 wv[kU][kWv];
+    // group g from register slot GS: first request the following group (or
+    // the next item's first group) into the other slot, then multiply, then
+    // park the requested activations in the other ring half
+    auto group = [&](int g, auto gs_c) __attribute__((always_inline)) {
+      constexpr int GS = decltype(gs_c)::value;
+      bool req = true;
+      if (g + 1 < ngr) {
+        load_group(cur, g + 1, wv[GS ^ 1], sc[GS ^ 1]);
+      } else if (has_next) {
+        nxt = setup_item<kFp8, kMode>(a, s_pre, s_off, next_item);
+        load_group(nxt, 0, wv[GS ^ 1], sc[GS ^ 1]);
+      } else {
+        req = false;
+      }
 #pragma unroll
       for (int u = 0; u < kU; ++u)
-#pragma unroll
-        for (int j = 0; j < kWv; ++j)
-          wv[u][j] = *reinterpret_cast<const uint4*>(wptr + (size_t)(kc + u * kST_KC) * welt + 16 * j);
-#pragma unroll
-      for (int u = 0; u < kU; ++u) chunk(kc + u * kST_KC, wv[u]);
+        if (g * kU + u < cur.nch) chunk(wv[GS][u], sc[GS][u], &s_act[(aset * kU + u) * kASlot]);
+      if (req) store_act(aset ^ 1);
+      __syncthreads();
+      aset ^= 1;
+    };
+    int g = 0;
+    for (; g + 1 < ngr; g += 2) {
+      group(g, std::integral_constant<int, 0>{});
+      group(g + 1, std::integral_constant<int, 1>{});
     }
-    for (; kc < K; kc += kST_KC) {
-      uint4 wv[kWv];
+    if (g < ngr) {
+      group(g, std::integral_constant<int, 0>{});
+      // the next item's first group landed in register slot 1: move it to slot 0
 #pragma unroll
-      for (int j = 0; j < kWv; ++j) wv[j] = *reinterpret_cast<const uint4*>(wptr + (size_t)kc * welt + 16 * j);
-      chunk(kc, wv);
+      for (int u = 0; u < kU; ++u) {
+#pragma unroll
+        for (int j = 0; j < kWv; ++j) wv[0][u][j] = wv[1][u][j];
+        sc[0][u] = sc[1][u];
+      }
     }
 
     // epilogue: element i of lane l is token row 4*(l/16)+i, weight row l%16
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * mb + 4 * q + i;  // row within this pass
-        const float v = acc[mb][i];
-        if (kMode == 0) {
-          const float up = __shfl_xor(v, 8, kWave);
-          if (rr < 8 && m < nrows) {
-            const float h = silu_fast(v) * up;
-            uint16_t* hp = routed ? static_cast<uint16_t*>(a.c) + (size_t)(row_base + m0 + m) * a.H
-                                  : static_cast<uint16_t*>(a.c_shared) + (size_t)(m0 + m) * a.Hs;
-            hp[nb * kST_N1 + rr] = f32_to_bf16(h);
-          }
-        } else if (m < nrows) {
-          if (routed) {
-            const float g = a.row_gate[row_base + m0 + m];
-            static_cast<uint16_t*>(a.c)[(size_t)(row_base + m0 + m) * a.D + nb * kST_N2 + rr] = f32_to_bf16(g * v);
-          } else {
-            static_cast<uint16_t*>(a.c_shared)[(size_t)(m0 + m) * a.D + nb * kST_N2 + rr] = f32_to_bf16(v);
-          }
-        }
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * q + i;
+      const float v = acc[i];
+      if (kMode == 0) {
+        const float up = __shfl_xor(v, 8, kWave);
+        if (rr < 8 && m < cur.nrows) cur.out[(size_t)m * cur.ldo + rr] = f32_to_bf16(silu_fast(v) * up);
+      } else if (m < cur.nrows) {
+        const float gv = cur.gate ? cur.gate[m] : 1.0f;
+        cur.out[(size_t)m * cur.ldo + rr] = f32_to_bf16(gv * v);
       }
     }
+    if (!has_next) break;
+    item = next_item;
+    cur = nxt;
   }
 }
 
-hipError_t launch_stream_gateup(const ExpertGemmArgs& a, int fp8, int n_waves, hipStream_t s) {
-  const int blocks = (n_waves + 3) / 4;
+hipError_t launch_stream_gateup(const ExpertGemmArgs& a, int fp8, int blocks, hipStream_t s) {
   if (fp8)
     hipLaunchKernelGGL((stream_gemm_kernel<true, 0>), dim3(blocks), dim3(256), 0, s, a);
   else
@@ -188,8 +269,7 @@ hipError_t launch_stream_gateup(const ExpertGemmArgs& a, int fp8, int n_waves, h
   return hipGetLastError();
 }
 
-hipError_t launch_stream_down(const ExpertGemmArgs& a, int fp8, int n_waves, hipStream_t s) {
-  const int blocks = (n_waves + 3) / 4;
+hipError_t launch_stream_down(const ExpertGemmArgs& a, int fp8, int blocks, hipStream_t s) {
   if (fp8)
     hipLaunchKernelGGL((stream_gemm_kernel<true, 1>), dim3(blocks), dim3(256), 0, s, a);
   else
