@@ -16,9 +16,10 @@
 // Down GEMM: Y[row] = g_row * (h[row] W_down^T), bf16, 256 output columns per
 // tile; the combine sums the K rows of each token in a fixed order.
 //
-// Tile 256 x 256, K step 64, 4 waves as 2 x 2, each wave 128 x 128 as 4 x 4
-// blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane, held in
-// AGPRs). A wave's four 32-row blocks are interleaved with the other row-wave's
+// Tile 256 x 256, K step 64, 8 waves (two per SIMD) as 2 x 4, each wave
+// 128 x 64 as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators
+// per lane, held in AGPRs); two waves per SIMD keep both the matrix pipe and the
+// LDS busy while the other waits. A wave's four 32-row blocks are interleaved with the other row-wave's
 // (blocks wm, wm+2, wm+4, wm+6), so a ragged last tile of an expert splits its
 // valid rows evenly; the tile body is instantiated per count of valid row
 // blocks, so blocks with no valid row cost no MFMA and the K loop stays
@@ -27,8 +28,8 @@
 // that the 16-byte fragment reads of consecutive rows hit distinct banks): the
 // next K step is loaded into registers while the current one is multiplied,
 // then written to the other buffer; one barrier per K step.
-// Blocks are mapped so that consecutive tiles (which share weight columns or
-// token rows) land on the same XCD and its L2.
+// Blocks are mapped so that runs of consecutive tiles (which share token rows)
+// land on one XCD and its L2, with runs spread round-robin over the XCDs.
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -36,6 +37,9 @@ namespace moe {
 namespace {
 constexpr int BM = kGB_BM, BN = 256, BK = kGB_BK, LDW = BK + 8;
 constexpr int kRows = BM + BN;  // LDS rows per buffer: A then B
+constexpr int kRun = 16;        // consecutive tiles per XCD run
+constexpr int kNC = 2;          // 32-column blocks per wave
+constexpr int kLd = 8;          // 16-byte global loads per thread per K step
 
 struct Tile {
   const uint16_t* a_rows;  // GEMM1: x; GEMM2: h of this problem (row 0 = row_base)
@@ -57,11 +61,11 @@ struct Tile {
 template <int kMode, int NRB>
 __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows * LDW]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int c8 = tid & 7, r0 = tid >> 3;
 
-  // loader: 16 chunks of 16 bytes per thread per K step, rows r0 + 32*j of
-  // the 512 LDS rows (j < 8: A rows, j >= 8: B rows), read as buffer loads:
+  // loader: 8 chunks of 16 bytes per thread per K step, rows r0 + 64*j of
+  // the 512 LDS rows (j < 4: A rows, j >= 4: B rows), read as buffer loads:
   // a 32-bit byte offset per row in a VGPR, the K position in a scalar offset.
   // Rows past the tile's valid rows (and columns past D) read a valid row
   // instead: their results are never stored, so every load is unconditional.
@@ -69,57 +73,57 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
       const_cast<uint16_t*>(t.a_rows), (short)0, t.a_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(t.w), (short)0, t.w_bytes, 0x00020000);
-  uint32_t voff[16];
+  uint32_t voff[kLd];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int m = r0 + 32 * j;
+  for (int j = 0; j < kLd / 2; ++j) {
+    const int m = r0 + 64 * j;
     const int mm = t.m0 + (m < t.vrows ? m : 0);
     const int row = (kMode == 0 && t.tok != nullptr) ? t.tok[mm] : mm;
     voff[j] = ((uint32_t)row * (uint32_t)t.lda + c8 * 8) * 2u;
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int b = r0 + 32 * j;  // 0..255
+  for (int j = 0; j < kLd / 2; ++j) {
+    const int b = r0 + 64 * j;  // 0..255
     int wrow = (kMode == 0) ? (b < 128 ? t.nt * 128 + b : t.Hp + t.nt * 128 + b - 128) : t.nt * BN + b;
     if (kMode == 1 && wrow >= t.D) wrow = 0;
-    voff[8 + j] = ((uint32_t)wrow * (uint32_t)t.K + c8 * 8) * 2u;
+    voff[kLd / 2 + j] = ((uint32_t)wrow * (uint32_t)t.K + c8 * 8) * 2u;
   }
   auto gload = [&](int j, int k0) __attribute__((always_inline)) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(j < 8 ? ra : rb, voff[j], k0 * 2, 0));
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(j < kLd / 2 ? ra : rb, voff[j], k0 * 2, 0));
   };
 
-  f32x16 acc[NRB > 0 ? NRB : 1][4];
+  f32x16 acc[NRB > 0 ? NRB : 1][kNC];
 #pragma unroll
   for (int i = 0; i < NRB; ++i)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < kNC; ++c)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][c][e] = 0.f;
 
-  // LDS B rows of this wave's four 32-column blocks
-  int bcol[4];
+  // LDS B rows of this wave's two 32-column blocks (gate/up: one W_gate block
+  // and the matching W_up block)
+  int bcol[kNC];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    bcol[c] = (kMode == 0) ? ((c < 2) ? 64 * wn + 32 * c : 128 + 64 * wn + 32 * (c - 2)) : 128 * wn + 32 * c;
+  for (int c = 0; c < kNC; ++c) bcol[c] = (kMode == 0) ? 128 * c + 32 * wn : 64 * wn + 32 * c;
   const int lr = lane & 31, lk = (lane >> 5) * 8;
 
-  uint4 pf[16];
+  uint4 pf[kLd];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) pf[j] = gload(j, 0);
+  for (int j = 0; j < kLd; ++j) pf[j] = gload(j, 0);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) *reinterpret_cast<uint4*>(&smem[0][(r0 + 32 * j) * LDW + c8 * 8]) = pf[j];
+  for (int j = 0; j < kLd; ++j) *reinterpret_cast<uint4*>(&smem[0][(r0 + 64 * j) * LDW + c8 * 8]) = pf[j];
   __syncthreads();
 
   // Fragments are double-buffered across the four 16-wide substeps of a K
   // step: the LDS reads of substep kk+1 are issued before the MFMAs of
   // substep kk, so their latency hides behind those MFMAs.
   constexpr int NA = NRB > 0 ? NRB : 1;
-  bf16x8 fb[2][4], fa[2][NA];
+  bf16x8 fb[2][kNC], fa[2][NA];
   auto read_frags = [&](const uint16_t* sbuf, int kk, int slot) __attribute__((always_inline)) {
     const uint16_t* sA = sbuf;
     const uint16_t* sB = sbuf + BM * LDW;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int c = 0; c < kNC; ++c)
       fb[slot][c] = *reinterpret_cast<const bf16x8*>(&sB[(bcol[c] + lr) * LDW + kk + lk]);
 #pragma unroll
     for (int i = 0; i < NRB; ++i)
@@ -129,7 +133,7 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
 #pragma unroll
     for (int i = 0; i < NRB; ++i)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < kNC; ++c)
         acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][c], acc[i][c], 0, 0, 0);
   };
 
@@ -138,9 +142,14 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
   // of the last two substeps, so the LDS writes overlap the matrix work.
   auto store_half = [&](int buf, int h) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 8 * h; j < 8 * h + 8; ++j)
-      *reinterpret_cast<uint4*>(&smem[buf][(r0 + 32 * j) * LDW + c8 * 8]) = pf[j];
+    for (int j = (kLd / 2) * h; j < (kLd / 2) * (h + 1); ++j)
+      *reinterpret_cast<uint4*>(&smem[buf][(r0 + 64 * j) * LDW + c8 * 8]) = pf[j];
   };
+  // instruction counts per substep, for the interleave below
+  constexpr int nr = kNC + NRB, nm = kNC * NRB, nw = kLd / 2;
+  constexpr int p1 = nr < nm ? nr : nm;              // (MFMA, LDS read) pairs
+  constexpr int p2 = nw < nm - p1 ? nw : nm - p1;    // then (MFMA, LDS write) pairs
+  constexpr int p3 = nw < nm ? nw : nm;              // substep 3: (MFMA, LDS write) pairs
 
   const int nk = t.K / BK;
   read_frags(smem[0], 0, 0);
@@ -150,18 +159,19 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
     // the step body has no branch (and the scheduler sees one region).
     const int knext = (kt + 1 < nk ? kt + 1 : kt) * BK;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) pf[j] = gload(j, knext);
+    for (int j = 0; j < kLd; ++j) pf[j] = gload(j, knext);
     // substeps 0, 1: next fragments interleaved with the MFMAs
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       read_frags(smem[cur], 16 * (s + 1), (s + 1) & 1);
       mfmas(s & 1);
 #pragma unroll
-      for (int q = 0; q < 4 + NRB; ++q) {
+      for (int q = 0; q < p1; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4 * NRB, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, nr - p1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, nm - p1, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     // substep 2: last fragments, then the first half of the next tile
@@ -169,26 +179,29 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
     store_half(cur ^ 1, 0);
     mfmas(0);
 #pragma unroll
-    for (int q = 0; q < 4 + NRB; ++q) {
+    for (int q = 0; q < p1; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < p2; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NRB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, nr - p1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, nw - p2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, nm - p1 - p2, 0);
     __builtin_amdgcn_sched_barrier(0);
     // substep 3: second half of the next tile
     store_half(cur ^ 1, 1);
     mfmas(1);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < p3; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NRB, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, nw - p3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, nm - p3, 0);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     read_frags(smem[cur ^ 1], 0, 0);
@@ -205,16 +218,13 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
       const int mr = t.m0 + m;
       uint16_t* cp = t.c + (size_t)mr * t.ldc;
       if (kMode == 0) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const float h = silu_fast(acc[i][c][e]) * acc[i][c + 2][e];
-          cp[t.nt * 128 + 64 * wn + 32 * c + lr] = f32_to_bf16(h);
-        }
+        const float h = silu_fast(acc[i][0][e]) * acc[i][1][e];
+        cp[t.nt * 128 + 32 * wn + lr] = f32_to_bf16(h);
       } else {
         const float g = t.gate ? t.gate[mr] : 1.0f;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int col = t.nt * BN + 128 * wn + 32 * c + lr;
+        for (int c = 0; c < kNC; ++c) {
+          const int col = t.nt * BN + 64 * wn + 32 * c + lr;
           if (col < t.D) cp[col] = f32_to_bf16(g * acc[i][c][e]);
         }
       }
@@ -223,15 +233,18 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
 }
 
 template <int kMode>  // 0: gate/up + SwiGLU, 1: down + gate scale
-__global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(ExpertGemmArgs a) {
+__global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][kRows * LDW];
 
+  // Tiles come in runs of kRun consecutive tiles (one row block of a problem
+  // against all its column tiles, sharing the gathered token rows); run r goes
+  // to XCD r % 8, so every XCD gets a mix of experts and of the shared
+  // expert's tiles while a run's blocks share that XCD's L2. Blocks are handed
+  // to the XCDs round-robin (block b runs on XCD b % 8).
   const int total = a.pre[a.E + 1];
-  const int chunk = (total + 7) >> 3;
   const int bid = blockIdx.x;
   const int slot = bid >> 3;
-  if (slot >= chunk) return;
-  const int tile = (bid & 7) * chunk + slot;
+  const int tile = ((slot / kRun) * 8 + (bid & 7)) * kRun + slot % kRun;
   if (tile >= total) return;
 
   const int p = find_problem(a.pre, a.E, tile);
@@ -273,7 +286,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
   }
 
   // valid 32-row blocks of this wave: wm + 2*i for i < nrb
-  const int wm = (threadIdx.x >> 6) >> 1;
+  const int wm = (threadIdx.x >> 6) >> 2;
   int nrb = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) nrb += (32 * (wm + 2 * i) < t.vrows) ? 1 : 0;
@@ -286,17 +299,23 @@ __global__ __launch_bounds__(256) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
   }
 }
 
+// blocks covering every tile index below max_items under the run mapping
+int grouped_blocks(int max_items) {
+  const int runs = (max_items + kRun - 1) / kRun;
+  return ((runs + 7) / 8) * 8 * kRun;
+}
+
 hipError_t launch_grouped_gateup_bf16(const ExpertGemmArgs& a, hipStream_t s) {
-  const int blocks = ((a.max_items + 7) / 8) * 8;
+  const int blocks = grouped_blocks(a.max_items);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<0>, dim3(blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<0>, dim3(blocks), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_grouped_down_bf16(const ExpertGemmArgs& a, hipStream_t s) {
-  const int blocks = ((a.max_items + 7) / 8) * 8;
+  const int blocks = grouped_blocks(a.max_items);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<1>, dim3(blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<1>, dim3(blocks), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
