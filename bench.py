@@ -172,6 +172,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=16)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run one plain 1 GiB device-to-device copy first (a known-size reference "
+                         "for hardware byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -189,6 +192,13 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
 
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("copy probe: 1 GiB read + 1 GiB written")
     res = run_prefill(args, torch, M, MI)
     cfg = res["cfg"]
     line = {

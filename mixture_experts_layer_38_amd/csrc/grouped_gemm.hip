@@ -28,8 +28,10 @@
 // that the 16-byte fragment reads of consecutive rows hit distinct banks): the
 // next K step is loaded into registers while the current one is multiplied,
 // then written to the other buffer; one barrier per K step.
-// Blocks are mapped so that runs of consecutive tiles (which share token rows)
-// land on one XCD and its L2, with runs spread round-robin over the XCDs.
+// Blocks are mapped so that runs of consecutive tiles land on one XCD and its
+// L2, with runs spread round-robin over the XCDs. Gate/up tiles are ordered
+// column-tile major (the two or three row blocks of an expert that read the
+// same weight slice run side by side); down tiles row-block major.
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -37,7 +39,8 @@ namespace moe {
 namespace {
 constexpr int BM = kGB_BM, BN = 256, BK = kGB_BK, LDW = BK + 8;
 constexpr int kRows = BM + BN;  // LDS rows per buffer: A then B
-constexpr int kRun = 16;        // consecutive tiles per XCD run
+// consecutive tiles per XCD run, per GEMM
+template <int kMode> constexpr int run_len() { return kMode == 0 ? 32 : 16; }
 constexpr int kNC = 2;          // 32-column blocks per wave
 constexpr int kLd = 8;          // 16-byte global loads per thread per K step
 
@@ -236,14 +239,14 @@ template <int kMode>  // 0: gate/up + SwiGLU, 1: down + gate scale
 __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][kRows * LDW];
 
-  // Tiles come in runs of kRun consecutive tiles (one row block of a problem
-  // against all its column tiles, sharing the gathered token rows); run r goes
-  // to XCD r % 8, so every XCD gets a mix of experts and of the shared
-  // expert's tiles while a run's blocks share that XCD's L2. Blocks are handed
-  // to the XCDs round-robin (block b runs on XCD b % 8).
+  // Tiles come in runs of kRun consecutive tiles; run r goes to XCD r % 8,
+  // so every XCD gets a mix of experts and of the shared expert's tiles while
+  // a run's blocks share that XCD's L2. Blocks are handed to the XCDs
+  // round-robin (block b runs on XCD b % 8).
   const int total = a.pre[a.E + 1];
   const int bid = blockIdx.x;
   const int slot = bid >> 3;
+  constexpr int kRun = run_len<kMode>();
   const int tile = ((slot / kRun) * 8 + (bid & 7)) * kRun + slot % kRun;
   if (tile >= total) return;
 
@@ -256,8 +259,14 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
   t.D = a.D;
   const int ntn = (kMode == 0) ? t.Hp / kG1_BNH : (a.D + BN - 1) / BN;  // D % 128 == 0: last tile may be half
   const int local = tile - a.pre[p];
-  t.m0 = (local / ntn) * BM;
-  t.nt = local % ntn;
+  if (kMode == 0) {  // column-tile major: the row blocks of one weight slice run together
+    const int nmt = (rows + BM - 1) / BM;
+    t.m0 = (local % nmt) * BM;
+    t.nt = local / nmt;
+  } else {           // row-block major: one row block against all its column tiles
+    t.m0 = (local / ntn) * BM;
+    t.nt = local % ntn;
+  }
   t.K = (kMode == 0) ? a.D : t.Hp;
   t.vrows = min(rows - t.m0, BM);
   if (kMode == 0) {
@@ -300,20 +309,20 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
 }
 
 // blocks covering every tile index below max_items under the run mapping
-int grouped_blocks(int max_items) {
-  const int runs = (max_items + kRun - 1) / kRun;
-  return ((runs + 7) / 8) * 8 * kRun;
+int grouped_blocks(int max_items, int run) {
+  const int runs = (max_items + run - 1) / run;
+  return ((runs + 7) / 8) * 8 * run;
 }
 
 hipError_t launch_grouped_gateup_bf16(const ExpertGemmArgs& a, hipStream_t s) {
-  const int blocks = grouped_blocks(a.max_items);
+  const int blocks = grouped_blocks(a.max_items, run_len<0>());
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(grouped_gemm_bf16_kernel<0>, dim3(blocks), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_grouped_down_bf16(const ExpertGemmArgs& a, hipStream_t s) {
-  const int blocks = grouped_blocks(a.max_items);
+  const int blocks = grouped_blocks(a.max_items, run_len<1>());
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(grouped_gemm_bf16_kernel<1>, dim3(blocks), dim3(512), 0, s, a);
   return hipGetLastError();
