@@ -238,6 +238,8 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
 template <int kMode>  // 0: gate/up + SwiGLU, 1: down + gate scale
 __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][kRows * LDW];
+  __shared__ int32_t s_pre[kMaxExperts + 2];
+  __shared__ int32_t s_off[kMaxExperts + 1];
 
   // Tiles come in runs of kRun consecutive tiles; run r goes to XCD r % 8,
   // so every XCD gets a mix of experts and of the shared expert's tiles while
@@ -250,15 +252,19 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
   const int tile = ((slot / kRun) * 8 + (bid & 7)) * kRun + slot % kRun;
   if (tile >= total) return;
 
-  const int p = find_problem(a.pre, a.E, tile);
+  // problem tables into LDS: one round trip, then the search stays on chip
+  for (int i = threadIdx.x; i < a.E + 2; i += blockDim.x) s_pre[i] = a.pre[i];
+  for (int i = threadIdx.x; i < a.E + 1; i += blockDim.x) s_off[i] = a.offsets[i];
+  __syncthreads();
+  const int p = find_problem(s_pre, a.E, tile);
   const bool routed = p < a.E;
-  const int rows = routed ? a.offsets[p + 1] - a.offsets[p] : a.T;
-  const int row_base = routed ? a.offsets[p] : 0;
+  const int rows = routed ? s_off[p + 1] - s_off[p] : a.T;
+  const int row_base = routed ? s_off[p] : 0;
   Tile t;
   t.Hp = routed ? a.H : a.Hs;
   t.D = a.D;
   const int ntn = (kMode == 0) ? t.Hp / kG1_BNH : (a.D + BN - 1) / BN;  // D % 128 == 0: last tile may be half
-  const int local = tile - a.pre[p];
+  const int local = tile - s_pre[p];
   if (kMode == 0) {  // column-tile major: the row blocks of one weight slice run together
     const int nmt = (rows + BM - 1) / BM;
     t.m0 = (local % nmt) * BM;
