@@ -16,6 +16,7 @@ struct moe_cfg {
   size_t ws_bytes;
   char* ws;
   float* logits;
+  uint16_t* w_split;
   int32_t* idx;
   float* gate;
   int32_t* counts;
@@ -163,6 +164,7 @@ moe_status moe_cfg_create(const moe_params* p, moe_cfg** out) {
   // partial-logit planes: router_splits(T) * T <= 32 * CUs + T for every T
   const size_t lg = (size_t)32 * c->num_cus + Tm;
   const size_t o_logits = take(lg * E * 4), o_idx = take(Tm * K * 4), o_gate = take(Tm * K * 4);
+  const size_t o_wsplit = (p->act_dtype == MOE_BF16) ? take(3 * E * D * 2) : 0;
   const size_t o_counts = take(E * 4), o_offsets = take((E + 1) * 4), o_cursor = take(E * 4);
   const size_t o_pre1 = take((E + 2) * 4), o_pre2 = take((E + 2) * 4);
   const size_t o_rt = take(Tm * K * 4), o_rg = take(Tm * K * 4), o_sr = take(Tm * K * 4);
@@ -175,6 +177,7 @@ moe_status moe_cfg_create(const moe_params* p, moe_cfg** out) {
     return MOE_ERR_OOM;
   }
   c->logits = (float*)(c->ws + o_logits);
+  c->w_split = (p->act_dtype == MOE_BF16) ? (uint16_t*)(c->ws + o_wsplit) : nullptr;
   c->idx = (int32_t*)(c->ws + o_idx);
   c->gate = (float*)(c->ws + o_gate);
   c->counts = (int32_t*)(c->ws + o_counts);
@@ -271,6 +274,7 @@ moe_status moe_router_forward(moe_cfg* c, const void* x, int T, const float* gat
   r.act_bf16 = c->p.act_dtype == MOE_BF16; r.score_fn = c->p.score_fn; r.norm = c->p.norm_topk;
   r.rsf = c->p.routed_scaling_factor;
   r.num_cus = c->num_cus;
+  r.w_split = c->w_split;
   hipError_t e = launch_router(r, s);
   return e == hipSuccess ? MOE_OK : hip_fail(c, e);
 }
@@ -331,6 +335,7 @@ moe_status moe_layer_forward(moe_cfg* c, const void* x, int T, const float* gate
   r.act_bf16 = p.act_dtype == MOE_BF16; r.score_fn = p.score_fn; r.norm = p.norm_topk;
   r.rsf = p.routed_scaling_factor;
   r.num_cus = c->num_cus;
+  r.w_split = c->w_split;
   if ((e = launch_router(r, s)) != hipSuccess) return hip_fail(c, e);
   mark(c, 1, s);
 

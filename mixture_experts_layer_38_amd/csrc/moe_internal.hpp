@@ -104,8 +104,11 @@ struct RouterArgs {
   int norm;
   float rsf;
   int num_cus;
-  int splits;  // set by launch_router
+  int splits;           // set by launch_router
+  uint16_t* w_split;    // [3][E][D] bf16 planes of gate_w (bf16 activations), or null
 };
+// from this many tokens on, bf16 activations take the bf16x3 logits kernel
+constexpr int kRouterX3MinTokens = 512;
 // number of partial-logit planes launch_router uses for T tokens
 int router_splits(int T, int D, int E, int num_cus);
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);

@@ -1,5 +1,6 @@
-// Router: fp32 logits on fp32 MFMA, then per-token scoring and group-limited
-// top-K selection in wavefront registers.
+// Router: fp32 logits (fp32 MFMA, or bf16 MFMA on exact bf16x3 weight splits
+// for bf16 activations), then per-token scoring and group-limited top-K
+// selection in wavefront registers.
 //
 // Follows the MoEGate forward of the DeepSeek-V2 walkthrough page (fp32 linear
 // map, softmax, greedy or group-limited greedy top-K) and the selection-only
@@ -109,6 +110,140 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
     }
   }
 }
+
+// ---------------------------------------------------------------------------
+// bf16 activations: the same fp32 logits on bf16 MFMA.
+// Each fp32 gate weight is split exactly into three bf16 terms,
+// w = hi + mid + lo: hi is w with its significand cut to 8 bits, mid the
+// remainder cut likewise, lo what is left (at most 8 significant bits, so
+// exactly a bf16). A product of two bf16 values is exact in fp32, so
+// x.w = x.hi + x.mid + x.lo is an fp32-accumulated dot product of exact
+// products, on the bf16 matrix cores (3x the work, 16x the fp32 MFMA rate).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void split_gate_w_kernel(const float* __restrict__ w,
+                                                           uint16_t* __restrict__ out, size_t n4) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;  // four weights per thread
+  if (i >= n4) return;
+  const float4 v = reinterpret_cast<const float4*>(w)[i];
+  const float f[4] = {v.x, v.y, v.z, v.w};
+  uint32_t h[4], m[4], l[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t hb = __float_as_uint(f[j]) & 0xFFFF0000u;
+    const float r = f[j] - __uint_as_float(hb);  // exact
+    const uint32_t mb = __float_as_uint(r) & 0xFFFF0000u;
+    const float q = r - __uint_as_float(mb);     // exact, at most 8 significant bits
+    h[j] = hb >> 16;
+    m[j] = mb >> 16;
+    l[j] = __float_as_uint(q) >> 16;
+  }
+  const size_t n = n4 * 4;
+  uint2* o = reinterpret_cast<uint2*>(out);
+  o[i] = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+  o[n / 4 + i] = make_uint2(m[0] | (m[1] << 16), m[2] | (m[3] << 16));
+  o[n / 2 + i] = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+}
+
+// Tile: 128 tokens x 128 experts per workgroup, K step 64, LDS double-buffered.
+// Wave w owns experts 32w..32w+31 of the tile for all 128 tokens (4 row blocks
+// of v_mfma_f32_32x32x16_bf16), so each activation fragment read from LDS feeds
+// the three weight planes. Lane l supplies row l%32 and k 8*(l/32)..+7 of each
+// 16-wide K slice; output element i of lane l is row 8*(i/4)+4*(l/32)+i%4,
+// column l%32. blockIdx.y selects a K split (own logits plane, as above).
+constexpr int kX3_BT = 128, kX3_BE = 128, kX3_BK = 64, kX3_LD = kX3_BK + 8;
+
+__global__ __launch_bounds__(256) void router_logits_x3_kernel(const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ wsplit,
+                                                               float* __restrict__ logits,
+                                                               int32_t* __restrict__ counts, int T, int D,
+                                                               int E, int kc, int n_et, int n_tiles) {
+  constexpr int kTile = kX3_BT * kX3_LD;
+  __shared__ __attribute__((aligned(16))) uint16_t sm[2][4][kTile];  // [buffer][x, hi, mid, lo]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x;
+  if (b == 0 && blockIdx.y == 0)
+    for (int e = tid; e < E; e += 256) counts[e] = 0;  // histogram of the select kernel
+  // blocks b and b+8 run on the same XCD; give them the two expert tiles of one token tile
+  const int pos = (b / 16) * 16 + (b % 8) * 2 + (b / 8) % 2;
+  if (pos >= n_tiles) return;
+  const int t0 = (pos / n_et) * kX3_BT, e0 = (pos % n_et) * kX3_BE;
+  const int kbeg = blockIdx.y * kc, kend = min(D, kbeg + kc);
+  const int nsteps = (kend - kbeg) / kX3_BK;
+  logits += (size_t)blockIdx.y * T * E;
+
+  // loader: row lr + 32*i, 8 columns at lc (4 rows of x and of each plane per thread)
+  const int lr = tid >> 3, lc = (tid & 7) * 8;
+  const uint16_t* gx = x + (size_t)min(t0 + lr, T - 1) * D + lc;
+  const uint16_t* gw = wsplit + (size_t)min(e0 + lr, E - 1) * D + lc;
+  size_t ox[4], ow[4];  // element offsets of the thread's rows (clamped into the operands)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ox[i] = (size_t)(min(t0 + lr + 32 * i, T - 1) - min(t0 + lr, T - 1)) * D;
+    ow[i] = (size_t)(min(e0 + lr + 32 * i, E - 1) - min(e0 + lr, E - 1)) * D;
+  }
+  const size_t plane = (size_t)E * D;
+  uint4 px[4], pw[12];
+#define X3_LOAD(k0)                                                                             \
+  {                                                                                             \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i) px[i] =                                       \
+        *reinterpret_cast<const uint4*>(gx + ox[i] + (k0));                                     \
+    _Pragma("unroll") for (int j = 0; j < 12; ++j) pw[j] =                                      \
+        *reinterpret_cast<const uint4*>(gw + (j >> 2) * plane + ow[j & 3] + (k0));              \
+  }
+#define X3_STORE(bf)                                                                            \
+  {                                                                                             \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                               \
+        *reinterpret_cast<uint4*>(&sm[bf][0][(lr + 32 * i) * kX3_LD + lc]) = px[i];             \
+    _Pragma("unroll") for (int j = 0; j < 12; ++j)                                              \
+        *reinterpret_cast<uint4*>(&sm[bf][1 + (j >> 2)][(lr + 32 * (j & 3)) * kX3_LD + lc]) = pw[j]; \
+  }
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
+
+  const int fr = lane & 31, fk = 8 * (lane >> 5);
+  if (nsteps > 0) {
+    X3_LOAD(kbeg);
+    X3_STORE(0);
+  }
+  __syncthreads();
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    // branch-free: the last step reloads its own K slice into the idle buffer
+    X3_LOAD(kbeg + min(st + 1, nsteps - 1) * kX3_BK);
+#pragma unroll
+    for (int ks = 0; ks < kX3_BK / 16; ++ks) {
+      bf16x8 bw[3], ax[4];
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+        bw[p] = *reinterpret_cast<const bf16x8*>(&sm[buf][1 + p][(32 * wave + fr) * kX3_LD + 16 * ks + fk]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        ax[m] = *reinterpret_cast<const bf16x8*>(&sm[buf][0][(32 * m + fr) * kX3_LD + 16 * ks + fk]);
+#pragma unroll
+      for (int p = 2; p >= 0; --p)  // smallest terms first
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ax[m], bw[p], acc[m], 0, 0, 0);
+    }
+    X3_STORE(buf ^ 1);
+    __syncthreads();
+  }
+  const int e = e0 + 32 * wave + fr;
+  if (e < E) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int t = t0 + 32 * m + 8 * (i / 4) + 4 * (lane >> 5) + i % 4;
+        if (t < T) logits[(size_t)t * E + e] = acc[m][i];
+      }
+  }
+}
+#undef X3_LOAD
+#undef X3_STORE
 
 // ---------------------------------------------------------------------------
 // Per-token scoring and selection; one wave per token, expert e = lane + 64*j.
@@ -240,20 +375,47 @@ int router_splits(int T, int D, int E, int num_cus) {
   return (D + kc - 1) / kc;
 }
 
+// K splits of the bf16x3 kernel: about one workgroup per CU, and never more
+// than 32*num_cus/T + 1 planes (the partial-logit workspace holds
+// 32*num_cus + T rows).
+static int router_x3_kc(int T, int D, int E, int num_cus) {
+  const int tiles = ((T + kX3_BT - 1) / kX3_BT) * ((E + kX3_BE - 1) / kX3_BE);
+  int sp = (num_cus + tiles - 1) / tiles;
+  const int cap = 32 * num_cus / T + 1;
+  sp = sp > cap ? cap : sp;
+  sp = sp > D / kX3_BK ? D / kX3_BK : sp;
+  sp = sp < 1 ? 1 : sp;
+  return ((D / sp + kX3_BK - 1) / kX3_BK) * kX3_BK;
+}
+
 hipError_t launch_router(const RouterArgs& a0, hipStream_t s) {
   RouterArgs a = a0;
-  const int sp0 = router_splits(a.T, a.D, a.E, a.num_cus);
-  const int kc = ((a.D / sp0 + 31) / 32) * 32;
-  a.splits = (a.D + kc - 1) / kc;
-  dim3 g1((a.T + 63) / 64, (a.E + 63) / 64, a.splits);
-  if (a.act_bf16)
-    hipLaunchKernelGGL(router_logits_kernel<true>, g1, dim3(256), 0, s, a.x, a.gate_w, a.logits,
-                       a.counts, a.T, a.D, a.E, kc);
-  else
-    hipLaunchKernelGGL(router_logits_kernel<false>, g1, dim3(256), 0, s, a.x, a.gate_w, a.logits,
-                       a.counts, a.T, a.D, a.E, kc);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  hipError_t err;
+  if (a.act_bf16 && a.w_split && a.T >= kRouterX3MinTokens) {
+    const int kc = router_x3_kc(a.T, a.D, a.E, a.num_cus);
+    a.splits = (a.D + kc - 1) / kc;
+    const size_t n4 = (size_t)a.E * a.D / 4;
+    hipLaunchKernelGGL(split_gate_w_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, a.gate_w,
+                       a.w_split, n4);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    const int n_et = (a.E + kX3_BE - 1) / kX3_BE;
+    const int n_tiles = ((a.T + kX3_BT - 1) / kX3_BT) * n_et;
+    dim3 g((n_tiles + 15) / 16 * 16, a.splits);
+    hipLaunchKernelGGL(router_logits_x3_kernel, g, dim3(256), 0, s, static_cast<const uint16_t*>(a.x),
+                       a.w_split, a.logits, a.counts, a.T, a.D, a.E, kc, n_et, n_tiles);
+  } else {
+    const int sp0 = router_splits(a.T, a.D, a.E, a.num_cus);
+    const int kc = ((a.D / sp0 + 31) / 32) * 32;
+    a.splits = (a.D + kc - 1) / kc;
+    dim3 g1((a.T + 63) / 64, (a.E + 63) / 64, a.splits);
+    if (a.act_bf16)
+      hipLaunchKernelGGL(router_logits_kernel<true>, g1, dim3(256), 0, s, a.x, a.gate_w, a.logits,
+                         a.counts, a.T, a.D, a.E, kc);
+    else
+      hipLaunchKernelGGL(router_logits_kernel<false>, g1, dim3(256), 0, s, a.x, a.gate_w, a.logits,
+                         a.counts, a.T, a.D, a.E, kc);
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return err;
   if (a.splits > 1) {
     const int n = a.T * a.E;
     hipLaunchKernelGGL(reduce_planes_kernel, dim3((n + 255) / 256), dim3(256), 0, s, a.logits, n, a.splits);

@@ -81,6 +81,13 @@ SMALL_FP8 = MI.LayerConfig("small_fp8", T=77, D=256, E=16, H=256, G=4, kg=2, K=4
                            bias="normal", norm=True, rsf=2.5, Hs=256, act="bf16", weight="fp8", bias_std=0.05)
 SMALL_F32 = MI.LayerConfig("small_f32", T=129, D=96, E=10, H=48, G=2, kg=1, K=3, score_fn="softmax",
                            bias="none", norm=False, rsf=1.5, Hs=40, act="f32", weight="f32")
+# bf16 activations from 512 tokens on take the bf16x3 logits kernel: 9 ragged token
+# tiles, a second expert tile holding 8 of its 128 experts, several K splits
+ROUTER_X3 = MI.LayerConfig("router_x3", T=1100, D=512, E=136, H=128, G=8, kg=3, K=5, score_fn="sigmoid",
+                           bias="normal", norm=True, rsf=2.5, Hs=128, act="bf16", weight="bf16", bias_std=0.05)
+ROUTER_X3_SOFTMAX = MI.LayerConfig("router_x3_softmax", T=640, D=256, E=64, H=128, G=1, kg=1, K=6,
+                                   score_fn="softmax", bias="none", norm=False, rsf=1.0, Hs=128, act="bf16",
+                                   weight="bf16")
 
 
 def test_generator_is_device_agnostic():
@@ -91,7 +98,7 @@ def test_generator_is_device_agnostic():
 
 
 def test_router_small_all_score_functions():
-    for cfg in (SMALL_BF16, SMALL_SIG, SMALL_F32, MI.CONFIGS["tiny_f32"]):
+    for cfg in (SMALL_BF16, SMALL_SIG, SMALL_F32, MI.CONFIGS["tiny_f32"], ROUTER_X3, ROUTER_X3_SOFTMAX):
         inp = MI.make_layer(cfg, DEV)
         layer = M.MoELayer.from_config(cfg)
         idx, gate, counts = layer.router(inp.x, inp.gate_w, inp.sel_bias)
