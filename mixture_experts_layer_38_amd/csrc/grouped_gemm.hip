@@ -62,7 +62,7 @@ struct Tile {
 }  // namespace
 
 template <int kMode, int NRB>
-__device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows * LDW]) {
+__device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows * LDW], float* s_gate) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
   const int c8 = tid & 7, r0 = tid >> 3;
@@ -109,6 +109,9 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
 #pragma unroll
   for (int c = 0; c < kNC; ++c) bcol[c] = (kMode == 0) ? 128 * c + 32 * wn : 64 * wn + 32 * c;
   const int lr = lane & 31, lk = (lane >> 5) * 8;
+
+  // down GEMM: the tile's gates into LDS for the epilogue
+  if (kMode == 1 && tid < BM) s_gate[tid] = (t.gate != nullptr && tid < t.vrows) ? t.gate[t.m0 + tid] : 1.0f;
 
   uint4 pf[kLd];
 #pragma unroll
@@ -212,25 +215,53 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
 
   // D layout of the 32x32 MFMA: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
   // column l%32.
+  if (kMode == 0) {
+    // h tile (256 x 128): each lane writes one bf16 per element
 #pragma unroll
-  for (int i = 0; i < NRB; ++i) {
+    for (int i = 0; i < NRB; ++i) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int m = 32 * (wm + 2 * i) + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      if (m >= t.vrows) continue;
-      const int mr = t.m0 + m;
-      uint16_t* cp = t.c + (size_t)mr * t.ldc;
-      if (kMode == 0) {
+      for (int e = 0; e < 16; ++e) {
+        const int m = 32 * (wm + 2 * i) + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (m >= t.vrows) continue;
         const float h = silu_fast(acc[i][0][e]) * acc[i][1][e];
-        cp[t.nt * 128 + 32 * wn + lr] = f32_to_bf16(h);
-      } else {
-        const float g = t.gate ? t.gate[mr] : 1.0f;
+        t.c[(size_t)(t.m0 + m) * t.ldc + t.nt * 128 + 32 * wn + lr] = f32_to_bf16(h);
+      }
+    }
+  } else {
+    // y tile (256 x 256): staged through LDS, then written as full 16-byte
+    // pieces of each row (the tile's rows are 512 contiguous bytes of y).
+    // Rows e, e+1 (e even) of a lane are adjacent rows of one column; an
+    // even lane swaps its row-(e+1) value for its odd neighbour's row-e
+    // value (DPP quad permute 1,0,3,2), so each lane writes two adjacent
+    // columns of one row as one 32-bit word.
+    constexpr int kLdo = BN + 8;  // staging row, elements (528 bytes)
+    uint16_t* so = &smem[0][0];
+    const bool odd = lane & 1;
+    __syncthreads();  // the last fragment reads of the K loop are done
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const int m = 32 * (wm + 2 * i) + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);  // row of element e
+        const float g0 = s_gate[m], g1 = s_gate[m + 1];
 #pragma unroll
         for (int c = 0; c < kNC; ++c) {
-          const int col = t.nt * BN + 64 * wn + 32 * c + lr;
-          if (col < t.D) cp[col] = f32_to_bf16(g * acc[i][c][e]);
+          const uint32_t b0 = f32_to_bf16(g0 * acc[i][c][e]), b1 = f32_to_bf16(g1 * acc[i][c][e + 1]);
+          const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? b0 : b1), 0xB1, 0xF, 0xF, false);
+          const int col = 64 * wn + 32 * c + lr;
+          const uint32_t w = odd ? (r | (b1 << 16)) : (b0 | (r << 16));
+          *reinterpret_cast<uint32_t*>(&so[(m + (odd ? 1 : 0)) * kLdo + (col & ~1)]) = w;
         }
       }
+    }
+    __syncthreads();
+    const int q = tid & 31;  // 16-byte piece of a row
+    const int col = t.nt * BN + 8 * q;
+    if (col < t.D) {  // D % 128 == 0: a piece is wholly inside or outside
+#pragma unroll 4
+      for (int r = tid >> 5; r < t.vrows; r += 16)
+        *reinterpret_cast<uint4*>(t.c + (size_t)(t.m0 + r) * t.ldc + col) =
+            *reinterpret_cast<const uint4*>(&so[r * kLdo + 8 * q]);
     }
   }
 }
@@ -240,6 +271,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][kRows * LDW];
   __shared__ int32_t s_pre[kMaxExperts + 2];
   __shared__ int32_t s_off[kMaxExperts + 1];
+  __shared__ float s_gate[BM];
 
   // Tiles come in runs of kRun consecutive tiles; run r goes to XCD r % 8,
   // so every XCD gets a mix of experts and of the shared expert's tiles while
@@ -306,11 +338,11 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
 #pragma unroll
   for (int i = 0; i < 4; ++i) nrb += (32 * (wm + 2 * i) < t.vrows) ? 1 : 0;
   switch (nrb) {
-    case 4: tile_body<kMode, 4>(t, smem); break;
-    case 3: tile_body<kMode, 3>(t, smem); break;
-    case 2: tile_body<kMode, 2>(t, smem); break;
-    case 1: tile_body<kMode, 1>(t, smem); break;
-    default: tile_body<kMode, 0>(t, smem); break;
+    case 4: tile_body<kMode, 4>(t, smem, s_gate); break;
+    case 3: tile_body<kMode, 3>(t, smem, s_gate); break;
+    case 2: tile_body<kMode, 2>(t, smem, s_gate); break;
+    case 1: tile_body<kMode, 1>(t, smem, s_gate); break;
+    default: tile_body<kMode, 0>(t, smem, s_gate); break;
   }
 }
 
