@@ -32,6 +32,46 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# HBM traffic of one gate/up GEMM launch on the V3 prefill workload, from two
+# rocprofv3 --pmc runs of this bench (FETCH_SIZE, then WRITE_SIZE; KiB per
+# dispatch, mean of 3 dispatches), each scaled by what the same counter reads
+# for the bench's 1 GiB device-to-device copy probe (FETCH_SIZE 524315.7 KiB
+# for 1048576 KiB read; WRITE_SIZE 1048576 KiB for 1048576 KiB written).
+# Valid only for the kernel sources with these hashes; otherwise reported null.
+GATEUP_COUNTERS = {
+    "sources": {"mixture_experts_layer_38_amd/csrc/grouped_gemm.hip":
+                "de5c00d82375edf6bae42e32b85236d9e0bc4b509745daba92b0499c1943b4f7",
+                "mixture_experts_layer_38_amd/csrc/moe_internal.hpp":
+                "12e0cdaae6f08df4632628f9635f7b872ddb06f7995dab9db8bb8fcc0c1d12f0"},
+    "workload": "v3_prefill",
+    "fetch_kib": 21728779.5, "write_kib": 589824.0,
+    "fetch_scale": 1048576.0 / 524315.7, "write_scale": 1.0,
+}
+
+
+def gateup_traffic(cfg):
+    """Calibrated HBM bytes per gate/up launch, or None when the counters do not
+    describe the kernel that was built (or another workload)."""
+    import hashlib
+    c = GATEUP_COUNTERS
+    if cfg.name != c["workload"]:
+        return None
+    for rel, digest in c["sources"].items():
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != digest:
+                return None
+    return round((c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024)
+
+
+def gateup_algorithmic_bytes(cfg):
+    """Each operand byte once: routed and shared gate/up weights, the gathered
+    token rows (T*K routed + T shared), and h written."""
+    w = 2 * (cfg.E * 2 * cfg.H * cfg.D + 2 * cfg.Hs * cfg.D)
+    x = 2 * (cfg.T * cfg.K + cfg.T) * cfg.D
+    h = 2 * (cfg.T * cfg.K * cfg.H + cfg.T * cfg.Hs)
+    return w + x + h
+
+
 def mfma_flops(cfg, T=None):
     T = cfg.T if T is None else T
     return 2.0 * T * (cfg.K * 3 * cfg.D * cfg.H + 3 * cfg.D * cfg.Hs)
@@ -73,7 +113,9 @@ def run_prefill(args, torch, M, MI):
     res = dict(cfg=cfg, inp=inp, ms=ms, stages=stage_avg, counts=counts.cpu().tolist(),
                mfma_frac=mfma_flops(cfg) / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
                roofline=dict(bound="mfma", achieved=round(g1_tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                             frac=round(g1_tflops / PEAK_BF16_TFLOPS, 4), traffic=None,
+                             frac=round(g1_tflops / PEAK_BF16_TFLOPS, 4), traffic=gateup_traffic(cfg),
+                             traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                             algorithmic_bytes=gateup_algorithmic_bytes(cfg),
                              kernel="grouped_gemm_bf16_kernel<0> (gate/up + SwiGLU)",
                              per_launch_flop=gateup_flops(cfg), avg_ms=round(g1_ms, 4)))
     del layer, out
