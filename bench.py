@@ -213,7 +213,7 @@ def main():
     ap.add_argument("--decode-config", default="v3_decode_fp8")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=16)
+    ap.add_argument("--cpu-sample", type=int, default=40)
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 1 GiB device-to-device copy first (a known-size reference "
                          "for hardware byte counters)")

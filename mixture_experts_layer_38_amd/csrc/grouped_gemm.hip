@@ -29,9 +29,11 @@
 // next K step is loaded into registers while the current one is multiplied,
 // then written to the other buffer; one barrier per K step.
 // Blocks are mapped so that runs of consecutive tiles land on one XCD and its
-// L2, with runs spread round-robin over the XCDs. Gate/up tiles are ordered
-// column-tile major (the two or three row blocks of an expert that read the
-// same weight slice run side by side); down tiles row-block major.
+// L2, with runs spread round-robin over the XCDs. Tiles are ordered
+// column-tile major, and an expert's rows are split evenly (in 32-row blocks)
+// over its two or three row tiles: the row tiles that read one weight slice
+// run side by side at the same pace, so the second and third reads of each
+// weight line hit that L2 (this halves the bytes fetched past L2).
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -39,8 +41,7 @@ namespace moe {
 namespace {
 constexpr int BM = kGB_BM, BN = 256, BK = kGB_BK, LDW = BK + 8;
 constexpr int kRows = BM + BN;  // LDS rows per buffer: A then B
-// consecutive tiles per XCD run, per GEMM
-template <int kMode> constexpr int run_len() { return kMode == 0 ? 32 : 16; }
+constexpr int kRun = 32;        // consecutive tiles per XCD run
 constexpr int kNC = 2;          // 32-column blocks per wave
 constexpr int kLd = 8;          // 16-byte global loads per thread per K step
 
@@ -280,7 +281,6 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
   const int total = a.pre[a.E + 1];
   const int bid = blockIdx.x;
   const int slot = bid >> 3;
-  constexpr int kRun = run_len<kMode>();
   const int tile = ((slot / kRun) * 8 + (bid & 7)) * kRun + slot % kRun;
   if (tile >= total) return;
 
@@ -295,18 +295,15 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
   Tile t;
   t.Hp = routed ? a.H : a.Hs;
   t.D = a.D;
-  const int ntn = (kMode == 0) ? t.Hp / kG1_BNH : (a.D + BN - 1) / BN;  // D % 128 == 0: last tile may be half
   const int local = tile - s_pre[p];
-  if (kMode == 0) {  // column-tile major: the row blocks of one weight slice run together
-    const int nmt = (rows + BM - 1) / BM;
-    t.m0 = (local % nmt) * BM;
-    t.nt = local / nmt;
-  } else {           // row-block major: one row block against all its column tiles
-    t.m0 = (local / ntn) * BM;
-    t.nt = local % ntn;
-  }
+  // an expert's rows are split evenly (in 32-row blocks) over its row tiles,
+  // so the tiles that share a weight slice run at the same pace
+  const int nmt = (rows + BM - 1) / BM;
+  const int rpt = ((rows + nmt - 1) / nmt + 31) & ~31;
+  t.m0 = (local % nmt) * rpt;  // column-tile major: the row tiles of one weight slice run together
+  t.nt = local / nmt;
   t.K = (kMode == 0) ? a.D : t.Hp;
-  t.vrows = min(rows - t.m0, BM);
+  t.vrows = min(rows - t.m0, rpt);
   if (kMode == 0) {
     t.a_rows = static_cast<const uint16_t*>(a.a);
     t.lda = a.D;
@@ -353,14 +350,14 @@ int grouped_blocks(int max_items, int run) {
 }
 
 hipError_t launch_grouped_gateup_bf16(const ExpertGemmArgs& a, hipStream_t s) {
-  const int blocks = grouped_blocks(a.max_items, run_len<0>());
+  const int blocks = grouped_blocks(a.max_items, kRun);
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(grouped_gemm_bf16_kernel<0>, dim3(blocks), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_grouped_down_bf16(const ExpertGemmArgs& a, hipStream_t s) {
-  const int blocks = grouped_blocks(a.max_items, run_len<1>());
+  const int blocks = grouped_blocks(a.max_items, kRun);
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(grouped_gemm_bf16_kernel<1>, dim3(blocks), dim3(512), 0, s, a);
   return hipGetLastError();
