@@ -35,17 +35,17 @@ def log(msg):
 # HBM traffic of one gate/up GEMM launch on the V3 prefill workload, from two
 # rocprofv3 --pmc runs of this bench (FETCH_SIZE, then WRITE_SIZE; KiB per
 # dispatch, mean of 3 dispatches), each scaled by what the same counter reads
-# for the bench's 1 GiB device-to-device copy probe (FETCH_SIZE 524315.7 KiB
+# for the bench's 1 GiB device-to-device copy probe (FETCH_SIZE 524315.1 KiB
 # for 1048576 KiB read; WRITE_SIZE 1048576 KiB for 1048576 KiB written).
 # Valid only for the kernel sources with these hashes; otherwise reported null.
 GATEUP_COUNTERS = {
     "sources": {"mixture_experts_layer_38_amd/csrc/grouped_gemm.hip":
-                "de5c00d82375edf6bae42e32b85236d9e0bc4b509745daba92b0499c1943b4f7",
+                "858428edc66b82a7db197ee66a82a3566c50323f6f3df1e41adada0012655892",
                 "mixture_experts_layer_38_amd/csrc/moe_internal.hpp":
                 "12e0cdaae6f08df4632628f9635f7b872ddb06f7995dab9db8bb8fcc0c1d12f0"},
     "workload": "v3_prefill",
-    "fetch_kib": 21728779.5, "write_kib": 589824.0,
-    "fetch_scale": 1048576.0 / 524315.7, "write_scale": 1.0,
+    "fetch_kib": 12353957.1, "write_kib": 589824.0,
+    "fetch_scale": 1048576.0 / 524315.1, "write_scale": 1.0,
 }
 
 
