@@ -32,8 +32,10 @@ hipError_t launch_histogram(const int32_t* idx, int32_t* counts, int n, int E, h
   hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(256), 0, s, counts, E);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || n == 0) return err;
-  int blocks = (n + 255) / 256;
-  if (blocks > 1024) blocks = 1024;
+  // at least 4096 entries per block: one LDS histogram each, then at most E
+  // global atomics per block
+  int blocks = (n + 4095) / 4096;
+  if (blocks > 128) blocks = 128;
   hipLaunchKernelGGL(histogram_kernel, dim3(blocks), dim3(256), 0, s, idx, counts, n, E);
   return hipGetLastError();
 }
@@ -88,12 +90,35 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(DispatchArgs a) {
   }
 }
 
+// Each block takes a chunk of kPermChunk (token, slot) entries: an LDS
+// histogram of the chunk, one global atomic per expert to reserve the chunk's
+// rows, then LDS atomics hand out rows inside each reservation. Row order
+// within an expert is arbitrary (no result depends on it: every row is
+// computed on its own and the combine adds a token's rows in slot order).
+constexpr int kPermChunk = 2048;
+
 __global__ __launch_bounds__(256) void dispatch_permute_kernel(DispatchArgs a) {
+  __shared__ int32_t cnt[kMaxExperts];
+  __shared__ int32_t base[kMaxExperts];
   const int n = a.T * a.K;
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+  const int i0 = blockIdx.x * kPermChunk, i1 = min(n, i0 + kPermChunk);
+  for (int e = threadIdx.x; e < a.E; e += 256) cnt[e] = 0;
+  __syncthreads();
+  for (int i = i0 + threadIdx.x; i < i1; i += 256) {
     const int e = a.idx[i];
-    if (e < 0 || e >= a.E) continue;  // skipped, as in the histogram
-    const int r = atomicAdd(&a.cursor[e], 1);
+    if (e >= 0 && e < a.E) atomicAdd(&cnt[e], 1);  // out-of-range entries are skipped, as in the histogram
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < a.E; e += 256) {
+    const int c = cnt[e];
+    base[e] = c ? atomicAdd(&a.cursor[e], c) : 0;
+    cnt[e] = 0;
+  }
+  __syncthreads();
+  for (int i = i0 + threadIdx.x; i < i1; i += 256) {
+    const int e = a.idx[i];
+    if (e < 0 || e >= a.E) continue;
+    const int r = base[e] + atomicAdd(&cnt[e], 1);
     a.row_token[r] = i / a.K;
     if (a.row_gate) a.row_gate[r] = a.gate[i];
     a.slot_row[i] = r;
@@ -106,9 +131,7 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   if (err != hipSuccess) return err;
   const int n = a.T * a.K;
   if (n == 0) return hipSuccess;
-  int blocks = (n + 255) / 256;
-  if (blocks > 2048) blocks = 2048;
-  hipLaunchKernelGGL(dispatch_permute_kernel, dim3(blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(dispatch_permute_kernel, dim3((n + kPermChunk - 1) / kPermChunk), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

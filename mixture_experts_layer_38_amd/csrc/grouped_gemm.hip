@@ -18,9 +18,9 @@
 //
 // Tile 256 x 256, K step 64, 8 waves (two per SIMD) as 2 x 4, each wave
 // 128 x 64 as 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators
-// per lane, held in AGPRs); two waves per SIMD keep both the matrix pipe and the
-// LDS busy while the other waits. A wave's four 32-row blocks are interleaved with the other row-wave's
-// (blocks wm, wm+2, wm+4, wm+6), so a ragged last tile of an expert splits its
+// per lane); two waves per SIMD keep both the matrix pipe and the LDS busy
+// while the other waits. A wave's four 32-row blocks are interleaved with the
+// other row-wave's (blocks wm, wm+2, wm+4, wm+6), so a ragged tile splits its
 // valid rows evenly; the tile body is instantiated per count of valid row
 // blocks, so blocks with no valid row cost no MFMA and the K loop stays
 // branch-free.
@@ -145,8 +145,9 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
   };
 
   // The next K step's tile, loaded into registers at the top of a step, is
-  // written to the other LDS buffer in two halves interleaved with the MFMAs
-  // of the last two substeps, so the LDS writes overlap the matrix work.
+  // written to the other LDS buffer interleaved with the MFMAs of the last
+  // substep: the loads get three quarters of a step to land, and the LDS
+  // writes overlap the matrix work.
   auto store_half = [&](int buf, int h) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = (kLd / 2) * h; j < (kLd / 2) * (h + 1); ++j)
@@ -155,8 +156,7 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
   // instruction counts per substep, for the interleave below
   constexpr int nr = kNC + NRB, nm = kNC * NRB, nw = kLd / 2;
   constexpr int p1 = nr < nm ? nr : nm;              // (MFMA, LDS read) pairs
-  constexpr int p2 = nw < nm - p1 ? nw : nm - p1;    // then (MFMA, LDS write) pairs
-  constexpr int p3 = nw < nm ? nw : nm;              // substep 3: (MFMA, LDS write) pairs
+  constexpr int p4 = 2 * nw < nm ? 2 * nw : nm;      // last substep: (MFMA, LDS write) pairs
 
   const int nk = t.K / BK;
   read_frags(smem[0], 0, 0);
@@ -167,7 +167,7 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
     const int knext = (kt + 1 < nk ? kt + 1 : kt) * BK;
 #pragma unroll
     for (int j = 0; j < kLd; ++j) pf[j] = gload(j, knext);
-    // substeps 0, 1: next fragments interleaved with the MFMAs
+    // substeps 0-2: next fragments interleaved with the MFMAs
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       read_frags(smem[cur], 16 * (s + 1), (s + 1) & 1);
@@ -181,34 +181,28 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
       __builtin_amdgcn_sched_group_barrier(0x008, nm - p1, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // substep 2: last fragments, then the first half of the next tile
+    // substep 2: last fragments
     read_frags(smem[cur], 48, 1);
-    store_half(cur ^ 1, 0);
     mfmas(0);
 #pragma unroll
     for (int q = 0; q < p1; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
-#pragma unroll
-    for (int q = 0; q < p2; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-    }
     __builtin_amdgcn_sched_group_barrier(0x100, nr - p1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x200, nw - p2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, nm - p1 - p2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, nm - p1, 0);
     __builtin_amdgcn_sched_barrier(0);
-    // substep 3: second half of the next tile
+    // substep 3: the whole next tile into the idle buffer
+    store_half(cur ^ 1, 0);
     store_half(cur ^ 1, 1);
     mfmas(1);
 #pragma unroll
-    for (int q = 0; q < p3; ++q) {
+    for (int q = 0; q < p4; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x200, nw - p3, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, nm - p3, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, 2 * nw - p4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, nm - p4, 0);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     read_frags(smem[cur ^ 1], 0, 0);

@@ -54,25 +54,56 @@ __device__ __forceinline__ uint32_t ordered_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Wave reductions without LDS traffic: four DPP steps (quad permutes 1,0,3,2
+// and 2,3,0,1, half-row mirror, row mirror) make every 16-lane row uniform,
+// then the four row values are read into scalar registers and combined in a
+// fixed order; every lane gets the result.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+template <int kCtrl>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+  const uint64_t w = ((uint64_t)dpp_u32<kCtrl>((uint32_t)(v >> 32)) << 32) | dpp_u32<kCtrl>((uint32_t)v);
+  return w > v ? w : v;
+}
+
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_u64<0xB1>(v);
+  v = dpp_max_u64<0x4E>(v);
+  v = dpp_max_u64<0x141>(v);
+  v = dpp_max_u64<0x140>(v);
+  uint64_t r = 0;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint64_t w = __shfl_xor(v, o, kWave);
-    v = w > v ? w : v;
+  for (int q = 0; q < 4; ++q) {
+    const uint64_t w = ((uint64_t)lane_u32((uint32_t)(v >> 32), 16 * q) << 32) | lane_u32((uint32_t)v, 16 * q);
+    r = w > r ? w : r;
   }
-  return v;
+  return r;
 }
 
 __device__ __forceinline__ float wave_max_f32(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  v = fmaxf(v, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x4E>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x141>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<0x140>(__float_as_uint(v))));
+  const float a = __uint_as_float(lane_u32(__float_as_uint(v), 0)), b = __uint_as_float(lane_u32(__float_as_uint(v), 16));
+  const float c = __uint_as_float(lane_u32(__float_as_uint(v), 32)), d = __uint_as_float(lane_u32(__float_as_uint(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
 }
 
 __device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  v += __uint_as_float(dpp_u32<0xB1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x4E>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x141>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<0x140>(__float_as_uint(v)));
+  const float a = __uint_as_float(lane_u32(__float_as_uint(v), 0)), b = __uint_as_float(lane_u32(__float_as_uint(v), 16));
+  const float c = __uint_as_float(lane_u32(__float_as_uint(v), 32)), d = __uint_as_float(lane_u32(__float_as_uint(v), 48));
+  return (a + b) + (c + d);
 }
 
 // problem p in [0, E]: routed expert p (< E) or the shared expert (== E).

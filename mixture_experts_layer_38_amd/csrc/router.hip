@@ -25,16 +25,13 @@ namespace moe {
 template <bool kBf16X>
 __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restrict__ xv,
                                                             const float* __restrict__ w,
-                                                            float* __restrict__ logits,
-                                                            int32_t* __restrict__ counts, int T,
+                                                            float* __restrict__ logits, int T,
                                                             int D, int E, int kc) {
   constexpr int BT = 64, BE = 64, BK = 32, LD = BK + 4;
   __shared__ __attribute__((aligned(16))) float sA[BT * LD];
   __shared__ __attribute__((aligned(16))) float sB[BE * LD];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t0 = blockIdx.x * BT, e0 = blockIdx.y * BE;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
-    for (int e = tid; e < E; e += 256) counts[e] = 0;  // histogram of the select kernel
   const int kbeg = blockIdx.z * kc, kend = min(D, kbeg + kc);
   logits += (size_t)blockIdx.z * T * E;
 
@@ -154,15 +151,12 @@ constexpr int kX3_BT = 128, kX3_BE = 128, kX3_BK = 64, kX3_LD = kX3_BK + 8;
 
 __global__ __launch_bounds__(256) void router_logits_x3_kernel(const uint16_t* __restrict__ x,
                                                                const uint16_t* __restrict__ wsplit,
-                                                               float* __restrict__ logits,
-                                                               int32_t* __restrict__ counts, int T, int D,
+                                                               float* __restrict__ logits, int T, int D,
                                                                int E, int kc, int n_et, int n_tiles) {
   constexpr int kTile = kX3_BT * kX3_LD;
   __shared__ __attribute__((aligned(16))) uint16_t sm[2][4][kTile];  // [buffer][x, hi, mid, lo]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
-  if (b == 0 && blockIdx.y == 0)
-    for (int e = tid; e < E; e += 256) counts[e] = 0;  // histogram of the select kernel
   // blocks b and b+8 run on the same XCD; give them the two expert tiles of one token tile
   const int pos = (b / 16) * 16 + (b % 8) * 2 + (b / 8) % 2;
   if (pos >= n_tiles) return;
@@ -248,8 +242,8 @@ __global__ __launch_bounds__(256) void router_logits_x3_kernel(const uint16_t* _
 // ---------------------------------------------------------------------------
 // Per-token scoring and selection; one wave per token, expert e = lane + 64*j.
 // ---------------------------------------------------------------------------
-constexpr int kVPL = kMaxExperts / kWave;  // values per lane
-
+// kVPL values per lane: experts lane, lane+64, ... (E <= 64*kVPL)
+template <int kVPL>
 __global__ __launch_bounds__(256) void router_select_kernel(RouterArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
@@ -295,15 +289,19 @@ __global__ __launch_bounds__(256) void router_select_kernel(RouterArgs a) {
 
   if (a.G > 1) {
     const int gs = E / a.G;
+    int grp[kVPL];  // group of expert lane + 64j (G for lanes past E)
+#pragma unroll
+    for (int j = 0; j < kVPL; ++j) {
+      const int e = lane + kWave * j;
+      grp[j] = (e < E) ? e / gs : a.G;
+    }
     // group maxima: lane g ends up holding max z over group g
     float gmax = -INFINITY;
     for (int g = 0; g < a.G; ++g) {
       float m = -INFINITY;
 #pragma unroll
-      for (int j = 0; j < kVPL; ++j) {
-        const int e = lane + kWave * j;
-        if (e < E && e / gs == g) m = fmaxf(m, z[j]);
-      }
+      for (int j = 0; j < kVPL; ++j)
+        if (grp[j] == g) m = fmaxf(m, z[j]);
       m = wave_max_f32(m);
       if (lane == g) gmax = m;
     }
@@ -317,10 +315,8 @@ __global__ __launch_bounds__(256) void router_select_kernel(RouterArgs a) {
       if (lane == g) key = 0;
     }
 #pragma unroll
-    for (int j = 0; j < kVPL; ++j) {
-      const int e = lane + kWave * j;
-      if (e < E && !((kept >> (e / gs)) & 1ull)) allowed &= ~(1u << j);
-    }
+    for (int j = 0; j < kVPL; ++j)
+      if (grp[j] < a.G && !((kept >> grp[j]) & 1ull)) allowed &= ~(1u << j);
   }
 
   int my_e = -1;
@@ -343,7 +339,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(RouterArgs a) {
 #pragma unroll
     for (int j = 0; j < kVPL; ++j)
       if (j == jw) mine = s[j];
-    const float se = __shfl(mine, e & 63, kWave);
+    const float se = __uint_as_float(lane_u32(__float_as_uint(mine), e & 63));
     if ((e & 63) == lane) allowed &= ~(1u << jw);
     sum_sel += se;
     if (lane == k) { my_e = e; my_s = se; }
@@ -354,7 +350,6 @@ __global__ __launch_bounds__(256) void router_select_kernel(RouterArgs a) {
     g *= a.rsf;
     a.idx[(size_t)t * a.K + lane] = my_e;
     a.gate[(size_t)t * a.K + lane] = g;
-    atomicAdd(&a.counts[my_e], 1);
   }
 }
 
@@ -402,7 +397,7 @@ hipError_t launch_router(const RouterArgs& a0, hipStream_t s) {
     const int n_tiles = ((a.T + kX3_BT - 1) / kX3_BT) * n_et;
     dim3 g((n_tiles + 15) / 16 * 16, a.splits);
     hipLaunchKernelGGL(router_logits_x3_kernel, g, dim3(256), 0, s, static_cast<const uint16_t*>(a.x),
-                       a.w_split, a.logits, a.counts, a.T, a.D, a.E, kc, n_et, n_tiles);
+                       a.w_split, a.logits, a.T, a.D, a.E, kc, n_et, n_tiles);
   } else {
     const int sp0 = router_splits(a.T, a.D, a.E, a.num_cus);
     const int kc = ((a.D / sp0 + 31) / 32) * 32;
@@ -410,10 +405,10 @@ hipError_t launch_router(const RouterArgs& a0, hipStream_t s) {
     dim3 g1((a.T + 63) / 64, (a.E + 63) / 64, a.splits);
     if (a.act_bf16)
       hipLaunchKernelGGL(router_logits_kernel<true>, g1, dim3(256), 0, s, a.x, a.gate_w, a.logits,
-                         a.counts, a.T, a.D, a.E, kc);
+                         a.T, a.D, a.E, kc);
     else
       hipLaunchKernelGGL(router_logits_kernel<false>, g1, dim3(256), 0, s, a.x, a.gate_w, a.logits,
-                         a.counts, a.T, a.D, a.E, kc);
+                         a.T, a.D, a.E, kc);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (a.splits > 1) {
@@ -421,8 +416,14 @@ hipError_t launch_router(const RouterArgs& a0, hipStream_t s) {
     hipLaunchKernelGGL(reduce_planes_kernel, dim3((n + 255) / 256), dim3(256), 0, s, a.logits, n, a.splits);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(router_select_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
-  return hipGetLastError();
+  if (a.E <= 2 * kWave)
+    hipLaunchKernelGGL(router_select_kernel<2>, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+  else if (a.E <= 4 * kWave)
+    hipLaunchKernelGGL(router_select_kernel<4>, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(router_select_kernel<kMaxExperts / kWave>, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  return launch_histogram(a.idx, a.counts, a.T * a.K, a.E, s);
 }
 
 }  // namespace moe

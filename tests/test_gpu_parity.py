@@ -88,6 +88,9 @@ ROUTER_X3 = MI.LayerConfig("router_x3", T=1100, D=512, E=136, H=128, G=8, kg=3, 
 ROUTER_X3_SOFTMAX = MI.LayerConfig("router_x3_softmax", T=640, D=256, E=64, H=128, G=1, kg=1, K=6,
                                    score_fn="softmax", bias="none", norm=False, rsf=1.0, Hs=128, act="bf16",
                                    weight="bf16")
+# more than 256 experts: eight values per lane in the select kernel, three expert tiles
+ROUTER_E384 = MI.LayerConfig("router_e384", T=700, D=256, E=384, H=128, G=12, kg=4, K=8, score_fn="sigmoid",
+                             bias="normal", norm=True, rsf=2.5, Hs=128, act="bf16", weight="bf16", bias_std=0.05)
 
 
 def test_generator_is_device_agnostic():
@@ -98,7 +101,8 @@ def test_generator_is_device_agnostic():
 
 
 def test_router_small_all_score_functions():
-    for cfg in (SMALL_BF16, SMALL_SIG, SMALL_F32, MI.CONFIGS["tiny_f32"], ROUTER_X3, ROUTER_X3_SOFTMAX):
+    for cfg in (SMALL_BF16, SMALL_SIG, SMALL_F32, MI.CONFIGS["tiny_f32"], ROUTER_X3, ROUTER_X3_SOFTMAX,
+                ROUTER_E384):
         inp = MI.make_layer(cfg, DEV)
         layer = M.MoELayer.from_config(cfg)
         idx, gate, counts = layer.router(inp.x, inp.gate_w, inp.sel_bias)
