@@ -72,13 +72,14 @@ hipError_t launch_simple_down_f32(const ExpertGemmArgs& a, int TK, hipStream_t s
 }
 
 // out[t] = [x[t]] + S[t] + sum_{k<K} Y[slot_row[t*K+k]], fp32, k in order.
-// One workgroup per token, 8 consecutive columns per thread.
+// One workgroup per token, 8 consecutive columns per thread and step.
 template <bool kYBf16, bool kXBf16, bool kOutBf16>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int t = blockIdx.x;
   int rows[kMaxTopK];
-  for (int k = 0; k < a.K; ++k) rows[k] = a.slot_row[(size_t)t * a.K + k];
-  for (int d0 = threadIdx.x * 8; d0 < a.D; d0 += 256 * 8) {
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) rows[k] = (k < a.K) ? a.slot_row[(size_t)t * a.K + k] : 0;
+  for (int d0 = threadIdx.x * 8; d0 < a.D; d0 += blockDim.x * 8) {
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
@@ -115,7 +116,27 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       }
     };
     if (a.y_shared) add_row(a.y_shared, (size_t)t);
-    for (int k = 0; k < a.K; ++k) add_row(a.y_routed, (size_t)rows[k]);
+    if (kYBf16) {
+      // every row load in flight before the adds, which still run in k order
+      uint4 v[kMaxTopK];
+#pragma unroll
+      for (int k = 0; k < kMaxTopK; ++k)
+        if (k < a.K)
+          v[k] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.y_routed) + (size_t)rows[k] * a.D + d0);
+#pragma unroll
+      for (int k = 0; k < kMaxTopK; ++k) {
+        if (k < a.K) {
+          const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += __uint_as_float(w[i] << 16);
+            acc[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
+          }
+        }
+      }
+    } else {
+      for (int k = 0; k < a.K; ++k) add_row(a.y_routed, (size_t)rows[k]);
+    }
     if (kOutBf16) {
       uint32_t w[4];
 #pragma unroll
@@ -134,7 +155,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const int code = (a.y_bf16 ? 4 : 0) | (a.act_bf16 ? 2 : 0) | (a.out_bf16 ? 1 : 0);
-  dim3 g(a.T), b(256);
+  // threads per token: the 8-column chunks of a row spread evenly over at
+  // most 256 threads (D = 7168: 224 threads x 4 chunks)
+  const int chunks = (a.D + 7) / 8, iters = (chunks + 255) / 256;
+  dim3 g(a.T), b((chunks + iters - 1) / iters);
   switch (code) {
     case 0: hipLaunchKernelGGL((combine_kernel<false, false, false>), g, b, 0, s, a); break;
     case 1: hipLaunchKernelGGL((combine_kernel<false, false, true>), g, b, 0, s, a); break;
