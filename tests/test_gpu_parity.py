@@ -6,6 +6,8 @@ on all tokens where the oracle finishes in seconds, else on a seeded token
 sample), and the edge cases (no tokens, one token, the maximum token count,
 repeat-run bit identity, bf16 output, routed-only runs).
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -209,6 +211,43 @@ def test_layer_edge_cases():
     # bf16 output is the fp32 output rounded
     ob, _, _ = _run_layer(inp, out_dtype="bf16")
     assert torch.equal(ob, o1.to(torch.bfloat16))
+
+
+SKEWED = MI.LayerConfig("skewed", T=1100, D=256, E=16, H=128, G=4, kg=2, K=3, score_fn="sigmoid",
+                        bias="normal", norm=True, rsf=2.5, Hs=128, act="bf16", weight="bf16", bias_std=0.05)
+
+
+@pytest.mark.parametrize("path", ["grouped", "stream"])
+def test_layer_skewed_routing(path):
+    """A +10 selection bias on experts 1, 2 (group 0) and 6 (group 1) sends
+    every token to them: three experts with all 1100 rows each (five row
+    tiles of 224, 224, 224, 224, 204 rows on the grouped path), the others
+    empty."""
+    inp = MI.make_layer(SKEWED, DEV)
+    b = inp.sel_bias.clone()
+    b[[1, 2, 6]] += 10.0
+    inp = dataclasses.replace(inp, sel_bias=b)
+    info, _ = _check_layer(inp, path=path)
+    idx, _, counts = M.MoELayer.from_config(SKEWED).router(inp.x, inp.gate_w, inp.sel_bias)
+    torch.cuda.synchronize()
+    c = counts.cpu().numpy()
+    assert c[1] == c[2] == c[6] == SKEWED.T and c.sum() == 3 * SKEWED.T
+
+
+DEGENERATE = MI.LayerConfig("every_kept_expert", T=600, D=256, E=16, H=128, G=4, kg=2, K=8, score_fn="softmax",
+                            bias="none", norm=True, rsf=1.0, Hs=128, act="bf16", weight="bf16")
+
+
+def test_layer_selects_every_expert_of_the_kept_groups():
+    """K = kg*E/G: the selection is exactly the two kept groups' eight experts,
+    so the group choice alone decides the routing; renormalised gates sum to 1."""
+    inp = MI.make_layer(DEGENERATE, DEV)
+    _check_layer(inp, path="grouped")
+    idx, gate, _ = M.MoELayer.from_config(DEGENERATE).router(inp.x, inp.gate_w, None)
+    torch.cuda.synchronize()
+    groups = np.sort(idx.cpu().numpy() // (DEGENERATE.E // DEGENERATE.G), axis=1)
+    assert np.all(groups[:, :4] == groups[:, :1]) and np.all(groups[:, 4:] == groups[:, 4:5])
+    assert np.allclose(gate.sum(dim=1).cpu().numpy(), 1.0, atol=1e-5)
 
 
 # ---------------------------------------------------------------------------
