@@ -94,8 +94,10 @@ typedef struct moe_cfg moe_cfg;
  * the current HIP device. Returns MOE_ERR_INVALID_ARG for an invalid layer
  * (E % G != 0, topk_group > G, K > topk_group*E/G, ...), MOE_ERR_UNSUPPORTED
  * for a dtype/shape this build does not run (bf16/fp8 weights need D, H, Hs
- * multiples of 128; f32 needs D % 32 == 0), MOE_ERR_OOM if the workspace does
- * not fit. On success *out owns the workspace until moe_cfg_destroy. */
+ * multiples of 128 and max_tokens*D*2, max_tokens*max(H,Hs)*2 and
+ * 2*max(H,Hs)*D*2 below 2^32 bytes; f32 needs D % 32 == 0), MOE_ERR_OOM if
+ * the workspace does not fit. On success *out owns the workspace until
+ * moe_cfg_destroy. */
 moe_status moe_cfg_create(const moe_params* p, moe_cfg** out);
 
 /* Frees the workspace (synchronises the device first). NULL is a no-op. */

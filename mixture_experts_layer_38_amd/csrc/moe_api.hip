@@ -65,6 +65,13 @@ moe_status validate(const moe_params* p) {
   if (p->dim % 32 != 0) return MOE_ERR_UNSUPPORTED;
   if (!f32 && (p->dim % 128 || p->hidden % 128 || p->shared_hidden % 128)) return MOE_ERR_UNSUPPORTED;
   if (fp8 && p->path == MOE_PATH_GROUPED) return MOE_ERR_UNSUPPORTED;
+  // the grouped GEMMs address x rows, an expert's h rows and one expert's
+  // weights with 32-bit byte offsets
+  const uint64_t hmax = (uint64_t)std::max(p->hidden, p->shared_hidden);
+  if (!f32 && ((uint64_t)p->max_tokens * p->dim * 2 > 0xFFFFFFFFull ||
+               (uint64_t)p->max_tokens * hmax * 2 > 0xFFFFFFFFull ||
+               (uint64_t)2 * hmax * p->dim * 2 > 0xFFFFFFFFull))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 

@@ -55,6 +55,8 @@ def test_invalid_layers_rejected(kw):
     dict(shared_hidden=1000),
     dict(weight="fp8", path="grouped"),      # fp8 runs on the streaming kernels only
     dict(n_routed=1024, n_group=8),          # E > 512
+    dict(max_tokens=400000, dim=7168),       # x rows past 32-bit byte offsets
+    dict(max_tokens=1100000, hidden=2048),   # an expert's h rows past 32-bit byte offsets
 ])
 def test_unsupported_layers_rejected(kw):
     st, h = M.create_cfg(_params(**kw))
