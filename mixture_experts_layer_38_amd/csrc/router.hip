@@ -353,12 +353,20 @@ __global__ __launch_bounds__(256) void router_select_kernel(RouterArgs a) {
   }
 }
 
-// plane 0 += planes 1 .. splits-1, in plane order (one thread per logit)
+// plane 0 += planes 1 .. splits-1, in plane order (one thread per logit);
+// eight planes are loaded at a time, then added in order
 __global__ __launch_bounds__(256) void reduce_planes_kernel(float* __restrict__ logits, int n, int splits) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   float v = logits[i];
-  for (int sp = 1; sp < splits; ++sp) v += logits[(size_t)sp * n + i];
+  for (int sp = 1; sp < splits; sp += 8) {
+    float t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = (sp + u < splits) ? logits[(size_t)(sp + u) * n + i] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (sp + u < splits) v += t[u];
+  }
   logits[i] = v;
 }
 
