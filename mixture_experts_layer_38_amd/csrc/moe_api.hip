@@ -168,8 +168,8 @@ moe_status moe_cfg_create(const moe_params* p, moe_cfg** out) {
   const size_t act = (p->weight_dtype == MOE_F32) ? 4 : 2;  // h and y element size
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + std::max<size_t>(bytes, 1)); return o; };
-  // partial-logit planes: router_splits(T) * T <= 32 * CUs + T for every T
-  const size_t lg = (size_t)32 * c->num_cus + Tm;
+  // partial-logit planes: router_splits(T) * T <= 64 * CUs + T for every T
+  const size_t lg = (size_t)64 * c->num_cus + Tm;
   const size_t o_logits = take(lg * E * 4), o_idx = take(Tm * K * 4), o_gate = take(Tm * K * 4);
   const size_t o_wsplit = (p->act_dtype == MOE_BF16) ? take(3 * E * D * 2) : 0;
   const size_t o_counts = take(E * 4), o_offsets = take((E + 1) * 4), o_cursor = take(E * 4);

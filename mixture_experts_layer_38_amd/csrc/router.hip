@@ -370,9 +370,11 @@ __global__ __launch_bounds__(256) void reduce_planes_kernel(float* __restrict__ 
   logits[i] = v;
 }
 
+// K splits of the fp32 kernel: about one workgroup per CU; at most
+// 64*num_cus/T + 1 planes, which the partial-logit workspace holds
 int router_splits(int T, int D, int E, int num_cus) {
   const int tiles = ((T + 63) / 64) * ((E + 63) / 64);
-  int sp = (num_cus / 2 + tiles - 1) / tiles;
+  int sp = (num_cus + tiles - 1) / tiles;
   sp = sp < 1 ? 1 : (sp > D / 32 ? D / 32 : sp);
   const int kc = ((D / sp + 31) / 32) * 32;
   return (D + kc - 1) / kc;
@@ -380,7 +382,7 @@ int router_splits(int T, int D, int E, int num_cus) {
 
 // K splits of the bf16x3 kernel: about one workgroup per CU, and never more
 // than 32*num_cus/T + 1 planes (the partial-logit workspace holds
-// 32*num_cus + T rows).
+// 64*num_cus + T rows).
 static int router_x3_kc(int T, int D, int E, int num_cus) {
   const int tiles = ((T + kX3_BT - 1) / kX3_BT) * ((E + kX3_BE - 1) / kX3_BE);
   int sp = (num_cus + tiles - 1) / tiles;
