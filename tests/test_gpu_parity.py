@@ -290,6 +290,11 @@ def test_layer_v3_prefill(layers):
     _check_layer(inp, tokens=_sample(inp.cfg.T, 24), routed_only=False)
 
 
+def test_layer_v3_ep8_shard(layers):
+    inp = layers("v3_ep8_shard")
+    _check_layer(inp, tokens=_sample(inp.cfg.T, 16), routed_only=False)
+
+
 def test_layer_v3_decode_fp8(layers):
     inp = layers("v3_decode_fp8")
     _check_layer(inp)
