@@ -108,9 +108,23 @@ def run_prefill(args, torch, M, MI):
     ms = (t1 - t0) * 1e3 / args.steps
     stage_avg = {k: v / max(calls, 1) for k, v in stages.items()}
     log(f"{args.steps} steps: {ms:.3f} ms/step; stages {stage_avg}")
+    # load balance between steps on this step's counts (bias update + statistics)
+    bias = (inp.sel_bias.clone() if inp.sel_bias is not None
+            else torch.zeros(cfg.E, dtype=torch.float32, device="cuda"))
+    for _ in range(10):
+        M.bias_update(counts, bias, 1e-3)
+        M.load_stats(counts)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(200):
+        M.bias_update(counts, bias, 1e-3)
+        M.load_stats(counts)
+    ev1.record()
+    ev1.synchronize()
+    balance_us = ev0.elapsed_time(ev1) * 1e3 / 200
     g1_ms = stage_avg["gate_up_gemm"]
     g1_tflops = gateup_flops(cfg) / (g1_ms * 1e-3) / 1e12
-    res = dict(cfg=cfg, inp=inp, ms=ms, stages=stage_avg, counts=counts.cpu().tolist(),
+    res = dict(cfg=cfg, inp=inp, ms=ms, stages=stage_avg, counts=counts.cpu().tolist(), balance_us=balance_us,
                mfma_frac=mfma_flops(cfg) / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
                roofline=dict(bound="mfma", achieved=round(g1_tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                              frac=round(g1_tflops / PEAK_BF16_TFLOPS, 4), traffic=gateup_traffic(cfg),
@@ -261,6 +275,7 @@ def main():
                    "weights": cfg.weight, "parallelism": "single GPU"},
         "mfma_frac": round(res["mfma_frac"], 4),
         "stages_ms": {k: round(v, 4) for k, v in res["stages"].items()},
+        "balance_update_and_stats_us": round(res["balance_us"], 2),
         "roofline": res["roofline"],
     }
     if not args.no_cpu_baseline:

@@ -143,6 +143,30 @@ moe_status moe_router_forward(moe_cfg* cfg, const void* x, int T, const float* g
 moe_status moe_dispatch_forward(moe_cfg* cfg, const int32_t* topk_idx, int T, int32_t* offsets,
                                 int32_t* row_token, int32_t* slot_row, void* stream);
 
+/* Load balance between steps (no cfg; stream-ordered; one small launch).
+ *
+ * moe_bias_update: the auxiliary-loss-free update of the DeepSeek-V3 basics
+ * page, section 1.2 -- after a step, an overloaded expert's selection bias is
+ * lowered by gamma and an underloaded expert's raised by gamma. Overloaded
+ * means expert_counts[e] * E > sum(expert_counts), underloaded < (decided in
+ * integers); at exactly the mean load the bias stays. sel_bias [E] fp32 is
+ * updated in place (each new value is the fp32 sum).
+ *   expert_counts [E] int32 >= 0 (e.g. the counts a forward wrote)
+ *   E in [1, 512]; gamma finite.
+ *
+ * moe_load_stats: the load statistics of the load-balance code in the
+ * DeepSeekMoE + MLA notes (page 3): with load_e = counts_e / sum(counts),
+ *   stats[0] = standard deviation of load over the experts (n-1 denominator)
+ *   stats[1] = mean_e (load_e - 1/E)^2   (the load term of the expert-level
+ *              balance loss, before its weight)
+ *   stats[2] = max_e counts_e / (sum(counts)/E) - 1   (maximum violation)
+ * all 0 when sum(counts) == 0. stats: 3 fp32 in device memory.
+ *
+ * Both return MOE_ERR_INVALID_ARG (and launch nothing) for a null pointer, E
+ * outside [1, 512] or a non-finite gamma. */
+moe_status moe_bias_update(const int32_t* expert_counts, int E, float gamma, float* sel_bias, void* stream);
+moe_status moe_load_stats(const int32_t* expert_counts, int E, float* stats, void* stream);
+
 /* Stage timing (observability): when enabled, moe_layer_forward records HIP
  * events on its stream around each stage -- 0 router, 1 dispatch, 2 gate/up
  * GEMM, 3 down GEMM, 4 combine -- for up to MOE_TIMING_CALLS calls.

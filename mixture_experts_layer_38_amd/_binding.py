@@ -72,9 +72,11 @@ def load_library() -> ctypes.CDLL:
     lib.moe_cfg_stage_times.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int)]
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_bias_update.argtypes = [vp, ctypes.c_int, ctypes.c_float, vp, vp]
+    lib.moe_load_stats.argtypes = [vp, ctypes.c_int, vp, vp]
     for f in ("moe_cfg_create", "moe_cfg_destroy", "moe_layer_forward", "moe_router_forward",
               "moe_dispatch_forward", "moe_cfg_last_hip_error", "moe_cfg_set_stage_timing",
-              "moe_cfg_stage_times"):
+              "moe_cfg_stage_times", "moe_bias_update", "moe_load_stats"):
         getattr(lib, f).restype = ctypes.c_int
     del i32p
     _lib = lib
@@ -228,3 +230,28 @@ class MoELayer:
                                            _ptr(row_token), _ptr(slot_row), _stream_handle(stream))
         self._check(st, "moe_dispatch_forward")
         return offsets, row_token[:T * p.top_k], slot_row[:T * p.top_k]
+
+
+def bias_update(expert_counts, sel_bias, gamma: float, stream=None):
+    """moe_bias_update: sel_bias [E] fp32 (device, updated in place) from
+    expert_counts [E] int32 (device)."""
+    E = expert_counts.shape[0]
+    if sel_bias.dtype != torch.float32 or not sel_bias.is_contiguous() or sel_bias.shape[0] != E:
+        raise ValueError("sel_bias must be a contiguous float32 tensor of E elements")
+    st = load_library().moe_bias_update(_ptr(expert_counts.to(torch.int32).contiguous()), E, float(gamma),
+                                        _ptr(sel_bias), _stream_handle(stream))
+    if st != MOE_OK:
+        raise MoEError(st, "moe_bias_update")
+    return sel_bias
+
+
+def load_stats(expert_counts, stream=None):
+    """moe_load_stats: tensor [3] fp32 = (std of load, mean (load - 1/E)^2,
+    max violation) from expert_counts [E] int32 (device)."""
+    E = expert_counts.shape[0]
+    stats = torch.empty((3,), dtype=torch.float32, device=expert_counts.device)
+    st = load_library().moe_load_stats(_ptr(expert_counts.to(torch.int32).contiguous()), E, _ptr(stats),
+                                       _stream_handle(stream))
+    if st != MOE_OK:
+        raise MoEError(st, "moe_load_stats")
+    return stats

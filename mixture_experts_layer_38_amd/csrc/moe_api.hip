@@ -286,6 +286,19 @@ moe_status moe_router_forward(moe_cfg* c, const void* x, int T, const float* gat
   return e == hipSuccess ? MOE_OK : hip_fail(c, e);
 }
 
+moe_status moe_bias_update(const int32_t* expert_counts, int E, float gamma, float* sel_bias, void* stream) {
+  if (!expert_counts || !sel_bias || E < 1 || E > kMaxExperts) return MOE_ERR_INVALID_ARG;
+  if (!(gamma == gamma) || gamma > 3.4e38f || gamma < -3.4e38f) return MOE_ERR_INVALID_ARG;  // NaN, inf
+  return launch_balance(expert_counts, E, gamma, sel_bias, nullptr, (hipStream_t)stream) == hipSuccess
+             ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_load_stats(const int32_t* expert_counts, int E, float* stats, void* stream) {
+  if (!expert_counts || !stats || E < 1 || E > kMaxExperts) return MOE_ERR_INVALID_ARG;
+  return launch_balance(expert_counts, E, 0.f, nullptr, stats, (hipStream_t)stream) == hipSuccess
+             ? MOE_OK : MOE_ERR_HIP;
+}
+
 moe_status moe_dispatch_forward(moe_cfg* c, const int32_t* topk_idx, int T, int32_t* offsets,
                                 int32_t* row_token, int32_t* slot_row, void* stream) {
   if (!c) return MOE_ERR_INVALID_ARG;

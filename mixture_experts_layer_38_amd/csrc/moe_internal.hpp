@@ -203,4 +203,7 @@ struct CombineArgs {
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 
+// one workgroup: bias update (bias != null) and/or load statistics (stats != null)
+hipError_t launch_balance(const int32_t* counts, int E, float gamma, float* bias, float* stats, hipStream_t s);
+
 }  // namespace moe

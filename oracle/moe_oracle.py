@@ -23,7 +23,10 @@ What it computes, and where the pages define it (page titles as printed):
   the affinity only to choose the top-K; the gate value comes from the
   original affinity.
 * "Transformer block" article (page 4), data-flow section: the scores may come
-  from softmax "or another activation" (sigmoid is used for the V3 shapes).
+  from softmax or from another activation (sigmoid is used for the V3 shapes).
+* "DeepSeek-V3 basics" (page 5), section 1.2, and the "DeepSeekMoE + MLA"
+  notes (page 3), load-balance section: the bias update after a step and the
+  load statistics (see bias_update and load_stats at the end).
 
 Readings where the pages are silent or garbled (the formula images are
 missing from the extracted pages):
@@ -255,3 +258,50 @@ def layer_forward(p: RouterParams, u: np.ndarray, gate_w: np.ndarray, sel_bias, 
 def near_tie_tokens(routing: dict, window: float = 1e-6) -> np.ndarray:
     """Tokens whose K/K+1 or group-boundary selection-score gap is within the window."""
     return np.nonzero((routing["gap_k"] < window) | (routing["gap_g"] < window))[0]
+
+
+# ----------------------------------------------------------------------------
+# load balance between steps
+# ----------------------------------------------------------------------------
+
+
+def bias_update(counts, bias, gamma: float) -> np.ndarray:
+    """Auxiliary-loss-free balancing ("DeepSeek-V3 basics", page 5, section
+    1.2): after a step, an overloaded expert's selection bias goes down by
+    gamma and an underloaded expert's goes up by gamma. Reading: overloaded
+    means more assignments than the mean load sum(counts)/E, underloaded fewer;
+    at exactly the mean the bias stays. The bias is stored as float32, so the
+    new value is the float32 rounding of the exact sum."""
+    c = np.asarray(counts, dtype=np.int64)
+    E = c.shape[0]
+    total = int(c.sum())
+    b = np.asarray(bias, dtype=np.float32).astype(np.float64)
+    out = b.copy()
+    for e in range(E):
+        if c[e] * E > total:
+            out[e] = b[e] - float(np.float32(gamma))
+        elif c[e] * E < total:
+            out[e] = b[e] + float(np.float32(gamma))
+    return out.astype(np.float32)
+
+
+def load_stats(counts) -> dict:
+    """Load statistics of one step ("DeepSeekMoE + MLA" notes, page 3, load
+    balance code): load_e = counts_e / sum(counts); its standard deviation over
+    the experts with the n-1 denominator (as torch's std), the load term
+    mean_e (load_e - 1/E)^2 of the expert-level balance loss, and the maximum
+    violation max_e counts_e / mean - 1 with mean = sum(counts) / E. With no
+    assignments at all every statistic is 0."""
+    c = np.asarray(counts, dtype=np.float64)
+    E = c.shape[0]
+    total = c.sum()
+    if total == 0:  # no assignments: nothing is loaded (reading: all zero)
+        return {"load_std": 0.0, "load_loss": 0.0, "max_violation": 0.0}
+    load = c / total
+    mean = total / E
+    dev = load - load.mean()
+    return {
+        "load_std": float(np.sqrt((dev * dev).sum() / (E - 1))) if E > 1 else 0.0,
+        "load_loss": float(((load - 1.0 / E) ** 2).mean()),
+        "max_violation": float(c.max() / mean - 1.0),
+    }

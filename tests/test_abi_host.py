@@ -73,3 +73,23 @@ def test_null_arguments_rejected():
     assert lib.moe_router_forward(None, None, 0, None, None, None, None, None, None) == M.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch_forward(None, None, 0, None, None, None, None) == M.MOE_ERR_INVALID_ARG
     assert lib.moe_cfg_destroy(None) == M.MOE_OK
+
+
+def test_balance_entry_points_reject_bad_arguments():
+    """Null pointers, E outside [1, 512] and a non-finite gamma are refused
+    before anything is launched (host buffers stand in for device pointers)."""
+    lib = M.load_library()
+    counts = (ctypes.c_int32 * 8)()
+    buf = (ctypes.c_float * 8)()
+    c, b = ctypes.cast(counts, ctypes.c_void_p), ctypes.cast(buf, ctypes.c_void_p)
+    bad = M.MOE_ERR_INVALID_ARG
+    assert lib.moe_bias_update(None, 8, 0.01, b, None) == bad
+    assert lib.moe_bias_update(c, 8, 0.01, None, None) == bad
+    assert lib.moe_bias_update(c, 0, 0.01, b, None) == bad
+    assert lib.moe_bias_update(c, 513, 0.01, b, None) == bad
+    assert lib.moe_bias_update(c, 8, float("nan"), b, None) == bad
+    assert lib.moe_bias_update(c, 8, float("inf"), b, None) == bad
+    assert lib.moe_load_stats(None, 8, b, None) == bad
+    assert lib.moe_load_stats(c, 8, None, None) == bad
+    assert lib.moe_load_stats(c, 0, b, None) == bad
+    assert lib.moe_load_stats(c, 600, b, None) == bad

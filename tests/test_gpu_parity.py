@@ -15,6 +15,7 @@ import torch
 import mixture_experts_layer_38_amd as M
 import moe_inputs as MI
 from oracle import adapter as A
+from oracle import moe_oracle as O
 from tests.parity import TOL, check_routing, layer_error, near_tie_mask
 
 pytestmark = pytest.mark.gpu
@@ -248,6 +249,58 @@ def test_layer_selects_every_expert_of_the_kept_groups():
     groups = np.sort(idx.cpu().numpy() // (DEGENERATE.E // DEGENERATE.G), axis=1)
     assert np.all(groups[:, :4] == groups[:, :1]) and np.all(groups[:, 4:] == groups[:, 4:5])
     assert np.allclose(gate.sum(dim=1).cpu().numpy(), 1.0, atol=1e-5)
+
+
+def test_bias_update_and_load_stats_match_the_oracle():
+    """Bit-exact bias update (integer over/underload decision, fp32 sums) and
+    load statistics within 1e-6 relative, for E from 1 to 512, with experts
+    exactly at the mean load and with no assignments at all."""
+    rng = np.random.default_rng(11)
+    for E in (1, 12, 64, 256, 512):
+        # counts = mean + d with sum(d) = 0, d = 0 on the first E/8 experts
+        d = rng.integers(-30, 31, size=E)
+        tied = max(1, E // 8)
+        d[:tied] = 0
+        if E > tied:
+            rest = -int(d.sum())
+            d[tied:] += rest // (E - tied)
+            d[tied:tied + rest % (E - tied)] += 1
+        counts = (1000 + d).astype(np.int32)
+        assert counts.sum() == 1000 * E and np.all(counts[:tied] == 1000)
+        for cnt in (counts, np.zeros(E, dtype=np.int32)):
+            bias = (rng.standard_normal(E) * 0.1).astype(np.float32)
+            b = torch.tensor(bias, device=DEV)
+            c = torch.tensor(cnt, device=DEV)
+            M.bias_update(c, b, 1e-3)
+            st = M.load_stats(c).cpu().numpy()
+            torch.cuda.synchronize()
+            assert np.array_equal(b.cpu().numpy(), O.bias_update(cnt, bias, 1e-3)), E
+            ref = O.load_stats(cnt)
+            for i, k in enumerate(("load_std", "load_loss", "max_violation")):
+                assert abs(st[i] - ref[k]) <= 1e-6 * max(1.0, abs(ref[k])), (E, k, st[i], ref[k])
+
+
+def test_bias_update_closes_the_loop_on_the_gpu():
+    """Route, count, update the bias, repeat: each update equals the oracle's
+    update of the GPU's own counts, and the skewed load evens out."""
+    cfg = SMALL_SIG
+    inp = MI.make_layer(cfg, DEV)
+    layer = M.MoELayer.from_config(cfg)
+    bias = torch.zeros(cfg.E, dtype=torch.float32, device=DEV)
+    bias[:4] = 0.3
+    std0 = None
+    for step in range(40):
+        _, _, counts = layer.router(inp.x, inp.gate_w, bias)
+        before = bias.cpu().numpy()
+        M.bias_update(counts, bias, 0.01)
+        torch.cuda.synchronize()
+        cnt = counts.cpu().numpy()
+        assert np.array_equal(bias.cpu().numpy(), O.bias_update(cnt, before, 0.01)), step
+        if std0 is None:
+            std0 = O.load_stats(cnt)["load_std"]
+    _, _, counts = layer.router(inp.x, inp.gate_w, bias)
+    std = float(M.load_stats(counts)[0])
+    assert std < 0.5 * std0, (std, std0)
 
 
 # ---------------------------------------------------------------------------

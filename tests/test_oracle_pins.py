@@ -355,6 +355,63 @@ def test_permutation_equivariance():
 
 
 # ----------------------------------------------------------------------------
+# load balance between steps
+# ----------------------------------------------------------------------------
+
+
+def test_bias_update_rule_closed_forms():
+    """DeepSeek-V3 basics page, section 1.2: overloaded experts go down by
+    gamma, underloaded ones up, and an expert exactly at the mean load stays."""
+    b = np.array([0.5, -0.25, 0.0, 1.0], dtype=np.float32)
+    out = O.bias_update([5, 1, 3, 3], b, 0.125)  # mean load 3
+    assert out.dtype == np.float32
+    assert out.tolist() == [0.375, -0.125, 0.0, 1.0]
+    assert O.bias_update([2, 2, 2, 2], b, 0.125).tolist() == b.tolist()  # balanced: no change
+    assert O.bias_update([0, 0, 0, 0], b, 0.125).tolist() == b.tolist()  # nothing routed
+    # the new value is the float32 rounding of the exact sum
+    one = np.array([1.0], dtype=np.float32)
+    assert O.bias_update([0], one, 1e-8).tolist() == [1.0]
+    assert O.bias_update([1, 0], np.float32([1.0, 1.0]), 2.0 ** -20).tolist() == [1.0 - 2.0 ** -20, 1.0 + 2.0 ** -20]
+
+
+def test_bias_update_balances_a_skewed_router():
+    """Applied step after step with the oracle router, the rule removes most
+    of the imbalance that a skewed initial bias causes (its purpose in
+    section 1.2), and the gates stay those of the unbiased scores."""
+    T, D, E, K = 512, 32, 16, 2
+    u = RNG.standard_normal((T, D))
+    gw = RNG.standard_normal((E, D)) / math.sqrt(D)
+    p = O.RouterParams(E=E, K=K, G=4, kg=2, score_fn="sigmoid", norm=True, rsf=1.0)
+    b = np.zeros(E, dtype=np.float32)
+    b[:3] = 0.3  # three experts favoured
+    std0 = O.load_stats(O.route(u, gw, b.astype(np.float64), p)["counts"])["load_std"]
+    for _ in range(60):
+        R = O.route(u, gw, b.astype(np.float64), p)
+        b = O.bias_update(R["counts"], b, 0.01)
+    R = O.route(u, gw, b.astype(np.float64), p)
+    assert O.load_stats(R["counts"])["load_std"] < 0.35 * std0
+    s = O.affinity(O.router_logits(u, gw), "sigmoid")
+    g = np.take_along_axis(s, R["idx"], 1)
+    assert np.allclose(R["gate"], g / g.sum(1, keepdims=True), atol=1e-12)
+
+
+def test_load_stats_closed_forms():
+    E = 8
+    z = O.load_stats(np.full(E, 5))
+    assert z == {"load_std": 0.0, "load_loss": 0.0, "max_violation": 0.0}
+    one = O.load_stats(np.eye(E, dtype=np.int64)[3] * 40)  # every assignment on one expert
+    assert math.isclose(one["load_std"], 1 / math.sqrt(E), rel_tol=1e-12)
+    assert math.isclose(one["load_loss"], (E - 1) / E ** 2, rel_tol=1e-12)
+    assert math.isclose(one["max_violation"], E - 1, rel_tol=1e-12)
+    assert O.load_stats(np.zeros(E, dtype=np.int64)) == {"load_std": 0.0, "load_loss": 0.0, "max_violation": 0.0}
+    c = RNG.integers(0, 50, size=64)
+    st = O.load_stats(c)
+    load = torch.tensor(c, dtype=torch.float64) / c.sum()
+    assert math.isclose(st["load_std"], float(load.std()), rel_tol=1e-12)  # torch's n-1 std
+    assert math.isclose(st["max_violation"], c.max() * 64 / c.sum() - 1, rel_tol=1e-12)
+
+
+# ----------------------------------------------------------------------------
 # the pins must catch plausible mistakes
 # ----------------------------------------------------------------------------
 
@@ -390,3 +447,14 @@ def test_pins_catch_planted_bugs(monkeypatch):
     with pytest.raises(AssertionError):
         test_top1_moe_without_shared_or_residual()
     monkeypatch.setattr(O, "select_experts", good_sel)
+
+    good_bias = O.bias_update
+
+    def flipped(counts, bias, gamma):  # overloaded experts pushed further up
+        return good_bias(counts, bias, -gamma)
+    monkeypatch.setattr(O, "bias_update", flipped)
+    with pytest.raises(AssertionError):
+        test_bias_update_rule_closed_forms()
+    with pytest.raises(AssertionError):
+        test_bias_update_balances_a_skewed_router()
+    monkeypatch.setattr(O, "bias_update", good_bias)
