@@ -26,14 +26,18 @@
 // branch-free.
 // Both operands are staged through two LDS buffers (rows padded to 144 bytes so
 // that the 16-byte fragment reads of consecutive rows hit distinct banks): the
-// next K step is loaded into registers while the current one is multiplied,
-// then written to the other buffer; one barrier per K step.
+// weight rows of the next K step, and the token rows of the step after it
+// (two register slots: gathered rows are the slower ones to arrive), are
+// loaded into registers while the current step is multiplied, and the next
+// step is written to the other buffer; one barrier per K step.
 // Blocks are mapped so that runs of consecutive tiles land on one XCD and its
 // L2, with runs spread round-robin over the XCDs. Tiles are ordered
 // column-tile major, and an expert's rows are split evenly (in 32-row blocks)
 // over its two or three row tiles: the row tiles that read one weight slice
 // run side by side at the same pace, so the second and third reads of each
 // weight line hit that L2 (this halves the bytes fetched past L2).
+#include <type_traits>
+
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -114,11 +118,21 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
   // down GEMM: the tile's gates into LDS for the epilogue
   if (kMode == 1 && tid < BM) s_gate[tid] = (t.gate != nullptr && tid < t.vrows) ? t.gate[t.m0 + tid] : 1.0f;
 
-  uint4 pf[kLd];
+  // A rows (gathered token rows) are loaded two K steps ahead through two
+  // register slots; B rows (weights) one step ahead
+  const int nk = t.K / BK;
+  uint4 pa[2][kLd / 2], pb[kLd / 2];
 #pragma unroll
-  for (int j = 0; j < kLd; ++j) pf[j] = gload(j, 0);
+  for (int j = 0; j < kLd / 2; ++j) pa[0][j] = gload(j, 0);
 #pragma unroll
-  for (int j = 0; j < kLd; ++j) *reinterpret_cast<uint4*>(&smem[0][(r0 + 64 * j) * LDW + c8 * 8]) = pf[j];
+  for (int j = 0; j < kLd / 2; ++j) pb[j] = gload(kLd / 2 + j, 0);
+#pragma unroll
+  for (int j = 0; j < kLd / 2; ++j) pa[1][j] = gload(j, (nk > 1 ? 1 : 0) * BK);
+#pragma unroll
+  for (int j = 0; j < kLd / 2; ++j) *reinterpret_cast<uint4*>(&smem[0][(r0 + 64 * j) * LDW + c8 * 8]) = pa[0][j];
+#pragma unroll
+  for (int j = 0; j < kLd / 2; ++j)
+    *reinterpret_cast<uint4*>(&smem[0][(r0 + 64 * (kLd / 2 + j)) * LDW + c8 * 8]) = pb[j];
   __syncthreads();
 
   // Fragments are double-buffered across the four 16-wide substeps of a K
@@ -144,29 +158,37 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
         acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[slot][i], fb[slot][c], acc[i][c], 0, 0, 0);
   };
 
-  // The next K step's tile, loaded into registers at the top of a step, is
-  // written to the other LDS buffer interleaved with the MFMAs of the last
-  // substep: the loads get three quarters of a step to land, and the LDS
-  // writes overlap the matrix work.
-  auto store_half = [&](int buf, int h) __attribute__((always_inline)) {
+  // The next K step's tile is written to the other LDS buffer interleaved
+  // with the MFMAs of the last substep: its weight rows, loaded at the top of
+  // this step, get three quarters of a step to land, its token rows, loaded a
+  // step earlier, one and three quarters; the LDS writes overlap the matrix
+  // work.
+  auto store_a = [&](int buf, const uint4 (&v)[kLd / 2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = (kLd / 2) * h; j < (kLd / 2) * (h + 1); ++j)
-      *reinterpret_cast<uint4*>(&smem[buf][(r0 + 64 * j) * LDW + c8 * 8]) = pf[j];
+    for (int j = 0; j < kLd / 2; ++j) *reinterpret_cast<uint4*>(&smem[buf][(r0 + 64 * j) * LDW + c8 * 8]) = v[j];
+  };
+  auto store_b = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kLd / 2; ++j)
+      *reinterpret_cast<uint4*>(&smem[buf][(r0 + 64 * (kLd / 2 + j)) * LDW + c8 * 8]) = pb[j];
   };
   // instruction counts per substep, for the interleave below
   constexpr int nr = kNC + NRB, nm = kNC * NRB, nw = kLd / 2;
   constexpr int p1 = nr < nm ? nr : nm;              // (MFMA, LDS read) pairs
   constexpr int p4 = 2 * nw < nm ? 2 * nw : nm;      // last substep: (MFMA, LDS write) pairs
 
-  const int nk = t.K / BK;
   read_frags(smem[0], 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
+  auto kstep = [&](int kt, auto s_c) __attribute__((always_inline)) {
+    constexpr int S = decltype(s_c)::value;  // register slot of A(kt), refilled with A(kt+2)
     const int cur = kt & 1;
     // The last step reloads its own K slice and writes the idle buffer, so
     // the step body has no branch (and the scheduler sees one region).
     const int knext = (kt + 1 < nk ? kt + 1 : kt) * BK;
+    const int knext2 = (kt + 2 < nk ? kt + 2 : nk - 1) * BK;
 #pragma unroll
-    for (int j = 0; j < kLd; ++j) pf[j] = gload(j, knext);
+    for (int j = 0; j < kLd / 2; ++j) pa[S][j] = gload(j, knext2);
+#pragma unroll
+    for (int j = 0; j < kLd / 2; ++j) pb[j] = gload(kLd / 2 + j, knext);
     // substeps 0-2: next fragments interleaved with the MFMAs
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -193,8 +215,8 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
     __builtin_amdgcn_sched_group_barrier(0x008, nm - p1, 0);
     __builtin_amdgcn_sched_barrier(0);
     // substep 3: the whole next tile into the idle buffer
-    store_half(cur ^ 1, 0);
-    store_half(cur ^ 1, 1);
+    store_a(cur ^ 1, pa[S ^ 1]);
+    store_b(cur ^ 1);
     mfmas(1);
 #pragma unroll
     for (int q = 0; q < p4; ++q) {
@@ -206,7 +228,13 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     read_frags(smem[cur ^ 1], 0, 0);
+  };
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    kstep(kt, std::integral_constant<int, 0>{});
+    kstep(kt + 1, std::integral_constant<int, 1>{});
   }
+  if (kt < nk) kstep(kt, std::integral_constant<int, 0>{});
 
   // D layout of the 32x32 MFMA: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
   // column l%32.
