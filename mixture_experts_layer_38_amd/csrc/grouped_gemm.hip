@@ -1,5 +1,8 @@
 // Grouped bf16 MFMA GEMMs of the routed experts and the shared expert
-// (prefill-sized token counts).
+// (prefill-sized token counts), with bf16 weights or e4m3 weights (one fp32
+// scale per 128x128 block, the block-wise quantisation of the architecture
+// article, section 4): e4m3 weights are widened exactly to fp32, multiplied
+// by their block scale and rounded to bf16 as they are written to LDS.
 //
 // One launch covers every problem: routed expert e (its rows are the
 // expert-contiguous rows offsets[e] .. offsets[e+1]-1 built by the dispatch)
@@ -52,7 +55,9 @@ constexpr int kLd = 8;          // 16-byte global loads per thread per K step
 struct Tile {
   const uint16_t* a_rows;  // GEMM1: x; GEMM2: h of this problem (row 0 = row_base)
   const int32_t* tok;      // GEMM1 routed: row -> token map at row_base; null = identity
-  const uint16_t* w;       // weights of this problem
+  const void* w;           // weights of this problem (bf16, or e4m3 codes)
+  const float* ws;         // e4m3: the problem's 128x128 block scales, [rows/128][K/128]
+  int kbn;                 // e4m3: K/128
   uint16_t* c;             // output rows of this problem (row 0 = row_base)
   const float* gate;       // GEMM2 routed: gates at row_base; null = 1
   uint32_t a_bytes;        // extent of a_rows (buffer range)
@@ -66,7 +71,7 @@ struct Tile {
 };
 }  // namespace
 
-template <int kMode, int NRB>
+template <int kMode, int NRB, bool kW8>
 __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows * LDW], float* s_gate) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
@@ -80,7 +85,7 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(t.a_rows), (short)0, t.a_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(t.w), (short)0, t.w_bytes, 0x00020000);
+      const_cast<void*>(t.w), (short)0, t.w_bytes, 0x00020000);
   uint32_t voff[kLd];
 #pragma unroll
   for (int j = 0; j < kLd / 2; ++j) {
@@ -89,16 +94,27 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
     const int row = (kMode == 0 && t.tok != nullptr) ? t.tok[mm] : mm;
     voff[j] = ((uint32_t)row * (uint32_t)t.lda + c8 * 8) * 2u;
   }
+  // Weight (B) rows. bf16: rows r0 + 64*j (rows past D read row 0 instead).
+  // e4m3: thread tid takes B row tid/2, bytes 32*(tid%2) .. +31 of the
+  // 64-byte K slice (two loads), and the block scale of that row.
+  const float* wsrow = nullptr;
 #pragma unroll
   for (int j = 0; j < kLd / 2; ++j) {
-    const int b = r0 + 64 * j;  // 0..255
+    const int b = kW8 ? (tid >> 1) : r0 + 64 * j;
     int wrow = (kMode == 0) ? (b < 128 ? t.nt * 128 + b : t.Hp + t.nt * 128 + b - 128) : t.nt * BN + b;
     if (kMode == 1 && wrow >= t.D) wrow = 0;
-    voff[kLd / 2 + j] = ((uint32_t)wrow * (uint32_t)t.K + c8 * 8) * 2u;
+    if (kW8) {
+      voff[kLd / 2 + j] = (uint32_t)wrow * (uint32_t)t.K + 32u * (tid & 1) + 16u * j;
+      if (j == 0) wsrow = t.ws + (size_t)(wrow >> 7) * t.kbn;
+    } else {
+      voff[kLd / 2 + j] = ((uint32_t)wrow * (uint32_t)t.K + c8 * 8) * 2u;
+    }
   }
   auto gload = [&](int j, int k0) __attribute__((always_inline)) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(j < kLd / 2 ? ra : rb, voff[j], k0 * 2, 0));
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(j < kLd / 2 ? ra : rb, voff[j],
+                                                                           (j >= kLd / 2 && kW8) ? k0 : k0 * 2, 0));
   };
+  constexpr int kLdB = kW8 ? 2 : kLd / 2;  // 16-byte weight loads per thread per K step
 
   f32x16 acc[NRB > 0 ? NRB : 1][kNC];
 #pragma unroll
@@ -121,19 +137,15 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
   // A rows (gathered token rows) are loaded two K steps ahead through two
   // register slots; B rows (weights) one step ahead
   const int nk = t.K / BK;
-  uint4 pa[2][kLd / 2], pb[kLd / 2];
+  uint4 pa[2][kLd / 2], pb[kLdB];
+  float pbs = 1.0f;  // e4m3: block scale of the staged weight slice
 #pragma unroll
   for (int j = 0; j < kLd / 2; ++j) pa[0][j] = gload(j, 0);
 #pragma unroll
-  for (int j = 0; j < kLd / 2; ++j) pb[j] = gload(kLd / 2 + j, 0);
+  for (int j = 0; j < kLdB; ++j) pb[j] = gload(kLd / 2 + j, 0);
+  if (kW8) pbs = wsrow[0];
 #pragma unroll
   for (int j = 0; j < kLd / 2; ++j) pa[1][j] = gload(j, (nk > 1 ? 1 : 0) * BK);
-#pragma unroll
-  for (int j = 0; j < kLd / 2; ++j) *reinterpret_cast<uint4*>(&smem[0][(r0 + 64 * j) * LDW + c8 * 8]) = pa[0][j];
-#pragma unroll
-  for (int j = 0; j < kLd / 2; ++j)
-    *reinterpret_cast<uint4*>(&smem[0][(r0 + 64 * (kLd / 2 + j)) * LDW + c8 * 8]) = pb[j];
-  __syncthreads();
 
   // Fragments are double-buffered across the four 16-wide substeps of a K
   // step: the LDS reads of substep kk+1 are issued before the MFMAs of
@@ -168,10 +180,35 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
     for (int j = 0; j < kLd / 2; ++j) *reinterpret_cast<uint4*>(&smem[buf][(r0 + 64 * j) * LDW + c8 * 8]) = v[j];
   };
   auto store_b = [&](int buf) __attribute__((always_inline)) {
+    if (kW8) {
+      // 32 e4m3 codes -> exact fp32 -> times the block scale -> bf16 (RNE)
+      uint16_t* dst = &smem[buf][(BM + (tid >> 1)) * LDW + 32 * (tid & 1)];
 #pragma unroll
-    for (int j = 0; j < kLd / 2; ++j)
-      *reinterpret_cast<uint4*>(&smem[buf][(r0 + 64 * (kLd / 2 + j)) * LDW + c8 * 8]) = pb[j];
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t w[4] = {pb[j].x, pb[j].y, pb[j].z, pb[j].w};
+        uint32_t o[8];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[d], 1.0f, false);
+          const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w[d], 1.0f, true);
+          const bf16x2 a = {(__bf16)(lo.x * pbs), (__bf16)(lo.y * pbs)};
+          const bf16x2 b = {(__bf16)(hi.x * pbs), (__bf16)(hi.y * pbs)};
+          o[2 * d] = __builtin_bit_cast(uint32_t, a);
+          o[2 * d + 1] = __builtin_bit_cast(uint32_t, b);
+        }
+        *reinterpret_cast<uint4*>(dst + 16 * j) = make_uint4(o[0], o[1], o[2], o[3]);
+        *reinterpret_cast<uint4*>(dst + 16 * j + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kLd / 2; ++j)
+        *reinterpret_cast<uint4*>(&smem[buf][(r0 + 64 * (kLd / 2 + j)) * LDW + c8 * 8]) = pb[j];
+    }
   };
+#pragma unroll
+  for (int j = 0; j < kLd / 2; ++j) *reinterpret_cast<uint4*>(&smem[0][(r0 + 64 * j) * LDW + c8 * 8]) = pa[0][j];
+  store_b(0);
+  __syncthreads();
   // instruction counts per substep, for the interleave below
   constexpr int nr = kNC + NRB, nm = kNC * NRB, nw = kLd / 2;
   constexpr int p1 = nr < nm ? nr : nm;              // (MFMA, LDS read) pairs
@@ -188,7 +225,8 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
 #pragma unroll
     for (int j = 0; j < kLd / 2; ++j) pa[S][j] = gload(j, knext2);
 #pragma unroll
-    for (int j = 0; j < kLd / 2; ++j) pb[j] = gload(kLd / 2 + j, knext);
+    for (int j = 0; j < kLdB; ++j) pb[j] = gload(kLd / 2 + j, knext);
+    if (kW8) pbs = wsrow[knext >> 7];
     // substeps 0-2: next fragments interleaved with the MFMAs
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -289,7 +327,9 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
   }
 }
 
-template <int kMode>  // 0: gate/up + SwiGLU, 1: down + gate scale
+// kMode 0: gate/up + SwiGLU, 1: down + gate scale; kW8: e4m3 weights with
+// 128x128 block scales, widened to bf16 (times the scale) as they are staged
+template <int kMode, bool kW8>
 __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][kRows * LDW];
   __shared__ int32_t s_pre[kMaxExperts + 2];
@@ -314,6 +354,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
   const bool routed = p < a.E;
   const int rows = routed ? s_off[p + 1] - s_off[p] : a.T;
   const int row_base = routed ? s_off[p] : 0;
+  constexpr size_t kWB = kW8 ? 1 : 2;  // bytes per weight
   Tile t;
   t.Hp = routed ? a.H : a.Hs;
   t.D = a.D;
@@ -330,25 +371,29 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
     t.a_rows = static_cast<const uint16_t*>(a.a);
     t.lda = a.D;
     t.tok = routed ? a.row_token + row_base : nullptr;
-    t.w = routed ? static_cast<const uint16_t*>(a.w) + (size_t)p * 2 * t.Hp * a.D
-                 : static_cast<const uint16_t*>(a.w_shared);
+    t.w = routed ? static_cast<const char*>(a.w) + (size_t)p * 2 * t.Hp * a.D * kWB
+                 : static_cast<const char*>(a.w_shared);
+    t.kbn = a.D / 128;
+    t.ws = kW8 ? (routed ? a.w_scale + (size_t)p * (2 * t.Hp / 128) * t.kbn : a.w_shared_scale) : nullptr;
     t.c = routed ? static_cast<uint16_t*>(a.c) + (size_t)row_base * a.H : static_cast<uint16_t*>(a.c_shared);
     t.ldc = t.Hp;
     t.gate = nullptr;
     t.a_bytes = (uint32_t)((size_t)a.x_rows * a.D * 2);
-    t.w_bytes = (uint32_t)((size_t)2 * t.Hp * a.D * 2);
+    t.w_bytes = (uint32_t)((size_t)2 * t.Hp * a.D * kWB);
   } else {
     t.a_rows = routed ? static_cast<const uint16_t*>(a.a) + (size_t)row_base * a.H
                       : static_cast<const uint16_t*>(a.a_shared);
     t.lda = t.Hp;
     t.tok = nullptr;
-    t.w = routed ? static_cast<const uint16_t*>(a.w) + (size_t)p * a.D * t.Hp
-                 : static_cast<const uint16_t*>(a.w_shared);
+    t.w = routed ? static_cast<const char*>(a.w) + (size_t)p * a.D * t.Hp * kWB
+                 : static_cast<const char*>(a.w_shared);
+    t.kbn = t.Hp / 128;
+    t.ws = kW8 ? (routed ? a.w_scale + (size_t)p * (a.D / 128) * t.kbn : a.w_shared_scale) : nullptr;
     t.c = routed ? static_cast<uint16_t*>(a.c) + (size_t)row_base * a.D : static_cast<uint16_t*>(a.c_shared);
     t.ldc = a.D;
     t.gate = routed ? a.row_gate + row_base : nullptr;
     t.a_bytes = (uint32_t)((size_t)rows * t.Hp * 2);
-    t.w_bytes = (uint32_t)((size_t)a.D * t.Hp * 2);
+    t.w_bytes = (uint32_t)((size_t)a.D * t.Hp * kWB);
   }
 
   // valid 32-row blocks of this wave: wm + 2*i for i < nrb
@@ -357,11 +402,11 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
 #pragma unroll
   for (int i = 0; i < 4; ++i) nrb += (32 * (wm + 2 * i) < t.vrows) ? 1 : 0;
   switch (nrb) {
-    case 4: tile_body<kMode, 4>(t, smem, s_gate); break;
-    case 3: tile_body<kMode, 3>(t, smem, s_gate); break;
-    case 2: tile_body<kMode, 2>(t, smem, s_gate); break;
-    case 1: tile_body<kMode, 1>(t, smem, s_gate); break;
-    default: tile_body<kMode, 0>(t, smem, s_gate); break;
+    case 4: tile_body<kMode, 4, kW8>(t, smem, s_gate); break;
+    case 3: tile_body<kMode, 3, kW8>(t, smem, s_gate); break;
+    case 2: tile_body<kMode, 2, kW8>(t, smem, s_gate); break;
+    case 1: tile_body<kMode, 1, kW8>(t, smem, s_gate); break;
+    default: tile_body<kMode, 0, kW8>(t, smem, s_gate); break;
   }
 }
 
@@ -371,17 +416,23 @@ int grouped_blocks(int max_items, int run) {
   return ((runs + 7) / 8) * 8 * run;
 }
 
-hipError_t launch_grouped_gateup_bf16(const ExpertGemmArgs& a, hipStream_t s) {
+hipError_t launch_grouped_gateup(const ExpertGemmArgs& a, int fp8, hipStream_t s) {
   const int blocks = grouped_blocks(a.max_items, kRun);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<0>, dim3(blocks), dim3(512), 0, s, a);
+  if (fp8)
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<0, true>), dim3(blocks), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<0, false>), dim3(blocks), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_grouped_down_bf16(const ExpertGemmArgs& a, hipStream_t s) {
+hipError_t launch_grouped_down(const ExpertGemmArgs& a, int fp8, hipStream_t s) {
   const int blocks = grouped_blocks(a.max_items, kRun);
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(grouped_gemm_bf16_kernel<1>, dim3(blocks), dim3(512), 0, s, a);
+  if (fp8)
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<1, true>), dim3(blocks), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((grouped_gemm_bf16_kernel<1, false>), dim3(blocks), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

@@ -64,7 +64,6 @@ moe_status validate(const moe_params* p) {
   if (!(f32 || bf || fp8)) return MOE_ERR_UNSUPPORTED;
   if (p->dim % 32 != 0) return MOE_ERR_UNSUPPORTED;
   if (!f32 && (p->dim % 128 || p->hidden % 128 || p->shared_hidden % 128)) return MOE_ERR_UNSUPPORTED;
-  if (fp8 && p->path == MOE_PATH_GROUPED) return MOE_ERR_UNSUPPORTED;
   // the grouped GEMMs address x rows, an expert's h rows and one expert's
   // weights with 32-bit byte offsets
   const uint64_t hmax = (uint64_t)std::max(p->hidden, p->shared_hidden);
@@ -81,7 +80,6 @@ enum class Path { kF32, kGrouped, kStream };
 
 Path choose_path(const moe_params& p, int T) {
   if (p.weight_dtype == MOE_F32) return Path::kF32;
-  if (p.weight_dtype == MOE_FP8_E4M3) return Path::kStream;
   if (p.path == MOE_PATH_GROUPED) return Path::kGrouped;
   if (p.path == MOE_PATH_STREAM) return Path::kStream;
   return T > 256 ? Path::kGrouped : Path::kStream;
@@ -398,9 +396,9 @@ moe_status moe_layer_forward(moe_cfg* c, const void* x, int T, const float* gate
     g1.max_items = (int)(mblk * d.n1_routed + mblk_s * d.n1_shared);
     g2.max_items = (int)(mblk * d.n2_routed + mblk_s * d.n2_shared);
     if (path == Path::kGrouped) {
-      if ((e = launch_grouped_gateup_bf16(g1, s)) != hipSuccess) return hip_fail(c, e);
+      if ((e = launch_grouped_gateup(g1, fp8, s)) != hipSuccess) return hip_fail(c, e);
       mark(c, 3, s);
-      if ((e = launch_grouped_down_bf16(g2, s)) != hipSuccess) return hip_fail(c, e);
+      if ((e = launch_grouped_down(g2, fp8, s)) != hipSuccess) return hip_fail(c, e);
     } else {
       const int cap = c->num_cus * 2;  // persistent workgroups
       if ((e = launch_stream_gateup(g1, fp8, std::min(g1.max_items, cap), s)) != hipSuccess) return hip_fail(c, e);

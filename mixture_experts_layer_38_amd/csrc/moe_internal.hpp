@@ -12,6 +12,8 @@ namespace moe {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int kWave = 64;
@@ -184,8 +186,9 @@ struct ExpertGemmArgs {
   void* c;                  // GEMM1: h routed; GEMM2: y routed
   void* c_shared;           // GEMM1: h shared; GEMM2: y shared
 };
-hipError_t launch_grouped_gateup_bf16(const ExpertGemmArgs& a, hipStream_t s);
-hipError_t launch_grouped_down_bf16(const ExpertGemmArgs& a, hipStream_t s);
+// grouped (prefill) GEMMs; fp8: e4m3 weights with 128x128 block scales
+hipError_t launch_grouped_gateup(const ExpertGemmArgs& a, int fp8, hipStream_t s);
+hipError_t launch_grouped_down(const ExpertGemmArgs& a, int fp8, hipStream_t s);
 hipError_t launch_stream_gateup(const ExpertGemmArgs& a, int fp8, int blocks, hipStream_t s);
 hipError_t launch_stream_down(const ExpertGemmArgs& a, int fp8, int blocks, hipStream_t s);
 hipError_t launch_simple_gateup_f32(const ExpertGemmArgs& a, int TK, hipStream_t s);

@@ -202,11 +202,15 @@ CONFIGS = {
     # 32 local experts, each receiving ~16384*8*8/256 = 4096 rows, the shared
     # expert on the GPU's own 16384 tokens (local top-8 of 32 reproduces the
     # expert-GEMM shapes; the exchange itself is not part of this workload)
+    # the V3 prefill layer with the decode layer's e4m3 weights (128x128 block scales)
+    "v3_prefill_fp8": LayerConfig("v3_prefill_fp8", T=16384, D=7168, E=256, H=2048, G=8, kg=4, K=8,
+                                  score_fn="sigmoid", bias="normal", norm=True, rsf=2.5, Hs=2048,
+                                  act="bf16", weight="fp8"),
     "v3_ep8_shard": LayerConfig("v3_ep8_shard", T=16384, D=7168, E=32, H=2048, G=1, kg=1, K=8,
                                 score_fn="sigmoid", bias="normal", norm=True, rsf=2.5, Hs=2048,
                                 act="bf16", weight="bf16"),
 }
-# the five workloads; v3_ep8_shard is an extra shape for the sharding design
+# the five workloads; v3_ep8_shard (sharding design) and v3_prefill_fp8 are extra shapes
 CONFIG_ORDER = ["tiny_f32", "group_bf16", "v2_prefill", "v3_prefill", "v3_decode_fp8"]
 
 # tensor ids: one independent stream per tensor

@@ -53,7 +53,6 @@ def test_invalid_layers_rejected(kw):
     dict(dim=1000),                          # D % 32
     dict(hidden=500),                        # bf16 needs H % 128
     dict(shared_hidden=1000),
-    dict(weight="fp8", path="grouped"),      # fp8 runs on the streaming kernels only
     dict(n_routed=1024, n_group=8),          # E > 512
     dict(max_tokens=400000, dim=7168),       # x rows past 32-bit byte offsets
     dict(max_tokens=1100000, hidden=2048),   # an expert's h rows past 32-bit byte offsets

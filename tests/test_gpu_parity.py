@@ -159,14 +159,16 @@ def test_dispatch_is_a_valid_permutation():
 
 @pytest.mark.parametrize("cfg,path", [(SMALL_F32, "auto"), (MI.CONFIGS["tiny_f32"], "auto"),
                                       (SMALL_BF16, "grouped"), (SMALL_BF16, "stream"),
-                                      (SMALL_SIG, "grouped"), (SMALL_SIG, "stream"), (SMALL_FP8, "stream")],
+                                      (SMALL_SIG, "grouped"), (SMALL_SIG, "stream"), (SMALL_FP8, "stream"),
+                                      (SMALL_FP8, "grouped")],
                          ids=lambda v: v if isinstance(v, str) else v.name)
 def test_layer_small(cfg, path):
     inp = MI.make_layer(cfg, DEV)
     _check_layer(inp, path=path)
 
 
-def test_layer_fp8_every_code():
+@pytest.mark.parametrize("path", ["stream", "grouped"])
+def test_layer_fp8_every_code(path):
     """Expert weights drawn uniformly over all 254 finite e4m3 codes (tiny,
     subnormal and large values alike), so any mis-decoded code shows up."""
     cfg = SMALL_FP8
@@ -179,7 +181,7 @@ def test_layer_fp8_every_code():
         t.copy_(r.to(torch.uint8).to(t.device))
     for w in (inp.experts.gate_up, inp.experts.down, inp.shared.gate_up, inp.shared.down):
         every_code(w)
-    _check_layer(inp, path="stream")
+    _check_layer(inp, path=path)
 
 
 def test_layer_edge_cases():
@@ -212,6 +214,17 @@ def test_layer_edge_cases():
     # bf16 output is the fp32 output rounded
     ob, _, _ = _run_layer(inp, out_dtype="bf16")
     assert torch.equal(ob, o1.to(torch.bfloat16))
+
+
+# e4m3 weights at a prefill token count: the grouped GEMMs widen them to bf16
+# (times the block scale) as they stage them
+FP8_PREFILL = MI.LayerConfig("fp8_prefill", T=2100, D=1024, E=32, H=512, G=4, kg=2, K=4, score_fn="sigmoid",
+                             bias="normal", norm=True, rsf=2.5, Hs=512, act="bf16", weight="fp8", bias_std=0.02)
+
+
+def test_layer_fp8_prefill():
+    inp = MI.make_layer(FP8_PREFILL, DEV)
+    _check_layer(inp, tokens=_sample(FP8_PREFILL.T, 200))
 
 
 SKEWED = MI.LayerConfig("skewed", T=1100, D=256, E=16, H=128, G=4, kg=2, K=3, score_fn="sigmoid",
