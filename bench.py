@@ -35,17 +35,17 @@ def log(msg):
 # HBM traffic of one gate/up GEMM launch on the V3 prefill workload, from two
 # rocprofv3 --pmc runs of this bench (FETCH_SIZE, then WRITE_SIZE; KiB per
 # dispatch, mean of 3 dispatches), each scaled by what the same counter reads
-# for the bench's 1 GiB device-to-device copy probe (FETCH_SIZE 524315.1 KiB
+# for the bench's 1 GiB device-to-device copy probe (FETCH_SIZE 524315.3 KiB
 # for 1048576 KiB read; WRITE_SIZE 1048576 KiB for 1048576 KiB written).
 # Valid only for the kernel sources with these hashes; otherwise reported null.
 GATEUP_COUNTERS = {
     "sources": {"mixture_experts_layer_38_amd/csrc/grouped_gemm.hip":
-                "858428edc66b82a7db197ee66a82a3566c50323f6f3df1e41adada0012655892",
+                "1e58871534b13d9de8ad28d67c6e2d658980cdc99a1ab16b0cf1f4fe6df85363",
                 "mixture_experts_layer_38_amd/csrc/moe_internal.hpp":
-                "12e0cdaae6f08df4632628f9635f7b872ddb06f7995dab9db8bb8fcc0c1d12f0"},
+                "205b7a5fa5ea2bb1c4a8a4f8c0558c66231f0d9bda46a5d840259cd0dd530eed"},
     "workload": "v3_prefill",
-    "fetch_kib": 12353957.1, "write_kib": 589824.0,
-    "fetch_scale": 1048576.0 / 524315.1, "write_scale": 1.0,
+    "fetch_kib": 12477006.5, "write_kib": 645793.0,
+    "fetch_scale": 1048576.0 / 524315.3, "write_scale": 1.0,
 }
 
 
@@ -81,10 +81,20 @@ def gateup_flops(cfg):
     return 2.0 * cfg.T * (cfg.K * 2 * cfg.D * cfg.H + 2 * cfg.D * cfg.Hs)
 
 
+def gen_progress(cfg, torch):
+    """Logs every 32 experts, so that a slow generation (under a counter
+    profiler every dispatch is serialised) still shows its progress."""
+    def cb(e):
+        if (e + 1) % 32 == 0 or e + 1 == cfg.E:
+            torch.cuda.synchronize()
+            log(f"  experts {e + 1}/{cfg.E} generated")
+    return cb
+
+
 def run_prefill(args, torch, M, MI):
     cfg = MI.CONFIGS[args.config]
     log(f"generating {cfg.name} inputs on the GPU")
-    inp = MI.make_layer(cfg, "cuda")
+    inp = MI.make_layer(cfg, "cuda", progress=gen_progress(cfg, torch))
     layer = M.MoELayer.from_config(cfg)
     out = torch.empty((cfg.T, cfg.D), dtype=torch.float32, device="cuda")
     counts = torch.empty((cfg.E,), dtype=torch.int32, device="cuda")
@@ -148,7 +158,7 @@ def decode_bytes(cfg, n_touched):
 def run_decode(args, torch, M, MI):
     cfg = MI.CONFIGS[args.decode_config]
     log(f"generating {cfg.name} inputs on the GPU")
-    inp = MI.make_layer(cfg, "cuda")
+    inp = MI.make_layer(cfg, "cuda", progress=gen_progress(cfg, torch))
     layer = M.MoELayer.from_config(cfg)
     out = torch.empty((cfg.T, cfg.D), dtype=torch.float32, device="cuda")
     counts = torch.empty((cfg.E,), dtype=torch.int32, device="cuda")

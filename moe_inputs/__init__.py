@@ -304,8 +304,9 @@ def _store(gu32, dn32, dtype):
     return to_storage(gu32, dtype), to_storage(dn32, dtype), None, None
 
 
-def make_layer(cfg: LayerConfig, device="cpu") -> LayerInputs:
-    """All inputs of one layer, resident on `device`."""
+def make_layer(cfg: LayerConfig, device="cpu", progress=None) -> LayerInputs:
+    """All inputs of one layer, resident on `device`; `progress(e)` (optional)
+    is called after expert e's weights are written."""
     x = gen_x(cfg, device)
     gate_w = gen_gate_w(cfg, device)
     bias = gen_bias(cfg, device)
@@ -323,6 +324,8 @@ def make_layer(cfg: LayerConfig, device="cpu") -> LayerInputs:
         if sa is not None:
             gus[e].copy_(sa)
             dns[e].copy_(sb)
+        if progress is not None:
+            progress(e)
     experts = Weights(gu, dn, gus, dns)
     shared = None
     if cfg.Hs > 0:
