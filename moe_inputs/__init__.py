@@ -170,6 +170,7 @@ class LayerConfig:
     weight: str  # "f32" | "bf16" | "fp8"
     out: str = "f32"
     add_residual: bool = True
+    act_quant: bool = False  # expert GEMM inputs quantised to e4m3 per 1x128 block (fp8 weights)
     seed: int = 0
     bias_std: float = 0.01
 
@@ -198,19 +199,24 @@ CONFIGS = {
     "v3_decode_fp8": LayerConfig("v3_decode_fp8", T=64, D=7168, E=256, H=2048, G=8, kg=4, K=8,
                                  score_fn="sigmoid", bias="zipf", norm=True, rsf=2.5, Hs=2048,
                                  act="bf16", weight="fp8"),
-    # one GPU's share of the V3 prefill layer under 8-way expert parallelism:
-    # 32 local experts, each receiving ~16384*8*8/256 = 4096 rows, the shared
-    # expert on the GPU's own 16384 tokens (local top-8 of 32 reproduces the
-    # expert-GEMM shapes; the exchange itself is not part of this workload)
     # the V3 prefill layer with the decode layer's e4m3 weights (128x128 block scales)
     "v3_prefill_fp8": LayerConfig("v3_prefill_fp8", T=16384, D=7168, E=256, H=2048, G=8, kg=4, K=8,
                                   score_fn="sigmoid", bias="normal", norm=True, rsf=2.5, Hs=2048,
                                   act="bf16", weight="fp8"),
+    # the same with the expert GEMMs' inputs (token rows and h) quantised to
+    # e4m3 per 1x128 block, multiplied on the fp8 matrix cores
+    "v3_prefill_w8a8": LayerConfig("v3_prefill_w8a8", T=16384, D=7168, E=256, H=2048, G=8, kg=4, K=8,
+                                   score_fn="sigmoid", bias="normal", norm=True, rsf=2.5, Hs=2048,
+                                   act="bf16", weight="fp8", act_quant=True),
+    # one GPU's share of the V3 prefill layer under 8-way expert parallelism:
+    # 32 local experts, each receiving ~16384*8*8/256 = 4096 rows, the shared
+    # expert on the GPU's own 16384 tokens (local top-8 of 32 reproduces the
+    # expert-GEMM shapes; the exchange itself is not part of this workload)
     "v3_ep8_shard": LayerConfig("v3_ep8_shard", T=16384, D=7168, E=32, H=2048, G=1, kg=1, K=8,
                                 score_fn="sigmoid", bias="normal", norm=True, rsf=2.5, Hs=2048,
                                 act="bf16", weight="bf16"),
 }
-# the five workloads; v3_ep8_shard (sharding design) and v3_prefill_fp8 are extra shapes
+# the five workloads; v3_ep8_shard (sharding design), v3_prefill_fp8 and v3_prefill_w8a8 are extra shapes
 CONFIG_ORDER = ["tiny_f32", "group_bf16", "v2_prefill", "v3_prefill", "v3_decode_fp8"]
 
 # tensor ids: one independent stream per tensor

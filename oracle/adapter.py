@@ -65,4 +65,4 @@ def run_layer(inp, tokens=None, routing=None, with_shared=True, add_residual=Non
     shared = shared_expert_fn(inp.shared) if (with_shared and inp.shared is not None) else None
     return O.layer_forward(router_params(inp.cfg), u, decode_tensor(inp.gate_w), bias,
                            routed_expert_fn(inp.experts), shared, add_residual=r,
-                           tokens=tokens, routing=routing)
+                           tokens=tokens, routing=routing, act_quant=inp.cfg.act_quant)

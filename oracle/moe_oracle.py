@@ -38,7 +38,11 @@ missing from the extracted pages):
   indices are listed by descending selection score, then ascending index;
 * softmax is taken over all E logits before any masking;
 * gates: g_k = s[idx_k]; if normalised, g_k /= sum_k s[idx_k]; then g_k *= rsf;
-* the output includes the residual u_t when add_residual is set.
+* the output includes the residual u_t when add_residual is set;
+* e4m3 activations (architecture article, page 2, section 4.2, which fixes
+  fp8 GEMM inputs, fp32 accumulation and block-wise quantisation but not the
+  block shape): one fp32 scale per 1 x 128 block of a row, largest magnitude
+  / 448, codes rounded to nearest-even, decided in float32.
 
 Every routine below is pinned by tests in tests/test_oracle_pins.py (brute
 force on tiny inputs, closed forms, reductions to a dense FFN or to the dense
@@ -97,6 +101,65 @@ def dequant_e4m3_blocks(codes, scale, block: int = 128) -> np.ndarray:
     *lead, R, C = q.shape
     qb = q.reshape(*lead, R // block, block, C // block, block)
     return (qb * s[..., :, None, :, None]).reshape(q.shape)
+
+
+# ----------------------------------------------------------------------------
+# e4m3 activations with one scale per 1 x 128 block
+# ----------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+ACT_BLOCK = 128
+_E4M3_MAGNITUDES = None  # values of codes 0x00 .. 0x7E, increasing
+
+
+def encode_e4m3(values) -> np.ndarray:
+    """float32 values -> OCP E4M3 codes: the representable value nearest to the
+    value, ties to the even code (mantissa ending in 0). Readings: magnitudes
+    above 448 saturate to 448; the sign bit is the float32 sign bit, so -0
+    and negative values that round to zero give 0x80. Finite inputs only.
+    Found by searching the 127 non-negative finite values of the format
+    (decode_e4m3), not by bit manipulation."""
+    global _E4M3_MAGNITUDES
+    if _E4M3_MAGNITUDES is None:
+        _E4M3_MAGNITUDES = decode_e4m3(np.arange(0x7F))
+    table = _E4M3_MAGNITUDES
+    x = np.asarray(values, dtype=np.float32)
+    a = np.minimum(np.abs(x.astype(np.float64)), E4M3_MAX)
+    hi = np.minimum(np.searchsorted(table, a, side="left"), 0x7E)  # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - table[lo]
+    d_hi = table[hi] - a
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
+    return (code | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def quantize_act_1x128(values):
+    """Fine-grained activation quantisation (the architecture article,
+    section 4.2: fp8 inputs to the GEMMs, quantised block by block): each
+    run of 128 consecutive elements of a row gets one fp32 scale, its largest
+    magnitude divided by 448 (scale 1 for an all-zero block), and each element
+    becomes the e4m3 code of value / scale. Both divisions are float32
+    (correctly rounded), the precision the codes are decided in.
+    values [n, C] (exact in float32), C % 128 == 0 -> (codes uint8 [n, C],
+    scales float32 [n, C/128])."""
+    x = np.asarray(values, dtype=np.float32)
+    n, C = x.shape
+    if C % ACT_BLOCK:
+        raise ValueError("row length must be a multiple of 128")
+    xb = x.reshape(n, C // ACT_BLOCK, ACT_BLOCK)
+    amax = np.abs(xb).max(axis=2) if n else np.zeros((0, C // ACT_BLOCK), np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+        q = (xb / scale[:, :, None]).astype(np.float32)
+    return encode_e4m3(q).reshape(n, C), scale
+
+
+def dequant_act_1x128(codes, scales) -> np.ndarray:
+    """x_hat[r, c] = e4m3(codes[r, c]) * scales[r, c // 128], in float64."""
+    q = decode_e4m3(np.asarray(codes))
+    s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    n, C = q.shape
+    return (q.reshape(n, C // ACT_BLOCK, ACT_BLOCK) * s[:, :, None]).reshape(n, C)
 
 
 # ----------------------------------------------------------------------------
@@ -213,6 +276,21 @@ def swiglu_ffn(u: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.n
     return (silu(u @ w_gate.T) * (u @ w_up.T)) @ w_down.T
 
 
+def swiglu_ffn_e4m3_act(u: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """The same FFN with both GEMM inputs quantised to e4m3 per 1 x 128 block
+    (architecture article, section 4.2): u is quantised before the gate and
+    up projections; h = SiLU(gate) * up, rounded to float32 (the precision the
+    kernel holds it in), is quantised before the down projection. The
+    products and sums themselves are float64."""
+    u = np.asarray(u, np.float64)
+    if not np.array_equal(u.astype(np.float32).astype(np.float64), u):
+        raise ValueError("inputs must be exact in float32")
+    uq = dequant_act_1x128(*quantize_act_1x128(u.astype(np.float32)))
+    h = silu(uq @ w_gate.T) * (uq @ w_up.T)
+    hq = dequant_act_1x128(*quantize_act_1x128(h.astype(np.float32)))
+    return hq @ w_down.T
+
+
 def split_gate_up(gate_up: np.ndarray):
     """[2h, D] -> (W_gate = rows 0..h-1, W_up = rows h..2h-1)."""
     h = gate_up.shape[0] // 2
@@ -220,11 +298,14 @@ def split_gate_up(gate_up: np.ndarray):
 
 
 def layer_forward(p: RouterParams, u: np.ndarray, gate_w: np.ndarray, sel_bias, routed_expert,
-                  shared_expert=None, add_residual: bool = True, tokens=None, routing: dict | None = None):
+                  shared_expert=None, add_residual: bool = True, tokens=None, routing: dict | None = None,
+                  act_quant: bool = False):
     """out_t = [u_t] + FFN_shared(u_t) + sum_k g_{t,k} FFN_{idx_{t,k}}(u_t).
 
     routed_expert(e) -> (w_gate, w_up, w_down) float64 for routed expert e;
     shared_expert() -> the same for the fused shared expert, or None.
+    act_quant: every expert FFN (routed and shared) takes e4m3 activations
+    (swiglu_ffn_e4m3_act); the router still sees u unquantised.
     Routing is computed for every token (counts need all of them); the
     output only for `tokens` (default: all), in that order.
     Returns (out [len(tokens), D], routing dict).
@@ -240,16 +321,17 @@ def layer_forward(p: RouterParams, u: np.ndarray, gate_w: np.ndarray, sel_bias, 
     n, D = ut.shape
     # Y[i, k] = FFN_{idx[i, k]}(u_{tokens[i]}); each expert's weights are decoded once
     Y = np.zeros((n, p.K, D))
+    ffn = swiglu_ffn_e4m3_act if act_quant else swiglu_ffn
     for e in np.unique(idx):
         ii, kk = np.nonzero(idx == e)
-        Y[ii, kk] = swiglu_ffn(ut[ii], *routed_expert(int(e)))
+        Y[ii, kk] = ffn(ut[ii], *routed_expert(int(e)))
     out = np.zeros((n, D))
     if add_residual:
         out += ut
     if shared_expert is not None:
         sw = shared_expert()
         if sw is not None:
-            out += swiglu_ffn(ut, *sw)
+            out += ffn(ut, *sw)
     for k in range(p.K):
         out += gate[:, k:k + 1] * Y[:, k]
     return out, routing

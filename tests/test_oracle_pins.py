@@ -54,6 +54,96 @@ def test_e4m3_block_dequant_uses_the_right_block():
 
 
 # ----------------------------------------------------------------------------
+# e4m3 activations, one scale per 1 x 128 block
+# ----------------------------------------------------------------------------
+
+
+def _torch_e4m3(v):
+    """torch's own float32 -> float8_e4m3fn cast (round to nearest even)."""
+    return torch.from_numpy(np.asarray(v, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_encode_e4m3_matches_torch_cast():
+    table = O.decode_e4m3(np.arange(0x7F))  # 0 .. 448
+    mids = (table[:-1] + table[1:]) / 2  # every tie between neighbouring values
+    assert np.array_equal(mids.astype(np.float32).astype(np.float64), mids)
+    parts = [table, mids, RNG.uniform(-448, 448, 20000), RNG.standard_normal(20000) * 2.0 ** -7,
+             RNG.standard_normal(2000) * 2.0 ** -12, np.array([463.9])]
+    v = np.concatenate([np.concatenate([x, -x]) for x in parts]).astype(np.float32)
+    assert np.array_equal(O.encode_e4m3(v), _torch_e4m3(v))
+
+
+def test_encode_e4m3_round_trips_every_finite_code_and_saturates():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    assert np.array_equal(O.encode_e4m3(O.decode_e4m3(codes).astype(np.float32)), codes)
+    v = np.array([448.0, 463.9, 1e30, -1e30, -0.0, -2.0 ** -11, 2.0 ** -10, 3 * 2.0 ** -10], np.float32)
+    # saturation (reading), signed zero, ties to the even code among subnormals
+    assert O.encode_e4m3(v).tolist() == [0x7E, 0x7E, 0x7E, 0xFE, 0x80, 0x80, 0x00, 0x02]
+
+
+def test_quantize_act_closed_forms():
+    x = RNG.standard_normal((5, 384)).astype(np.float32)
+    x[1, 128:256] = 0  # an all-zero block
+    x[3, :128] *= np.float32(2.0 ** -14)  # a block mostly in the subnormal range of its scale
+    codes, scale = O.quantize_act_1x128(x)
+    assert codes.dtype == np.uint8 and scale.dtype == np.float32 and scale.shape == (5, 3)
+    for r in range(5):
+        for b in range(3):
+            blk = x[r, 128 * b:128 * (b + 1)]
+            amax = np.abs(blk).max()
+            if amax == 0:
+                assert scale[r, b] == 1 and not codes[r, 128 * b:128 * (b + 1)].any()
+                continue
+            assert scale[r, b] == amax / np.float32(448)
+            j = int(np.argmax(np.abs(blk)))
+            assert codes[r, 128 * b + j] == (0xFE if blk[j] < 0 else 0x7E)  # the block maximum maps to 448
+    # codes are torch's cast of value / scale
+    q = (x.reshape(5, 3, 128) / scale[:, :, None]).astype(np.float32)
+    assert np.array_equal(codes, _torch_e4m3(q).reshape(5, 384))
+    # within half a quantum: 2^-4 relative in e4m3's normal range, 2^-10 * scale below it
+    xh = O.dequant_act_1x128(codes, scale)
+    sc = np.repeat(scale.astype(np.float64), 128, axis=1)
+    bound = np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * sc) * (1 + 1e-6)
+    assert np.all(np.abs(xh - x) <= bound)
+
+
+def test_quantize_act_blocks_are_independent_and_scale_exactly():
+    x = RNG.standard_normal((3, 256)).astype(np.float32)
+    c0, s0 = O.quantize_act_1x128(x)
+    y = x.copy()
+    y[:, 128:] *= np.float32(32.0)  # exact
+    c1, s1 = O.quantize_act_1x128(y)
+    assert np.array_equal(c0, c1)
+    assert np.array_equal(s1[:, 0], s0[:, 0]) and np.array_equal(s1[:, 1], s0[:, 1] * np.float32(32.0))
+    e, se = O.quantize_act_1x128(np.zeros((0, 128), np.float32))
+    assert e.shape == (0, 128) and se.shape == (0, 1)
+
+
+def test_e4m3_act_ffn_within_the_quantisation_error():
+    """Both GEMM inputs quantised: the FFN stays within a few e4m3 quanta of
+    the exact one, even with blocks whose magnitudes differ by 10^3 (a scale
+    applied to the wrong block would not)."""
+    rng = np.random.default_rng(77)
+    D, h = 256, 128
+    u = rng.standard_normal((40, D))
+    u[:, :128] *= 1000.0
+    u = u.astype(np.float32).astype(np.float64)
+    wg = rng.uniform(-1, 1, (h, D)) / math.sqrt(D) / 100
+    wu = rng.uniform(-1, 1, (h, D)) / math.sqrt(D) / 100
+    wd = rng.uniform(-1, 1, (D, h)) / math.sqrt(h)
+    exact = O.swiglu_ffn(u, wg, wu, wd)
+    quant = O.swiglu_ffn_e4m3_act(u, wg, wu, wd)
+    rel = np.linalg.norm(quant - exact) / np.linalg.norm(exact)
+    assert 1e-3 < rel < 0.08  # quantisation error (about 4 % here), far above float rounding
+    # the routed and shared FFNs of the layer take the quantised form
+    p = O.RouterParams(E=4, K=2)
+    gw = RNG.standard_normal((4, D))
+    out, r = O.layer_forward(p, u, gw, None, lambda e: (wg, wu, wd), lambda: (wg, wu, wd),
+                             add_residual=False, act_quant=True)
+    assert np.allclose(out, quant * (1 + r["gate"].sum(axis=1, keepdims=True)), rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
 # router
 # ----------------------------------------------------------------------------
 
@@ -458,3 +548,38 @@ def test_pins_catch_planted_bugs(monkeypatch):
     with pytest.raises(AssertionError):
         test_bias_update_balances_a_skewed_router()
     monkeypatch.setattr(O, "bias_update", good_bias)
+
+    good_enc = O.encode_e4m3
+
+    def ties_up(v):  # ties rounded away from zero instead of to even
+        x = np.asarray(v, np.float32)
+        return good_enc(x * np.float32(1 + 2.0 ** -20))
+    monkeypatch.setattr(O, "encode_e4m3", ties_up)
+    with pytest.raises(AssertionError):
+        test_encode_e4m3_matches_torch_cast()
+    monkeypatch.setattr(O, "encode_e4m3", good_enc)
+
+    good_deq = O.dequant_act_1x128
+
+    def reversed_blocks(codes, scales):  # block scales applied to the wrong blocks
+        return good_deq(codes, np.asarray(scales)[:, ::-1])
+    monkeypatch.setattr(O, "dequant_act_1x128", reversed_blocks)
+    with pytest.raises(AssertionError):
+        test_e4m3_act_ffn_within_the_quantisation_error()
+    with pytest.raises(AssertionError):
+        test_quantize_act_closed_forms()
+    monkeypatch.setattr(O, "dequant_act_1x128", good_deq)
+
+    good_q = O.quantize_act_1x128
+
+    def off_by_one(values):  # scale from 447 instead of the format's largest value
+        x = np.asarray(values, np.float32)
+        codes, scale = good_q(x)
+        n, C = x.shape
+        amax = np.abs(x.reshape(n, C // 128, 128)).max(axis=2)
+        s2 = np.where(amax > 0, amax / np.float32(447), np.float32(1)).astype(np.float32)
+        return O.encode_e4m3((x.reshape(n, C // 128, 128) / s2[:, :, None]).astype(np.float32)).reshape(n, C), s2
+    monkeypatch.setattr(O, "quantize_act_1x128", off_by_one)
+    with pytest.raises(AssertionError):
+        test_quantize_act_closed_forms()
+    monkeypatch.setattr(O, "quantize_act_1x128", good_q)
