@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "routed tokens/s per MoE layer (V3-shape T=16384) + %MFMA peak; decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 
 
@@ -65,10 +66,16 @@ def gateup_traffic(cfg):
 
 def gateup_algorithmic_bytes(cfg):
     """Each operand byte once: routed and shared gate/up weights, the gathered
-    token rows (T*K routed + T shared), and h written."""
-    w = 2 * (cfg.E * 2 * cfg.H * cfg.D + 2 * cfg.Hs * cfg.D)
-    x = 2 * (cfg.T * cfg.K + cfg.T) * cfg.D
-    h = 2 * (cfg.T * cfg.K * cfg.H + cfg.T * cfg.Hs)
+    token rows (T*K routed + T shared), and h written; e4m3 operands count one
+    byte per element plus their fp32 block scales."""
+    wb = 1 if cfg.weight == "fp8" else 2
+    ab = 1 if cfg.act_quant else 2
+    wrows = cfg.E * 2 * cfg.H + 2 * cfg.Hs
+    w = wb * wrows * cfg.D + (4 * (wrows // 128) * (cfg.D // 128) if cfg.weight == "fp8" else 0)
+    xrows = cfg.T * cfg.K + cfg.T
+    x = ab * xrows * cfg.D + (4 * xrows * (cfg.D // 128) if cfg.act_quant else 0)
+    hel = cfg.T * cfg.K * cfg.H + cfg.T * cfg.Hs
+    h = ab * hel + (4 * hel // 128 if cfg.act_quant else 0)
     return w + x + h
 
 
@@ -134,14 +141,18 @@ def run_prefill(args, torch, M, MI):
     balance_us = ev0.elapsed_time(ev1) * 1e3 / 200
     g1_ms = stage_avg["gate_up_gemm"]
     g1_tflops = gateup_flops(cfg) / (g1_ms * 1e-3) / 1e12
+    # e4m3 activations multiply on the fp8 matrix cores (their own peak); the
+    # gate/up stage then also holds the token-row quantiser
+    peak = PEAK_FP8_TFLOPS if cfg.act_quant else PEAK_BF16_TFLOPS
+    kernel = ("grouped_gemm_f8_kernel<0> (gate/up + SwiGLU + h to e4m3; stage includes quant_e4m3_kernel)"
+              if cfg.act_quant else "grouped_gemm_bf16_kernel<0> (gate/up + SwiGLU)")
     res = dict(cfg=cfg, inp=inp, ms=ms, stages=stage_avg, counts=counts.cpu().tolist(), balance_us=balance_us,
-               mfma_frac=mfma_flops(cfg) / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
-               roofline=dict(bound="mfma", achieved=round(g1_tflops, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                             frac=round(g1_tflops / PEAK_BF16_TFLOPS, 4), traffic=gateup_traffic(cfg),
+               mfma_frac=mfma_flops(cfg) / (ms * 1e-3) / (peak * 1e12),
+               roofline=dict(bound="mfma", achieved=round(g1_tflops, 2), peak=peak, unit="TFLOP/s",
+                             frac=round(g1_tflops / peak, 4), traffic=gateup_traffic(cfg),
                              traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                              algorithmic_bytes=gateup_algorithmic_bytes(cfg),
-                             kernel="grouped_gemm_bf16_kernel<0> (gate/up + SwiGLU)",
-                             per_launch_flop=gateup_flops(cfg), avg_ms=round(g1_ms, 4)))
+                             kernel=kernel, per_launch_flop=gateup_flops(cfg), avg_ms=round(g1_ms, 4)))
     del layer, out
     return res
 
@@ -278,11 +289,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp8" if cfg.act_quant else "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "D": cfg.D, "E": cfg.E, "H": cfg.H, "G": cfg.G,
                    "topk_group": cfg.kg, "K": cfg.K, "Hs": cfg.Hs, "score": cfg.score_fn,
-                   "weights": cfg.weight, "parallelism": "single GPU"},
+                   "weights": cfg.weight, "activations": "e4m3 1x128" if cfg.act_quant else cfg.act,
+                   "parallelism": "single GPU"},
         "mfma_frac": round(res["mfma_frac"], 4),
         "stages_ms": {k: round(v, 4) for k, v in res["stages"].items()},
         "balance_update_and_stats_us": round(res["balance_us"], 2),

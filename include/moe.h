@@ -52,6 +52,18 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype;
 /* Which expert-GEMM kernels run. AUTO picks by token count. */
 typedef enum { MOE_PATH_AUTO = 0, MOE_PATH_GROUPED = 1, MOE_PATH_STREAM = 2 } moe_path;
 
+/* Expert-GEMM inputs (architecture article, section 4.2: fp8 GEMM inputs with
+ * fp32 accumulation and block-wise quantisation).
+ * NONE: the expert GEMMs multiply bf16 token rows and bf16 h.
+ * E4M3_1X128 (FP8_E4M3 weights and BF16 x only): the token rows and h are
+ * quantised to e4m3 with one fp32 scale per 1 x 128 block of a row (largest
+ * magnitude / 448, codes rounded to nearest even, see
+ * moe_quantize_e4m3_1x128) and multiplied on the fp8 matrix cores with the
+ * weights' 128 x 128 block scales; accumulation is fp32. The router still
+ * reads x unquantised. Runs the grouped kernels at every token count
+ * (path STREAM is rejected with MOE_ERR_UNSUPPORTED). */
+typedef enum { MOE_ACT_QUANT_NONE = 0, MOE_ACT_QUANT_E4M3_1X128 = 1 } moe_act_quant;
+
 typedef struct {
   int dim;            /* D: model dim (row length of x and out) */
   int n_routed;       /* E: routed experts, 1..512 */
@@ -71,6 +83,7 @@ typedef struct {
   int add_residual;   /* 1: out includes x (h'_t = u_t + ...) */
   int max_tokens;     /* largest T any call on this cfg may pass */
   int path;           /* moe_path */
+  int act_quant;      /* moe_act_quant */
 } moe_params;
 
 /* Expert weights in nn.Linear layout [out, in], row-major, dtype weight_dtype.
@@ -142,6 +155,21 @@ moe_status moe_router_forward(moe_cfg* cfg, const void* x, int T, const float* g
  * unique. */
 moe_status moe_dispatch_forward(moe_cfg* cfg, const int32_t* topk_idx, int T, int32_t* offsets,
                                 int32_t* row_token, int32_t* slot_row, void* stream);
+
+/* The activation quantiser of MOE_ACT_QUANT_E4M3_1X128 alone (architecture
+ * article, section 4.2, block-wise fp8 quantisation):
+ *   x      [rows][cols] bf16 (input; finite values)
+ *   codes  [rows][cols] uint8 OCP e4m3 codes (output)
+ *   scales [rows][cols/128] fp32 (output)
+ * Each block b of 128 consecutive values of a row gets scale = amax / 448
+ * (fp32, correctly rounded; 1 when the block is all zero) and each value v
+ * the e4m3 code nearest to v / scale (fp32 division), ties to the even code;
+ * the block maximum maps to +-448; the code's sign bit is v's sign bit.
+ * cols must be a positive multiple of 128 and rows * cols at most 2^34;
+ * rows == 0 launches nothing. MOE_ERR_INVALID_ARG (nothing launched) for a
+ * null pointer with rows > 0 or a bad size. No cfg; stream-ordered. */
+moe_status moe_quantize_e4m3_1x128(const void* x, int rows, int cols, uint8_t* codes, float* scales,
+                                   void* stream);
 
 /* Load balance between steps (no cfg; stream-ordered; one small launch).
  *

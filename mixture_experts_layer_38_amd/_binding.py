@@ -20,6 +20,7 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_OOM, MOE_ERR_HIP = 0, 
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_PATH_AUTO, MOE_PATH_GROUPED, MOE_PATH_STREAM = 0, 1, 2
+MOE_ACT_QUANT_NONE, MOE_ACT_QUANT_E4M3_1X128 = 0, 1
 
 _DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
 _TORCH_OF = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16, MOE_FP8_E4M3: torch.uint8}
@@ -30,7 +31,7 @@ class MoeParams(ctypes.Structure):
                                              "topk_group", "score_fn", "norm_topk")] + \
                [("routed_scaling_factor", ctypes.c_float)] + \
                [(n, ctypes.c_int) for n in ("act_dtype", "weight_dtype", "out_dtype", "add_residual",
-                                             "max_tokens", "path")]
+                                             "max_tokens", "path", "act_quant")]
 
 
 class MoeWeights(ctypes.Structure):
@@ -74,9 +75,10 @@ def load_library() -> ctypes.CDLL:
     lib.moe_status_string.restype = ctypes.c_char_p
     lib.moe_bias_update.argtypes = [vp, ctypes.c_int, ctypes.c_float, vp, vp]
     lib.moe_load_stats.argtypes = [vp, ctypes.c_int, vp, vp]
+    lib.moe_quantize_e4m3_1x128.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp, vp]
     for f in ("moe_cfg_create", "moe_cfg_destroy", "moe_layer_forward", "moe_router_forward",
               "moe_dispatch_forward", "moe_cfg_last_hip_error", "moe_cfg_set_stage_timing",
-              "moe_cfg_stage_times", "moe_bias_update", "moe_load_stats"):
+              "moe_cfg_stage_times", "moe_bias_update", "moe_load_stats", "moe_quantize_e4m3_1x128"):
         getattr(lib, f).restype = ctypes.c_int
     del i32p
     _lib = lib
@@ -106,7 +108,7 @@ def _stream_handle(stream) -> ctypes.c_void_p:
 
 def make_params(*, dim, n_routed, hidden, shared_hidden, top_k, n_group=1, topk_group=1,
                 score_fn="softmax", norm_topk=False, routed_scaling_factor=1.0, act="bf16", weight="bf16",
-                out="f32", add_residual=True, max_tokens, path="auto") -> MoeParams:
+                out="f32", add_residual=True, max_tokens, path="auto", act_quant=False) -> MoeParams:
     return MoeParams(dim=dim, n_routed=n_routed, hidden=hidden, shared_hidden=shared_hidden, top_k=top_k,
                      n_group=n_group, topk_group=topk_group,
                      score_fn={"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}.get(score_fn, score_fn),
@@ -114,7 +116,8 @@ def make_params(*, dim, n_routed, hidden, shared_hidden, top_k, n_group=1, topk_
                      act_dtype=_DTYPE_CODE.get(act, act), weight_dtype=_DTYPE_CODE.get(weight, weight),
                      out_dtype=_DTYPE_CODE.get(out, out), add_residual=int(bool(add_residual)),
                      max_tokens=max_tokens,
-                     path={"auto": MOE_PATH_AUTO, "grouped": MOE_PATH_GROUPED, "stream": MOE_PATH_STREAM}.get(path, path))
+                     path={"auto": MOE_PATH_AUTO, "grouped": MOE_PATH_GROUPED, "stream": MOE_PATH_STREAM}.get(path, path),
+                     act_quant=int(act_quant))
 
 
 def create_cfg(params: MoeParams) -> tuple[int, ctypes.c_void_p]:
@@ -146,11 +149,13 @@ class MoELayer:
     @classmethod
     def from_config(cls, cfg, max_tokens=None, path="auto", **overrides):
         """From an object with the fields of a layer description (T, D, E, H,
-        G, kg, K, score_fn, norm, rsf, Hs, act, weight, out, add_residual)."""
+        G, kg, K, score_fn, norm, rsf, Hs, act, weight, out, add_residual, and
+        optionally act_quant)."""
         kw = dict(dim=cfg.D, n_routed=cfg.E, hidden=cfg.H, shared_hidden=cfg.Hs, top_k=cfg.K, n_group=cfg.G,
                   topk_group=cfg.kg, score_fn=cfg.score_fn, norm_topk=cfg.norm, routed_scaling_factor=cfg.rsf,
                   act=cfg.act, weight=cfg.weight, out=cfg.out, add_residual=cfg.add_residual,
-                  max_tokens=cfg.T if max_tokens is None else max_tokens, path=path)
+                  max_tokens=cfg.T if max_tokens is None else max_tokens, path=path,
+                  act_quant=getattr(cfg, "act_quant", False))
         kw.update(overrides)
         return cls(make_params(**kw))
 
@@ -255,3 +260,18 @@ def load_stats(expert_counts, stream=None):
     if st != MOE_OK:
         raise MoEError(st, "moe_load_stats")
     return stats
+
+
+def quantize_e4m3_1x128(x, stream=None):
+    """moe_quantize_e4m3_1x128: (codes uint8 [rows, cols], scales fp32
+    [rows, cols/128]) of a contiguous cuda bf16 tensor x [rows, cols]."""
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous() or x.dim() != 2:
+        raise ValueError("x must be a contiguous cuda bf16 tensor [rows, cols]")
+    rows, cols = x.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, max(cols // 128, 1)), dtype=torch.float32, device=x.device)
+    st = load_library().moe_quantize_e4m3_1x128(_ptr(x), rows, cols, _ptr(codes), _ptr(scales),
+                                                _stream_handle(stream))
+    if st != MOE_OK:
+        raise MoEError(st, "moe_quantize_e4m3_1x128")
+    return codes, scales[:, :cols // 128]

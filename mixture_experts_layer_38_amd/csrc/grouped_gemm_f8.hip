@@ -1,0 +1,403 @@
+// Grouped GEMMs of the routed experts and the shared expert with both inputs
+// in e4m3 (the fp8 GEMMs of the architecture article, section 4.2: fp8
+// inputs, fp32 accumulation, block-wise quantisation): token rows and h carry
+// one fp32 scale per 1 x 128 block of a row, weights one per 128 x 128 block.
+//
+// One K step is 128 elements, i.e. one scale block of both operands. Per step
+// and 32 x 32 output block, two v_mfma_scale_f32_32x32x64_f8f6f4 (unit
+// hardware scale) form the block's exact-in-fp32 partial sum of code
+// products, which is added to the fp32 accumulator times (row scale x weight
+// scale) -- the per-block promotion that the block scales require.
+//
+// Gate/up GEMM: a tile loads 128 W_gate rows and the matching 128 W_up rows,
+// h = SiLU(gate) * up is formed in fp32 and, per 1 x 128 block of each row
+// (the tile's 128 h columns are exactly one block), quantised to e4m3 in the
+// epilogue: h leaves the kernel as codes + scales, ready for the down GEMM.
+// Token rows are gathered (codes and their scales) through the dispatch's
+// row -> token map. Down GEMM: Y[row] = g_row * (h[row] W_down^T), bf16.
+//
+// Tile 128 x 256, 8 waves (two per SIMD) as 2 x 4, each wave 64 x 64 = 2 x 2
+// blocks of 32 x 32 (64 fp32 accumulators per lane); a wave's two 32-row
+// blocks are interleaved with the other row-wave's (blocks wm, wm + 2), and
+// the tile body is instantiated per count of valid row blocks. Operands are
+// staged through two LDS buffers (rows padded to 144 bytes): the weight rows
+// of the next K step and the token rows (and their scales) of the step after
+// it are loaded into registers while the current step is multiplied; one
+// barrier per step. Tile order and the even split of an expert's rows over
+// its row tiles follow the bf16 grouped GEMMs (runs of 32 tiles per XCD,
+// column-tile major).
+#include <type_traits>
+
+#include "moe_internal.hpp"
+
+namespace moe {
+
+namespace {
+constexpr int BM = kF8_BM, BN = 256, BK = kF8_BK, LDB = BK + 16;  // LDS row stride in bytes
+constexpr int kRowsL = BM + BN;                                   // LDS rows per buffer: A then B
+constexpr int kBufBytes = kRowsL * LDB;
+constexpr int kRun = 32;
+constexpr int kLdA = 2, kLdB = 4;  // 16-byte global loads per thread per K step
+constexpr int kHLd = BK + 4;       // gate/up epilogue: fp32 h staging row (floats)
+constexpr int kYLd = BN + 8;       // down epilogue: bf16 y staging row (elements)
+static_assert(BM * kHLd * 4 <= 2 * kBufBytes, "h staging fits the operand buffers");
+static_assert(BM * kYLd * 2 <= 2 * kBufBytes, "y staging fits the operand buffers");
+
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+struct TileF8 {
+  const uint8_t* a_rows;  // GEMM1: x codes; GEMM2: h codes of this problem (row 0 = row_base)
+  const int32_t* tok;     // GEMM1 routed: row -> token map at row_base; null = identity
+  const float* a_scale;   // scales of a_rows' rows, [.][a_sld]
+  int a_sld;              // K / 128
+  const uint8_t* w;       // e4m3 weights of this problem
+  const float* ws;        // their 128x128 block scales, [rows/128][K/128]
+  void* c;                // GEMM1: h codes (row 0 = row_base); GEMM2: y bf16
+  float* c_scale;         // GEMM1: h scales, [.][c_sld]
+  int c_sld;              // Hp / 128
+  const float* gate;      // GEMM2 routed: gates at row_base; null = 1
+  uint32_t a_bytes, w_bytes;
+  int lda, ldc, K, Hp, D;
+  int m0, vrows, nt;
+};
+
+// 32 bytes of one LDS row as two 16-byte reads (rows are 16-byte aligned)
+__device__ __forceinline__ i32x8 lds_frag(const uint8_t* p) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(p), hi = *reinterpret_cast<const uint4*>(p + 16);
+  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+__device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  // format 0 = e4m3 for both operands; E8M0 scale 127 = 2^0
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+}  // namespace
+
+template <int kMode, int NRB>
+__device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kBufBytes], float (*s_asc)[512],
+                                             float* s_gate) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int c16 = tid & 7, r0 = tid >> 3;
+
+  // loader: 16-byte pieces; A rows r0 and r0 + 64 (128 bytes = one K step
+  // each), B rows r0 + 64*j. Rows past the valid ones read a valid row
+  // instead (never stored), so every load is unconditional.
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(t.a_rows), (short)0, t.a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(t.w), (short)0, t.w_bytes, 0x00020000);
+  uint32_t voa[kLdA], vob[kLdB];
+#pragma unroll
+  for (int j = 0; j < kLdA; ++j) {
+    const int m = r0 + 64 * j;
+    const int mm = t.m0 + (m < t.vrows ? m : 0);
+    const int row = (kMode == 0 && t.tok != nullptr) ? t.tok[mm] : mm;
+    voa[j] = (uint32_t)row * (uint32_t)t.lda + c16 * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < kLdB; ++j) {
+    const int b = r0 + 64 * j;
+    int wrow = (kMode == 0) ? (b < 128 ? t.nt * 128 + b : t.Hp + t.nt * 128 + b - 128) : t.nt * BN + b;
+    if (kMode == 1 && wrow >= t.D) wrow = 0;
+    vob[j] = (uint32_t)wrow * (uint32_t)t.K + c16 * 16;
+  }
+  // row scales: thread tid stages the scale of A row tid % 128 (threads
+  // past 128 write a copy that is never read, so the K loop has no branch)
+  const float* asrow;
+  {
+    const int m = tid & (BM - 1);
+    const int mm = t.m0 + (m < t.vrows ? m : 0);
+    const int row = (kMode == 0 && t.tok != nullptr) ? t.tok[mm] : mm;
+    asrow = t.a_scale + (size_t)row * t.a_sld;
+  }
+  // weight scales of this wave's two 32-column blocks (one 128-row block each)
+  const float* wsr[2];
+  if (kMode == 0) {
+    wsr[0] = t.ws + (size_t)t.nt * t.a_sld;                    // W_gate rows nt*128 ..
+    wsr[1] = t.ws + (size_t)(t.Hp / 128 + t.nt) * t.a_sld;     // W_up rows Hp + nt*128 ..
+  } else {
+    int cb = (t.nt * BN + 64 * wn) >> 7;
+    if (cb * 128 >= t.D) cb = 0;
+    wsr[0] = wsr[1] = t.ws + (size_t)cb * t.a_sld;
+  }
+
+  auto gload_a = [&](int j, int k0) __attribute__((always_inline)) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, voa[j], k0, 0));
+  };
+  auto gload_b = [&](int j, int k0) __attribute__((always_inline)) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, vob[j], k0, 0));
+  };
+
+  f32x16 acc[NRB > 0 ? NRB : 1][2];
+#pragma unroll
+  for (int i = 0; i < NRB; ++i)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][c][e] = 0.f;
+
+  int bcol[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) bcol[c] = (kMode == 0) ? 128 * c + 32 * wn : 64 * wn + 32 * c;
+  const int lr = lane & 31, lk = (lane >> 5) * 32;
+
+  if (kMode == 1 && tid < BM) s_gate[tid] = (t.gate != nullptr && tid < t.vrows) ? t.gate[t.m0 + tid] : 1.0f;
+
+  const int nk = t.K / BK;
+  uint4 pa[2][kLdA], pb[kLdB];
+  float pas[2] = {1.f, 1.f};
+#pragma unroll
+  for (int j = 0; j < kLdA; ++j) pa[0][j] = gload_a(j, 0);
+  pas[0] = asrow[0];
+#pragma unroll
+  for (int j = 0; j < kLdB; ++j) pb[j] = gload_b(j, 0);
+  {
+    const int k1 = nk > 1 ? 1 : 0;
+#pragma unroll
+    for (int j = 0; j < kLdA; ++j) pa[1][j] = gload_a(j, k1 * BK);
+    pas[1] = asrow[k1];
+  }
+
+  auto store = [&](int buf, const uint4 (&va)[kLdA], float vas) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kLdA; ++j) *reinterpret_cast<uint4*>(&smem[buf][(r0 + 64 * j) * LDB + c16 * 16]) = va[j];
+#pragma unroll
+    for (int j = 0; j < kLdB; ++j)
+      *reinterpret_cast<uint4*>(&smem[buf][(BM + r0 + 64 * j) * LDB + c16 * 16]) = pb[j];
+    s_asc[buf][tid] = vas;
+  };
+  store(0, pa[0], pas[0]);
+  __syncthreads();
+
+  auto kstep = [&](int kt, auto s_c) __attribute__((always_inline)) {
+    constexpr int S = decltype(s_c)::value;  // register slot of A(kt), refilled with A(kt+2)
+    const int cur = kt & 1;
+    const int knext = kt + 1 < nk ? kt + 1 : kt;
+    const int knext2 = kt + 2 < nk ? kt + 2 : nk - 1;
+#pragma unroll
+    for (int j = 0; j < kLdA; ++j) pa[S][j] = gload_a(j, knext2 * BK);
+    pas[S] = asrow[knext2];
+#pragma unroll
+    for (int j = 0; j < kLdB; ++j) pb[j] = gload_b(j, knext * BK);
+    const float sw0 = wsr[0][kt], sw1 = wsr[1][kt];
+
+    const uint8_t* sA = smem[cur];
+    const uint8_t* sB = smem[cur] + BM * LDB;
+    i32x8 fa[NRB > 0 ? NRB : 1][2], fb[2][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) fb[c][h] = lds_frag(&sB[(bcol[c] + lr) * LDB + 64 * h + lk]);
+#pragma unroll
+      for (int i = 0; i < NRB; ++i) fa[i][h] = lds_frag(&sA[(32 * (wm + 2 * i) + lr) * LDB + 64 * h + lk]);
+    }
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+      // scales of this lane's 16 rows of block i: rows 8*q + 4*(lane/32) + 0..3
+      float sa[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&s_asc[cur][32 * (wm + 2 * i) + 8 * q + 4 * (lane >> 5)]);
+        sa[4 * q] = v.x; sa[4 * q + 1] = v.y; sa[4 * q + 2] = v.z; sa[4 * q + 3] = v.w;
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        f32x16 p = {};
+        p = mfma_f8(fa[i][0], fb[c][0], p);
+        p = mfma_f8(fa[i][1], fb[c][1], p);
+        const float sw = c == 0 ? sw0 : sw1;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][c][e] = __builtin_fmaf(p[e], sa[e] * sw, acc[i][c][e]);
+      }
+    }
+    // the next step's operands into the idle buffer (the last step rewrites
+    // its own slice: the body stays branch-free)
+    store(cur ^ 1, pa[S ^ 1], pas[S ^ 1]);
+    __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    kstep(kt, std::integral_constant<int, 0>{});
+    kstep(kt + 1, std::integral_constant<int, 1>{});
+  }
+  if (kt < nk) kstep(kt, std::integral_constant<int, 0>{});
+
+  // D layout of the 32x32 MFMA: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
+  // column l%32. The K loop ended with a barrier: the operand buffers are free.
+  if (kMode == 0) {
+    // h tile (128 x 128 fp32) into LDS, then each row's block is quantised:
+    // four lanes per row, 32 columns each
+    float* sh = reinterpret_cast<float*>(&smem[0][0]);
+#pragma unroll
+    for (int i = 0; i < NRB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = 32 * (wm + 2 * i) + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        sh[m * kHLd + 32 * wn + lr] = silu_fast(acc[i][0][e]) * acc[i][1][e];
+      }
+    __syncthreads();
+    const int r = tid >> 2, q = tid & 3;
+    if (r < t.vrows) {  // the four lanes of a row are in or out together
+      float v[32];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const f32x4 x4 = *reinterpret_cast<const f32x4*>(&sh[r * kHLd + 32 * q + 4 * j]);
+        v[4 * j] = x4.x; v[4 * j + 1] = x4.y; v[4 * j + 2] = x4.z; v[4 * j + 3] = x4.w;
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      amax = fmaxf(amax, __uint_as_float(dpp_u32<0xB1>(__float_as_uint(amax))));
+      amax = fmaxf(amax, __uint_as_float(dpp_u32<0x4E>(__float_as_uint(amax))));
+      const float s = e4m3_block_scale(amax);
+      uint32_t w[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        w[j] = e4m3_code(v[4 * j] / s) | (e4m3_code(v[4 * j + 1] / s) << 8) | (e4m3_code(v[4 * j + 2] / s) << 16) |
+               (e4m3_code(v[4 * j + 3] / s) << 24);
+      uint8_t* dst = static_cast<uint8_t*>(t.c) + (size_t)(t.m0 + r) * t.ldc + t.nt * 128 + 32 * q;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+      if (q == 0) t.c_scale[(size_t)(t.m0 + r) * t.c_sld + t.nt] = s;
+    }
+  } else {
+    // y tile (128 x 256 bf16) staged through LDS, then written as 16-byte
+    // pieces of each row. Rows e, e+1 (e even) of a lane are adjacent rows of
+    // one column; an even lane swaps its row-(e+1) value for its odd
+    // neighbour's row-e value (DPP quad permute 1,0,3,2), so each lane writes
+    // two adjacent columns of one row as one 32-bit word.
+    uint16_t* so = reinterpret_cast<uint16_t*>(&smem[0][0]);
+    const bool odd = lane & 1;
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) {
+        const int m = 32 * (wm + 2 * i) + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const float g0 = s_gate[m], g1 = s_gate[m + 1];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const uint32_t b0 = f32_to_bf16(g0 * acc[i][c][e]), b1 = f32_to_bf16(g1 * acc[i][c][e + 1]);
+          const uint32_t rr = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? b0 : b1), 0xB1, 0xF, 0xF, false);
+          const int col = 64 * wn + 32 * c + lr;
+          const uint32_t w = odd ? (rr | (b1 << 16)) : (b0 | (rr << 16));
+          *reinterpret_cast<uint32_t*>(&so[(m + (odd ? 1 : 0)) * kYLd + (col & ~1)]) = w;
+        }
+      }
+    }
+    __syncthreads();
+    const int q = tid & 31;  // 16-byte piece of a row
+    const int col = t.nt * BN + 8 * q;
+    if (col < t.D) {  // D % 128 == 0: a piece is wholly inside or outside
+      uint16_t* cy = static_cast<uint16_t*>(t.c);
+#pragma unroll 4
+      for (int r = tid >> 5; r < t.vrows; r += 16)
+        *reinterpret_cast<uint4*>(cy + (size_t)(t.m0 + r) * t.ldc + col) =
+            *reinterpret_cast<const uint4*>(&so[r * kYLd + 8 * q]);
+    }
+  }
+}
+
+// kMode 0: gate/up + SwiGLU + h quantisation, 1: down + gate scale
+template <int kMode>
+__global__ __launch_bounds__(512) void grouped_gemm_f8_kernel(ExpertGemmArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][kBufBytes];
+  __shared__ __attribute__((aligned(16))) float s_asc[2][512];  // row scales (entries 0..127 used)
+  __shared__ int32_t s_pre[kMaxExperts + 2];
+  __shared__ int32_t s_off[kMaxExperts + 1];
+  __shared__ float s_gate[BM];
+
+  // runs of kRun consecutive tiles, run r on XCD r % 8 (block b runs on XCD b % 8)
+  const int total = a.pre[a.E + 1];
+  const int bid = blockIdx.x;
+  const int slot = bid >> 3;
+  const int tile = ((slot / kRun) * 8 + (bid & 7)) * kRun + slot % kRun;
+  if (tile >= total) return;
+
+  for (int i = threadIdx.x; i < a.E + 2; i += blockDim.x) s_pre[i] = a.pre[i];
+  for (int i = threadIdx.x; i < a.E + 1; i += blockDim.x) s_off[i] = a.offsets[i];
+  __syncthreads();
+  // workgroup-uniform values (scalar registers)
+  const int p = __builtin_amdgcn_readfirstlane(find_problem(s_pre, a.E, tile));
+  const bool routed = p < a.E;
+  const int rows = __builtin_amdgcn_readfirstlane(routed ? s_off[p + 1] - s_off[p] : a.T);
+  const int row_base = __builtin_amdgcn_readfirstlane(routed ? s_off[p] : 0);
+  const int local = __builtin_amdgcn_readfirstlane(tile - s_pre[p]);
+  TileF8 t;
+  t.Hp = routed ? a.H : a.Hs;
+  t.D = a.D;
+  const int nmt = (rows + BM - 1) / BM;
+  const int rpt = ((rows + nmt - 1) / nmt + 31) & ~31;
+  t.m0 = (local % nmt) * rpt;
+  t.nt = local / nmt;
+  t.K = (kMode == 0) ? a.D : t.Hp;
+  t.vrows = min(rows - t.m0, rpt);
+  t.a_sld = t.K / 128;
+  if (kMode == 0) {
+    t.a_rows = static_cast<const uint8_t*>(a.a);
+    t.lda = a.D;
+    t.tok = routed ? a.row_token + row_base : nullptr;
+    t.a_scale = a.a_scale;  // x scales, indexed by token
+    t.w = routed ? static_cast<const uint8_t*>(a.w) + (size_t)p * 2 * t.Hp * a.D
+                 : static_cast<const uint8_t*>(a.w_shared);
+    t.ws = routed ? a.w_scale + (size_t)p * (2 * t.Hp / 128) * t.a_sld : a.w_shared_scale;
+    t.c = routed ? static_cast<void*>(static_cast<uint8_t*>(a.c) + (size_t)row_base * a.H) : a.c_shared;
+    t.c_scale = routed ? a.c_scale + (size_t)row_base * (a.H / 128) : a.c_shared_scale;
+    t.c_sld = t.Hp / 128;
+    t.ldc = t.Hp;
+    t.gate = nullptr;
+    t.a_bytes = (uint32_t)((size_t)a.x_rows * a.D);
+    t.w_bytes = (uint32_t)((size_t)2 * t.Hp * a.D);
+  } else {
+    t.a_rows = routed ? static_cast<const uint8_t*>(a.a) + (size_t)row_base * a.H
+                      : static_cast<const uint8_t*>(a.a_shared);
+    t.lda = t.Hp;
+    t.tok = nullptr;
+    t.a_scale = routed ? a.a_scale + (size_t)row_base * (a.H / 128) : a.a_shared_scale;
+    t.w = routed ? static_cast<const uint8_t*>(a.w) + (size_t)p * a.D * t.Hp
+                 : static_cast<const uint8_t*>(a.w_shared);
+    t.ws = routed ? a.w_scale + (size_t)p * (a.D / 128) * t.a_sld : a.w_shared_scale;
+    t.c = routed ? static_cast<void*>(static_cast<uint16_t*>(a.c) + (size_t)row_base * a.D) : a.c_shared;
+    t.c_scale = nullptr;
+    t.c_sld = 0;
+    t.ldc = a.D;
+    t.gate = routed ? a.row_gate + row_base : nullptr;
+    t.a_bytes = (uint32_t)((size_t)rows * t.Hp);
+    t.w_bytes = (uint32_t)((size_t)a.D * t.Hp);
+  }
+
+  // valid 32-row blocks of this wave: wm + 2*i for i < nrb
+  const int wm = (threadIdx.x >> 6) >> 2;
+  int nrb = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) nrb += (32 * (wm + 2 * i) < t.vrows) ? 1 : 0;
+  switch (nrb) {
+    case 2: tile_body_f8<kMode, 2>(t, smem, s_asc, s_gate); break;
+    case 1: tile_body_f8<kMode, 1>(t, smem, s_asc, s_gate); break;
+    default: tile_body_f8<kMode, 0>(t, smem, s_asc, s_gate); break;
+  }
+}
+
+namespace {
+int grouped_blocks_f8(int max_items) {
+  const int runs = (max_items + kRun - 1) / kRun;
+  return ((runs + 7) / 8) * 8 * kRun;
+}
+}  // namespace
+
+hipError_t launch_grouped_gateup_f8(const ExpertGemmArgs& a, hipStream_t s) {
+  const int blocks = grouped_blocks_f8(a.max_items);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((grouped_gemm_f8_kernel<0>), dim3(blocks), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_down_f8(const ExpertGemmArgs& a, hipStream_t s) {
+  const int blocks = grouped_blocks_f8(a.max_items);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((grouped_gemm_f8_kernel<1>), dim3(blocks), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -31,6 +31,11 @@ struct moe_cfg {
   void* h_shared;
   void* y_routed;
   void* y_shared;
+  // e4m3 activations: x codes and scales, h scales (h codes use h_routed / h_shared)
+  uint8_t* xq;
+  float* xs;
+  float* hs_routed;
+  float* hs_shared;
   int last_hip_error;
   // stage timing
   bool timing;
@@ -56,12 +61,15 @@ moe_status validate(const moe_params* p) {
   if (p->out_dtype != MOE_F32 && p->out_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
   if (p->max_tokens < 0) return MOE_ERR_INVALID_ARG;
   if (p->path < MOE_PATH_AUTO || p->path > MOE_PATH_STREAM) return MOE_ERR_INVALID_ARG;
+  if (p->act_quant != MOE_ACT_QUANT_NONE && p->act_quant != MOE_ACT_QUANT_E4M3_1X128) return MOE_ERR_INVALID_ARG;
   if (!(p->routed_scaling_factor == p->routed_scaling_factor)) return MOE_ERR_INVALID_ARG;  // NaN
   // dtype combinations this build runs
   const bool f32 = p->act_dtype == MOE_F32 && p->weight_dtype == MOE_F32;
   const bool bf = p->act_dtype == MOE_BF16 && p->weight_dtype == MOE_BF16;
   const bool fp8 = p->act_dtype == MOE_BF16 && p->weight_dtype == MOE_FP8_E4M3;
   if (!(f32 || bf || fp8)) return MOE_ERR_UNSUPPORTED;
+  // e4m3 activations: fp8 weights, bf16 x, grouped kernels only
+  if (p->act_quant == MOE_ACT_QUANT_E4M3_1X128 && (!fp8 || p->path == MOE_PATH_STREAM)) return MOE_ERR_UNSUPPORTED;
   if (p->dim % 32 != 0) return MOE_ERR_UNSUPPORTED;
   if (!f32 && (p->dim % 128 || p->hidden % 128 || p->shared_hidden % 128)) return MOE_ERR_UNSUPPORTED;
   // the grouped GEMMs address x rows, an expert's h rows and one expert's
@@ -76,10 +84,11 @@ moe_status validate(const moe_params* p) {
 
 size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 
-enum class Path { kF32, kGrouped, kStream };
+enum class Path { kF32, kGrouped, kGroupedF8, kStream };
 
 Path choose_path(const moe_params& p, int T) {
   if (p.weight_dtype == MOE_F32) return Path::kF32;
+  if (p.act_quant == MOE_ACT_QUANT_E4M3_1X128) return Path::kGroupedF8;
   if (p.path == MOE_PATH_GROUPED) return Path::kGrouped;
   if (p.path == MOE_PATH_STREAM) return Path::kStream;
   return T > 256 ? Path::kGrouped : Path::kStream;
@@ -100,6 +109,11 @@ void fill_dispatch_geometry(const moe_params& p, Path path, int T, DispatchArgs*
   d->shared_rows = p.shared_hidden > 0 ? T : 0;
   if (path == Path::kGrouped) {
     d->bm = kGB_BM;
+    d->n1_routed = p.hidden / kG1_BNH;
+    d->n1_shared = p.shared_hidden / kG1_BNH;
+    d->n2_routed = d->n2_shared = (p.dim + kG2_BN - 1) / kG2_BN;
+  } else if (path == Path::kGroupedF8) {
+    d->bm = kF8_BM;
     d->n1_routed = p.hidden / kG1_BNH;
     d->n1_shared = p.shared_hidden / kG1_BNH;
     d->n2_routed = d->n2_shared = (p.dim + kG2_BN - 1) / kG2_BN;
@@ -175,6 +189,9 @@ moe_status moe_cfg_create(const moe_params* p, moe_cfg** out) {
   const size_t o_rt = take(Tm * K * 4), o_rg = take(Tm * K * 4), o_sr = take(Tm * K * 4);
   const size_t o_hr = take(Tm * K * H * act), o_hs = take(Tm * Hs * act);
   const size_t o_yr = take(Tm * K * D * act), o_ys = take(Tm * D * act);
+  const bool aq = p->act_quant == MOE_ACT_QUANT_E4M3_1X128;
+  const size_t o_xq = aq ? take(Tm * D) : 0, o_xs = aq ? take(Tm * (D / 128) * 4) : 0;
+  const size_t o_hsr = aq ? take(Tm * K * (H / 128) * 4) : 0, o_hss = aq ? take(Tm * (Hs / 128) * 4) : 0;
   c->ws_bytes = off;
   if (hipMalloc((void**)&c->ws, c->ws_bytes) != hipSuccess) {
     (void)hipGetLastError();
@@ -197,6 +214,12 @@ moe_status moe_cfg_create(const moe_params* p, moe_cfg** out) {
   c->h_shared = c->ws + o_hs;
   c->y_routed = c->ws + o_yr;
   c->y_shared = c->ws + o_ys;
+  if (aq) {
+    c->xq = (uint8_t*)(c->ws + o_xq);
+    c->xs = (float*)(c->ws + o_xs);
+    c->hs_routed = (float*)(c->ws + o_hsr);
+    c->hs_shared = (float*)(c->ws + o_hss);
+  }
   *out = c;
   return MOE_OK;
 }
@@ -282,6 +305,17 @@ moe_status moe_router_forward(moe_cfg* c, const void* x, int T, const float* gat
   r.w_split = c->w_split;
   hipError_t e = launch_router(r, s);
   return e == hipSuccess ? MOE_OK : hip_fail(c, e);
+}
+
+moe_status moe_quantize_e4m3_1x128(const void* x, int rows, int cols, uint8_t* codes, float* scales,
+                                   void* stream) {
+  if (rows < 0 || cols <= 0 || cols % kActBlock != 0) return MOE_ERR_INVALID_ARG;
+  if ((uint64_t)rows * (uint64_t)cols > (1ull << 34)) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!x || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  return launch_quant_e4m3(static_cast<const uint16_t*>(x), rows, cols, codes, scales, (hipStream_t)stream) ==
+                 hipSuccess
+             ? MOE_OK : MOE_ERR_HIP;
 }
 
 moe_status moe_bias_update(const int32_t* expert_counts, int E, float gamma, float* sel_bias, void* stream) {
@@ -399,6 +433,17 @@ moe_status moe_layer_forward(moe_cfg* c, const void* x, int T, const float* gate
       if ((e = launch_grouped_gateup(g1, fp8, s)) != hipSuccess) return hip_fail(c, e);
       mark(c, 3, s);
       if ((e = launch_grouped_down(g2, fp8, s)) != hipSuccess) return hip_fail(c, e);
+    } else if (path == Path::kGroupedF8) {
+      // token rows to e4m3 (counted in the gate/up stage), then both GEMMs on
+      // codes + block scales; the gate/up GEMM writes h as codes + scales
+      if ((e = launch_quant_e4m3(static_cast<const uint16_t*>(x), T, p.dim, c->xq, c->xs, s)) != hipSuccess)
+        return hip_fail(c, e);
+      g1.a = c->xq; g1.a_scale = c->xs;
+      g1.c_scale = c->hs_routed; g1.c_shared_scale = c->hs_shared;
+      g2.a_scale = c->hs_routed; g2.a_shared_scale = c->hs_shared;
+      if ((e = launch_grouped_gateup_f8(g1, s)) != hipSuccess) return hip_fail(c, e);
+      mark(c, 3, s);
+      if ((e = launch_grouped_down_f8(g2, s)) != hipSuccess) return hip_fail(c, e);
     } else {
       const int cap = c->num_cus * 2;  // persistent workgroups
       if ((e = launch_stream_gateup(g1, fp8, std::min(g1.max_items, cap), s)) != hipSuccess) return hip_fail(c, e);

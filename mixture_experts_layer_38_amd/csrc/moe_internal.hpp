@@ -26,6 +26,10 @@ constexpr int kGB_BM = 256;   // rows (tokens) per tile
 constexpr int kG1_BNH = 128;  // hidden columns per gate/up tile (128 gate + 128 up rows of W)
 constexpr int kG2_BN = 256;   // output columns per down tile
 constexpr int kGB_BK = 64;    // K step
+// Grouped GEMMs on e4m3 activations and weights (fp8 matrix cores).
+constexpr int kF8_BM = 128;   // rows (tokens) per tile
+constexpr int kF8_BK = 128;   // K step = one scale block (elements = bytes)
+constexpr int kActBlock = 128;  // activation quantisation block (1 x 128)
 // Weight-streaming path (small token counts): token rows and columns per workgroup item.
 constexpr int kST_BM = 16;
 constexpr int kST_N1 = 32;    // hidden columns per gate/up item (32 gate + 32 up rows)
@@ -50,6 +54,29 @@ __device__ __forceinline__ float silu_fast(float z) {
   float e = __builtin_amdgcn_exp2f(-z * 1.4426950408889634f);
   return z * __builtin_amdgcn_rcpf(1.0f + e);
 }
+
+// float32 -> OCP e4m3 code (1 sign, 4 exponent bits with bias 7, 3 mantissa
+// bits; largest finite 448), rounded to nearest even; magnitudes past 448
+// saturate to 448; the sign bit is the float32 sign bit. Normal range: round
+// the float32 significand to 3 bits at bit 20 and rebias the exponent; below
+// 2^-6 the codes are the multiples of 2^-9, rounded by v_rndne_f32.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x3C800000u) {  // |v| >= 2^-6
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+    code = code > 0x7Eu ? 0x7Eu : code;
+  } else {
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  }
+  return ((u >> 24) & 0x80u) | code;
+}
+
+// scale of one 1 x 128 activation block: largest magnitude / 448 (IEEE
+// division), 1 for an all-zero block
+__device__ __forceinline__ float e4m3_block_scale(float amax) { return amax > 0.f ? amax / 448.0f : 1.0f; }
 
 __device__ __forceinline__ uint32_t ordered_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -185,10 +212,21 @@ struct ExpertGemmArgs {
   const float* w_shared_scale;
   void* c;                  // GEMM1: h routed; GEMM2: y routed
   void* c_shared;           // GEMM1: h shared; GEMM2: y shared
+  // e4m3 activations only: 1x128 block scales of the A rows and of h
+  const float* a_scale;         // GEMM1: x scales [x_rows][D/128]; GEMM2: h routed scales [T*K][H/128]
+  const float* a_shared_scale;  // GEMM2: h shared scales [T][Hs/128]
+  float* c_scale;               // GEMM1: h routed scales
+  float* c_shared_scale;        // GEMM1: h shared scales
 };
 // grouped (prefill) GEMMs; fp8: e4m3 weights with 128x128 block scales
 hipError_t launch_grouped_gateup(const ExpertGemmArgs& a, int fp8, hipStream_t s);
 hipError_t launch_grouped_down(const ExpertGemmArgs& a, int fp8, hipStream_t s);
+// grouped GEMMs on e4m3 activations (1x128 block scales) and e4m3 weights
+// (128x128 block scales), fp8 MFMA; the gate/up GEMM writes h as e4m3 + scales
+hipError_t launch_grouped_gateup_f8(const ExpertGemmArgs& a, hipStream_t s);
+hipError_t launch_grouped_down_f8(const ExpertGemmArgs& a, hipStream_t s);
+// x bf16 [rows][cols] -> e4m3 codes [rows][cols] + scales [rows][cols/128]
+hipError_t launch_quant_e4m3(const uint16_t* x, int rows, int cols, uint8_t* q, float* scale, hipStream_t s);
 hipError_t launch_stream_gateup(const ExpertGemmArgs& a, int fp8, int blocks, hipStream_t s);
 hipError_t launch_stream_down(const ExpertGemmArgs& a, int fp8, int blocks, hipStream_t s);
 hipError_t launch_simple_gateup_f32(const ExpertGemmArgs& a, int TK, hipStream_t s);

@@ -41,6 +41,7 @@ def test_status_strings():
     dict(score_fn=7),
     dict(out=2),                             # fp8 output
     dict(path=9),
+    dict(act_quant=2),                       # no such activation quantisation
 ])
 def test_invalid_layers_rejected(kw):
     st, h = M.create_cfg(_params(**kw))
@@ -56,6 +57,9 @@ def test_invalid_layers_rejected(kw):
     dict(n_routed=1024, n_group=8),          # E > 512
     dict(max_tokens=400000, dim=7168),       # x rows past 32-bit byte offsets
     dict(max_tokens=1100000, hidden=2048),   # an expert's h rows past 32-bit byte offsets
+    dict(act_quant=True),                    # e4m3 activations need e4m3 weights
+    dict(act_quant=True, act="f32", weight="fp8"),
+    dict(act_quant=True, weight="fp8", path="stream"),  # e4m3 activations run on the grouped kernels only
 ])
 def test_unsupported_layers_rejected(kw):
     st, h = M.create_cfg(_params(**kw))
@@ -92,3 +96,20 @@ def test_balance_entry_points_reject_bad_arguments():
     assert lib.moe_load_stats(c, 8, None, None) == bad
     assert lib.moe_load_stats(c, 0, b, None) == bad
     assert lib.moe_load_stats(c, 600, b, None) == bad
+
+
+def test_quantizer_entry_point_rejects_bad_arguments():
+    """Sizes and null pointers are checked before anything is launched; an
+    empty input launches nothing (host buffers stand in for device pointers)."""
+    lib = M.load_library()
+    buf = (ctypes.c_uint8 * 1024)()
+    b = ctypes.cast(buf, ctypes.c_void_p)
+    bad = M.MOE_ERR_INVALID_ARG
+    assert lib.moe_quantize_e4m3_1x128(b, 2, 100, b, b, None) == bad      # cols % 128
+    assert lib.moe_quantize_e4m3_1x128(b, 2, 0, b, b, None) == bad
+    assert lib.moe_quantize_e4m3_1x128(b, -1, 128, b, b, None) == bad
+    assert lib.moe_quantize_e4m3_1x128(b, 1 << 20, 1 << 15, b, b, None) == bad  # past 2^34 elements
+    assert lib.moe_quantize_e4m3_1x128(None, 2, 128, b, b, None) == bad
+    assert lib.moe_quantize_e4m3_1x128(b, 2, 128, None, b, None) == bad
+    assert lib.moe_quantize_e4m3_1x128(b, 2, 128, b, None, None) == bad
+    assert lib.moe_quantize_e4m3_1x128(None, 0, 128, None, None, None) == M.MOE_OK

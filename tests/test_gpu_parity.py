@@ -227,6 +227,84 @@ def test_layer_fp8_prefill():
     _check_layer(inp, tokens=_sample(FP8_PREFILL.T, 200))
 
 
+# e4m3 activations with 1x128 block scales on the fp8 matrix cores: token rows
+# and h quantised, weights e4m3 with 128x128 block scales; 128-row tiles.
+# small_w8a8: 2 K steps in both GEMMs; w8a8_odd: 3 K steps (a tail step) in
+# the gate/up GEMM and the shared down GEMM, 1 in the routed down GEMM;
+# w8a8_prefill: about 260 rows per expert, three row tiles each
+SMALL_W8A8 = SMALL_FP8.with_(name="small_w8a8", act_quant=True)
+W8A8_ODD = MI.LayerConfig("w8a8_odd", T=300, D=384, E=16, H=128, G=4, kg=2, K=3, score_fn="sigmoid",
+                          bias="normal", norm=True, rsf=2.5, Hs=384, act="bf16", weight="fp8", bias_std=0.05,
+                          act_quant=True)
+W8A8_PREFILL = FP8_PREFILL.with_(name="w8a8_prefill", act_quant=True)
+
+
+@pytest.mark.parametrize("cfg", [SMALL_W8A8, W8A8_ODD, W8A8_PREFILL], ids=lambda c: c.name)
+def test_layer_e4m3_activations(cfg):
+    inp = MI.make_layer(cfg, DEV)
+    _check_layer(inp, tokens=_sample(cfg.T, 200))
+
+
+def test_layer_e4m3_activations_every_code_and_edges():
+    """Weights over all finite e4m3 codes; then T = 1 and T = max_tokens, and
+    repeat runs bit-identical."""
+    cfg = SMALL_W8A8
+    inp = MI.make_layer(cfg, DEV)
+    g = torch.Generator().manual_seed(9)
+    for w in (inp.experts.gate_up, inp.experts.down, inp.shared.gate_up, inp.shared.down):
+        r = torch.randint(0, 254, w.shape, generator=g, dtype=torch.int32)
+        w.copy_(torch.where(r >= 0x7F, r + 1, r).to(torch.uint8).to(DEV))
+    _check_layer(inp)
+    layer = M.MoELayer.from_config(cfg)
+    R = A.route_inputs(inp)
+    for T in (1, cfg.T):
+        o = layer.forward(inp.x[:T].contiguous(), inp.gate_w, inp.sel_bias, inp.experts, inp.shared)
+        torch.cuda.synchronize()
+        ref, _ = A.run_layer(inp, tokens=np.arange(T), routing=R)
+        err = layer_error(o, ref, A.decode_tensor(inp.x)[:T], True, exclude=near_tie_mask(R)[:T])
+        assert err["max"] <= TOL["fp8"], (T, err)
+    o1 = layer.forward(inp.x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared)
+    o2 = layer.forward(inp.x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def _quant_parity(x_bf16_cpu, rows=None):
+    """GPU quantiser vs the oracle, bit for bit, on all rows or the given ones."""
+    codes, scales = M.quantize_e4m3_1x128(x_bf16_cpu.to(DEV).contiguous())
+    torch.cuda.synchronize()
+    xs = x_bf16_cpu if rows is None else x_bf16_cpu[torch.as_tensor(rows)]
+    rc, rs = O.quantize_act_1x128(O.decode_bf16(xs.view(torch.int16).numpy()).astype(np.float32))
+    gc, gs = codes.cpu().numpy(), scales.cpu().numpy()
+    if rows is not None:
+        gc, gs = gc[rows], gs[rows]
+    assert np.array_equal(gs.view(np.uint32), rs.view(np.uint32)), "scales differ"
+    bad = np.argwhere(gc != rc)
+    assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:3].tolist()}"
+
+
+def test_quantizer_matches_the_oracle_bit_for_bit():
+    g = torch.Generator().manual_seed(11)
+    rows, cols = 301, 1024
+    mag = torch.logspace(-25, 25, rows, dtype=torch.float64)[:, None]
+    x = (torch.randn((rows, cols), generator=g, dtype=torch.float64) * mag).to(torch.bfloat16)
+    x[3] = 0.0                                   # all-zero blocks
+    x[4] = -0.0                                  # negative zeros
+    x[5, :] = 0.0
+    x[5, 200] = -3.0                             # a single value per block
+    # scale exactly 1 (block maximum 448) and every midpoint between two e4m3
+    # values (exact in bf16): ties to the even code, each sign
+    t = O.decode_e4m3(np.arange(0x7F))
+    mids = torch.from_numpy(np.concatenate([[448.0], (t[:-1] + t[1:]) / 2, [-448.0]]))
+    x[6] = torch.cat([mids, -mids]).repeat(cols // 256).to(torch.bfloat16)
+    x[7] = torch.full((cols,), 448.0, dtype=torch.bfloat16)  # every value the block maximum
+    _quant_parity(x)
+    # a single row and an empty input
+    _quant_parity(x[:1].clone())
+    c0, s0 = M.quantize_e4m3_1x128(torch.empty((0, 256), dtype=torch.bfloat16, device=DEV))
+    assert c0.shape == (0, 256) and s0.shape == (0, 2)
+
+
 SKEWED = MI.LayerConfig("skewed", T=1100, D=256, E=16, H=128, G=4, kg=2, K=3, score_fn="sigmoid",
                         bias="normal", norm=True, rsf=2.5, Hs=128, act="bf16", weight="bf16", bias_std=0.05)
 
@@ -358,6 +436,14 @@ def test_layer_v3_prefill(layers):
 
 def test_layer_v3_ep8_shard(layers):
     inp = layers("v3_ep8_shard")
+    _check_layer(inp, tokens=_sample(inp.cfg.T, 16), routed_only=False)
+
+
+def test_layer_v3_prefill_w8a8(layers):
+    """The V3 prefill layer with e4m3 activations, at full size; the
+    quantiser bit for bit on sampled token rows of the same x."""
+    inp = layers("v3_prefill_w8a8")
+    _quant_parity(inp.x.cpu(), rows=_sample(inp.cfg.T, 64, seed=3))
     _check_layer(inp, tokens=_sample(inp.cfg.T, 16), routed_only=False)
 
 
