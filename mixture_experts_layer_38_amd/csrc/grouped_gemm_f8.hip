@@ -67,9 +67,9 @@ __device__ __forceinline__ i32x8 lds_frag(const uint8_t* p) {
   return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
-__device__ __forceinline__ f32x16 mfma_f8(const i32x8& a, const i32x8& b, const f32x16& c) {
+__device__ __forceinline__ f32x4 mfma_f8(const i32x8& a, const i32x8& b, const f32x4& c) {
   // format 0 = e4m3 for both operands; E8M0 scale 127 = 2^0
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 }  // namespace
 
@@ -112,11 +112,12 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
     const int row = (kMode == 0 && t.tok != nullptr) ? t.tok[mm] : mm;
     asrow = t.a_scale + (size_t)row * t.a_sld;
   }
-  // weight scales of this wave's two 32-column blocks (one 128-row block each)
+  // weight scales: gate/up, one 128-row block of W_gate and one of W_up;
+  // down, the 128-row block of W_down holding this wave's 64 columns
   const float* wsr[2];
   if (kMode == 0) {
-    wsr[0] = t.ws + (size_t)t.nt * t.a_sld;                    // W_gate rows nt*128 ..
-    wsr[1] = t.ws + (size_t)(t.Hp / 128 + t.nt) * t.a_sld;     // W_up rows Hp + nt*128 ..
+    wsr[0] = t.ws + (size_t)t.nt * t.a_sld;
+    wsr[1] = t.ws + (size_t)(t.Hp / 128 + t.nt) * t.a_sld;
   } else {
     int cb = (t.nt * BN + 64 * wn) >> 7;
     if (cb * 128 >= t.D) cb = 0;
@@ -130,24 +131,25 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, vob[j], k0, 0));
   };
 
-  f32x16 acc[NRB > 0 ? NRB : 1][2];
+  // 16 x 16 output blocks: row block i (rows 16*(wm + 2i) ..), column block
+  // c (gate/up: c < 2 the wave's two W_gate blocks, c >= 2 the matching W_up
+  // blocks; down: 64*wn + 16c)
+  constexpr int NA = NRB > 0 ? NRB : 1;
+  f32x4 acc[NA][4];
 #pragma unroll
-  for (int i = 0; i < NRB; ++i)
+  for (int i = 0; i < NA; ++i)
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < 4; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int bcol[4];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][c][e] = 0.f;
-
-  int bcol[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) bcol[c] = (kMode == 0) ? 128 * c + 32 * wn : 64 * wn + 32 * c;
-  const int lr = lane & 31, lk = (lane >> 5) * 32;
+  for (int c = 0; c < 4; ++c) bcol[c] = (kMode == 0) ? 128 * (c >> 1) + 32 * wn + 16 * (c & 1) : 64 * wn + 16 * c;
+  const int lr = lane & 15, lk = (lane >> 4) * 32;
 
   if (kMode == 1 && tid < BM) s_gate[tid] = (t.gate != nullptr && tid < t.vrows) ? t.gate[t.m0 + tid] : 1.0f;
 
   const int nk = t.K / BK;
   uint4 pa[2][kLdA], pb[kLdB];
-  float pas[2] = {1.f, 1.f};
+  float pas[2];
 #pragma unroll
   for (int j = 0; j < kLdA; ++j) pa[0][j] = gload_a(j, 0);
   pas[0] = asrow[0];
@@ -160,16 +162,42 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
     pas[1] = asrow[k1];
   }
 
-  auto store = [&](int buf, const uint4 (&va)[kLdA], float vas) __attribute__((always_inline)) {
+  auto store_a = [&](int buf, const uint4 (&va)[kLdA], float vas) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kLdA; ++j) *reinterpret_cast<uint4*>(&smem[buf][(r0 + 64 * j) * LDB + c16 * 16]) = va[j];
+    s_asc[buf][tid] = vas;
+  };
+  auto store_b = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < kLdB; ++j)
       *reinterpret_cast<uint4*>(&smem[buf][(BM + r0 + 64 * j) * LDB + c16 * 16]) = pb[j];
-    s_asc[buf][tid] = vas;
   };
-  store(0, pa[0], pas[0]);
+  store_a(0, pa[0], pas[0]);
+  store_b(0);
   __syncthreads();
+
+  // fragments: lane l holds row (or column) l % 16, K bytes 32*(l/16) .. +31
+  i32x8 fa[NA], fb[4];
+  f32x4 sa[NA];
+  auto read_a = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+      fa[i] = lds_frag(&smem[buf][(16 * (wm + 2 * i) + lr) * LDB + lk]);
+      // scales of this lane's rows 16*(wm + 2i) + 4*(l/16) + 0..3
+      sa[i] = *reinterpret_cast<const f32x4*>(&s_asc[buf][16 * (wm + 2 * i) + 4 * (lane >> 4)]);
+    }
+  };
+  auto read_b = [&](int buf, int c) __attribute__((always_inline)) {
+    fb[c] = lds_frag(&smem[buf][(BM + bcol[c] + lr) * LDB + lk]);
+  };
+  auto block = [&](int i, int c, float sw) __attribute__((always_inline)) {
+    const f32x4 p = mfma_f8(fa[i], fb[c], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[i][c][e] = __builtin_fmaf(p[e], sa[i][e] * sw, acc[i][c][e]);
+  };
+  read_a(0);
+  read_b(0, 0);
+  read_b(0, 1);
 
   auto kstep = [&](int kt, auto s_c) __attribute__((always_inline)) {
     constexpr int S = decltype(s_c)::value;  // register slot of A(kt), refilled with A(kt+2)
@@ -182,40 +210,27 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
 #pragma unroll
     for (int j = 0; j < kLdB; ++j) pb[j] = gload_b(j, knext * BK);
     const float sw0 = wsr[0][kt], sw1 = wsr[1][kt];
-
-    const uint8_t* sA = smem[cur];
-    const uint8_t* sB = smem[cur] + BM * LDB;
-    i32x8 fa[NRB > 0 ? NRB : 1][2], fb[2][2];
+    // columns 2, 3 are read while columns 0, 1 are multiplied
+    read_b(cur, 2);
+    read_b(cur, 3);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) fb[c][h] = lds_frag(&sB[(bcol[c] + lr) * LDB + 64 * h + lk]);
+      for (int i = 0; i < NRB; ++i) block(i, c, sw0);
+    __builtin_amdgcn_sched_barrier(0);
+    // the next step's operands go to the idle buffer while columns 2, 3 are
+    // multiplied (the last step rewrites its own slice: no branch)
+    store_a(cur ^ 1, pa[S ^ 1], pas[S ^ 1]);
+    store_b(cur ^ 1);
 #pragma unroll
-      for (int i = 0; i < NRB; ++i) fa[i][h] = lds_frag(&sA[(32 * (wm + 2 * i) + lr) * LDB + 64 * h + lk]);
-    }
+    for (int c = 2; c < 4; ++c)
 #pragma unroll
-    for (int i = 0; i < NRB; ++i) {
-      // scales of this lane's 16 rows of block i: rows 8*q + 4*(lane/32) + 0..3
-      float sa[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(&s_asc[cur][32 * (wm + 2 * i) + 8 * q + 4 * (lane >> 5)]);
-        sa[4 * q] = v.x; sa[4 * q + 1] = v.y; sa[4 * q + 2] = v.z; sa[4 * q + 3] = v.w;
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        f32x16 p = {};
-        p = mfma_f8(fa[i][0], fb[c][0], p);
-        p = mfma_f8(fa[i][1], fb[c][1], p);
-        const float sw = c == 0 ? sw0 : sw1;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][c][e] = __builtin_fmaf(p[e], sa[e] * sw, acc[i][c][e]);
-      }
-    }
-    // the next step's operands into the idle buffer (the last step rewrites
-    // its own slice: the body stays branch-free)
-    store(cur ^ 1, pa[S ^ 1], pas[S ^ 1]);
+      for (int i = 0; i < NRB; ++i) block(i, c, kMode == 0 ? sw1 : sw0);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+    read_a(cur ^ 1);
+    read_b(cur ^ 1, 0);
+    read_b(cur ^ 1, 1);
   };
   int kt = 0;
   for (; kt + 1 < nk; kt += 2) {
@@ -223,9 +238,10 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
     kstep(kt + 1, std::integral_constant<int, 1>{});
   }
   if (kt < nk) kstep(kt, std::integral_constant<int, 0>{});
+  __syncthreads();  // the fragment reads issued after the last step are done
 
-  // D layout of the 32x32 MFMA: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
-  // column l%32. The K loop ended with a barrier: the operand buffers are free.
+  // D layout of the 16x16 MFMA: element j of lane l is row 4*(l/16) + j,
+  // column l%16.
   if (kMode == 0) {
     // h tile (128 x 128 fp32) into LDS, then each row's block is quantised:
     // four lanes per row, 32 columns each
@@ -233,10 +249,12 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
 #pragma unroll
     for (int i = 0; i < NRB; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = 32 * (wm + 2 * i) + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        sh[m * kHLd + 32 * wn + lr] = silu_fast(acc[i][0][e]) * acc[i][1][e];
-      }
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = 16 * (wm + 2 * i) + 4 * (lane >> 4) + e;
+          sh[m * kHLd + 32 * wn + 16 * c + lr] = silu_fast(acc[i][c][e]) * acc[i][c + 2][e];
+        }
     __syncthreads();
     const int r = tid >> 2, q = tid & 3;
     if (r < t.vrows) {  // the four lanes of a row are in or out together
@@ -273,14 +291,14 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
 #pragma unroll
     for (int i = 0; i < NRB; ++i) {
 #pragma unroll
-      for (int e = 0; e < 16; e += 2) {
-        const int m = 32 * (wm + 2 * i) + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      for (int e = 0; e < 4; e += 2) {
+        const int m = 16 * (wm + 2 * i) + 4 * (lane >> 4) + e;
         const float g0 = s_gate[m], g1 = s_gate[m + 1];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < 4; ++c) {
           const uint32_t b0 = f32_to_bf16(g0 * acc[i][c][e]), b1 = f32_to_bf16(g1 * acc[i][c][e + 1]);
           const uint32_t rr = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? b0 : b1), 0xB1, 0xF, 0xF, false);
-          const int col = 64 * wn + 32 * c + lr;
+          const int col = 64 * wn + 16 * c + lr;
           const uint32_t w = odd ? (rr | (b1 << 16)) : (b0 | (rr << 16));
           *reinterpret_cast<uint32_t*>(&so[(m + (odd ? 1 : 0)) * kYLd + (col & ~1)]) = w;
         }
@@ -367,12 +385,14 @@ __global__ __launch_bounds__(512) void grouped_gemm_f8_kernel(ExpertGemmArgs a) 
     t.w_bytes = (uint32_t)((size_t)a.D * t.Hp);
   }
 
-  // valid 32-row blocks of this wave: wm + 2*i for i < nrb
+  // valid 16-row blocks of this wave: wm + 2*i for i < nrb
   const int wm = (threadIdx.x >> 6) >> 2;
   int nrb = 0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) nrb += (32 * (wm + 2 * i) < t.vrows) ? 1 : 0;
+  for (int i = 0; i < 4; ++i) nrb += (16 * (wm + 2 * i) < t.vrows) ? 1 : 0;
   switch (nrb) {
+    case 4: tile_body_f8<kMode, 4>(t, smem, s_asc, s_gate); break;
+    case 3: tile_body_f8<kMode, 3>(t, smem, s_asc, s_gate); break;
     case 2: tile_body_f8<kMode, 2>(t, smem, s_asc, s_gate); break;
     case 1: tile_body_f8<kMode, 1>(t, smem, s_asc, s_gate); break;
     default: tile_body_f8<kMode, 0>(t, smem, s_asc, s_gate); break;
