@@ -27,6 +27,9 @@ What it computes, and where the pages define it (page titles as printed):
 * "DeepSeek-V3 basics" (page 5), section 1.2, and the "DeepSeekMoE + MLA"
   notes (page 3), load-balance section: the bias update after a step and the
   load statistics (see bias_update and load_stats at the end).
+* "Transformer block" article (page 4), training data-flow section, step 6:
+  back-propagation updates the experts and the router; layer_backward gives
+  those gradients by the chain rule through this forward.
 
 Readings where the pages are silent or garbled (the formula images are
 missing from the extracted pages):
@@ -335,6 +338,89 @@ def layer_forward(p: RouterParams, u: np.ndarray, gate_w: np.ndarray, sel_bias, 
     for k in range(p.K):
         out += gate[:, k:k + 1] * Y[:, k]
     return out, routing
+
+
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    """d/dz SiLU(z) = sigma(z) (1 + z (1 - sigma(z)))."""
+    with np.errstate(over="ignore"):
+        sg = 1.0 / (1.0 + np.exp(-z))
+    return sg * (1.0 + z * (1.0 - sg))
+
+
+def swiglu_ffn_backward(u, w_gate, w_up, w_down, dy):
+    """Gradients of sum(dy * FFN(u)) for FFN(u) = W_down (SiLU(W_gate u) *
+    (W_up u)): returns (du, dW_gate, dW_up, dW_down, y) with y = FFN(u)."""
+    a = u @ w_gate.T
+    b = u @ w_up.T
+    sa = silu(a)
+    h = sa * b
+    y = h @ w_down.T
+    dW_down = dy.T @ h
+    dh = dy @ w_down
+    da = dh * b * silu_grad(a)
+    db = dh * sa
+    return da @ w_gate + db @ w_up, da.T @ u, db.T @ u, dW_down, y
+
+
+def gate_score_grad(s_sel: np.ndarray, d_gate: np.ndarray, norm: bool, rsf: float) -> np.ndarray:
+    """dL/ds for the K selected scores from dL/dg, g_k = rsf * s_k (/ S with
+    S = sum_j s_j when normalised): d g_k / d s_j = rsf (delta_jk / S - s_k / S^2)."""
+    if not norm:
+        return rsf * d_gate
+    S = s_sel.sum(axis=1, keepdims=True)
+    return rsf * (d_gate / S - (d_gate * s_sel).sum(axis=1, keepdims=True) / S ** 2)
+
+
+def layer_backward(p: RouterParams, u: np.ndarray, gate_w: np.ndarray, sel_bias, routed_expert, d_out,
+                   shared_expert=None, add_residual: bool = True, routing: dict | None = None):
+    """Gradients of L = sum(d_out * out) for out = layer_forward(...), by the
+    chain rule through the forward's definition. The expert choice (group
+    limit and top-K) is piecewise constant, so it is held fixed and carries
+    no gradient; the gradient reaches the router through the gate values
+    g_k = rsf * s_k [/ sum_j s_j], then through the score function to the
+    logits, x and gate_w. The selection bias changes only the choice, so it
+    gets no gradient (the bias rule updates it between steps).
+
+    Returns dict(dx [T, D], d_gate_w [E, D], d_routed {e: (dW_gate, dW_up,
+    dW_down)} for every expert that received a token, d_shared (dW_gate,
+    dW_up, dW_down) or None, d_gate [T, K] = dL/dg, routing)."""
+    u = np.asarray(u, np.float64)
+    d_out = np.asarray(d_out, np.float64)
+    if routing is None:
+        routing = route(u, gate_w, sel_bias, p)
+    T, D = u.shape
+    idx, gate, s = routing["idx"], routing["gate"], routing["scores"]
+    dx = d_out.copy() if add_residual else np.zeros((T, D))
+    d_gate = np.zeros((T, p.K))
+    d_routed = {}
+    for e in np.unique(idx):
+        ii, kk = np.nonzero(idx == e)  # a token picks an expert at most once
+        wg, wu, wd = routed_expert(int(e))
+        dy = gate[ii, kk][:, None] * d_out[ii]
+        du, dwg, dwu, dwd, y = swiglu_ffn_backward(u[ii], wg, wu, wd, dy)
+        dx[ii] += du
+        d_gate[ii, kk] = (d_out[ii] * y).sum(axis=1)
+        d_routed[int(e)] = (dwg, dwu, dwd)
+    d_shared = None
+    if shared_expert is not None:
+        sw = shared_expert()
+        if sw is not None:
+            du, dwg, dwu, dwd, _ = swiglu_ffn_backward(u, *sw, d_out)
+            dx += du
+            d_shared = (dwg, dwu, dwd)
+    # gates -> selected scores -> all scores -> logits
+    rows = np.arange(T)[:, None]
+    ds_sel = gate_score_grad(s[rows, idx], d_gate, p.norm, p.rsf)
+    ds = np.zeros_like(s)
+    ds[rows, idx] = ds_sel
+    if p.score_fn == "sigmoid":
+        dlogit = ds * s * (1.0 - s)
+    else:
+        dlogit = s * (ds - (s * ds).sum(axis=1, keepdims=True))
+    gw = np.asarray(gate_w, np.float64)
+    dx += dlogit @ gw
+    return dict(dx=dx, d_gate_w=dlogit.T @ u, d_routed=d_routed, d_shared=d_shared, d_gate=d_gate,
+                routing=routing)
 
 
 def near_tie_tokens(routing: dict, window: float = 1e-6) -> np.ndarray:

@@ -7,6 +7,7 @@ storage formats. A dropped term, a wrong sign or index, or a transposed
 operand in the oracle fails at least one of them (test_pins_catch_planted_bugs
 plants such mistakes in a copy of the oracle and checks that they are caught).
 """
+import dataclasses
 import itertools
 import math
 
@@ -502,6 +503,95 @@ def test_load_stats_closed_forms():
 
 
 # ----------------------------------------------------------------------------
+# backward: the chain rule against central finite differences
+# ----------------------------------------------------------------------------
+
+
+def _bwd_problem(score_fn, norm, G, kg, seed, shared=True):
+    """A small layer whose routing has no near-tie (every selection gap well
+    above the finite-difference step), as float64 arrays."""
+    T, D, E, h, K = 10, 12, 8, 6, 3
+    for s in range(seed, seed + 200):
+        rng = np.random.default_rng(s)
+        u = rng.standard_normal((T, D))
+        gw = rng.standard_normal((E, D)) / math.sqrt(D)
+        bias = rng.standard_normal(E) * 0.05
+        ex = {e: (rng.standard_normal((h, D)) / math.sqrt(D), rng.standard_normal((h, D)) / math.sqrt(D),
+                  rng.standard_normal((D, h)) / math.sqrt(h)) for e in range(E)}
+        sh = (rng.standard_normal((2 * h, D)) / math.sqrt(D), rng.standard_normal((2 * h, D)) / math.sqrt(D),
+              rng.standard_normal((D, 2 * h)) / math.sqrt(2 * h)) if shared else None
+        dout = rng.standard_normal((T, D))
+        p = O.RouterParams(E=E, K=K, G=G, kg=kg, score_fn=score_fn, norm=norm, rsf=2.5)
+        r = O.route(u, gw, bias, p)
+        if min(r["gap_k"].min(), r["gap_g"].min()) > 1e-3:
+            return p, u, gw, bias, ex, sh, dout
+    raise AssertionError("no tie-free draw")
+
+
+def _loss(p, u, gw, bias, ex, sh, dout):
+    out, _ = O.layer_forward(p, u, gw, bias, lambda e: ex[e], (lambda: sh) if sh is not None else None)
+    return float((dout * out).sum())
+
+
+def _fd(f, arr, picks, eps=1e-6):
+    g = []
+    for ix in picks:
+        old = arr[ix]
+        arr[ix] = old + eps
+        fp = f()
+        arr[ix] = old - eps
+        fm = f()
+        arr[ix] = old
+        g.append((fp - fm) / (2 * eps))
+    return np.array(g)
+
+
+@pytest.mark.parametrize("score_fn,norm,G,kg", [("sigmoid", True, 4, 2), ("softmax", False, 1, 1),
+                                                ("softmax", True, 4, 3), ("sigmoid", False, 2, 1)])
+def test_layer_backward_matches_finite_differences(score_fn, norm, G, kg):
+    p, u, gw, bias, ex, sh, dout = _bwd_problem(score_fn, norm, G, kg, seed=3)
+    g = O.layer_backward(p, u, gw, bias, lambda e: ex[e], dout, (lambda: sh))
+    f = lambda: _loss(p, u, gw, bias, ex, sh, dout)  # noqa: E731
+    rng = np.random.default_rng(0)
+
+    def check(arr, grad, n=12):
+        picks = [tuple(int(rng.integers(0, d)) for d in arr.shape) for _ in range(n)]
+        num = _fd(f, arr, picks)
+        ana = np.array([grad[ix] for ix in picks])
+        scale = max(np.abs(ana).max(), 1e-3)
+        assert np.abs(num - ana).max() <= 1e-6 * scale, (num, ana)
+
+    check(u, g["dx"])
+    check(gw, g["d_gate_w"])
+    used = sorted(g["d_routed"])
+    for e in used[:3]:
+        for w, dw in zip(ex[e], g["d_routed"][e]):
+            check(w, dw, n=6)
+    for w, dw in zip(sh, g["d_shared"]):
+        check(w, dw, n=6)
+    # an expert nobody chose gets no gradient: the loss does not depend on it
+    unused = [e for e in range(p.E) if e not in g["d_routed"]]
+    for e in unused[:1]:
+        assert np.all(_fd(f, ex[e][0], [(0, 0), (1, 2)]) == 0.0)
+    # the selection bias only moves the choice: zero derivative
+    assert np.all(np.abs(_fd(f, bias, [(0,), (3,), (5,)])) < 1e-9)
+
+
+def test_layer_backward_residual_and_routed_only():
+    p, u, gw, bias, ex, sh, dout = _bwd_problem("sigmoid", True, 4, 2, seed=11, shared=False)
+    g1 = O.layer_backward(p, u, gw, bias, lambda e: ex[e], dout, None, add_residual=True)
+    g0 = O.layer_backward(p, u, gw, bias, lambda e: ex[e], dout, None, add_residual=False)
+    assert np.allclose(g1["dx"] - g0["dx"], dout, rtol=0, atol=1e-12)  # the residual passes d_out through
+    assert g1["d_shared"] is None
+    # dL/dg is the expert output against d_out: recover it from the forward
+    out_a, R = O.layer_forward(p, u, gw, bias, lambda e: ex[e], None, add_residual=False)
+    t, k = 4, 1
+    e = int(R["idx"][t, k])
+    y = O.swiglu_ffn(u[t:t + 1], *ex[e])[0]
+    assert math.isclose(g0["d_gate"][t, k], float(dout[t] @ y), rel_tol=1e-12)
+
+
+# ----------------------------------------------------------------------------
 # the pins must catch plausible mistakes
 # ----------------------------------------------------------------------------
 
@@ -583,3 +673,25 @@ def test_pins_catch_planted_bugs(monkeypatch):
     with pytest.raises(AssertionError):
         test_quantize_act_closed_forms()
     monkeypatch.setattr(O, "quantize_act_1x128", good_q)
+
+    good_sg = O.silu_grad
+    monkeypatch.setattr(O, "silu_grad", lambda z: 1.0 / (1.0 + np.exp(-z)))  # sigma(z) for SiLU'(z)
+    with pytest.raises(AssertionError):
+        test_layer_backward_matches_finite_differences("sigmoid", True, 4, 2)
+    monkeypatch.setattr(O, "silu_grad", good_sg)
+
+    good_bwd = O.swiglu_ffn_backward
+
+    def swapped_bwd(u, wg, wu, wd, dy):  # dW_gate and dW_up exchanged
+        du, dwg, dwu, dwd, y = good_bwd(u, wg, wu, wd, dy)
+        return du, dwu, dwg, dwd, y
+    monkeypatch.setattr(O, "swiglu_ffn_backward", swapped_bwd)
+    with pytest.raises(AssertionError):
+        test_layer_backward_matches_finite_differences("softmax", False, 1, 1)
+    monkeypatch.setattr(O, "swiglu_ffn_backward", good_bwd)
+
+    good_gsg = O.gate_score_grad
+    monkeypatch.setattr(O, "gate_score_grad", lambda s_sel, dg, norm, rsf: good_gsg(s_sel, dg, False, rsf))
+    with pytest.raises(AssertionError):  # the renormalisation's coupling term dropped
+        test_layer_backward_matches_finite_differences("sigmoid", True, 4, 2)
+    monkeypatch.setattr(O, "gate_score_grad", good_gsg)
