@@ -84,6 +84,8 @@ typedef struct {
   int max_tokens;     /* largest T any call on this cfg may pass */
   int path;           /* moe_path */
   int act_quant;      /* moe_act_quant */
+  int backward;       /* 1: also allocate the workspace of moe_layer_backward
+                         (BF16 x and BF16 weights only) */
 } moe_params;
 
 /* Expert weights in nn.Linear layout [out, in], row-major, dtype weight_dtype.
@@ -134,6 +136,39 @@ moe_status moe_layer_forward(moe_cfg* cfg, const void* x, int T, const float* ga
                              const moe_weights* shared_w, void* out, int32_t* expert_counts,
                              void* stream);
 
+/* Gradients of a layer (the back-propagation step of the training data flow
+ * in the "Transformer block" article, which updates experts and router):
+ * for L = sum(d_out * out), with out = moe_layer_forward on the same inputs.
+ * The expert choice (group limit and top-K) is piecewise constant, so it is
+ * held fixed; the gradient reaches the router through the gate values
+ * g_k = rsf * s_k (/ sum of the K chosen s when norm_topk), then through the
+ * score function to the logits, x and gate_w. sel_bias only changes the
+ * choice and gets no gradient (moe_bias_update adjusts it).
+ *   d_out         [T][D] fp32 (input)
+ *   dx            [T][D] fp32 dL/dx (includes d_out itself when add_residual)
+ *   d_gate_w      [E][D] fp32 dL/dgate_w
+ *   d_expert_w    fp32 dL/dW in the layout of moe_weights: gate_up
+ *                 [E][2H][D], down [E][D][H]; every expert is written
+ *                 (zeros for an expert that received no token)
+ *   d_shared_w    the same for the shared expert ([2Hs][D], [D][Hs]);
+ *                 required iff shared_hidden > 0
+ * Other arguments as moe_layer_forward. The cfg must have been created with
+ * backward = 1, BF16 x and BF16 weights (else MOE_ERR_UNSUPPORTED). The
+ * routing is recomputed (same kernels as the forward, so the same choice),
+ * and the gate/up pre-activations are recomputed rather than stored.
+ * Products run on bf16 MFMA with fp32 accumulation: d_out and gate_w are
+ * rounded to bf16 for them, the intermediates [a | u], g*h, [dA | dU] and
+ * the per-slot dx rows are bf16. T == 0 zeroes every output. */
+typedef struct {
+  float* gate_up;
+  float* down;
+} moe_weight_grads;
+
+moe_status moe_layer_backward(moe_cfg* cfg, const void* x, int T, const float* gate_w, const float* sel_bias,
+                              const moe_weights* expert_w, const moe_weights* shared_w, const float* d_out,
+                              float* dx, float* d_gate_w, const moe_weight_grads* d_expert_w,
+                              const moe_weight_grads* d_shared_w, void* stream);
+
 /* The router alone (the MoEGate forward plus the selection bias):
  *   topk_idx [T][K] int32, listed by descending z then ascending index
  *   topk_gate [T][K] fp32 gate values in the same order
@@ -150,8 +185,9 @@ moe_status moe_router_forward(moe_cfg* cfg, const void* x, int T, const float* g
  *   offsets     [E+1]  int32: rows of expert e are offsets[e] .. offsets[e+1]-1
  *   row_token   [T*K]  int32: token of each expert-contiguous row
  *   slot_row    [T*K]  int32: row that holds (t, k), at index t*K + k
- * Rows of one expert may come in any order (the kernels that consume them do
- * not depend on it); offsets, and the set of tokens of each expert, are
+ * The permutation is stable: the row of (t, k) with expert e is
+ * offsets[e] + #{(t', k') before (t, k) in row-major order with expert e},
+ * so an expert's rows hold its tokens in ascending order and every output is
  * unique. */
 moe_status moe_dispatch_forward(moe_cfg* cfg, const int32_t* topk_idx, int T, int32_t* offsets,
                                 int32_t* row_token, int32_t* slot_row, void* stream);

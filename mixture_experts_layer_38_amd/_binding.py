@@ -31,12 +31,16 @@ class MoeParams(ctypes.Structure):
                                              "topk_group", "score_fn", "norm_topk")] + \
                [("routed_scaling_factor", ctypes.c_float)] + \
                [(n, ctypes.c_int) for n in ("act_dtype", "weight_dtype", "out_dtype", "add_residual",
-                                             "max_tokens", "path", "act_quant")]
+                                             "max_tokens", "path", "act_quant", "backward")]
 
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [("gate_up", ctypes.c_void_p), ("down", ctypes.c_void_p),
                 ("gate_up_scale", ctypes.c_void_p), ("down_scale", ctypes.c_void_p)]
+
+
+class MoeWeightGrads(ctypes.Structure):
+    _fields_ = [("gate_up", ctypes.c_void_p), ("down", ctypes.c_void_p)]
 
 
 class MoEError(RuntimeError):
@@ -76,9 +80,13 @@ def load_library() -> ctypes.CDLL:
     lib.moe_bias_update.argtypes = [vp, ctypes.c_int, ctypes.c_float, vp, vp]
     lib.moe_load_stats.argtypes = [vp, ctypes.c_int, vp, vp]
     lib.moe_quantize_e4m3_1x128.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+    lib.moe_layer_backward.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.POINTER(MoeWeights),
+                                       ctypes.POINTER(MoeWeights), vp, vp, vp, ctypes.POINTER(MoeWeightGrads),
+                                       ctypes.POINTER(MoeWeightGrads), vp]
     for f in ("moe_cfg_create", "moe_cfg_destroy", "moe_layer_forward", "moe_router_forward",
               "moe_dispatch_forward", "moe_cfg_last_hip_error", "moe_cfg_set_stage_timing",
-              "moe_cfg_stage_times", "moe_bias_update", "moe_load_stats", "moe_quantize_e4m3_1x128"):
+              "moe_cfg_stage_times", "moe_bias_update", "moe_load_stats", "moe_quantize_e4m3_1x128",
+              "moe_layer_backward"):
         getattr(lib, f).restype = ctypes.c_int
     del i32p
     _lib = lib
@@ -108,7 +116,8 @@ def _stream_handle(stream) -> ctypes.c_void_p:
 
 def make_params(*, dim, n_routed, hidden, shared_hidden, top_k, n_group=1, topk_group=1,
                 score_fn="softmax", norm_topk=False, routed_scaling_factor=1.0, act="bf16", weight="bf16",
-                out="f32", add_residual=True, max_tokens, path="auto", act_quant=False) -> MoeParams:
+                out="f32", add_residual=True, max_tokens, path="auto", act_quant=False,
+                backward=False) -> MoeParams:
     return MoeParams(dim=dim, n_routed=n_routed, hidden=hidden, shared_hidden=shared_hidden, top_k=top_k,
                      n_group=n_group, topk_group=topk_group,
                      score_fn={"softmax": MOE_SCORE_SOFTMAX, "sigmoid": MOE_SCORE_SIGMOID}.get(score_fn, score_fn),
@@ -117,7 +126,7 @@ def make_params(*, dim, n_routed, hidden, shared_hidden, top_k, n_group=1, topk_
                      out_dtype=_DTYPE_CODE.get(out, out), add_residual=int(bool(add_residual)),
                      max_tokens=max_tokens,
                      path={"auto": MOE_PATH_AUTO, "grouped": MOE_PATH_GROUPED, "stream": MOE_PATH_STREAM}.get(path, path),
-                     act_quant=int(act_quant))
+                     act_quant=int(act_quant), backward=int(bool(backward)))
 
 
 def create_cfg(params: MoeParams) -> tuple[int, ctypes.c_void_p]:
@@ -209,6 +218,37 @@ class MoELayer:
                                         _ptr(expert_counts), _stream_handle(stream))
         self._check(st, "moe_layer_forward")
         return out
+
+    def backward(self, x, gate_w, sel_bias, experts, shared, d_out, stream=None):
+        """Gradients of sum(d_out * forward(...)) (moe_layer_backward); the cfg
+        needs backward=True. Returns dict(dx [T, D], d_gate_w [E, D],
+        d_gate_up [E, 2H, D], d_down [E, D, H], d_shared_gate_up [2Hs, D],
+        d_shared_down [D, Hs]) of fp32 tensors (shared ones None without a
+        shared expert)."""
+        p = self.params
+        self._check_x(x)
+        T = x.shape[0]
+        dev = x.device
+        if d_out.dtype != torch.float32 or not d_out.is_contiguous() or tuple(d_out.shape) != (T, p.dim):
+            raise ValueError("d_out must be a contiguous float32 tensor [T, D]")
+        f32 = dict(dtype=torch.float32, device=dev)
+        g = dict(dx=torch.empty((T, p.dim), **f32), d_gate_w=torch.empty((p.n_routed, p.dim), **f32),
+                 d_gate_up=torch.empty((p.n_routed, 2 * p.hidden, p.dim), **f32),
+                 d_down=torch.empty((p.n_routed, p.dim, p.hidden), **f32),
+                 d_shared_gate_up=None, d_shared_down=None)
+        dg = MoeWeightGrads(g["d_gate_up"].data_ptr(), g["d_down"].data_ptr())
+        dsg = None
+        if p.shared_hidden > 0:
+            g["d_shared_gate_up"] = torch.empty((2 * p.shared_hidden, p.dim), **f32)
+            g["d_shared_down"] = torch.empty((p.dim, p.shared_hidden), **f32)
+            dsg = MoeWeightGrads(g["d_shared_gate_up"].data_ptr(), g["d_shared_down"].data_ptr())
+        ew, sw = _weights(experts), _weights(shared)
+        st = self.lib.moe_layer_backward(self.handle, _ptr(x), T, _ptr(gate_w), _ptr(sel_bias), ctypes.byref(ew),
+                                         None if sw is None else ctypes.byref(sw), _ptr(d_out), _ptr(g["dx"]),
+                                         _ptr(g["d_gate_w"]), ctypes.byref(dg),
+                                         None if dsg is None else ctypes.byref(dsg), _stream_handle(stream))
+        self._check(st, "moe_layer_backward")
+        return g
 
     def router(self, x, gate_w, sel_bias, stream=None):
         """(topk_idx [T, K] int32, topk_gate [T, K] fp32, expert_counts [E] int32)."""

@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
-SOURCES = ["moe_api.hip", "router.hip", "dispatch.hip", "grouped_gemm.hip", "grouped_gemm_f8.hip", "stream_gemm.hip",
+SOURCES = ["moe_api.hip", "router.hip", "dispatch.hip", "grouped_gemm.hip", "grouped_gemm_f8.hip", "grouped_gemm_bwd.hip",
+           "stream_gemm.hip",
            "simple_f32.hip", "balance.hip", "quant_e4m3.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -76,7 +76,6 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(DispatchArgs a) {
   const int o2 = block_exclusive_scan(it2, &tot2);
   if (p < a.E) {
     a.offsets[p] = off;
-    a.cursor[p] = off;
     if (a.counts_out) a.counts_out[p] = cnt;
   }
   if (p == a.E) a.offsets[p] = tot0;
@@ -90,38 +89,81 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(DispatchArgs a) {
   }
 }
 
-// Each block takes a chunk of kPermChunk (token, slot) entries: an LDS
-// histogram of the chunk, one global atomic per expert to reserve the chunk's
-// rows, then LDS atomics hand out rows inside each reservation. Row order
-// within an expert is arbitrary (no result depends on it: every row is
-// computed on its own and the combine adds a token's rows in slot order).
-constexpr int kPermChunk = 2048;
+// The permutation is stable: the row of entry (t, k) with expert e is
+// offsets[e] + #{(t', k') before (t, k) with expert e}, i.e. an expert's rows
+// hold its tokens in ascending order (the scope's definition of the step), so
+// every sum over an expert's rows (the weight gradients of the backward pass)
+// runs in one order on every call. Entries are split into chunks of
+// kPermChunk, one wave each: (A) each chunk's expert histogram, (B) per
+// expert, the first row of each chunk (offsets plus the earlier chunks'
+// counts), (C) each wave walks its chunk in order, 64 entries at a time,
+// ranking equal experts among the lanes with ballots.
+constexpr int kPermChunk = kDispatchChunk;
+
+__global__ __launch_bounds__(256) void dispatch_chunk_count_kernel(DispatchArgs a) {
+  __shared__ int32_t cnt[4][kMaxExperts];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = a.T * a.K;
+  const int nchunks = (n + kPermChunk - 1) / kPermChunk;
+  const int chunk = blockIdx.x * 4 + w;
+  for (int e = lane; e < a.E; e += 64) cnt[w][e] = 0;
+  __syncthreads();
+  if (chunk < nchunks) {
+    const int i1 = min(n, (chunk + 1) * kPermChunk);
+    for (int i = chunk * kPermChunk + lane; i < i1; i += 64) {
+      const int e = a.idx[i];
+      if (e >= 0 && e < a.E) atomicAdd(&cnt[w][e], 1);  // out-of-range entries are skipped, as in the histogram
+    }
+  }
+  __syncthreads();
+  if (chunk < nchunks)
+    for (int e = lane; e < a.E; e += 64) a.chunk_base[(size_t)chunk * a.E + e] = cnt[w][e];
+}
+
+__global__ __launch_bounds__(256) void dispatch_chunk_scan_kernel(DispatchArgs a) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= a.E) return;
+  const int nchunks = (a.T * a.K + kPermChunk - 1) / kPermChunk;
+  int acc = a.offsets[e];
+  for (int c = 0; c < nchunks; ++c) {
+    const int v = a.chunk_base[(size_t)c * a.E + e];
+    a.chunk_base[(size_t)c * a.E + e] = acc;
+    acc += v;
+  }
+}
 
 __global__ __launch_bounds__(256) void dispatch_permute_kernel(DispatchArgs a) {
-  __shared__ int32_t cnt[kMaxExperts];
-  __shared__ int32_t base[kMaxExperts];
+  __shared__ int32_t run[4][kMaxExperts];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = a.T * a.K;
-  const int i0 = blockIdx.x * kPermChunk, i1 = min(n, i0 + kPermChunk);
-  for (int e = threadIdx.x; e < a.E; e += 256) cnt[e] = 0;
+  const int nchunks = (n + kPermChunk - 1) / kPermChunk;
+  const int chunk = blockIdx.x * 4 + w;
+  if (chunk < nchunks)
+    for (int e = lane; e < a.E; e += 64) run[w][e] = a.chunk_base[(size_t)chunk * a.E + e];
   __syncthreads();
-  for (int i = i0 + threadIdx.x; i < i1; i += 256) {
-    const int e = a.idx[i];
-    if (e >= 0 && e < a.E) atomicAdd(&cnt[e], 1);  // out-of-range entries are skipped, as in the histogram
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < a.E; e += 256) {
-    const int c = cnt[e];
-    base[e] = c ? atomicAdd(&a.cursor[e], c) : 0;
-    cnt[e] = 0;
-  }
-  __syncthreads();
-  for (int i = i0 + threadIdx.x; i < i1; i += 256) {
-    const int e = a.idx[i];
-    if (e < 0 || e >= a.E) continue;
-    const int r = base[e] + atomicAdd(&cnt[e], 1);
-    a.row_token[r] = i / a.K;
-    if (a.row_gate) a.row_gate[r] = a.gate[i];
-    a.slot_row[i] = r;
+  if (chunk >= nchunks) return;  // no barrier below: waves of a block work alone from here
+  const int i1 = min(n, (chunk + 1) * kPermChunk);
+  for (int g0 = chunk * kPermChunk; g0 < i1; g0 += 64) {
+    const int i = g0 + lane;
+    int e = i < i1 ? a.idx[i] : -1;
+    if (e >= a.E) e = -1;
+    // lanes holding the same expert, one distinct expert per round
+    uint64_t todo = __ballot(e >= 0), mine = 0;
+    while (todo) {
+      const int v = __shfl(e, __ffsll((unsigned long long)todo) - 1);
+      const uint64_t m = __ballot(e == v);
+      if (e == v) mine = m;
+      todo &= ~m;
+    }
+    const int base = e >= 0 ? run[w][e] : 0;
+    if (e >= 0) {
+      const int r = base + __popcll(mine & ((1ull << lane) - 1ull));
+      a.row_token[r] = i / a.K;
+      if (a.row_gate) a.row_gate[r] = a.gate[i];
+      a.slot_row[i] = r;
+      // the highest lane of the expert's group moves the expert's next row on
+      if ((mine >> lane) == 1ull) run[w][e] = base + __popcll(mine);
+    }
   }
 }
 
@@ -131,7 +173,11 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   if (err != hipSuccess) return err;
   const int n = a.T * a.K;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(dispatch_permute_kernel, dim3((n + kPermChunk - 1) / kPermChunk), dim3(256), 0, s, a);
+  const int nchunks = (n + kPermChunk - 1) / kPermChunk;
+  const int blocks = (nchunks + 3) / 4;
+  hipLaunchKernelGGL(dispatch_chunk_count_kernel, dim3(blocks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(dispatch_chunk_scan_kernel, dim3((a.E + 255) / 256), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(dispatch_permute_kernel, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -59,6 +59,7 @@ struct Tile {
   const float* ws;         // e4m3: the problem's 128x128 block scales, [rows/128][K/128]
   int kbn;                 // e4m3: K/128
   uint16_t* c;             // output rows of this problem (row 0 = row_base)
+  uint16_t* c2;            // recompute mode: g * h rows of this problem
   const float* gate;       // GEMM2 routed: gates at row_base; null = 1
   uint32_t a_bytes;        // extent of a_rows (buffer range)
   uint32_t w_bytes;        // extent of w
@@ -91,7 +92,7 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
   for (int j = 0; j < kLd / 2; ++j) {
     const int m = r0 + 64 * j;
     const int mm = t.m0 + (m < t.vrows ? m : 0);
-    const int row = (kMode == 0 && t.tok != nullptr) ? t.tok[mm] : mm;
+    const int row = (kMode != 1 && t.tok != nullptr) ? t.tok[mm] : mm;
     voff[j] = ((uint32_t)row * (uint32_t)t.lda + c8 * 8) * 2u;
   }
   // Weight (B) rows. bf16: rows r0 + 64*j (rows past D read row 0 instead).
@@ -101,7 +102,7 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
 #pragma unroll
   for (int j = 0; j < kLd / 2; ++j) {
     const int b = kW8 ? (tid >> 1) : r0 + 64 * j;
-    int wrow = (kMode == 0) ? (b < 128 ? t.nt * 128 + b : t.Hp + t.nt * 128 + b - 128) : t.nt * BN + b;
+    int wrow = (kMode != 1) ? (b < 128 ? t.nt * 128 + b : t.Hp + t.nt * 128 + b - 128) : t.nt * BN + b;
     if (kMode == 1 && wrow >= t.D) wrow = 0;
     if (kW8) {
       voff[kLd / 2 + j] = (uint32_t)wrow * (uint32_t)t.K + 32u * (tid & 1) + 16u * j;
@@ -128,7 +129,7 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
   // and the matching W_up block)
   int bcol[kNC];
 #pragma unroll
-  for (int c = 0; c < kNC; ++c) bcol[c] = (kMode == 0) ? 128 * c + 32 * wn : 64 * wn + 32 * c;
+  for (int c = 0; c < kNC; ++c) bcol[c] = (kMode != 1) ? 128 * c + 32 * wn : 64 * wn + 32 * c;
   const int lr = lane & 31, lk = (lane >> 5) * 8;
 
   // down GEMM: the tile's gates into LDS for the epilogue
@@ -288,6 +289,24 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
         t.c[(size_t)(t.m0 + m) * t.ldc + t.nt * 128 + 32 * wn + lr] = f32_to_bf16(h);
       }
     }
+  } else if (kMode == 2) {
+    // recompute for the backward pass: the pre-activations a = x W_gate^T and
+    // u = x W_up^T (one bf16 row of 2*Hp: a then u) and g * SiLU(a) * u
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = 32 * (wm + 2 * i) + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (m >= t.vrows) continue;
+        const float av = acc[i][0][e], uv = acc[i][1][e];
+        const int col = t.nt * 128 + 32 * wn + lr;
+        uint16_t* crow = t.c + (size_t)(t.m0 + m) * t.ldc;
+        crow[col] = f32_to_bf16(av);
+        crow[t.Hp + col] = f32_to_bf16(uv);
+        const float g = t.gate != nullptr ? t.gate[t.m0 + m] : 1.0f;
+        t.c2[(size_t)(t.m0 + m) * t.Hp + col] = f32_to_bf16(g * silu_fast(av) * uv);
+      }
+    }
   } else {
     // y tile (256 x 256): staged through LDS, then written as full 16-byte
     // pieces of each row (the tile's rows are 512 contiguous bytes of y).
@@ -327,7 +346,8 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
   }
 }
 
-// kMode 0: gate/up + SwiGLU, 1: down + gate scale; kW8: e4m3 weights with
+// kMode 0: gate/up + SwiGLU, 1: down + gate scale, 2: gate/up pre-activations
+// and g * h for the backward pass; kW8: e4m3 weights with
 // 128x128 block scales, widened to bf16 (times the scale) as they are staged
 template <int kMode, bool kW8>
 __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a) {
@@ -365,9 +385,9 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
   const int rpt = ((rows + nmt - 1) / nmt + 31) & ~31;
   t.m0 = (local % nmt) * rpt;  // column-tile major: the row tiles of one weight slice run together
   t.nt = local / nmt;
-  t.K = (kMode == 0) ? a.D : t.Hp;
+  t.K = (kMode != 1) ? a.D : t.Hp;
   t.vrows = min(rows - t.m0, rpt);
-  if (kMode == 0) {
+  if (kMode != 1) {
     t.a_rows = static_cast<const uint16_t*>(a.a);
     t.lda = a.D;
     t.tok = routed ? a.row_token + row_base : nullptr;
@@ -375,9 +395,17 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
                  : static_cast<const char*>(a.w_shared);
     t.kbn = a.D / 128;
     t.ws = kW8 ? (routed ? a.w_scale + (size_t)p * (2 * t.Hp / 128) * t.kbn : a.w_shared_scale) : nullptr;
-    t.c = routed ? static_cast<uint16_t*>(a.c) + (size_t)row_base * a.H : static_cast<uint16_t*>(a.c_shared);
-    t.ldc = t.Hp;
-    t.gate = nullptr;
+    if (kMode == 2) {
+      t.c = routed ? static_cast<uint16_t*>(a.c) + (size_t)row_base * 2 * a.H : static_cast<uint16_t*>(a.c_shared);
+      t.c2 = routed ? static_cast<uint16_t*>(a.c2) + (size_t)row_base * a.H : static_cast<uint16_t*>(a.c2_shared);
+      t.ldc = 2 * t.Hp;
+      t.gate = routed ? a.row_gate + row_base : nullptr;
+    } else {
+      t.c = routed ? static_cast<uint16_t*>(a.c) + (size_t)row_base * a.H : static_cast<uint16_t*>(a.c_shared);
+      t.c2 = nullptr;
+      t.ldc = t.Hp;
+      t.gate = nullptr;
+    }
     t.a_bytes = (uint32_t)((size_t)a.x_rows * a.D * 2);
     t.w_bytes = (uint32_t)((size_t)2 * t.Hp * a.D * kWB);
   } else {
@@ -390,6 +418,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
     t.kbn = t.Hp / 128;
     t.ws = kW8 ? (routed ? a.w_scale + (size_t)p * (a.D / 128) * t.kbn : a.w_shared_scale) : nullptr;
     t.c = routed ? static_cast<uint16_t*>(a.c) + (size_t)row_base * a.D : static_cast<uint16_t*>(a.c_shared);
+    t.c2 = nullptr;
     t.ldc = a.D;
     t.gate = routed ? a.row_gate + row_base : nullptr;
     t.a_bytes = (uint32_t)((size_t)rows * t.Hp * 2);
@@ -423,6 +452,13 @@ hipError_t launch_grouped_gateup(const ExpertGemmArgs& a, int fp8, hipStream_t s
     hipLaunchKernelGGL((grouped_gemm_bf16_kernel<0, true>), dim3(blocks), dim3(512), 0, s, a);
   else
     hipLaunchKernelGGL((grouped_gemm_bf16_kernel<0, false>), dim3(blocks), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_recompute(const ExpertGemmArgs& a, hipStream_t s) {
+  const int blocks = grouped_blocks(a.max_items, kRun);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<2, false>), dim3(blocks), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

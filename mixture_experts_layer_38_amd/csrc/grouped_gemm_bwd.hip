@@ -1,0 +1,570 @@
+// Backward pass of the layer (the back-propagation step of the training data
+// flow in the "Transformer block" article): gradients of L = <d_out, out> with
+// respect to x, gate_w and the routed and shared expert weights, with the
+// expert choice held fixed and the gradient reaching the router through the
+// gate values.
+//
+// Every product is one grouped bf16 MFMA GEMM C[m][n] = sum_k A[m][k] B[n][k]
+// (fp32 accumulation) over 128 x 128 tiles, K step 64, 4 waves of 64 x 64
+// (2 x 2 blocks of v_mfma_f32_32x32x16_bf16), operands staged through two LDS
+// buffers in [row][k] layout. The right operand is always stored k-major
+// (B[n][k] = stored[k][n]: the weights read "the other way" than the
+// forward, or activations summed over rows for the weight gradients) and is
+// transposed while it is staged: a thread loads 4 k-rows x 8 consecutive n
+// (four 16-byte loads) and writes 8 rows of 4 k (v_perm_b32 pairs, 8-byte LDS
+// stores). The left operand is either natural (k contiguous, 16-byte chunks)
+// or k-major and transposed the same way. k-major operands past the valid
+// K (an expert's ragged row count) are zero-filled, so the weight gradients
+// of experts with few rows come out exact.
+//
+//   kDgradH   dH   = dOut[tok] W_down          (rows x H; epilogue: SwiGLU
+//                                                backward -> [dA | dU], and
+//                                                the partial sums of dL/dg)
+//   kDgradX   dXr  = [dA | dU] [W_gate; W_up]  (rows x D, bf16)
+//   kWgradD   dW_down = dOut[tok]^T (g h)      (D x H per expert, fp32)
+//   kWgradGU  dW_gu   = [dA | dU]^T x[tok]     (2H x D per expert, fp32)
+//   kRouterW  d gate_w = dlogit^T x            (E x D, split over T, fp32 planes)
+//   kRouterX  dx_r     = dlogit gate_w         (T x D, fp32)
+#include <type_traits>
+
+#include "moe_internal.hpp"
+
+namespace moe {
+
+namespace {
+constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;  // LDS row: 72 bf16 (144 bytes)
+constexpr int kRowsL = BM + BN;
+constexpr int kThreads = 256;
+
+enum : int { kDgradH = 0, kDgradX = 1, kWgradD = 2, kWgradGU = 3, kRouterW = 4, kRouterX = 5 };
+
+struct BwdTile {
+  const uint16_t* a;   // A storage (natural: rows m; k-major: rows k)
+  const int32_t* amap; // row map of A's storage rows (null = identity)
+  uint32_t a_bytes;
+  int lda;
+  const uint16_t* b;   // B storage, k-major (rows k)
+  const int32_t* bmap;
+  uint32_t b_bytes;
+  int ldb;
+  int M, N, K;         // valid extents
+  int m0, n0, k0, k1;  // tile origin; K range [k0, k1)
+  void* c;             // output (row m0 / col n0 not applied)
+  int ldc;
+  // kDgradH epilogue
+  const uint16_t* au;  // [a | u] rows
+  const float* gate;   // row gates (null = 1)
+  float* part;         // partial dL/dg sums, [rows][npart]
+  int npart, Hp;
+};
+
+__device__ __forceinline__ uint4 bload(const __amdgpu_buffer_rsrc_t& r, uint32_t voff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+__device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+}  // namespace
+
+template <int kMode, bool kAT>
+__device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRowsL * LDK], float* s_red) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(t.a), (short)0,
+                                                                      t.a_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(t.b), (short)0,
+                                                                      t.b_bytes, 0x00020000);
+  // natural loader: rows r0 + 32j, 16-byte chunk c8 of the 64-wide K step
+  const int c8 = tid & 7, r0 = tid >> 3;
+  // k-major loader: k rows 4*kg .. +3 of the step, columns 8*mg .. +7 of the tile
+  const int kg = tid >> 4, mg = tid & 15;
+
+  uint32_t aoff[4];
+  if (!kAT) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int m = t.m0 + r0 + 32 * j;
+      m = m < t.M ? m : t.M - 1;
+      const int row = t.amap ? t.amap[m] : m;
+      aoff[j] = ((uint32_t)row * (uint32_t)t.lda + c8 * 8) * 2u;
+    }
+  }
+  // k-major operands: byte offset of column 8*mg (rows added per step)
+  const uint32_t acol = (uint32_t)(t.m0 + 8 * mg) * 2u, bcol = (uint32_t)(t.n0 + 8 * mg) * 2u;
+
+  uint4 sa_[4], sb_[4];
+  auto load_kmajor = [&](const __amdgpu_buffer_rsrc_t& r, const int32_t* map, int ld, uint32_t col, int k0,
+                         uint4 (&v)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int k = k0 + 4 * kg + q;
+      const bool ok = k < t.k1;
+      const int kk = ok ? k : t.k0;
+      const int row = map ? map[kk] : kk;
+      const uint4 x = bload(r, (uint32_t)row * (uint32_t)ld * 2u + col);
+      v[q] = ok ? x : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto load = [&](int k0) __attribute__((always_inline)) {
+    if (kAT) {
+      load_kmajor(ra, t.amap, t.lda, acol, k0, sa_);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sa_[j] = bload(ra, aoff[j] + (uint32_t)k0 * 2u);
+    }
+    load_kmajor(rb, t.bmap, t.ldb, bcol, k0, sb_);
+  };
+  // 4 k-rows x 8 columns -> 8 LDS rows of 4 k (8 bytes each)
+  auto store_kmajor = [&](uint16_t* base, const uint4 (&v)[4]) __attribute__((always_inline)) {
+    const uint32_t w[4][4] = {{v[0].x, v[0].y, v[0].z, v[0].w}, {v[1].x, v[1].y, v[1].z, v[1].w},
+                              {v[2].x, v[2].y, v[2].z, v[2].w}, {v[3].x, v[3].y, v[3].z, v[3].w}};
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      // dword p of each k-row holds columns 2p (low half) and 2p+1 (high half)
+      const uint32_t lo01 = __builtin_amdgcn_perm(w[1][p], w[0][p], 0x05040100u);
+      const uint32_t lo23 = __builtin_amdgcn_perm(w[3][p], w[2][p], 0x05040100u);
+      const uint32_t hi01 = __builtin_amdgcn_perm(w[1][p], w[0][p], 0x07060302u);
+      const uint32_t hi23 = __builtin_amdgcn_perm(w[3][p], w[2][p], 0x07060302u);
+      *reinterpret_cast<uint2*>(&base[(8 * mg + 2 * p) * LDK + 4 * kg]) = make_uint2(lo01, lo23);
+      *reinterpret_cast<uint2*>(&base[(8 * mg + 2 * p + 1) * LDK + 4 * kg]) = make_uint2(hi01, hi23);
+    }
+  };
+  auto store = [&](int buf) __attribute__((always_inline)) {
+    if (kAT) {
+      store_kmajor(&smem[buf][0], sa_);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&smem[buf][(r0 + 32 * j) * LDK + c8 * 8]) = sa_[j];
+    }
+    store_kmajor(&smem[buf][BM * LDK], sb_);
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][c][e] = 0.f;
+
+  const int lr = lane & 31, lk = (lane >> 5) * 8;
+  const int nk = (t.k1 - t.k0 + BK - 1) / BK;
+  if (nk > 0) {  // an expert without rows: no loads, zero gradient
+    load(t.k0);
+    store(0);
+  }
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) load(t.k0 + (kt + 1) * BK);
+    const uint16_t* sA = smem[cur];
+    const uint16_t* sB = smem[cur] + BM * LDK;
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 16) {
+      bf16x8 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(&sA[(64 * wm + 32 * i + lr) * LDK + kk + lk]);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) fb[c] = *reinterpret_cast<const bf16x8*>(&sB[(64 * wn + 32 * c + lr) * LDK + kk + lk]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[c], acc[i][c], 0, 0, 0);
+    }
+    if (more) store(cur ^ 1);
+    __syncthreads();
+  }
+
+  // D layout of the 32x32 MFMA: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
+  // column l%32.
+  if (kMode == kDgradH) {
+    // dH = g * acc; [dA | dU] = dH * u * SiLU'(a) | dH * SiLU(a); the row's
+    // partial dL/dg = sum over this tile's columns of acc * SiLU(a) * u
+    uint16_t* dau = static_cast<uint16_t*>(t.c);
+    float rs[2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int m = t.m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        float sum = 0.f;
+        if (m < t.M) {
+          const float g = t.gate ? t.gate[m] : 1.0f;
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int n = t.n0 + 64 * wn + 32 * c + lr;
+            const float av = bf16f(t.au[(size_t)m * 2 * t.Hp + n]);
+            const float uv = bf16f(t.au[(size_t)m * 2 * t.Hp + t.Hp + n]);
+            const float sg = 1.0f / (1.0f + __expf(-av));
+            const float sl = av * sg;
+            const float dh = g * acc[i][c][e];
+            dau[(size_t)m * t.ldc + n] = f32_to_bf16(dh * uv * sg * (1.0f + av * (1.0f - sg)));
+            dau[(size_t)m * t.ldc + t.Hp + n] = f32_to_bf16(dh * sl);
+            sum += acc[i][c][e] * sl * uv;
+          }
+        }
+        rs[i][e] = sum;
+      }
+    // sum over the 32 lanes of a row group: 16-lane rows by DPP, then the two
+    // rows through LDS with the other column wave, in a fixed order
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float v = rs[i][e];
+        v += __uint_as_float(dpp_u32<0xB1>(__float_as_uint(v)));
+        v += __uint_as_float(dpp_u32<0x4E>(__float_as_uint(v)));
+        v += __uint_as_float(dpp_u32<0x141>(__float_as_uint(v)));
+        v += __uint_as_float(dpp_u32<0x140>(__float_as_uint(v)));
+        rs[i][e] = v;
+      }
+    // s_red[wn][half of 32][row]: lanes 0, 16 (rows of lane group 0), 32, 48
+    if ((lane & 15) == 0) {
+      const int half = (lane >> 4) & 1;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = 64 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          s_red[(wn * 2 + half) * BM + r] = rs[i][e];
+        }
+    }
+    __syncthreads();
+    if (tid < BM && t.m0 + tid < t.M) {
+      const float v = (s_red[tid] + s_red[BM + tid]) + (s_red[2 * BM + tid] + s_red[3 * BM + tid]);
+      t.part[(size_t)(t.m0 + tid) * t.npart + t.n0 / BN] = v;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int n = t.n0 + 64 * wn + 32 * c + lr;
+        if (n >= t.N) continue;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int m = t.m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          if (m >= t.M) continue;
+          if (kMode == kDgradX)
+            static_cast<uint16_t*>(t.c)[(size_t)m * t.ldc + n] = f32_to_bf16(acc[i][c][e]);
+          else
+            static_cast<float*>(t.c)[(size_t)m * t.ldc + n] = acc[i][c][e];
+        }
+      }
+  }
+}
+
+// One launch per product; tiles enumerate (problem, m tile, n tile) as the
+// mode's geometry says.
+template <int kMode>
+__global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2][kRowsL * LDK];
+  __shared__ float s_red[4 * BM];
+  const int tile = blockIdx.x;
+  BwdTile t;
+  t.au = nullptr; t.gate = nullptr; t.part = nullptr; t.npart = 0; t.Hp = 0;
+  t.amap = nullptr; t.bmap = nullptr;
+  if (kMode == kDgradH || kMode == kDgradX) {
+    // grouped over problems with ragged rows: tile prefix per problem
+    if (tile >= a.pre[a.E + 1]) return;
+    const int p = __builtin_amdgcn_readfirstlane(find_problem(a.pre, a.E, tile));
+    const bool routed = p < a.E;
+    const int rows = routed ? a.offsets[p + 1] - a.offsets[p] : a.T;
+    const int rb = routed ? a.offsets[p] : 0;
+    const int Hp = routed ? a.H : a.Hs;
+    const int local = tile - a.pre[p];
+    const int nmt = (rows + BM - 1) / BM;
+    t.m0 = (local % nmt) * BM;
+    t.n0 = (local / nmt) * BN;
+    t.M = rows;
+    t.k0 = 0;
+    if (kMode == kDgradH) {
+      // A = dOut rows (bf16), gathered; B[n = h][k = d] = W_down[d][h]
+      t.a = a.dout;
+      t.amap = routed ? a.row_token + rb : nullptr;
+      t.a_bytes = (uint32_t)((size_t)a.T * a.D * 2);
+      t.lda = a.D;
+      t.b = routed ? a.w_down + (size_t)p * a.D * a.H : a.w_down_shared;
+      t.b_bytes = (uint32_t)((size_t)a.D * Hp * 2);
+      t.ldb = Hp;
+      t.N = Hp;
+      t.K = a.D;
+      t.k1 = a.D;
+      t.c = routed ? static_cast<void*>(a.dau + (size_t)rb * 2 * a.H) : static_cast<void*>(a.dau_shared);
+      t.ldc = 2 * Hp;
+      t.au = routed ? a.au + (size_t)rb * 2 * a.H : a.au_shared;
+      t.gate = routed ? a.row_gate + rb : nullptr;
+      t.part = routed ? a.part + (size_t)rb * (a.H / BN) : a.part_shared;
+      t.npart = Hp / BN;
+      t.Hp = Hp;
+    } else {
+      // A = [dA | dU] rows; B[n = d][k = j] = W_gu[j][d]
+      t.a = routed ? a.dau + (size_t)rb * 2 * a.H : a.dau_shared;
+      t.a_bytes = (uint32_t)((size_t)rows * 2 * Hp * 2);
+      t.lda = 2 * Hp;
+      t.b = routed ? a.w_gu + (size_t)p * 2 * a.H * a.D : a.w_gu_shared;
+      t.b_bytes = (uint32_t)((size_t)2 * Hp * a.D * 2);
+      t.ldb = a.D;
+      t.N = a.D;
+      t.K = 2 * Hp;
+      t.k1 = 2 * Hp;
+      t.c = routed ? static_cast<void*>(a.dxr + (size_t)rb * a.D) : static_cast<void*>(a.dxs);
+      t.ldc = a.D;
+    }
+    bwd_tile<kMode, false>(t, smem, s_red);
+  } else if (kMode == kWgradD || kMode == kWgradGU) {
+    // every problem (experts, then the shared expert) gets its full weight
+    // gradient; experts without rows get zeros
+    const int Mr = kMode == kWgradD ? a.D : 2 * a.H, Nr = kMode == kWgradD ? a.H : a.D;
+    const int Ms = kMode == kWgradD ? a.D : 2 * a.Hs, Ns = kMode == kWgradD ? a.Hs : a.D;
+    const int per_r = (Mr / BM) * (Nr / BN), per_s = (Ms / BM) * (Ns / BN);
+    const int total = a.E * per_r + (a.Hs > 0 ? per_s : 0);
+    if (tile >= total) return;
+    const bool routed = tile < a.E * per_r;
+    const int p = routed ? tile / per_r : a.E;
+    const int local = routed ? tile % per_r : tile - a.E * per_r;
+    const int M = routed ? Mr : Ms, N = routed ? Nr : Ns, Hp = routed ? a.H : a.Hs;
+    const int rows = routed ? a.offsets[p + 1] - a.offsets[p] : a.T;
+    const int rb = routed ? a.offsets[p] : 0;
+    const int nnt = N / BN;
+    t.m0 = (local / nnt) * BM;
+    t.n0 = (local % nnt) * BN;
+    t.M = M;
+    t.N = N;
+    t.K = rows;
+    t.k0 = 0;
+    t.k1 = rows;
+    if (kMode == kWgradD) {
+      // A[m = d][k = r] = dOut[tok(r)][d]; B[n = h][k = r] = (g h)[r][h]
+      t.a = a.dout;
+      t.amap = routed ? a.row_token + rb : nullptr;
+      t.a_bytes = (uint32_t)((size_t)a.T * a.D * 2);
+      t.lda = a.D;
+      t.b = routed ? a.gh + (size_t)rb * a.H : a.gh_shared;
+      t.b_bytes = (uint32_t)((size_t)(rows > 0 ? rows : 1) * Hp * 2);
+      t.ldb = Hp;
+      t.c = routed ? static_cast<void*>(a.dw_down + (size_t)p * a.D * a.H) : static_cast<void*>(a.dw_down_shared);
+      t.ldc = Hp;
+    } else {
+      // A[m = j][k = r] = [dA | dU][r][j]; B[n = d][k = r] = x[tok(r)][d]
+      t.a = routed ? a.dau + (size_t)rb * 2 * a.H : a.dau_shared;
+      t.a_bytes = (uint32_t)((size_t)(rows > 0 ? rows : 1) * 2 * Hp * 2);
+      t.lda = 2 * Hp;
+      t.b = a.x;
+      t.bmap = routed ? a.row_token + rb : nullptr;
+      t.b_bytes = (uint32_t)((size_t)a.T * a.D * 2);
+      t.ldb = a.D;
+      t.c = routed ? static_cast<void*>(a.dw_gu + (size_t)p * 2 * a.H * a.D) : static_cast<void*>(a.dw_gu_shared);
+      t.ldc = a.D;
+    }
+    bwd_tile<kMode, true>(t, smem, s_red);
+  } else if (kMode == kRouterW) {
+    // d gate_w planes: A[m = e][k = t] = dlogit[t][e]; B[n = d][k = t] = x[t][d]; K split over planes
+    const int nmt = (a.Ep + BM - 1) / BM, nnt = a.D / BN;
+    const int per = nmt * nnt;
+    if (tile >= per * a.splits) return;
+    const int z = tile / per, local = tile % per;
+    const int kc = ((a.T + a.splits - 1) / a.splits + BK - 1) / BK * BK;
+    t.m0 = (local / nnt) * BM;
+    t.n0 = (local % nnt) * BN;
+    t.M = a.E;
+    t.N = a.D;
+    t.K = a.T;
+    t.k0 = min(z * kc, a.T);
+    t.k1 = min(t.k0 + kc, a.T);
+    t.a = a.dlogit;
+    t.a_bytes = (uint32_t)((size_t)a.T * a.Ep * 2);
+    t.lda = a.Ep;
+    t.b = a.x;
+    t.b_bytes = (uint32_t)((size_t)a.T * a.D * 2);
+    t.ldb = a.D;
+    t.c = a.gw_planes + (size_t)z * a.E * a.D;
+    t.ldc = a.D;
+    bwd_tile<kMode, true>(t, smem, s_red);
+  } else {
+    // dx_r = dlogit gate_w: A = dlogit rows (K = Ep, zero-padded); B[n = d][k = e] = gate_w[e][d]
+    const int nnt = a.D / BN;
+    if (tile >= ((a.T + BM - 1) / BM) * nnt) return;
+    t.m0 = (tile / nnt) * BM;
+    t.n0 = (tile % nnt) * BN;
+    t.M = a.T;
+    t.N = a.D;
+    t.K = a.Ep;
+    t.k0 = 0;
+    t.k1 = a.Ep;
+    t.a = a.dlogit;
+    t.a_bytes = (uint32_t)((size_t)a.T * a.Ep * 2);
+    t.lda = a.Ep;
+    t.b = a.gw_bf16;
+    t.b_bytes = (uint32_t)((size_t)a.Ep * a.D * 2);
+    t.ldb = a.D;
+    t.c = a.dx_router;
+    t.ldc = a.D;
+    bwd_tile<kMode, false>(t, smem, s_red);
+  }
+}
+
+namespace {
+
+// fp32 -> bf16 (RNE), rows of `cols` values into rows of `ldd` (zero padding)
+__global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ src, int rows, int cols, int srows,
+                                                     uint16_t* __restrict__ dst, int ldd) {
+  const size_t n = (size_t)rows * ldd;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const int r = (int)(i / ldd), c = (int)(i % ldd);
+    dst[i] = (r < srows && c < cols) ? f32_to_bf16(src[(size_t)r * cols + c]) : (uint16_t)0;
+  }
+}
+
+// pre[p] = tiles of problems < p: ceil(rows_p / 128) row tiles x n_p column tiles
+__global__ void tile_prefix_kernel(const int32_t* __restrict__ offsets, int E, int shared_rows, int n_routed,
+                                   int n_shared, int32_t* __restrict__ pre) {
+  if (threadIdx.x != 0) return;
+  int acc = 0;
+  for (int p = 0; p <= E; ++p) {
+    pre[p] = acc;
+    const int rows = p < E ? offsets[p + 1] - offsets[p] : shared_rows;
+    acc += ((rows + BM - 1) / BM) * (p < E ? n_routed : n_shared);
+  }
+  pre[E + 1] = acc;
+}
+
+// router backward, one wave per token: dL/dg from the partial sums, through
+// the renormalisation and rsf to the selected scores, through the score
+// function to dlogit (bf16, row padded with zeros to Ep)
+__global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict__ logits,
+                                                         const int32_t* __restrict__ idx,
+                                                         const int32_t* __restrict__ slot_row,
+                                                         const float* __restrict__ part, int npart, int T, int E,
+                                                         int Ep, int K, int score_fn, int norm, float rsf,
+                                                         uint16_t* __restrict__ dlogit) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  const float* l = logits + (size_t)t * E;
+  // scores (fp32, as the forward)
+  float mx = -3.4e38f;
+  if (score_fn == MOE_SCORE_SOFTMAX) {
+    for (int e = lane; e < E; e += 64) mx = fmaxf(mx, l[e]);
+    mx = wave_max_f32(mx);
+  }
+  float den = 0.f;
+  if (score_fn == MOE_SCORE_SOFTMAX) {
+    for (int e = lane; e < E; e += 64) den += __expf(l[e] - mx);
+    den = wave_sum_f32(den);
+  }
+  auto score = [&](int e) {
+    return score_fn == MOE_SCORE_SOFTMAX ? __expf(l[e] - mx) / den : 1.0f / (1.0f + __expf(-l[e]));
+  };
+  // selected scores and dL/dg (lane k < K holds slot k)
+  float ss = 0.f, dg = 0.f;
+  int ek = -1;
+  if (lane < K) {
+    ek = idx[(size_t)t * K + lane];
+    ss = score(ek);
+    const float* pr = part + (size_t)slot_row[(size_t)t * K + lane] * npart;
+    for (int j = 0; j < npart; ++j) dg += pr[j];
+  }
+  float ds = rsf * dg;
+  if (norm) {
+    const float S = wave_sum_f32(ss);
+    const float sdg = wave_sum_f32(ss * dg);
+    ds = rsf * (dg / S - sdg / (S * S));
+  }
+  // sum_j s_j ds_j over the selected (softmax)
+  const float sds = wave_sum_f32(lane < K ? ss * ds : 0.f);
+  for (int e = lane; e < Ep; e += 64) {
+    float v = 0.f;
+    if (e < E) {
+      // ds at e: from the lane that holds e, if selected
+      float dse = 0.f;
+      for (int k = 0; k < K; ++k) {
+        const int ei = __shfl(ek, k);
+        const float dsk = __shfl(ds, k);
+        if (ei == e) dse = dsk;
+      }
+      const float se = score(e);
+      v = score_fn == MOE_SCORE_SOFTMAX ? se * (dse - sds) : dse * se * (1.0f - se);
+    }
+    dlogit[(size_t)t * Ep + e] = f32_to_bf16(v);
+  }
+}
+
+// dx[t] = [d_out[t]] + dX_shared[t] + sum_k dX_rows[slot(t,k)] + dx_router[t]
+__global__ __launch_bounds__(256) void dx_combine_kernel(const float* __restrict__ dout,
+                                                         const uint16_t* __restrict__ dxr,
+                                                         const uint16_t* __restrict__ dxs,
+                                                         const float* __restrict__ dx_router,
+                                                         const int32_t* __restrict__ slot_row, int T, int D, int K,
+                                                         int add_residual, float* __restrict__ dx) {
+  const int t = blockIdx.x;
+  const int* sr = slot_row + (size_t)t * K;
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float v = add_residual ? dout[(size_t)t * D + d] : 0.f;
+    if (dxs) v += bf16f(dxs[(size_t)t * D + d]);
+    for (int k = 0; k < K; ++k) v += bf16f(dxr[(size_t)sr[k] * D + d]);
+    v += dx_router[(size_t)t * D + d];
+    dx[(size_t)t * D + d] = v;
+  }
+}
+
+// out[i] = sum over planes in order
+__global__ __launch_bounds__(256) void planes_sum_kernel(const float* __restrict__ planes, size_t n, int splits,
+                                                         float* __restrict__ out) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    float v = 0.f;
+    for (int z = 0; z < splits; ++z) v += planes[(size_t)z * n + i];
+    out[i] = v;
+  }
+}
+
+int grid_for(size_t n) { return (int)std::min<size_t>((n + 255) / 256, 8192); }
+
+}  // namespace
+
+hipError_t launch_layer_backward(const BwdArgs& a, hipStream_t s) {
+  hipError_t e;
+  // dOut and gate_w to bf16 (gate_w rows padded with zeros to Ep)
+  hipLaunchKernelGGL(to_bf16_kernel, dim3(grid_for((size_t)a.T * a.D)), dim3(256), 0, s, a.dout_f32, a.T, a.D, a.T,
+                     a.dout, a.D);
+  hipLaunchKernelGGL(to_bf16_kernel, dim3(grid_for((size_t)a.Ep * a.D)), dim3(256), 0, s, a.gate_w, a.Ep, a.D, a.E,
+                     a.gw_bf16, a.D);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // tile prefixes of the two row-grouped products
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, a.offsets, a.E, a.Hs > 0 ? a.T : 0, a.H / BN,
+                     a.Hs / BN, a.pre_h);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, a.offsets, a.E, a.Hs > 0 ? a.T : 0, a.D / BN,
+                     a.D / BN, a.pre_x);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const long mblk = (long)(a.T * a.K + BM - 1) / BM + a.E, mblk_s = a.Hs > 0 ? (a.T + BM - 1) / BM : 0;
+  BwdArgs b = a;
+  b.pre = a.pre_h;
+  const int tiles_h = (int)(mblk * (a.H / BN) + mblk_s * (a.Hs / BN));
+  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kDgradH>, dim3(tiles_h), dim3(kThreads), 0, s, b);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // router backward needs every dL/dg partial
+  hipLaunchKernelGGL(router_bwd_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a.logits, a.idx, a.slot_row, a.part,
+                     a.H / BN, a.T, a.E, a.Ep, a.K, a.score_fn, a.norm, a.rsf, a.dlogit);
+  b.pre = a.pre_x;
+  const int tiles_x = (int)(mblk * (a.D / BN) + mblk_s * (a.D / BN));
+  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kDgradX>, dim3(tiles_x), dim3(kThreads), 0, s, b);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int tiles_wd = a.E * (a.D / BM) * (a.H / BN) + (a.Hs > 0 ? (a.D / BM) * (a.Hs / BN) : 0);
+  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kWgradD>, dim3(tiles_wd), dim3(kThreads), 0, s, a);
+  const int tiles_wgu = a.E * (2 * a.H / BM) * (a.D / BN) + (a.Hs > 0 ? (2 * a.Hs / BM) * (a.D / BN) : 0);
+  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kWgradGU>, dim3(tiles_wgu), dim3(kThreads), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int tiles_rw = ((a.Ep + BM - 1) / BM) * (a.D / BN) * a.splits;
+  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kRouterW>, dim3(tiles_rw), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(planes_sum_kernel, dim3(grid_for((size_t)a.E * a.D)), dim3(256), 0, s, a.gw_planes,
+                     (size_t)a.E * a.D, a.splits, a.d_gate_w);
+  const int tiles_rx = ((a.T + BM - 1) / BM) * (a.D / BN);
+  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kRouterX>, dim3(tiles_rx), dim3(kThreads), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(dx_combine_kernel, dim3(a.T), dim3(256), 0, s, a.dout_f32, a.dxr, a.Hs > 0 ? a.dxs : nullptr,
+                     a.dx_router, a.slot_row, a.T, a.D, a.K, a.add_residual, a.dx);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -21,7 +21,7 @@ struct moe_cfg {
   float* gate;
   int32_t* counts;
   int32_t* offsets;
-  int32_t* cursor;
+  int32_t* chunk_base;
   int32_t* pre1;
   int32_t* pre2;
   int32_t* row_token;
@@ -36,6 +36,21 @@ struct moe_cfg {
   float* xs;
   float* hs_routed;
   float* hs_shared;
+  // backward workspace (g*h uses h_routed / h_shared, the dx rows y_routed / y_shared)
+  int Ep, bwd_splits;
+  uint16_t* dout_bf;
+  uint16_t* gw_bf;
+  uint16_t* au;
+  uint16_t* au_shared;
+  uint16_t* dau;
+  uint16_t* dau_shared;
+  float* part;
+  float* part_shared;
+  uint16_t* dlogit;
+  float* dx_router;
+  float* gw_planes;
+  int32_t* pre_h;
+  int32_t* pre_x;
   int last_hip_error;
   // stage timing
   bool timing;
@@ -62,6 +77,7 @@ moe_status validate(const moe_params* p) {
   if (p->max_tokens < 0) return MOE_ERR_INVALID_ARG;
   if (p->path < MOE_PATH_AUTO || p->path > MOE_PATH_STREAM) return MOE_ERR_INVALID_ARG;
   if (p->act_quant != MOE_ACT_QUANT_NONE && p->act_quant != MOE_ACT_QUANT_E4M3_1X128) return MOE_ERR_INVALID_ARG;
+  if (p->backward != 0 && p->backward != 1) return MOE_ERR_INVALID_ARG;
   if (!(p->routed_scaling_factor == p->routed_scaling_factor)) return MOE_ERR_INVALID_ARG;  // NaN
   // dtype combinations this build runs
   const bool f32 = p->act_dtype == MOE_F32 && p->weight_dtype == MOE_F32;
@@ -70,6 +86,8 @@ moe_status validate(const moe_params* p) {
   if (!(f32 || bf || fp8)) return MOE_ERR_UNSUPPORTED;
   // e4m3 activations: fp8 weights, bf16 x, grouped kernels only
   if (p->act_quant == MOE_ACT_QUANT_E4M3_1X128 && (!fp8 || p->path == MOE_PATH_STREAM)) return MOE_ERR_UNSUPPORTED;
+  // the backward pass: bf16 activations and weights
+  if (p->backward && (!bf || p->act_quant != MOE_ACT_QUANT_NONE)) return MOE_ERR_UNSUPPORTED;
   if (p->dim % 32 != 0) return MOE_ERR_UNSUPPORTED;
   if (!f32 && (p->dim % 128 || p->hidden % 128 || p->shared_hidden % 128)) return MOE_ERR_UNSUPPORTED;
   // the grouped GEMMs address x rows, an expert's h rows and one expert's
@@ -79,6 +97,8 @@ moe_status validate(const moe_params* p) {
                (uint64_t)p->max_tokens * hmax * 2 > 0xFFFFFFFFull ||
                (uint64_t)2 * hmax * p->dim * 2 > 0xFFFFFFFFull))
     return MOE_ERR_UNSUPPORTED;
+  // backward: the shared expert's [dA | dU] rows (T x 2*Hs bf16) are addressed the same way
+  if (p->backward && (uint64_t)p->max_tokens * 2 * hmax * 2 > 0xFFFFFFFFull) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -146,6 +166,17 @@ __global__ void zero_counts_kernel(int32_t* p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
 }
 
+__global__ void zero_f32_kernel(float* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0.f;
+}
+
+hipError_t zero_f32(float* p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)std::min<size_t>((n + 255) / 256, 16384)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
@@ -184,7 +215,7 @@ moe_status moe_cfg_create(const moe_params* p, moe_cfg** out) {
   const size_t lg = (size_t)64 * c->num_cus + Tm;
   const size_t o_logits = take(lg * E * 4), o_idx = take(Tm * K * 4), o_gate = take(Tm * K * 4);
   const size_t o_wsplit = (p->act_dtype == MOE_BF16) ? take(3 * E * D * 2) : 0;
-  const size_t o_counts = take(E * 4), o_offsets = take((E + 1) * 4), o_cursor = take(E * 4);
+  const size_t o_counts = take(E * 4), o_offsets = take((E + 1) * 4), o_chunk = take(((Tm * K + kDispatchChunk - 1) / kDispatchChunk + 1) * E * 4);
   const size_t o_pre1 = take((E + 2) * 4), o_pre2 = take((E + 2) * 4);
   const size_t o_rt = take(Tm * K * 4), o_rg = take(Tm * K * 4), o_sr = take(Tm * K * 4);
   const size_t o_hr = take(Tm * K * H * act), o_hs = take(Tm * Hs * act);
@@ -192,6 +223,18 @@ moe_status moe_cfg_create(const moe_params* p, moe_cfg** out) {
   const bool aq = p->act_quant == MOE_ACT_QUANT_E4M3_1X128;
   const size_t o_xq = aq ? take(Tm * D) : 0, o_xs = aq ? take(Tm * (D / 128) * 4) : 0;
   const size_t o_hsr = aq ? take(Tm * K * (H / 128) * 4) : 0, o_hss = aq ? take(Tm * (Hs / 128) * 4) : 0;
+  const bool bw = p->backward != 0;
+  const size_t Ep = (E + 63) / 64 * 64;
+  // d gate_w: K (tokens) split so that about two tiles per CU run
+  const int rw_tiles = (int)((Ep + 127) / 128) * (int)(D / 128);
+  const int splits = bw ? std::max(1, std::min(32, (2 * c->num_cus + rw_tiles - 1) / std::max(rw_tiles, 1))) : 0;
+  const size_t o_dout = bw ? take(Tm * D * 2) : 0, o_gw = bw ? take(Ep * D * 2) : 0;
+  const size_t o_au = bw ? take(Tm * K * 2 * H * 2) : 0, o_aus = bw ? take(Tm * 2 * Hs * 2) : 0;
+  const size_t o_dau = bw ? take(Tm * K * 2 * H * 2) : 0, o_daus = bw ? take(Tm * 2 * Hs * 2) : 0;
+  const size_t o_part = bw ? take(Tm * K * (H / 128) * 4) : 0, o_parts = bw ? take(Tm * (Hs / 128) * 4) : 0;
+  const size_t o_dlog = bw ? take(Tm * Ep * 2) : 0, o_dxr = bw ? take(Tm * D * 4) : 0;
+  const size_t o_planes = bw ? take((size_t)splits * E * D * 4) : 0;
+  const size_t o_preh = bw ? take((E + 2) * 4) : 0, o_prex = bw ? take((E + 2) * 4) : 0;
   c->ws_bytes = off;
   if (hipMalloc((void**)&c->ws, c->ws_bytes) != hipSuccess) {
     (void)hipGetLastError();
@@ -204,7 +247,7 @@ moe_status moe_cfg_create(const moe_params* p, moe_cfg** out) {
   c->gate = (float*)(c->ws + o_gate);
   c->counts = (int32_t*)(c->ws + o_counts);
   c->offsets = (int32_t*)(c->ws + o_offsets);
-  c->cursor = (int32_t*)(c->ws + o_cursor);
+  c->chunk_base = (int32_t*)(c->ws + o_chunk);
   c->pre1 = (int32_t*)(c->ws + o_pre1);
   c->pre2 = (int32_t*)(c->ws + o_pre2);
   c->row_token = (int32_t*)(c->ws + o_rt);
@@ -214,6 +257,23 @@ moe_status moe_cfg_create(const moe_params* p, moe_cfg** out) {
   c->h_shared = c->ws + o_hs;
   c->y_routed = c->ws + o_yr;
   c->y_shared = c->ws + o_ys;
+  if (bw) {
+    c->Ep = (int)Ep;
+    c->bwd_splits = splits;
+    c->dout_bf = (uint16_t*)(c->ws + o_dout);
+    c->gw_bf = (uint16_t*)(c->ws + o_gw);
+    c->au = (uint16_t*)(c->ws + o_au);
+    c->au_shared = (uint16_t*)(c->ws + o_aus);
+    c->dau = (uint16_t*)(c->ws + o_dau);
+    c->dau_shared = (uint16_t*)(c->ws + o_daus);
+    c->part = (float*)(c->ws + o_part);
+    c->part_shared = (float*)(c->ws + o_parts);
+    c->dlogit = (uint16_t*)(c->ws + o_dlog);
+    c->dx_router = (float*)(c->ws + o_dxr);
+    c->gw_planes = (float*)(c->ws + o_planes);
+    c->pre_h = (int32_t*)(c->ws + o_preh);
+    c->pre_x = (int32_t*)(c->ws + o_prex);
+  }
   if (aq) {
     c->xq = (uint8_t*)(c->ws + o_xq);
     c->xs = (float*)(c->ws + o_xs);
@@ -342,7 +402,7 @@ moe_status moe_dispatch_forward(moe_cfg* c, const int32_t* topk_idx, int T, int3
   if (e != hipSuccess) return hip_fail(c, e);
   DispatchArgs d{};
   d.idx = topk_idx; d.gate = nullptr; d.counts = c->counts; d.counts_out = nullptr;
-  d.offsets = offsets; d.cursor = c->cursor; d.row_token = row_token; d.row_gate = nullptr;
+  d.offsets = offsets; d.chunk_base = c->chunk_base; d.row_token = row_token; d.row_gate = nullptr;
   d.slot_row = slot_row; d.pre1 = c->pre1; d.pre2 = c->pre2;
   d.T = T; d.K = c->p.top_k; d.E = c->p.n_routed;
   fill_dispatch_geometry(c->p, choose_path(c->p, T), T, &d);
@@ -394,7 +454,7 @@ moe_status moe_layer_forward(moe_cfg* c, const void* x, int T, const float* gate
   // 2. dispatch
   DispatchArgs d{};
   d.idx = c->idx; d.gate = c->gate; d.counts = c->counts; d.counts_out = expert_counts;
-  d.offsets = c->offsets; d.cursor = c->cursor; d.row_token = c->row_token; d.row_gate = c->row_gate;
+  d.offsets = c->offsets; d.chunk_base = c->chunk_base; d.row_token = c->row_token; d.row_gate = c->row_gate;
   d.slot_row = c->slot_row; d.pre1 = c->pre1; d.pre2 = c->pre2;
   d.T = T; d.K = p.top_k; d.E = p.n_routed;
   fill_dispatch_geometry(p, path, T, &d);
@@ -461,6 +521,92 @@ moe_status moe_layer_forward(moe_cfg* c, const void* x, int T, const float* gate
   cb.out_bf16 = p.out_dtype == MOE_BF16; cb.add_residual = p.add_residual;
   if ((e = launch_combine(cb, s)) != hipSuccess) return hip_fail(c, e);
   mark(c, 5, s);
+  return MOE_OK;
+}
+
+moe_status moe_layer_backward(moe_cfg* c, const void* x, int T, const float* gate_w, const float* sel_bias,
+                              const moe_weights* expert_w, const moe_weights* shared_w, const float* d_out,
+                              float* dx, float* d_gate_w, const moe_weight_grads* d_expert_w,
+                              const moe_weight_grads* d_shared_w, void* stream) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  const moe_params& p = c->p;
+  if (!p.backward) return MOE_ERR_UNSUPPORTED;
+  if (T < 0 || T > p.max_tokens) return MOE_ERR_INVALID_ARG;
+  if (!on_cfg_device(c)) return MOE_ERR_INVALID_ARG;
+  const bool has_shared = p.shared_hidden > 0;
+  if (!gate_w || !d_gate_w || !expert_w || !expert_w->gate_up || !expert_w->down || !d_expert_w ||
+      !d_expert_w->gate_up || !d_expert_w->down)
+    return MOE_ERR_INVALID_ARG;
+  if (has_shared && (!shared_w || !shared_w->gate_up || !shared_w->down || !d_shared_w || !d_shared_w->gate_up ||
+                     !d_shared_w->down))
+    return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !d_out || !dx)) return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const size_t E = p.n_routed, D = p.dim, H = p.hidden, Hs = p.shared_hidden;
+  hipError_t e;
+  if (T == 0) {
+    if ((e = zero_f32(d_gate_w, E * D, s)) != hipSuccess) return hip_fail(c, e);
+    if ((e = zero_f32(d_expert_w->gate_up, E * 2 * H * D, s)) != hipSuccess) return hip_fail(c, e);
+    if ((e = zero_f32(d_expert_w->down, E * D * H, s)) != hipSuccess) return hip_fail(c, e);
+    if (has_shared) {
+      if ((e = zero_f32(d_shared_w->gate_up, 2 * Hs * D, s)) != hipSuccess) return hip_fail(c, e);
+      if ((e = zero_f32(d_shared_w->down, D * Hs, s)) != hipSuccess) return hip_fail(c, e);
+    }
+    return MOE_OK;
+  }
+
+  // routing and dispatch exactly as the forward (grouped geometry for the recompute)
+  RouterArgs r{};
+  r.x = x; r.gate_w = gate_w; r.bias = sel_bias; r.logits = c->logits;
+  r.idx = c->idx; r.gate = c->gate; r.counts = c->counts;
+  r.T = T; r.D = p.dim; r.E = p.n_routed; r.G = p.n_group; r.kg = p.topk_group; r.K = p.top_k;
+  r.act_bf16 = 1; r.score_fn = p.score_fn; r.norm = p.norm_topk;
+  r.rsf = p.routed_scaling_factor;
+  r.num_cus = c->num_cus;
+  r.w_split = c->w_split;
+  if ((e = launch_router(r, s)) != hipSuccess) return hip_fail(c, e);
+  DispatchArgs d{};
+  d.idx = c->idx; d.gate = c->gate; d.counts = c->counts; d.counts_out = nullptr;
+  d.offsets = c->offsets; d.chunk_base = c->chunk_base; d.row_token = c->row_token; d.row_gate = c->row_gate;
+  d.slot_row = c->slot_row; d.pre1 = c->pre1; d.pre2 = c->pre2;
+  d.T = T; d.K = p.top_k; d.E = p.n_routed;
+  fill_dispatch_geometry(p, Path::kGrouped, T, &d);
+  if ((e = launch_dispatch(d, s)) != hipSuccess) return hip_fail(c, e);
+
+  // gate/up recompute: [a | u] and g * h
+  const int TK = T * p.top_k;
+  ExpertGemmArgs g{};
+  g.offsets = c->offsets; g.row_token = c->row_token; g.row_gate = c->row_gate; g.pre = c->pre1;
+  g.E = p.n_routed; g.T = has_shared ? T : 0; g.D = p.dim; g.H = p.hidden; g.Hs = p.shared_hidden;
+  g.x_rows = T;
+  g.a = x; g.w = expert_w->gate_up; g.w_shared = has_shared ? shared_w->gate_up : nullptr;
+  g.c = c->au; g.c_shared = c->au_shared; g.c2 = c->h_routed; g.c2_shared = c->h_shared;
+  const long mblk = (long)(TK + d.bm - 1) / d.bm + p.n_routed;
+  const long mblk_s = has_shared ? (T + d.bm - 1) / d.bm : 0;
+  g.max_items = (int)(mblk * d.n1_routed + mblk_s * d.n1_shared);
+  if ((e = launch_grouped_recompute(g, s)) != hipSuccess) return hip_fail(c, e);
+
+  BwdArgs b{};
+  b.E = p.n_routed; b.T = T; b.D = p.dim; b.H = p.hidden; b.Hs = p.shared_hidden; b.K = p.top_k;
+  b.Ep = c->Ep; b.splits = c->bwd_splits;
+  b.score_fn = p.score_fn; b.norm = p.norm_topk; b.rsf = p.routed_scaling_factor; b.add_residual = p.add_residual;
+  b.offsets = c->offsets; b.row_token = c->row_token; b.row_gate = c->row_gate; b.slot_row = c->slot_row;
+  b.idx = c->idx; b.logits = c->logits; b.pre_h = c->pre_h; b.pre_x = c->pre_x;
+  b.x = static_cast<const uint16_t*>(x); b.dout_f32 = d_out; b.gate_w = gate_w;
+  b.w_gu = static_cast<const uint16_t*>(expert_w->gate_up);
+  b.w_down = static_cast<const uint16_t*>(expert_w->down);
+  b.w_gu_shared = has_shared ? static_cast<const uint16_t*>(shared_w->gate_up) : nullptr;
+  b.w_down_shared = has_shared ? static_cast<const uint16_t*>(shared_w->down) : nullptr;
+  b.dout = c->dout_bf; b.gw_bf16 = c->gw_bf;
+  b.au = c->au; b.au_shared = c->au_shared;
+  b.gh = static_cast<const uint16_t*>(c->h_routed); b.gh_shared = static_cast<const uint16_t*>(c->h_shared);
+  b.dau = c->dau; b.dau_shared = c->dau_shared; b.part = c->part; b.part_shared = c->part_shared;
+  b.dxr = static_cast<uint16_t*>(c->y_routed); b.dxs = static_cast<uint16_t*>(c->y_shared);
+  b.dlogit = c->dlogit; b.dx_router = c->dx_router; b.gw_planes = c->gw_planes;
+  b.dx = dx; b.d_gate_w = d_gate_w; b.dw_gu = d_expert_w->gate_up; b.dw_down = d_expert_w->down;
+  b.dw_gu_shared = has_shared ? d_shared_w->gate_up : nullptr;
+  b.dw_down_shared = has_shared ? d_shared_w->down : nullptr;
+  if ((e = launch_layer_backward(b, s)) != hipSuccess) return hip_fail(c, e);
   return MOE_OK;
 }
 

@@ -30,6 +30,7 @@ constexpr int kGB_BK = 64;    // K step
 constexpr int kF8_BM = 128;   // rows (tokens) per tile
 constexpr int kF8_BK = 128;   // K step = one scale block (elements = bytes)
 constexpr int kActBlock = 128;  // activation quantisation block (1 x 128)
+constexpr int kDispatchChunk = 512;  // (token, slot) entries per wave in the stable permutation
 // Weight-streaming path (small token counts): token rows and columns per workgroup item.
 constexpr int kST_BM = 16;
 constexpr int kST_N1 = 32;    // hidden columns per gate/up item (32 gate + 32 up rows)
@@ -179,7 +180,7 @@ struct DispatchArgs {
   int32_t* counts;        // [E] (input: histogram)
   int32_t* counts_out;    // [E] user copy or null
   int32_t* offsets;       // [E+1]
-  int32_t* cursor;        // [E]
+  int32_t* chunk_base;    // [ceil(T*K/512)][E] first row of each chunk's entries of each expert
   int32_t* row_token;     // [T*K]
   float* row_gate;        // [T*K] or null
   int32_t* slot_row;      // [T*K]
@@ -217,10 +218,16 @@ struct ExpertGemmArgs {
   const float* a_shared_scale;  // GEMM2: h shared scales [T][Hs/128]
   float* c_scale;               // GEMM1: h routed scales
   float* c_shared_scale;        // GEMM1: h shared scales
+  // backward recompute (gate/up mode 2): c, c_shared receive [a | u] rows,
+  // c2, c2_shared receive g * h rows
+  void* c2;
+  void* c2_shared;
 };
 // grouped (prefill) GEMMs; fp8: e4m3 weights with 128x128 block scales
 hipError_t launch_grouped_gateup(const ExpertGemmArgs& a, int fp8, hipStream_t s);
 hipError_t launch_grouped_down(const ExpertGemmArgs& a, int fp8, hipStream_t s);
+// gate/up GEMM that writes the pre-activations [a | u] and g * h (bf16) for the backward pass
+hipError_t launch_grouped_recompute(const ExpertGemmArgs& a, hipStream_t s);
 // grouped GEMMs on e4m3 activations (1x128 block scales) and e4m3 weights
 // (128x128 block scales), fp8 MFMA; the gate/up GEMM writes h as e4m3 + scales
 hipError_t launch_grouped_gateup_f8(const ExpertGemmArgs& a, hipStream_t s);
@@ -243,6 +250,58 @@ struct CombineArgs {
   int add_residual;
 };
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
+
+// backward pass (after the router, the dispatch and the gate/up recompute)
+struct BwdArgs {
+  int E, T, D, H, Hs, K;
+  int Ep;          // E rounded up to a multiple of 64 (dlogit rows, gate_w rows)
+  int splits;      // K splits of the d gate_w product
+  int score_fn, norm;
+  float rsf;
+  int add_residual;
+  // routing and dispatch of the forward
+  const int32_t* offsets;   // [E+1]
+  const int32_t* row_token; // [T*K]
+  const float* row_gate;    // [T*K]
+  const int32_t* slot_row;  // [T*K]
+  const int32_t* idx;       // [T*K]
+  const float* logits;      // [T][E]
+  const int32_t* pre;       // set per launch
+  int32_t* pre_h;           // [E+2] tile prefix of the dH product
+  int32_t* pre_x;           // [E+2] tile prefix of the dX product
+  // inputs
+  const uint16_t* x;        // [T][D] bf16
+  const float* dout_f32;    // [T][D]
+  const float* gate_w;      // [E][D] fp32
+  const uint16_t* w_gu;     // [E][2H][D]
+  const uint16_t* w_down;   // [E][D][H]
+  const uint16_t* w_gu_shared;
+  const uint16_t* w_down_shared;
+  // workspace
+  uint16_t* dout;           // [T][D] bf16 copy of d_out
+  uint16_t* gw_bf16;        // [Ep][D]
+  const uint16_t* au;       // [T*K][2H] recomputed [a | u]
+  const uint16_t* au_shared;
+  const uint16_t* gh;       // [T*K][H] g * h
+  const uint16_t* gh_shared;
+  uint16_t* dau;            // [T*K][2H] [dA | dU]
+  uint16_t* dau_shared;
+  float* part;              // [T*K][H/128] partial dL/dg
+  float* part_shared;       // [T][Hs/128]
+  uint16_t* dxr;            // [T*K][D]
+  uint16_t* dxs;            // [T][D]
+  uint16_t* dlogit;         // [T][Ep]
+  float* dx_router;         // [T][D]
+  float* gw_planes;         // [splits][E][D]
+  // outputs (fp32)
+  float* dx;                // [T][D]
+  float* d_gate_w;          // [E][D]
+  float* dw_gu;             // [E][2H][D]
+  float* dw_down;           // [E][D][H]
+  float* dw_gu_shared;      // [2Hs][D]
+  float* dw_down_shared;    // [D][Hs]
+};
+hipError_t launch_layer_backward(const BwdArgs& a, hipStream_t s);
 
 // one workgroup: bias update (bias != null) and/or load statistics (stats != null)
 hipError_t launch_balance(const int32_t* counts, int E, float gamma, float* bias, float* stats, hipStream_t s);

@@ -60,10 +60,19 @@ def test_invalid_layers_rejected(kw):
     dict(act_quant=True),                    # e4m3 activations need e4m3 weights
     dict(act_quant=True, act="f32", weight="fp8"),
     dict(act_quant=True, weight="fp8", path="stream"),  # e4m3 activations run on the grouped kernels only
+    dict(backward=True, weight="fp8"),       # the backward pass takes bf16 weights
+    dict(backward=True, act="f32", weight="f32"),
 ])
 def test_unsupported_layers_rejected(kw):
     st, h = M.create_cfg(_params(**kw))
     assert st == M.MOE_ERR_UNSUPPORTED and not h.value
+
+
+def test_backward_flag_must_be_0_or_1():
+    p = _params()
+    p.backward = 2
+    st, h = M.create_cfg(p)
+    assert st == M.MOE_ERR_INVALID_ARG and not h.value
 
 
 def test_null_arguments_rejected():
@@ -75,6 +84,8 @@ def test_null_arguments_rejected():
     assert lib.moe_layer_forward(None, None, 0, None, None, None, None, None, None, None) == M.MOE_ERR_INVALID_ARG
     assert lib.moe_router_forward(None, None, 0, None, None, None, None, None, None) == M.MOE_ERR_INVALID_ARG
     assert lib.moe_dispatch_forward(None, None, 0, None, None, None, None) == M.MOE_ERR_INVALID_ARG
+    assert lib.moe_layer_backward(None, None, 0, None, None, None, None, None, None, None, None, None,
+                                  None) == M.MOE_ERR_INVALID_ARG
     assert lib.moe_cfg_destroy(None) == M.MOE_OK
 
 

@@ -136,25 +136,32 @@ def test_router_forced_expert_and_all_ties():
     assert torch.allclose(gate.cpu(), torch.full((cfg.T, cfg.K), cfg.rsf / cfg.K))
 
 
-def test_dispatch_is_a_valid_permutation():
-    cfg = SMALL_SIG
-    layer = M.MoELayer.from_config(cfg)
+def test_dispatch_is_the_stable_permutation():
+    """Rows by the definition: (t, k) with expert e goes to offsets[e] plus the
+    number of earlier entries with expert e (several chunks of 512 entries, a
+    skewed case where one expert takes most tokens, and E = 512)."""
     rng = np.random.default_rng(3)
-    for T in (1, 77, 517):
-        idx = np.stack([rng.choice(cfg.E, size=cfg.K, replace=False) for _ in range(T)]).astype(np.int32)
-        off, row_token, slot_row = layer.dispatch(torch.from_numpy(idx).to(DEV))
-        torch.cuda.synchronize()
-        off, row_token, slot_row = off.cpu().numpy(), row_token.cpu().numpy(), slot_row.cpu().numpy()
-        cnt = np.bincount(idx.ravel(), minlength=cfg.E)
-        assert np.array_equal(off, np.concatenate([[0], np.cumsum(cnt)]))
-        for e in range(cfg.E):
-            seg = row_token[off[e]:off[e + 1]]
-            assert np.array_equal(np.sort(seg), np.nonzero((idx == e).any(axis=1))[0])
-        for t in range(T):
-            for k in range(cfg.K):
-                r = slot_row[t * cfg.K + k]
-                e = idx[t, k]
-                assert off[e] <= r < off[e + 1] and row_token[r] == t
+    for cfg, Ts in ((SMALL_SIG, (1, 77, 517, 1400)), (ROUTER_E384.with_(E=512, G=16, kg=4), (900,))):
+        layer = M.MoELayer.from_config(cfg.with_(T=max(Ts)))
+        for T in Ts:
+            for skew in (False, True):
+                p = np.ones(cfg.E)
+                if skew:
+                    p[3] = 50.0 * cfg.E
+                p /= p.sum()
+                idx = np.stack([rng.choice(cfg.E, size=cfg.K, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+                off, row_token, slot_row = layer.dispatch(torch.from_numpy(idx).to(DEV))
+                torch.cuda.synchronize()
+                off, row_token, slot_row = off.cpu().numpy(), row_token.cpu().numpy(), slot_row.cpu().numpy()
+                cnt = np.bincount(idx.ravel(), minlength=cfg.E)
+                assert np.array_equal(off, np.concatenate([[0], np.cumsum(cnt)]))
+                seen = np.zeros(cfg.E, np.int64)
+                want_slot = np.empty(T * cfg.K, np.int64)
+                for i, e in enumerate(idx.ravel()):
+                    want_slot[i] = off[e] + seen[e]
+                    seen[e] += 1
+                assert np.array_equal(slot_row, want_slot)
+                assert np.array_equal(row_token[want_slot], np.arange(T * cfg.K) // cfg.K)
 
 
 @pytest.mark.parametrize("cfg,path", [(SMALL_F32, "auto"), (MI.CONFIGS["tiny_f32"], "auto"),
@@ -303,6 +310,80 @@ def test_quantizer_matches_the_oracle_bit_for_bit():
     _quant_parity(x[:1].clone())
     c0, s0 = M.quantize_e4m3_1x128(torch.empty((0, 256), dtype=torch.bfloat16, device=DEV))
     assert c0.shape == (0, 256) and s0.shape == (0, 2)
+
+
+# ---------------------------------------------------------------------------
+# backward pass: gradients against the oracle's chain rule
+# ---------------------------------------------------------------------------
+
+BWD_SIG = MI.LayerConfig("bwd_sigmoid", T=300, D=256, E=16, H=128, G=4, kg=2, K=3, score_fn="sigmoid",
+                         bias="normal", norm=True, rsf=2.5, Hs=256, act="bf16", weight="bf16", bias_std=0.05)
+BWD_SOFTMAX = MI.LayerConfig("bwd_softmax", T=200, D=384, E=40, H=256, G=1, kg=1, K=4, score_fn="softmax",
+                             bias="none", norm=False, rsf=1.5, Hs=128, act="bf16", weight="bf16")
+BWD_GROUP = MI.LayerConfig("bwd_group", T=1000, D=1024, E=64, H=512, G=8, kg=3, K=6, score_fn="softmax",
+                           bias="none", norm=False, rsf=1.0, Hs=1024, act="bf16", weight="bf16")
+
+
+def _rel(a, b):
+    a = a.detach().float().cpu().numpy().astype(np.float64) if torch.is_tensor(a) else a
+    return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-30))
+
+
+def _check_backward(cfg, add_residual=True, with_shared=True, seed=5):
+    inp = MI.make_layer(cfg, DEV)
+    over = {} if with_shared else {"shared_hidden": 0}
+    layer = M.MoELayer.from_config(cfg, backward=True, add_residual=add_residual, **over)
+    g = torch.Generator().manual_seed(seed)
+    d_out = torch.randn((cfg.T, cfg.D), generator=g).to(DEV)
+    shared = inp.shared if with_shared else None
+    got = layer.backward(inp.x, inp.gate_w, inp.sel_bias, inp.experts, shared, d_out)
+    torch.cuda.synchronize()
+    R = A.route_inputs(inp)
+    assert not near_tie_mask(R).any(), "a near-tie token: pick another seed for this case"
+    u = A.decode_tensor(inp.x)
+    bias = None if inp.sel_bias is None else A.decode_tensor(inp.sel_bias)
+    ref = O.layer_backward(A.router_params(cfg), u, A.decode_tensor(inp.gate_w), bias,
+                           A.routed_expert_fn(inp.experts), d_out.cpu().numpy().astype(np.float64),
+                           A.shared_expert_fn(shared) if with_shared else None, add_residual=add_residual,
+                           routing=R)
+    tol = TOL["bf16"]
+    dx = got["dx"].cpu().numpy().astype(np.float64)
+    e_dx = np.abs(dx - ref["dx"]).max(axis=1) / np.maximum(np.abs(ref["dx"]).max(axis=1), 1e-30)
+    errs = {"dx": float(e_dx.max()), "d_gate_w": _rel(got["d_gate_w"], ref["d_gate_w"])}
+    worst_w = 0.0
+    for e in range(cfg.E):
+        if e not in ref["d_routed"]:
+            assert not got["d_gate_up"][e].any() and not got["d_down"][e].any(), f"unused expert {e} not zero"
+            continue
+        dwg, dwu, dwd = ref["d_routed"][e]
+        worst_w = max(worst_w, _rel(got["d_gate_up"][e], np.concatenate([dwg, dwu], 0)),
+                      _rel(got["d_down"][e], dwd))
+    errs["d_experts"] = worst_w
+    if with_shared:
+        dwg, dwu, dwd = ref["d_shared"]
+        errs["d_shared"] = max(_rel(got["d_shared_gate_up"], np.concatenate([dwg, dwu], 0)),
+                               _rel(got["d_shared_down"], dwd))
+    print(f"{cfg.name} backward errors {errs}")
+    for k, v in errs.items():
+        assert v <= tol, (k, v)
+    return layer, inp, d_out, got
+
+
+@pytest.mark.parametrize("cfg", [BWD_SIG, BWD_SOFTMAX, BWD_GROUP], ids=lambda c: c.name)
+def test_backward_matches_the_oracle(cfg):
+    _check_backward(cfg)
+
+
+def test_backward_routed_only_and_repeatable():
+    layer, inp, d_out, g1 = _check_backward(BWD_SIG, add_residual=False, with_shared=False)
+    g2 = layer.backward(inp.x, inp.gate_w, inp.sel_bias, inp.experts, None, d_out)
+    torch.cuda.synchronize()
+    for k in ("dx", "d_gate_w", "d_gate_up", "d_down"):
+        assert torch.equal(g1[k], g2[k]), k  # no float atomics: bit-identical repeats
+    # T = 0 zeroes every gradient
+    g0 = layer.backward(inp.x[:0], inp.gate_w, inp.sel_bias, inp.experts, None, d_out[:0])
+    torch.cuda.synchronize()
+    assert not g0["d_gate_w"].any() and not g0["d_gate_up"].any() and not g0["d_down"].any()
 
 
 SKEWED = MI.LayerConfig("skewed", T=1100, D=256, E=16, H=128, G=4, kg=2, K=3, score_fn="sigmoid",
