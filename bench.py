@@ -88,6 +88,41 @@ def gateup_flops(cfg):
     return 2.0 * cfg.T * (cfg.K * 2 * cfg.D * cfg.H + 2 * cfg.D * cfg.Hs)
 
 
+def backward_flops(cfg):
+    """MFMA work of the backward pass: the gate/up recompute, the two data
+    gradients and the two weight gradients of the experts (each as much as
+    the forward's product), and the router's two products (E padded to 64)."""
+    ep = (cfg.E + 63) // 64 * 64
+    return gateup_flops(cfg) + 2 * mfma_flops(cfg) + 4.0 * cfg.T * ep * cfg.D
+
+
+def run_backward(args, torch, M, cfg, inp):
+    """Backward steps on the forward's inputs: fp32 gradients of every expert,
+    the shared expert, gate_w and x for a random d_out (HIP events on the
+    stream the library runs on)."""
+    layer = M.MoELayer.from_config(cfg, backward=True)
+    d_out = torch.randn((cfg.T, cfg.D), generator=torch.Generator(device="cuda").manual_seed(8), device="cuda")
+    for _ in range(2):
+        g = layer.backward(inp.x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared, d_out)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = max(3, args.steps // 4)
+    ev0.record()
+    for _ in range(n):
+        g = layer.backward(inp.x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared, d_out)
+    ev1.record()
+    ev1.synchronize()
+    ms = ev0.elapsed_time(ev1) / n
+    flop = backward_flops(cfg)
+    log(f"backward: {ms:.3f} ms/step ({n} steps)")
+    del g, layer
+    torch.cuda.empty_cache()
+    return {"ms": round(ms, 4), "steps": n, "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+            "mfma_flop": flop, "achieved_tflops": round(flop / (ms * 1e-3) / 1e12, 2),
+            "frac_of_bf16_peak": round(flop / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+            "gradients": "fp32 (x, gate_w, every expert, shared expert)"}
+
+
 def gen_progress(cfg, torch):
     """Logs every 32 experts, so that a slow generation (under a counter
     profiler every dispatch is serialised) still shows its progress."""
@@ -154,6 +189,9 @@ def run_prefill(args, torch, M, MI):
                              algorithmic_bytes=gateup_algorithmic_bytes(cfg),
                              kernel=kernel, per_launch_flop=gateup_flops(cfg), avg_ms=round(g1_ms, 4)))
     del layer, out
+    torch.cuda.empty_cache()
+    if not args.no_backward and cfg.weight == "bf16" and cfg.act == "bf16" and not cfg.act_quant:
+        res["backward"] = run_backward(args, torch, M, cfg, inp)
     return res
 
 
@@ -248,6 +286,7 @@ def main():
     ap.add_argument("--decode-config", default="v3_decode_fp8")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
     ap.add_argument("--cpu-sample", type=int, default=40)
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 1 GiB device-to-device copy first (a known-size reference "
@@ -300,6 +339,8 @@ def main():
         "balance_update_and_stats_us": round(res["balance_us"], 2),
         "roofline": res["roofline"],
     }
+    if "backward" in res:
+        line["backward"] = res["backward"]
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {args.cpu_sample} tokens")
         line["cpu_baseline"] = cpu_baseline(res, args.cpu_sample)

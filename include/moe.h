@@ -144,8 +144,9 @@ moe_status moe_layer_forward(moe_cfg* cfg, const void* x, int T, const float* ga
  * g_k = rsf * s_k (/ sum of the K chosen s when norm_topk), then through the
  * score function to the logits, x and gate_w. sel_bias only changes the
  * choice and gets no gradient (moe_bias_update adjusts it).
- *   d_out         [T][D] fp32 (input)
- *   dx            [T][D] fp32 dL/dx (includes d_out itself when add_residual)
+ *   d_out         [T][D] fp32 (input; 16-byte aligned)
+ *   dx            [T][D] fp32 dL/dx (includes d_out itself when add_residual;
+ *                 16-byte aligned)
  *   d_gate_w      [E][D] fp32 dL/dgate_w
  *   d_expert_w    fp32 dL/dW in the layout of moe_weights: gate_up
  *                 [E][2H][D], down [E][D][H]; every expert is written

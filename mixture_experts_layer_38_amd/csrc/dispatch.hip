@@ -94,9 +94,10 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(DispatchArgs a) {
 // hold its tokens in ascending order (the scope's definition of the step), so
 // every sum over an expert's rows (the weight gradients of the backward pass)
 // runs in one order on every call. Entries are split into chunks of
-// kPermChunk, one wave each: (A) each chunk's expert histogram, (B) per
-// expert, the first row of each chunk (offsets plus the earlier chunks'
-// counts), (C) each wave walks its chunk in order, 64 entries at a time,
+// kPermChunk (128), one wave each: (A) each chunk's expert histogram, (B)
+// per expert (one wave, shuffle scan), the first row of each chunk (offsets
+// plus the earlier chunks' counts), (C) each wave walks its chunk in order,
+// 64 entries at a time,
 // ranking equal experts among the lanes with ballots.
 constexpr int kPermChunk = kDispatchChunk;
 
@@ -117,18 +118,28 @@ __global__ __launch_bounds__(256) void dispatch_chunk_count_kernel(DispatchArgs 
   }
   __syncthreads();
   if (chunk < nchunks)
-    for (int e = lane; e < a.E; e += 64) a.chunk_base[(size_t)chunk * a.E + e] = cnt[w][e];
+    for (int e = lane; e < a.E; e += 64) a.chunk_base[(size_t)e * nchunks + chunk] = cnt[w][e];
 }
 
+// one wave per expert: exclusive scan of its chunk counts (contiguous), plus
+// the expert's first row
 __global__ __launch_bounds__(256) void dispatch_chunk_scan_kernel(DispatchArgs a) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (e >= a.E) return;
   const int nchunks = (a.T * a.K + kPermChunk - 1) / kPermChunk;
-  int acc = a.offsets[e];
-  for (int c = 0; c < nchunks; ++c) {
-    const int v = a.chunk_base[(size_t)c * a.E + e];
-    a.chunk_base[(size_t)c * a.E + e] = acc;
-    acc += v;
+  int32_t* base = a.chunk_base + (size_t)e * nchunks;
+  int carry = a.offsets[e];
+  for (int c0 = 0; c0 < nchunks; c0 += 64) {
+    const int c = c0 + lane;
+    const int v = c < nchunks ? base[c] : 0;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += u;
+    }
+    if (c < nchunks) base[c] = carry + incl - v;
+    carry += __shfl(incl, 63);
   }
 }
 
@@ -139,7 +150,7 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(DispatchArgs a) {
   const int nchunks = (n + kPermChunk - 1) / kPermChunk;
   const int chunk = blockIdx.x * 4 + w;
   if (chunk < nchunks)
-    for (int e = lane; e < a.E; e += 64) run[w][e] = a.chunk_base[(size_t)chunk * a.E + e];
+    for (int e = lane; e < a.E; e += 64) run[w][e] = a.chunk_base[(size_t)e * nchunks + chunk];
   __syncthreads();
   if (chunk >= nchunks) return;  // no barrier below: waves of a block work alone from here
   const int i1 = min(n, (chunk + 1) * kPermChunk);
@@ -176,7 +187,7 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   const int nchunks = (n + kPermChunk - 1) / kPermChunk;
   const int blocks = (nchunks + 3) / 4;
   hipLaunchKernelGGL(dispatch_chunk_count_kernel, dim3(blocks), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(dispatch_chunk_scan_kernel, dim3((a.E + 255) / 256), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(dispatch_chunk_scan_kernel, dim3((a.E + 3) / 4), dim3(256), 0, s, a);
   hipLaunchKernelGGL(dispatch_permute_kernel, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -63,6 +63,12 @@ __device__ __forceinline__ uint4 bload(const __amdgpu_buffer_rsrc_t& r, uint32_t
 }
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// LDS layout: row r holds its 64 k values as eight 16-byte chunks, chunk c at
+// position c ^ ((r >> 4) & 7) (rows padded to 144 bytes). With this swizzle
+// the fragment reads (16 rows x one chunk per 16 lanes) and the transposed
+// 8-byte stores (rows 8 apart, 4 k each) both fall on distinct banks.
+__device__ __forceinline__ int lds_at(int r, int k) { return r * LDK + ((((k >> 3) ^ (r >> 4)) & 7) << 3) + (k & 7); }
 }  // namespace
 
 template <int kMode, bool kAT>
@@ -125,8 +131,8 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
       const uint32_t lo23 = __builtin_amdgcn_perm(w[3][p], w[2][p], 0x05040100u);
       const uint32_t hi01 = __builtin_amdgcn_perm(w[1][p], w[0][p], 0x07060302u);
       const uint32_t hi23 = __builtin_amdgcn_perm(w[3][p], w[2][p], 0x07060302u);
-      *reinterpret_cast<uint2*>(&base[(8 * mg + 2 * p) * LDK + 4 * kg]) = make_uint2(lo01, lo23);
-      *reinterpret_cast<uint2*>(&base[(8 * mg + 2 * p + 1) * LDK + 4 * kg]) = make_uint2(hi01, hi23);
+      *reinterpret_cast<uint2*>(&base[lds_at(8 * mg + 2 * p, 4 * kg)]) = make_uint2(lo01, lo23);
+      *reinterpret_cast<uint2*>(&base[lds_at(8 * mg + 2 * p + 1, 4 * kg)]) = make_uint2(hi01, hi23);
     }
   };
   auto store = [&](int buf) __attribute__((always_inline)) {
@@ -134,7 +140,7 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
       store_kmajor(&smem[buf][0], sa_);
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&smem[buf][(r0 + 32 * j) * LDK + c8 * 8]) = sa_[j];
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&smem[buf][lds_at(r0 + 32 * j, c8 * 8)]) = sa_[j];
     }
     store_kmajor(&smem[buf][BM * LDK], sb_);
   };
@@ -164,9 +170,9 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
     for (int kk = 0; kk < BK; kk += 16) {
       bf16x8 fa[2], fb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(&sA[(64 * wm + 32 * i + lr) * LDK + kk + lk]);
+      for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(&sA[lds_at(64 * wm + 32 * i + lr, kk + lk)]);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) fb[c] = *reinterpret_cast<const bf16x8*>(&sB[(64 * wn + 32 * c + lr) * LDK + kk + lk]);
+      for (int c = 0; c < 2; ++c) fb[c] = *reinterpret_cast<const bf16x8*>(&sB[lds_at(64 * wn + 32 * c + lr, kk + lk)]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -417,17 +423,33 @@ __global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ 
   }
 }
 
-// pre[p] = tiles of problems < p: ceil(rows_p / 128) row tiles x n_p column tiles
-__global__ void tile_prefix_kernel(const int32_t* __restrict__ offsets, int E, int shared_rows, int n_routed,
-                                   int n_shared, int32_t* __restrict__ pre) {
-  if (threadIdx.x != 0) return;
-  int acc = 0;
-  for (int p = 0; p <= E; ++p) {
-    pre[p] = acc;
+// pre[p] = tiles of problems < p: ceil(rows_p / 128) row tiles x n_p column
+// tiles (one thread per problem, E + 1 <= 1024, block scan through LDS)
+__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* __restrict__ offsets, int E,
+                                                           int shared_rows, int n_routed, int n_shared,
+                                                           int32_t* __restrict__ pre) {
+  __shared__ int wsum[16];
+  const int p = threadIdx.x, lane = p & 63, w = p >> 6;
+  int v = 0;
+  if (p <= E) {
     const int rows = p < E ? offsets[p + 1] - offsets[p] : shared_rows;
-    acc += ((rows + BM - 1) / BM) * (p < E ? n_routed : n_shared);
+    v = ((rows + BM - 1) / BM) * (p < E ? n_routed : n_shared);
   }
-  pre[E + 1] = acc;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int base = 0, all = 0;
+  for (int q = 0; q < 16; ++q) {
+    if (q < w) base += wsum[q];
+    all += wsum[q];
+  }
+  if (p <= E) pre[p] = base + incl - v;
+  if (p == 0) pre[E + 1] = all;
 }
 
 // router backward, one wave per token: dL/dg from the partial sums, through
@@ -498,14 +520,55 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(const float* __restrict
                                                          const float* __restrict__ dx_router,
                                                          const int32_t* __restrict__ slot_row, int T, int D, int K,
                                                          int add_residual, float* __restrict__ dx) {
+  // 8 consecutive columns per thread (D % 128 == 0): 16-byte bf16 row loads,
+  // all K rows requested before the sums, which run in slot order
   const int t = blockIdx.x;
   const int* sr = slot_row + (size_t)t * K;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float v = add_residual ? dout[(size_t)t * D + d] : 0.f;
-    if (dxs) v += bf16f(dxs[(size_t)t * D + d]);
-    for (int k = 0; k < K; ++k) v += bf16f(dxr[(size_t)sr[k] * D + d]);
-    v += dx_router[(size_t)t * D + d];
-    dx[(size_t)t * D + d] = v;
+  int rows[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) rows[k] = k < K ? sr[k] : 0;
+  for (int d = 8 * threadIdx.x; d < D; d += 8 * blockDim.x) {
+    float v[8];
+    const f32x4 r0 = *reinterpret_cast<const f32x4*>(dx_router + (size_t)t * D + d);
+    const f32x4 r1 = *reinterpret_cast<const f32x4*>(dx_router + (size_t)t * D + d + 4);
+    v[0] = r0.x; v[1] = r0.y; v[2] = r0.z; v[3] = r0.w; v[4] = r1.x; v[5] = r1.y; v[6] = r1.z; v[7] = r1.w;
+    float acc[8];
+    if (add_residual) {
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(dout + (size_t)t * D + d);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(dout + (size_t)t * D + d + 4);
+      acc[0] = a0.x; acc[1] = a0.y; acc[2] = a0.z; acc[3] = a0.w; acc[4] = a1.x; acc[5] = a1.y; acc[6] = a1.z;
+      acc[7] = a1.w;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+    }
+    if (dxs) {
+      const uint4 s4 = *reinterpret_cast<const uint4*>(dxs + (size_t)t * D + d);
+      const uint32_t w[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += __uint_as_float(w[q] << 16);
+        acc[2 * q + 1] += __uint_as_float(w[q] & 0xFFFF0000u);
+      }
+    }
+    uint4 rk[kMaxTopK];
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k)
+      if (k < K) rk[k] = *reinterpret_cast<const uint4*>(dxr + (size_t)rows[k] * D + d);
+#pragma unroll
+    for (int k = 0; k < kMaxTopK; ++k) {
+      if (k >= K) break;
+      const uint32_t w[4] = {rk[k].x, rk[k].y, rk[k].z, rk[k].w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += __uint_as_float(w[q] << 16);
+        acc[2 * q + 1] += __uint_as_float(w[q] & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) acc[q] += v[q];
+    *reinterpret_cast<f32x4*>(dx + (size_t)t * D + d) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    *reinterpret_cast<f32x4*>(dx + (size_t)t * D + d + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
   }
 }
 
@@ -532,9 +595,9 @@ hipError_t launch_layer_backward(const BwdArgs& a, hipStream_t s) {
                      a.gw_bf16, a.D);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // tile prefixes of the two row-grouped products
-  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, a.offsets, a.E, a.Hs > 0 ? a.T : 0, a.H / BN,
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.Hs > 0 ? a.T : 0, a.H / BN,
                      a.Hs / BN, a.pre_h);
-  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(64), 0, s, a.offsets, a.E, a.Hs > 0 ? a.T : 0, a.D / BN,
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.Hs > 0 ? a.T : 0, a.D / BN,
                      a.D / BN, a.pre_x);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long mblk = (long)(a.T * a.K + BM - 1) / BM + a.E, mblk_s = a.Hs > 0 ? (a.T + BM - 1) / BM : 0;

@@ -541,6 +541,8 @@ moe_status moe_layer_backward(moe_cfg* c, const void* x, int T, const float* gat
                      !d_shared_w->down))
     return MOE_ERR_INVALID_ARG;
   if (T > 0 && (!x || !d_out || !dx)) return MOE_ERR_INVALID_ARG;
+  // d_out and dx are read and written 16 bytes at a time
+  if (((uintptr_t)d_out | (uintptr_t)dx) & 15) return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
   const size_t E = p.n_routed, D = p.dim, H = p.hidden, Hs = p.shared_hidden;
   hipError_t e;

@@ -30,7 +30,7 @@ constexpr int kGB_BK = 64;    // K step
 constexpr int kF8_BM = 128;   // rows (tokens) per tile
 constexpr int kF8_BK = 128;   // K step = one scale block (elements = bytes)
 constexpr int kActBlock = 128;  // activation quantisation block (1 x 128)
-constexpr int kDispatchChunk = 512;  // (token, slot) entries per wave in the stable permutation
+constexpr int kDispatchChunk = 128;  // (token, slot) entries per wave in the stable permutation
 // Weight-streaming path (small token counts): token rows and columns per workgroup item.
 constexpr int kST_BM = 16;
 constexpr int kST_N1 = 32;    // hidden columns per gate/up item (32 gate + 32 up rows)
@@ -180,7 +180,7 @@ struct DispatchArgs {
   int32_t* counts;        // [E] (input: histogram)
   int32_t* counts_out;    // [E] user copy or null
   int32_t* offsets;       // [E+1]
-  int32_t* chunk_base;    // [ceil(T*K/512)][E] first row of each chunk's entries of each expert
+  int32_t* chunk_base;    // [E][ceil(T*K/128)] first row of each chunk's entries of each expert
   int32_t* row_token;     // [T*K]
   float* row_gate;        // [T*K] or null
   int32_t* slot_row;      // [T*K]

@@ -423,6 +423,49 @@ def layer_backward(p: RouterParams, u: np.ndarray, gate_w: np.ndarray, sel_bias,
                 routing=routing)
 
 
+def layer_backward_sample(p: RouterParams, u: np.ndarray, gate_w: np.ndarray, routed_expert, d_out,
+                          routing: dict, tokens, experts, shared_expert=None, add_residual: bool = True):
+    """The same gradients as layer_backward, on a sample: dx for `tokens` and
+    the weight gradients of the routed `experts` (from all their tokens).
+    Each expert's and each token's share is computed on its own rows, with the
+    same steps as layer_backward; d gate_w needs every token and is not
+    returned. Returns dict(dx [len(tokens), D], d_routed {e: ...})."""
+    u = np.asarray(u, np.float64)
+    d_out = np.asarray(d_out, np.float64)
+    tokens = np.asarray(tokens)
+    idx, gate, s = routing["idx"], routing["gate"], routing["scores"]
+    n, D = len(tokens), u.shape[1]
+    dx = d_out[tokens].copy() if add_residual else np.zeros((n, D))
+    d_gate = np.zeros((n, p.K))
+    sel = idx[tokens]
+    for e in np.unique(sel):  # each expert's weights decoded once
+        jj, kk = np.nonzero(sel == e)
+        tt = tokens[jj]
+        wg, wu, wd = routed_expert(int(e))
+        du, _, _, _, y = swiglu_ffn_backward(u[tt], wg, wu, wd, gate[tt, kk][:, None] * d_out[tt])
+        dx[jj] += du
+        d_gate[jj, kk] = (d_out[tt] * y).sum(axis=1)
+    if shared_expert is not None:
+        sw = shared_expert()
+        if sw is not None:
+            du, _, _, _, _ = swiglu_ffn_backward(u[tokens], *sw, d_out[tokens])
+            dx += du
+    rows = np.arange(n)[:, None]
+    ds_sel = gate_score_grad(s[tokens][rows, idx[tokens]], d_gate, p.norm, p.rsf)
+    ds = np.zeros((n, s.shape[1]))
+    ds[rows, idx[tokens]] = ds_sel
+    st = s[tokens]
+    dlogit = ds * st * (1.0 - st) if p.score_fn == "sigmoid" else st * (ds - (st * ds).sum(axis=1, keepdims=True))
+    dx += dlogit @ np.asarray(gate_w, np.float64)
+    d_routed = {}
+    for e in experts:
+        ii, kk = np.nonzero(idx == e)
+        wg, wu, wd = routed_expert(int(e))
+        _, dwg, dwu, dwd, _ = swiglu_ffn_backward(u[ii], wg, wu, wd, gate[ii, kk][:, None] * d_out[ii])
+        d_routed[int(e)] = (dwg, dwu, dwd)
+    return dict(dx=dx, d_routed=d_routed)
+
+
 def near_tie_tokens(routing: dict, window: float = 1e-6) -> np.ndarray:
     """Tokens whose K/K+1 or group-boundary selection-score gap is within the window."""
     return np.nonzero((routing["gap_k"] < window) | (routing["gap_g"] < window))[0]

@@ -528,6 +528,43 @@ def test_layer_v3_prefill_w8a8(layers):
     _check_layer(inp, tokens=_sample(inp.cfg.T, 16), routed_only=False)
 
 
+def test_backward_v3_prefill_sampled(layers):
+    """The backward pass at the V3 prefill shape: dx on sampled tokens and the
+    weight gradients of two experts (all their tokens), against the oracle on
+    the GPU's own expert choice (near-tie tokens may pick either side)."""
+    inp = layers("v3_prefill")
+    cfg = inp.cfg
+    layer = M.MoELayer.from_config(cfg, backward=True)
+    d_out = torch.randn((cfg.T, cfg.D), generator=torch.Generator().manual_seed(8)).to(DEV)
+    got = layer.backward(inp.x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared, d_out)
+    idx, _, _ = layer.router(inp.x, inp.gate_w, inp.sel_bias)
+    torch.cuda.synchronize()
+    R = A.route_inputs(inp)
+    near = near_tie_mask(R)
+    gidx = idx.cpu().numpy().astype(np.int64)
+    R = dict(R)
+    R["idx"] = np.where(near[:, None], gidx, R["idx"])
+    R["gate"] = O.gate_values(R["scores"], R["idx"], cfg.norm, cfg.rsf)
+    tokens = _sample(cfg.T, 12, seed=4)
+    tokens = tokens[~near[tokens]]
+    load = np.bincount(R["idx"].ravel(), minlength=cfg.E)
+    experts = [int(np.argmax(load)), int(np.argmin(np.where(load > 0, load, 1 << 30)))]
+    ref = O.layer_backward_sample(A.router_params(cfg), A.decode_tensor(inp.x), A.decode_tensor(inp.gate_w),
+                                  A.routed_expert_fn(inp.experts), d_out.cpu().numpy().astype(np.float64), R,
+                                  tokens, experts, A.shared_expert_fn(inp.shared), add_residual=cfg.add_residual)
+    dx = got["dx"][torch.as_tensor(tokens, device=DEV)].cpu().numpy().astype(np.float64)
+    e_dx = float((np.abs(dx - ref["dx"]).max(axis=1) / np.abs(ref["dx"]).max(axis=1)).max())
+    e_w = 0.0
+    for e in experts:
+        dwg, dwu, dwd = ref["d_routed"][e]
+        e_w = max(e_w, _rel(got["d_gate_up"][e], np.concatenate([dwg, dwu], 0)), _rel(got["d_down"][e], dwd))
+    print(f"v3 backward: dx err {e_dx} over {len(tokens)} tokens, expert grads err {e_w} "
+          f"(experts {experts}, rows {load[experts].tolist()}), near-tie tokens {int(near.sum())}")
+    assert e_dx <= TOL["bf16"] and e_w <= TOL["bf16"]
+    del got
+    torch.cuda.empty_cache()
+
+
 def test_layer_v3_decode_fp8(layers):
     inp = layers("v3_decode_fp8")
     _check_layer(inp)

@@ -577,6 +577,18 @@ def test_layer_backward_matches_finite_differences(score_fn, norm, G, kg):
     assert np.all(np.abs(_fd(f, bias, [(0,), (3,), (5,)])) < 1e-9)
 
 
+def test_sampled_backward_equals_the_full_one():
+    p, u, gw, bias, ex, sh, dout = _bwd_problem("softmax", True, 4, 3, seed=21)
+    full = O.layer_backward(p, u, gw, bias, lambda e: ex[e], dout, (lambda: sh))
+    toks = np.array([0, 3, 7])
+    used = sorted(full["d_routed"])[:2]
+    smp = O.layer_backward_sample(p, u, gw, lambda e: ex[e], dout, full["routing"], toks, used, (lambda: sh))
+    assert np.allclose(smp["dx"], full["dx"][toks], rtol=1e-12, atol=1e-12)
+    for e in used:
+        for a_, b_ in zip(smp["d_routed"][e], full["d_routed"][e]):
+            assert np.allclose(a_, b_, rtol=1e-12, atol=1e-12)
+
+
 def test_layer_backward_residual_and_routed_only():
     p, u, gw, bias, ex, sh, dout = _bwd_problem("sigmoid", True, 4, 2, seed=11, shared=False)
     g1 = O.layer_backward(p, u, gw, bias, lambda e: ex[e], dout, None, add_residual=True)
