@@ -5,9 +5,9 @@
 // gate values.
 //
 // Every product is one grouped bf16 MFMA GEMM C[m][n] = sum_k A[m][k] B[n][k]
-// (fp32 accumulation) over 128 x 128 tiles, K step 64, 4 waves of 64 x 64
-// (2 x 2 blocks of v_mfma_f32_32x32x16_bf16), operands staged through two LDS
-// buffers in [row][k] layout. The right operand is always stored k-major
+// (fp32 accumulation) over 256 x 256 tiles, K step 64, 8 waves (two per SIMD)
+// of 128 x 64 (4 x 2 blocks of v_mfma_f32_32x32x16_bf16), operands staged
+// through two LDS buffers in [row][k] layout. The right operand is always stored k-major
 // (B[n][k] = stored[k][n]: the weights read "the other way" than the
 // forward, or activations summed over rows for the weight gradients) and is
 // transposed while it is staged: a thread loads 4 k-rows x 8 consecutive n
@@ -32,9 +32,9 @@
 namespace moe {
 
 namespace {
-constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;  // LDS row: 72 bf16 (144 bytes)
+constexpr int BM = 256, BN = 256, BK = 64, LDK = BK + 8;  // LDS row: 72 bf16 (144 bytes)
 constexpr int kRowsL = BM + BN;
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 
 enum : int { kDgradH = 0, kDgradX = 1, kWgradD = 2, kWgradGU = 3, kRouterW = 4, kRouterX = 5 };
 
@@ -62,6 +62,8 @@ __device__ __forceinline__ uint4 bload(const __amdgpu_buffer_rsrc_t& r, uint32_t
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
 
+__host__ __device__ constexpr int cdiv(int x, int y) { return (x + y - 1) / y; }
+
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // LDS layout: row r holds its 64 k values as eight 16-byte chunks, chunk c at
@@ -75,21 +77,21 @@ template <int kMode, bool kAT>
 __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRowsL * LDK], float* s_red) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(t.a), (short)0,
                                                                       t.a_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(t.b), (short)0,
                                                                       t.b_bytes, 0x00020000);
-  // natural loader: rows r0 + 32j, 16-byte chunk c8 of the 64-wide K step
+  // natural loader: rows r0 + 64j, 16-byte chunk c8 of the 64-wide K step
   const int c8 = tid & 7, r0 = tid >> 3;
   // k-major loader: k rows 4*kg .. +3 of the step, columns 8*mg .. +7 of the tile
-  const int kg = tid >> 4, mg = tid & 15;
+  const int kg = tid >> 5, mg = tid & 31;
 
   uint32_t aoff[4];
   if (!kAT) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      int m = t.m0 + r0 + 32 * j;
+      int m = t.m0 + r0 + 64 * j;
       m = m < t.M ? m : t.M - 1;
       const int row = t.amap ? t.amap[m] : m;
       aoff[j] = ((uint32_t)row * (uint32_t)t.lda + c8 * 8) * 2u;
@@ -140,14 +142,14 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
       store_kmajor(&smem[buf][0], sa_);
     } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&smem[buf][lds_at(r0 + 32 * j, c8 * 8)]) = sa_[j];
+      for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&smem[buf][lds_at(r0 + 64 * j, c8 * 8)]) = sa_[j];
     }
     store_kmajor(&smem[buf][BM * LDK], sb_);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -168,13 +170,13 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
     const uint16_t* sB = smem[cur] + BM * LDK;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 fa[2], fb[2];
+      bf16x8 fa[4], fb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(&sA[lds_at(64 * wm + 32 * i + lr, kk + lk)]);
+      for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(&sA[lds_at(128 * wm + 32 * i + lr, kk + lk)]);
 #pragma unroll
       for (int c = 0; c < 2; ++c) fb[c] = *reinterpret_cast<const bf16x8*>(&sB[lds_at(64 * wn + 32 * c + lr, kk + lk)]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int c = 0; c < 2; ++c) acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[c], acc[i][c], 0, 0, 0);
     }
@@ -188,18 +190,19 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
     // dH = g * acc; [dA | dU] = dH * u * SiLU'(a) | dH * SiLU(a); the row's
     // partial dL/dg = sum over this tile's columns of acc * SiLU(a) * u
     uint16_t* dau = static_cast<uint16_t*>(t.c);
-    float rs[2][16];
+    float rs[4][16];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int m = t.m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int m = t.m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         float sum = 0.f;
         if (m < t.M) {
           const float g = t.gate ? t.gate[m] : 1.0f;
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
             const int n = t.n0 + 64 * wn + 32 * c + lr;
+            if (n >= t.N) continue;
             const float av = bf16f(t.au[(size_t)m * 2 * t.Hp + n]);
             const float uv = bf16f(t.au[(size_t)m * 2 * t.Hp + t.Hp + n]);
             const float sg = 1.0f / (1.0f + __expf(-av));
@@ -213,9 +216,9 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
         rs[i][e] = sum;
       }
     // sum over the 32 lanes of a row group: 16-lane rows by DPP, then the two
-    // rows through LDS with the other column wave, in a fixed order
+    // rows and the four column waves through LDS, in a fixed order
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         float v = rs[i][e];
@@ -229,28 +232,30 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
     if ((lane & 15) == 0) {
       const int half = (lane >> 4) & 1;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int r = 64 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const int r = 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
           s_red[(wn * 2 + half) * BM + r] = rs[i][e];
         }
     }
     __syncthreads();
     if (tid < BM && t.m0 + tid < t.M) {
-      const float v = (s_red[tid] + s_red[BM + tid]) + (s_red[2 * BM + tid] + s_red[3 * BM + tid]);
+      float v = 0.f;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v += s_red[q * BM + tid];
       t.part[(size_t)(t.m0 + tid) * t.npart + t.n0 / BN] = v;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int n = t.n0 + 64 * wn + 32 * c + lr;
         if (n >= t.N) continue;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int m = t.m0 + 64 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const int m = t.m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
           if (m >= t.M) continue;
           if (kMode == kDgradX)
             static_cast<uint16_t*>(t.c)[(size_t)m * t.ldc + n] = f32_to_bf16(acc[i][c][e]);
@@ -266,7 +271,7 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
 template <int kMode>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][kRowsL * LDK];
-  __shared__ float s_red[4 * BM];
+  float* s_red = reinterpret_cast<float*>(&smem[0][0]);  // epilogue only (8 x BM), after the K loop
   const int tile = blockIdx.x;
   BwdTile t;
   t.au = nullptr; t.gate = nullptr; t.part = nullptr; t.npart = 0; t.Hp = 0;
@@ -301,8 +306,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
       t.ldc = 2 * Hp;
       t.au = routed ? a.au + (size_t)rb * 2 * a.H : a.au_shared;
       t.gate = routed ? a.row_gate + rb : nullptr;
-      t.part = routed ? a.part + (size_t)rb * (a.H / BN) : a.part_shared;
-      t.npart = Hp / BN;
+      t.part = routed ? a.part + (size_t)rb * cdiv(a.H, BN) : a.part_shared;
+      t.npart = cdiv(Hp, BN);
       t.Hp = Hp;
     } else {
       // A = [dA | dU] rows; B[n = d][k = j] = W_gu[j][d]
@@ -324,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
     // gradient; experts without rows get zeros
     const int Mr = kMode == kWgradD ? a.D : 2 * a.H, Nr = kMode == kWgradD ? a.H : a.D;
     const int Ms = kMode == kWgradD ? a.D : 2 * a.Hs, Ns = kMode == kWgradD ? a.Hs : a.D;
-    const int per_r = (Mr / BM) * (Nr / BN), per_s = (Ms / BM) * (Ns / BN);
+    const int per_r = cdiv(Mr, BM) * cdiv(Nr, BN), per_s = cdiv(Ms, BM) * cdiv(Ns, BN);
     const int total = a.E * per_r + (a.Hs > 0 ? per_s : 0);
     if (tile >= total) return;
     const bool routed = tile < a.E * per_r;
@@ -333,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
     const int M = routed ? Mr : Ms, N = routed ? Nr : Ns, Hp = routed ? a.H : a.Hs;
     const int rows = routed ? a.offsets[p + 1] - a.offsets[p] : a.T;
     const int rb = routed ? a.offsets[p] : 0;
-    const int nnt = N / BN;
+    const int nnt = cdiv(N, BN);
     t.m0 = (local / nnt) * BM;
     t.n0 = (local % nnt) * BN;
     t.M = M;
@@ -367,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
     bwd_tile<kMode, true>(t, smem, s_red);
   } else if (kMode == kRouterW) {
     // d gate_w planes: A[m = e][k = t] = dlogit[t][e]; B[n = d][k = t] = x[t][d]; K split over planes
-    const int nmt = (a.Ep + BM - 1) / BM, nnt = a.D / BN;
+    const int nmt = cdiv(a.Ep, BM), nnt = cdiv(a.D, BN);
     const int per = nmt * nnt;
     if (tile >= per * a.splits) return;
     const int z = tile / per, local = tile % per;
@@ -390,8 +395,8 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
     bwd_tile<kMode, true>(t, smem, s_red);
   } else {
     // dx_r = dlogit gate_w: A = dlogit rows (K = Ep, zero-padded); B[n = d][k = e] = gate_w[e][d]
-    const int nnt = a.D / BN;
-    if (tile >= ((a.T + BM - 1) / BM) * nnt) return;
+    const int nnt = cdiv(a.D, BN);
+    if (tile >= cdiv(a.T, BM) * nnt) return;
     t.m0 = (tile / nnt) * BM;
     t.n0 = (tile % nnt) * BN;
     t.M = a.T;
@@ -521,17 +526,10 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(const float* __restrict
                                                          const int32_t* __restrict__ slot_row, int T, int D, int K,
                                                          int add_residual, float* __restrict__ dx) {
   // 8 consecutive columns per thread (D % 128 == 0): 16-byte bf16 row loads,
-  // all K rows requested before the sums, which run in slot order
+  // four slot rows requested at a time, added in slot order
   const int t = blockIdx.x;
   const int* sr = slot_row + (size_t)t * K;
-  int rows[kMaxTopK];
-#pragma unroll
-  for (int k = 0; k < kMaxTopK; ++k) rows[k] = k < K ? sr[k] : 0;
   for (int d = 8 * threadIdx.x; d < D; d += 8 * blockDim.x) {
-    float v[8];
-    const f32x4 r0 = *reinterpret_cast<const f32x4*>(dx_router + (size_t)t * D + d);
-    const f32x4 r1 = *reinterpret_cast<const f32x4*>(dx_router + (size_t)t * D + d + 4);
-    v[0] = r0.x; v[1] = r0.y; v[2] = r0.z; v[3] = r0.w; v[4] = r1.x; v[5] = r1.y; v[6] = r1.z; v[7] = r1.w;
     float acc[8];
     if (add_residual) {
       const f32x4 a0 = *reinterpret_cast<const f32x4*>(dout + (size_t)t * D + d);
@@ -542,31 +540,28 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(const float* __restrict
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] = 0.f;
     }
-    if (dxs) {
-      const uint4 s4 = *reinterpret_cast<const uint4*>(dxs + (size_t)t * D + d);
+    auto add8 = [&](const uint4 s4) __attribute__((always_inline)) {
       const uint32_t w[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         acc[2 * q] += __uint_as_float(w[q] << 16);
         acc[2 * q + 1] += __uint_as_float(w[q] & 0xFFFF0000u);
       }
+    };
+    if (dxs) add8(*reinterpret_cast<const uint4*>(dxs + (size_t)t * D + d));
+    for (int k0 = 0; k0 < K; k0 += 4) {
+      uint4 rk[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        rk[u] = k0 + u < K ? *reinterpret_cast<const uint4*>(dxr + (size_t)sr[k0 + u] * D + d) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (k0 + u < K) add8(rk[u]);
     }
-    uint4 rk[kMaxTopK];
-#pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k)
-      if (k < K) rk[k] = *reinterpret_cast<const uint4*>(dxr + (size_t)rows[k] * D + d);
-#pragma unroll
-    for (int k = 0; k < kMaxTopK; ++k) {
-      if (k >= K) break;
-      const uint32_t w[4] = {rk[k].x, rk[k].y, rk[k].z, rk[k].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += __uint_as_float(w[q] << 16);
-        acc[2 * q + 1] += __uint_as_float(w[q] & 0xFFFF0000u);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) acc[q] += v[q];
+    const f32x4 r0 = *reinterpret_cast<const f32x4*>(dx_router + (size_t)t * D + d);
+    const f32x4 r1 = *reinterpret_cast<const f32x4*>(dx_router + (size_t)t * D + d + 4);
+    acc[0] += r0.x; acc[1] += r0.y; acc[2] += r0.z; acc[3] += r0.w;
+    acc[4] += r1.x; acc[5] += r1.y; acc[6] += r1.z; acc[7] += r1.w;
     *reinterpret_cast<f32x4*>(dx + (size_t)t * D + d) = f32x4{acc[0], acc[1], acc[2], acc[3]};
     *reinterpret_cast<f32x4*>(dx + (size_t)t * D + d + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
   }
@@ -595,34 +590,35 @@ hipError_t launch_layer_backward(const BwdArgs& a, hipStream_t s) {
                      a.gw_bf16, a.D);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // tile prefixes of the two row-grouped products
-  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.Hs > 0 ? a.T : 0, a.H / BN,
-                     a.Hs / BN, a.pre_h);
-  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.Hs > 0 ? a.T : 0, a.D / BN,
-                     a.D / BN, a.pre_x);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.Hs > 0 ? a.T : 0,
+                     cdiv(a.H, BN), cdiv(a.Hs, BN), a.pre_h);
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.Hs > 0 ? a.T : 0,
+                     cdiv(a.D, BN), cdiv(a.D, BN), a.pre_x);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const long mblk = (long)(a.T * a.K + BM - 1) / BM + a.E, mblk_s = a.Hs > 0 ? (a.T + BM - 1) / BM : 0;
   BwdArgs b = a;
   b.pre = a.pre_h;
-  const int tiles_h = (int)(mblk * (a.H / BN) + mblk_s * (a.Hs / BN));
+  const int tiles_h = (int)(mblk * cdiv(a.H, BN) + mblk_s * cdiv(a.Hs, BN));
   hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kDgradH>, dim3(tiles_h), dim3(kThreads), 0, s, b);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // router backward needs every dL/dg partial
   hipLaunchKernelGGL(router_bwd_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a.logits, a.idx, a.slot_row, a.part,
-                     a.H / BN, a.T, a.E, a.Ep, a.K, a.score_fn, a.norm, a.rsf, a.dlogit);
+                     cdiv(a.H, BN), a.T, a.E, a.Ep, a.K, a.score_fn, a.norm, a.rsf, a.dlogit);
   b.pre = a.pre_x;
-  const int tiles_x = (int)(mblk * (a.D / BN) + mblk_s * (a.D / BN));
+  const int tiles_x = (int)(mblk * cdiv(a.D, BN) + mblk_s * cdiv(a.D, BN));
   hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kDgradX>, dim3(tiles_x), dim3(kThreads), 0, s, b);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int tiles_wd = a.E * (a.D / BM) * (a.H / BN) + (a.Hs > 0 ? (a.D / BM) * (a.Hs / BN) : 0);
+  const int tiles_wd = a.E * cdiv(a.D, BM) * cdiv(a.H, BN) + (a.Hs > 0 ? cdiv(a.D, BM) * cdiv(a.Hs, BN) : 0);
   hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kWgradD>, dim3(tiles_wd), dim3(kThreads), 0, s, a);
-  const int tiles_wgu = a.E * (2 * a.H / BM) * (a.D / BN) + (a.Hs > 0 ? (2 * a.Hs / BM) * (a.D / BN) : 0);
+  const int tiles_wgu =
+      a.E * cdiv(2 * a.H, BM) * cdiv(a.D, BN) + (a.Hs > 0 ? cdiv(2 * a.Hs, BM) * cdiv(a.D, BN) : 0);
   hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kWgradGU>, dim3(tiles_wgu), dim3(kThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int tiles_rw = ((a.Ep + BM - 1) / BM) * (a.D / BN) * a.splits;
+  const int tiles_rw = cdiv(a.Ep, BM) * cdiv(a.D, BN) * a.splits;
   hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kRouterW>, dim3(tiles_rw), dim3(kThreads), 0, s, a);
   hipLaunchKernelGGL(planes_sum_kernel, dim3(grid_for((size_t)a.E * a.D)), dim3(256), 0, s, a.gw_planes,
                      (size_t)a.E * a.D, a.splits, a.d_gate_w);
-  const int tiles_rx = ((a.T + BM - 1) / BM) * (a.D / BN);
+  const int tiles_rx = cdiv(a.T, BM) * cdiv(a.D, BN);
   hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kRouterX>, dim3(tiles_rx), dim3(kThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(dx_combine_kernel, dim3(a.T), dim3(256), 0, s, a.dout_f32, a.dxr, a.Hs > 0 ? a.dxs : nullptr,

@@ -225,9 +225,9 @@ moe_status moe_cfg_create(const moe_params* p, moe_cfg** out) {
   const size_t o_hsr = aq ? take(Tm * K * (H / 128) * 4) : 0, o_hss = aq ? take(Tm * (Hs / 128) * 4) : 0;
   const bool bw = p->backward != 0;
   const size_t Ep = (E + 63) / 64 * 64;
-  // d gate_w: K (tokens) split so that about two tiles per CU run
-  const int rw_tiles = (int)((Ep + 127) / 128) * (int)(D / 128);
-  const int splits = bw ? std::max(1, std::min(32, (2 * c->num_cus + rw_tiles - 1) / std::max(rw_tiles, 1))) : 0;
+  // d gate_w: K (tokens) split so that about one 256 x 256 tile per CU runs
+  const int rw_tiles = (int)((Ep + 255) / 256) * (int)((D + 255) / 256);
+  const int splits = bw ? std::max(1, std::min(32, (c->num_cus + rw_tiles - 1) / std::max(rw_tiles, 1))) : 0;
   const size_t o_dout = bw ? take(Tm * D * 2) : 0, o_gw = bw ? take(Ep * D * 2) : 0;
   const size_t o_au = bw ? take(Tm * K * 2 * H * 2) : 0, o_aus = bw ? take(Tm * 2 * Hs * 2) : 0;
   const size_t o_dau = bw ? take(Tm * K * 2 * H * 2) : 0, o_daus = bw ? take(Tm * 2 * Hs * 2) : 0;
