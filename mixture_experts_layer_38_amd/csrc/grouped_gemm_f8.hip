@@ -4,10 +4,12 @@
 // one fp32 scale per 1 x 128 block of a row, weights one per 128 x 128 block.
 //
 // One K step is 128 elements, i.e. one scale block of both operands. Per step
-// and 32 x 32 output block, two v_mfma_scale_f32_32x32x64_f8f6f4 (unit
-// hardware scale) form the block's exact-in-fp32 partial sum of code
-// products, which is added to the fp32 accumulator times (row scale x weight
-// scale) -- the per-block promotion that the block scales require.
+// and 16 x 16 output block, one v_mfma_scale_f32_16x16x128_f8f6f4 (unit
+// hardware scale: the fp32 block scales are not powers of two) forms the
+// block's partial sum of code products, which is added to the fp32
+// accumulator times (row scale x weight scale) -- the per-block promotion
+// that the block scales require. A lane's four accumulator rows are
+// consecutive, so its row scales are one 16-byte LDS read per row block.
 //
 // Gate/up GEMM: a tile loads 128 W_gate rows and the matching 128 W_up rows,
 // h = SiLU(gate) * up is formed in fp32 and, per 1 x 128 block of each row
@@ -16,13 +18,15 @@
 // Token rows are gathered (codes and their scales) through the dispatch's
 // row -> token map. Down GEMM: Y[row] = g_row * (h[row] W_down^T), bf16.
 //
-// Tile 128 x 256, 8 waves (two per SIMD) as 2 x 4, each wave 64 x 64 = 2 x 2
-// blocks of 32 x 32 (64 fp32 accumulators per lane); a wave's two 32-row
-// blocks are interleaved with the other row-wave's (blocks wm, wm + 2), and
-// the tile body is instantiated per count of valid row blocks. Operands are
+// Tile 128 x 256, 8 waves (two per SIMD) as 2 x 4, each wave 64 x 64 = 4 x 4
+// blocks of 16 x 16 (64 fp32 accumulators per lane); a wave's four 16-row
+// blocks are interleaved with the other row-wave's (blocks wm + 2i), and the
+// tile body is instantiated per count of valid row blocks. Operands are
 // staged through two LDS buffers (rows padded to 144 bytes): the weight rows
 // of the next K step and the token rows (and their scales) of the step after
-// it are loaded into registers while the current step is multiplied; one
+// it are loaded into registers while the current step is multiplied; the
+// second pair of column blocks is read from LDS behind the first pair's
+// MFMAs, and the next step's tile is written behind the second pair's; one
 // barrier per step. Tile order and the even split of an expert's rows over
 // its row tiles follow the bf16 grouped GEMMs (runs of 32 tiles per XCD,
 // column-tile major).
