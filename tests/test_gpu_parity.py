@@ -384,6 +384,23 @@ def test_backward_routed_only_and_repeatable():
     g0 = layer.backward(inp.x[:0], inp.gate_w, inp.sel_bias, inp.experts, None, d_out[:0])
     torch.cuda.synchronize()
     assert not g0["d_gate_w"].any() and not g0["d_gate_up"].any() and not g0["d_down"].any()
+    # T = 1: one row per chosen expert, every other expert zero
+    x1, d1 = inp.x[:1].contiguous(), d_out[:1].contiguous()
+    gt = layer.backward(x1, inp.gate_w, inp.sel_bias, inp.experts, None, d1)
+    torch.cuda.synchronize()
+    cfg = BWD_SIG
+    bias = None if inp.sel_bias is None else A.decode_tensor(inp.sel_bias)
+    ref = O.layer_backward(A.router_params(cfg), A.decode_tensor(inp.x)[:1], A.decode_tensor(inp.gate_w), bias,
+                           A.routed_expert_fn(inp.experts), d1.cpu().numpy().astype(np.float64), None,
+                           add_residual=False)
+    assert _rel(gt["dx"], ref["dx"]) <= TOL["bf16"] and _rel(gt["d_gate_w"], ref["d_gate_w"]) <= TOL["bf16"]
+    for e in range(cfg.E):
+        if e in ref["d_routed"]:
+            dwg, dwu, dwd = ref["d_routed"][e]
+            assert _rel(gt["d_gate_up"][e], np.concatenate([dwg, dwu], 0)) <= TOL["bf16"]
+            assert _rel(gt["d_down"][e], dwd) <= TOL["bf16"]
+        else:
+            assert not gt["d_gate_up"][e].any() and not gt["d_down"][e].any()
 
 
 SKEWED = MI.LayerConfig("skewed", T=1100, D=256, E=16, H=128, G=4, kg=2, K=3, score_fn="sigmoid",
