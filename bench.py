@@ -36,17 +36,17 @@ def log(msg):
 # HBM traffic of one gate/up GEMM launch on the V3 prefill workload, from two
 # rocprofv3 --pmc runs of this bench (FETCH_SIZE, then WRITE_SIZE; KiB per
 # dispatch, mean of 3 dispatches), each scaled by what the same counter reads
-# for the bench's 1 GiB device-to-device copy probe (FETCH_SIZE 524316.0 KiB
+# for the bench's 1 GiB device-to-device copy probe (FETCH_SIZE 524315.9 KiB
 # for 1048576 KiB read; WRITE_SIZE 1048576 KiB for 1048576 KiB written).
 # Valid only for the kernel sources with these hashes; otherwise reported null.
 GATEUP_COUNTERS = {
     "sources": {"mixture_experts_layer_38_amd/csrc/grouped_gemm.hip":
-                "f87849196ae6184cc93f6eeab2e3d17fc8ac0d9d86105969a08266dddd45e7ad",
+                "1b8084ef998c803f565fa473792bf2e473d915863869386f39dec2ecb5e05a9e",
                 "mixture_experts_layer_38_amd/csrc/moe_internal.hpp":
                 "c2cbb7252603f07395f28ffaa0720056db5db2139a3255d195211492576a9bd2"},
     "workload": "v3_prefill",
-    "fetch_kib": 12603933.5, "write_kib": 645792.3,
-    "fetch_scale": 1048576.0 / 524316.0, "write_scale": 1.0,
+    "fetch_kib": 11754397.8, "write_kib": 645792.5,
+    "fetch_scale": 1048576.0 / 524315.9, "write_scale": 1.0,
 }
 
 

@@ -38,7 +38,10 @@
 // column-tile major, and an expert's rows are split evenly (in 32-row blocks)
 // over its two or three row tiles: the row tiles that read one weight slice
 // run side by side at the same pace, so the second and third reads of each
-// weight line hit that L2 (this halves the bytes fetched past L2).
+// weight line hit that L2 (this halves the bytes fetched past L2). The shared
+// expert (every token, dozens of row tiles) goes in groups of four row tiles,
+// column-tile major inside a group: a run then covers 4 row tiles x 8 weight
+// slices, which share both operands through L2.
 #include <type_traits>
 
 #include "moe_internal.hpp"
@@ -383,8 +386,20 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
   // so the tiles that share a weight slice run at the same pace
   const int nmt = (rows + BM - 1) / BM;
   const int rpt = ((rows + nmt - 1) / nmt + 31) & ~31;
-  t.m0 = (local % nmt) * rpt;  // column-tile major: the row tiles of one weight slice run together
-  t.nt = local / nmt;
+  if (routed) {
+    t.m0 = (local % nmt) * rpt;  // column-tile major: the row tiles of one weight slice run together
+    t.nt = local / nmt;
+  } else {
+    // the shared expert (every token: many row tiles): groups of 4 row tiles,
+    // column-tile major inside a group, so a run of consecutive tiles covers
+    // a few row tiles x a few weight slices and both operands stay in L2
+    const int ncols = (s_pre[p + 1] - s_pre[p]) / nmt;
+    const int g0 = (local / (4 * ncols)) * 4;
+    const int gsz = min(4, nmt - g0);
+    const int idx = local - g0 * ncols;
+    t.m0 = (g0 + idx % gsz) * rpt;
+    t.nt = idx / gsz;
+  }
   t.K = (kMode != 1) ? a.D : t.Hp;
   t.vrows = min(rows - t.m0, rpt);
   if (kMode != 1) {
