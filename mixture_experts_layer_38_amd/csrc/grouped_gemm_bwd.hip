@@ -101,26 +101,45 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
   const uint32_t acol = (uint32_t)(t.m0 + 8 * mg) * 2u, bcol = (uint32_t)(t.n0 + 8 * mg) * 2u;
 
   uint4 sa_[4], sb_[4];
-  auto load_kmajor = [&](const __amdgpu_buffer_rsrc_t& r, const int32_t* map, int ld, uint32_t col, int k0,
-                         uint4 (&v)[4]) __attribute__((always_inline)) {
+  // storage rows of this thread's 4 k-rows of a step (through the row map
+  // for gathered operands), found one step before their data is requested so
+  // the map read and the row read are not a chain of two loads in one step
+  struct KRows {
+    int row[4];
+    int ok;  // bit q: k-row q is inside [k0, k1) (else zero-filled)
+  };
+  auto krows = [&](const int32_t* map, int k0) __attribute__((always_inline)) {
+    KRows r;
+    r.ok = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int k = k0 + 4 * kg + q;
       const bool ok = k < t.k1;
       const int kk = ok ? k : t.k0;
-      const int row = map ? map[kk] : kk;
-      const uint4 x = bload(r, (uint32_t)row * (uint32_t)ld * 2u + col);
-      v[q] = ok ? x : make_uint4(0u, 0u, 0u, 0u);
+      r.row[q] = map ? map[kk] : kk;
+      r.ok |= (ok ? 1 : 0) << q;
+    }
+    return r;
+  };
+  auto load_kmajor = [&](const __amdgpu_buffer_rsrc_t& r, const KRows& kr, int ld, uint32_t col,
+                         uint4 (&v)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 x = bload(r, (uint32_t)kr.row[q] * (uint32_t)ld * 2u + col);
+      v[q] = ((kr.ok >> q) & 1) ? x : make_uint4(0u, 0u, 0u, 0u);
     }
   };
+  KRows kra, krb;  // rows of the next load
   auto load = [&](int k0) __attribute__((always_inline)) {
     if (kAT) {
-      load_kmajor(ra, t.amap, t.lda, acol, k0, sa_);
+      load_kmajor(ra, kra, t.lda, acol, sa_);
+      kra = krows(t.amap, k0 + BK);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) sa_[j] = bload(ra, aoff[j] + (uint32_t)k0 * 2u);
     }
-    load_kmajor(rb, t.bmap, t.ldb, bcol, k0, sb_);
+    load_kmajor(rb, krb, t.ldb, bcol, sb_);
+    krb = krows(t.bmap, k0 + BK);
   };
   // 4 k-rows x 8 columns -> 8 LDS rows of 4 k (8 bytes each)
   auto store_kmajor = [&](uint16_t* base, const uint4 (&v)[4]) __attribute__((always_inline)) {
@@ -158,6 +177,8 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
   const int lr = lane & 31, lk = (lane >> 5) * 8;
   const int nk = (t.k1 - t.k0 + BK - 1) / BK;
   if (nk > 0) {  // an expert without rows: no loads, zero gradient
+    if (kAT) kra = krows(t.amap, t.k0);
+    krb = krows(t.bmap, t.k0);
     load(t.k0);
     store(0);
   }
