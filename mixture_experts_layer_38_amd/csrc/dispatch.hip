@@ -178,11 +178,82 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(DispatchArgs a) {
   }
 }
 
+// Up to 1024 entries (decode-sized batches): the scan and the stable
+// permutation in one workgroup, the 64-entry chunks being its 16 waves and
+// the per-chunk counts living in LDS -- one launch instead of four.
+constexpr int kSmallDispatch = 1024;
+
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
+  __shared__ int32_t cnt[16][kMaxExperts];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  // offsets and item prefixes, as dispatch_scan_kernel
+  const int p = tid;
+  const int rows = (p < a.E) ? a.counts[p] : (p == a.E ? a.shared_rows : 0);
+  const int c0 = (p < a.E) ? rows : 0;
+  const int mblocks = (rows + a.bm - 1) / a.bm;
+  const int it1 = (p <= a.E) ? mblocks * (p < a.E ? a.n1_routed : a.n1_shared) : 0;
+  const int it2 = (p <= a.E) ? mblocks * (p < a.E ? a.n2_routed : a.n2_shared) : 0;
+  int tot0, tot1, tot2;
+  const int off = block_exclusive_scan(c0, &tot0);
+  const int o1 = block_exclusive_scan(it1, &tot1);
+  const int o2 = block_exclusive_scan(it2, &tot2);
+  if (p < a.E) {
+    a.offsets[p] = off;
+    if (a.counts_out) a.counts_out[p] = c0;
+  }
+  if (p == a.E) a.offsets[p] = tot0;
+  if (p <= a.E) {
+    a.pre1[p] = o1;
+    a.pre2[p] = o2;
+  }
+  if (p == a.E + 1) {
+    a.pre1[p] = tot1;
+    a.pre2[p] = tot2;
+  }
+  // per-wave (chunk) expert counts
+  for (int e = lane; e < a.E; e += 64) cnt[w][e] = 0;
+  __syncthreads();
+  const int n = a.T * a.K;
+  const int i = tid;
+  int e = i < n ? a.idx[i] : -1;
+  if (e >= a.E) e = -1;  // out-of-range entries are skipped, as in the histogram
+  if (e >= 0) atomicAdd(&cnt[w][e], 1);
+  __syncthreads();
+  // per expert: the first row of each chunk's entries
+  if (p < a.E) {
+    int acc = off;
+    for (int c = 0; c < 16; ++c) {
+      const int v = cnt[c][p];
+      cnt[c][p] = acc;
+      acc += v;
+    }
+  }
+  __syncthreads();
+  // each wave ranks equal experts among its lanes (lane order = entry order)
+  uint64_t todo = __ballot(e >= 0), mine = 0;
+  while (todo) {
+    const int v = __shfl(e, __ffsll((unsigned long long)todo) - 1);
+    const uint64_t m = __ballot(e == v);
+    if (e == v) mine = m;
+    todo &= ~m;
+  }
+  if (e >= 0) {
+    const int r = cnt[w][e] + __popcll(mine & ((1ull << lane) - 1ull));
+    a.row_token[r] = i / a.K;
+    if (a.row_gate) a.row_gate[r] = a.gate[i];
+    a.slot_row[i] = r;
+  }
+}
+
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
+  const int n = a.T * a.K;
+  if (n > 0 && n <= kSmallDispatch) {
+    hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, s, a);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int n = a.T * a.K;
   if (n == 0) return hipSuccess;
   const int nchunks = (n + kPermChunk - 1) / kPermChunk;
   const int blocks = (nchunks + 3) / 4;

@@ -138,10 +138,11 @@ def test_router_forced_expert_and_all_ties():
 
 def test_dispatch_is_the_stable_permutation():
     """Rows by the definition: (t, k) with expert e goes to offsets[e] plus the
-    number of earlier entries with expert e (several chunks of 512 entries, a
-    skewed case where one expert takes most tokens, and E = 512)."""
+    number of earlier entries with expert e (batches of up to 1024 entries take
+    the one-workgroup path, larger ones the chunked one: both sides of that
+    boundary, a skewed case where one expert takes most tokens, and E = 512)."""
     rng = np.random.default_rng(3)
-    for cfg, Ts in ((SMALL_SIG, (1, 77, 517, 1400)), (ROUTER_E384.with_(E=512, G=16, kg=4), (900,))):
+    for cfg, Ts in ((SMALL_SIG, (1, 77, 170, 171, 517, 1400)), (ROUTER_E384.with_(E=512, G=16, kg=4), (128, 129, 900))):
         layer = M.MoELayer.from_config(cfg.with_(T=max(Ts)))
         for T in Ts:
             for skew in (False, True):
