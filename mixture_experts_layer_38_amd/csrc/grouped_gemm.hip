@@ -90,7 +90,7 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
       const_cast<uint16_t*>(t.a_rows), (short)0, t.a_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(t.w), (short)0, t.w_bytes, 0x00020000);
-  uint32_t voff[kLd];
+  uint32_t voff[kLd / 2];
 #pragma unroll
   for (int j = 0; j < kLd / 2; ++j) {
     const int m = r0 + 64 * j;
@@ -98,25 +98,38 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
     const int row = (kMode != 1 && t.tok != nullptr) ? t.tok[mm] : mm;
     voff[j] = ((uint32_t)row * (uint32_t)t.lda + c8 * 8) * 2u;
   }
-  // Weight (B) rows. bf16: rows r0 + 64*j (rows past D read row 0 instead).
-  // e4m3: thread tid takes B row tid/2, bytes 32*(tid%2) .. +31 of the
-  // 64-byte K slice (two loads), and the block scale of that row.
+  // Weight (B) rows: one VGPR offset for the thread's first row, the other
+  // rows' distance (uniform) in the scalar offset. bf16: rows r0 + 64*j
+  // (gate/up: W_gate rows nt*128 + r0 + {0, 64}, then the same W_up rows;
+  // down rows past D read row nt*256 + r0 instead). e4m3: thread tid takes B
+  // row tid/2, bytes 32*(tid%2) .. +31 of the 64-byte K slice (two loads),
+  // and the block scale of that row.
+  uint32_t vb;
+  uint32_t bd[kLd / 2];
   const float* wsrow = nullptr;
-#pragma unroll
-  for (int j = 0; j < kLd / 2; ++j) {
-    const int b = kW8 ? (tid >> 1) : r0 + 64 * j;
+  if (kW8) {
+    const int b = tid >> 1;
     int wrow = (kMode != 1) ? (b < 128 ? t.nt * 128 + b : t.Hp + t.nt * 128 + b - 128) : t.nt * BN + b;
     if (kMode == 1 && wrow >= t.D) wrow = 0;
-    if (kW8) {
-      voff[kLd / 2 + j] = (uint32_t)wrow * (uint32_t)t.K + 32u * (tid & 1) + 16u * j;
-      if (j == 0) wsrow = t.ws + (size_t)(wrow >> 7) * t.kbn;
-    } else {
-      voff[kLd / 2 + j] = ((uint32_t)wrow * (uint32_t)t.K + c8 * 8) * 2u;
+    vb = (uint32_t)wrow * (uint32_t)t.K + 32u * (tid & 1);
+    wsrow = t.ws + (size_t)(wrow >> 7) * t.kbn;
+#pragma unroll
+    for (int j = 0; j < kLd / 2; ++j) bd[j] = 16u * j;
+  } else {
+    const int wrow = (kMode != 1) ? t.nt * 128 + r0 : t.nt * BN + r0;
+    vb = ((uint32_t)wrow * (uint32_t)t.K + c8 * 8) * 2u;
+#pragma unroll
+    for (int j = 0; j < kLd / 2; ++j) {
+      int dr = (kMode != 1) ? (j & 1) * 64 + (j >> 1) * t.Hp : 64 * j;
+      if (kMode == 1 && t.nt * BN + 64 * j >= t.D) dr = 0;
+      bd[j] = (uint32_t)dr * (uint32_t)t.K * 2u;
     }
   }
   auto gload = [&](int j, int k0) __attribute__((always_inline)) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(j < kLd / 2 ? ra : rb, voff[j],
-                                                                           (j >= kLd / 2 && kW8) ? k0 : k0 * 2, 0));
+    return j < kLd / 2
+               ? __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, voff[j], k0 * 2, 0))
+               : __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rb, vb, (kW8 ? k0 : k0 * 2) + bd[j - kLd / 2], 0));
   };
   constexpr int kLdB = kW8 ? 2 : kLd / 2;  // 16-byte weight loads per thread per K step
 
@@ -135,8 +148,8 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
   for (int c = 0; c < kNC; ++c) bcol[c] = (kMode != 1) ? 128 * c + 32 * wn : 64 * wn + 32 * c;
   const int lr = lane & 31, lk = (lane >> 5) * 8;
 
-  // down GEMM: the tile's gates into LDS for the epilogue
-  if (kMode == 1 && tid < BM) s_gate[tid] = (t.gate != nullptr && tid < t.vrows) ? t.gate[t.m0 + tid] : 1.0f;
+  // down GEMM and recompute: the tile's gates into LDS for the epilogue
+  if (kMode != 0 && tid < BM) s_gate[tid] = (t.gate != nullptr && tid < t.vrows) ? t.gate[t.m0 + tid] : 1.0f;
 
   // A rows (gathered token rows) are loaded two K steps ahead through two
   // register slots; B rows (weights) one step ahead
@@ -226,11 +239,16 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
     // the step body has no branch (and the scheduler sees one region).
     const int knext = (kt + 1 < nk ? kt + 1 : kt) * BK;
     const int knext2 = (kt + 2 < nk ? kt + 2 : nk - 1) * BK;
-#pragma unroll
-    for (int j = 0; j < kLd / 2; ++j) pa[S][j] = gload(j, knext2);
+    // Weight rows of the next step first, token rows of the step after it
+    // last: loads complete in issue order for the wait counter, so waiting
+    // for the weights at the end of this step leaves the token rows in flight.
 #pragma unroll
     for (int j = 0; j < kLdB; ++j) pb[j] = gload(kLd / 2 + j, knext);
     if (kW8) pbs = wsrow[knext >> 7];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kLd / 2; ++j) pa[S][j] = gload(j, knext2);
+    __builtin_amdgcn_sched_barrier(0);
     // substeps 0-2: next fragments interleaved with the MFMAs
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -280,36 +298,47 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
 
   // D layout of the 32x32 MFMA: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
   // column l%32.
-  if (kMode == 0) {
-    // h tile (256 x 128): each lane writes one bf16 per element
+  // A 256 x 128 bf16 tile whose element (m, 32*wn + lr) is val(i, e) in this
+  // lane is staged through LDS (rows of 136 elements), then written as full
+  // 16-byte pieces of its rows (256 contiguous bytes each) to dst (row 0 = the
+  // tile's first row, row length ldc). Rows e, e+1 (e even) of a lane are
+  // adjacent rows of one column; an even lane swaps its row-(e+1) value for
+  // its odd neighbour's row-e value (DPP quad permute 1,0,3,2), so each lane
+  // writes two adjacent columns of one row as one 32-bit word.
+  auto store_tile128 = [&](auto val, uint16_t* dst, int ldc) __attribute__((always_inline)) {
+    constexpr int kLdh = 128 + 8;
+    uint16_t* so = &smem[0][0];
+    const bool odd = lane & 1;
+    __syncthreads();  // the staging area is free (K loop or previous tile done)
 #pragma unroll
     for (int i = 0; i < NRB; ++i) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
+      for (int e = 0; e < 16; e += 2) {
         const int m = 32 * (wm + 2 * i) + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (m >= t.vrows) continue;
-        const float h = silu_fast(acc[i][0][e]) * acc[i][1][e];
-        t.c[(size_t)(t.m0 + m) * t.ldc + t.nt * 128 + 32 * wn + lr] = f32_to_bf16(h);
+        const uint32_t b0 = f32_to_bf16(val(i, e, m)), b1 = f32_to_bf16(val(i, e + 1, m + 1));
+        const uint32_t r = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? b0 : b1), 0xB1, 0xF, 0xF, false);
+        const uint32_t w = odd ? (r | (b1 << 16)) : (b0 | (r << 16));
+        *reinterpret_cast<uint32_t*>(&so[(m + (odd ? 1 : 0)) * kLdh + ((32 * wn + lr) & ~1)]) = w;
       }
     }
+    __syncthreads();
+    const int q = tid & 15;  // 16-byte piece of a row
+#pragma unroll 4
+    for (int r = tid >> 4; r < t.vrows; r += 32)
+      *reinterpret_cast<uint4*>(dst + (size_t)(t.m0 + r) * ldc + 8 * q) =
+          *reinterpret_cast<const uint4*>(&so[r * kLdh + 8 * q]);
+  };
+  if (kMode == 0) {
+    // h tile (256 x 128)
+    store_tile128([&](int i, int e, int) { return silu_fast(acc[i][0][e]) * acc[i][1][e]; },
+                  t.c + t.nt * 128, t.ldc);
   } else if (kMode == 2) {
     // recompute for the backward pass: the pre-activations a = x W_gate^T and
     // u = x W_up^T (one bf16 row of 2*Hp: a then u) and g * SiLU(a) * u
-#pragma unroll
-    for (int i = 0; i < NRB; ++i) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = 32 * (wm + 2 * i) + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (m >= t.vrows) continue;
-        const float av = acc[i][0][e], uv = acc[i][1][e];
-        const int col = t.nt * 128 + 32 * wn + lr;
-        uint16_t* crow = t.c + (size_t)(t.m0 + m) * t.ldc;
-        crow[col] = f32_to_bf16(av);
-        crow[t.Hp + col] = f32_to_bf16(uv);
-        const float g = t.gate != nullptr ? t.gate[t.m0 + m] : 1.0f;
-        t.c2[(size_t)(t.m0 + m) * t.Hp + col] = f32_to_bf16(g * silu_fast(av) * uv);
-      }
-    }
+    store_tile128([&](int i, int e, int) { return acc[i][0][e]; }, t.c + t.nt * 128, t.ldc);
+    store_tile128([&](int i, int e, int) { return acc[i][1][e]; }, t.c + t.Hp + t.nt * 128, t.ldc);
+    store_tile128([&](int i, int e, int m) { return s_gate[m] * silu_fast(acc[i][0][e]) * acc[i][1][e]; },
+                  t.c2 + t.nt * 128, t.Hp);
   } else {
     // y tile (256 x 256): staged through LDS, then written as full 16-byte
     // pieces of each row (the tile's rows are 512 contiguous bytes of y).
