@@ -92,7 +92,7 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
       const_cast<uint8_t*>(t.a_rows), (short)0, t.a_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(t.w), (short)0, t.w_bytes, 0x00020000);
-  uint32_t voa[kLdA], vob[kLdB];
+  uint32_t voa[kLdA];
 #pragma unroll
   for (int j = 0; j < kLdA; ++j) {
     const int m = r0 + 64 * j;
@@ -100,12 +100,16 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
     const int row = (kMode == 0 && t.tok != nullptr) ? t.tok[mm] : mm;
     voa[j] = (uint32_t)row * (uint32_t)t.lda + c16 * 16;
   }
+  // B rows r0 + 64*j: one VGPR offset for row r0, the other rows' distance
+  // (uniform) in the scalar offset (gate/up: W_gate rows nt*128 + r0 +
+  // {0, 64}, then the same W_up rows; down rows past D read row nt*256 + r0)
+  const uint32_t vob = (uint32_t)((kMode == 0) ? t.nt * 128 + r0 : t.nt * BN + r0) * (uint32_t)t.K + c16 * 16;
+  uint32_t bd[kLdB];
 #pragma unroll
   for (int j = 0; j < kLdB; ++j) {
-    const int b = r0 + 64 * j;
-    int wrow = (kMode == 0) ? (b < 128 ? t.nt * 128 + b : t.Hp + t.nt * 128 + b - 128) : t.nt * BN + b;
-    if (kMode == 1 && wrow >= t.D) wrow = 0;
-    vob[j] = (uint32_t)wrow * (uint32_t)t.K + c16 * 16;
+    int dr = (kMode == 0) ? (j & 1) * 64 + (j >> 1) * t.Hp : 64 * j;
+    if (kMode == 1 && t.nt * BN + 64 * j >= t.D) dr = 0;
+    bd[j] = (uint32_t)dr * (uint32_t)t.K;
   }
   // row scales: thread tid stages the scale of A row tid % 128 (threads
   // past 128 write a copy that is never read, so the K loop has no branch)
@@ -118,21 +122,29 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
   }
   // weight scales: gate/up, one 128-row block of W_gate and one of W_up;
   // down, the 128-row block of W_down holding this wave's 64 columns
-  const float* wsr[2];
+  // (read through vector loads one K step ahead: a scalar load in the loop
+  // would make every LDS wait after it wait for the scalar load too)
+  uint32_t wso[2];
   if (kMode == 0) {
-    wsr[0] = t.ws + (size_t)t.nt * t.a_sld;
-    wsr[1] = t.ws + (size_t)(t.Hp / 128 + t.nt) * t.a_sld;
+    wso[0] = (uint32_t)(t.nt * t.a_sld) * 4u;
+    wso[1] = (uint32_t)((t.Hp / 128 + t.nt) * t.a_sld) * 4u;
   } else {
     int cb = (t.nt * BN + 64 * wn) >> 7;
     if (cb * 128 >= t.D) cb = 0;
-    wsr[0] = wsr[1] = t.ws + (size_t)cb * t.a_sld;
+    wso[0] = wso[1] = (uint32_t)(cb * t.a_sld) * 4u;
   }
+  const uint32_t ws_bytes = (uint32_t)(((kMode == 0) ? 2 * t.Hp : t.D) / 128 * t.a_sld) * 4u;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(t.ws), (short)0,
+                                                                      ws_bytes, 0x00020000);
+  auto load_ws = [&](int c, int kb) __attribute__((always_inline)) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 0u, wso[c] + 4u * kb, 0));
+  };
 
   auto gload_a = [&](int j, int k0) __attribute__((always_inline)) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, voa[j], k0, 0));
   };
   auto gload_b = [&](int j, int k0) __attribute__((always_inline)) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, vob[j], k0, 0));
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, vob, k0 + bd[j], 0));
   };
 
   // 16 x 16 output blocks: row block i (rows 16*(wm + 2i) ..), column block
@@ -159,6 +171,7 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
   pas[0] = asrow[0];
 #pragma unroll
   for (int j = 0; j < kLdB; ++j) pb[j] = gload_b(j, 0);
+  float swc[2] = {load_ws(0, 0), load_ws(1, 0)};  // weight scales of the step being multiplied
   {
     const int k1 = nk > 1 ? 1 : 0;
 #pragma unroll
@@ -208,12 +221,19 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
     const int cur = kt & 1;
     const int knext = kt + 1 < nk ? kt + 1 : kt;
     const int knext2 = kt + 2 < nk ? kt + 2 : nk - 1;
+    // weights (and their scales) of the next step first, token rows of the
+    // step after it last: loads complete in issue order for the wait
+    // counter, so waiting for the weights leaves the token rows in flight
+#pragma unroll
+    for (int j = 0; j < kLdB; ++j) pb[j] = gload_b(j, knext * BK);
+    const float sw0 = swc[0], sw1 = swc[1];
+    swc[0] = load_ws(0, knext);
+    swc[1] = load_ws(1, knext);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < kLdA; ++j) pa[S][j] = gload_a(j, knext2 * BK);
     pas[S] = asrow[knext2];
-#pragma unroll
-    for (int j = 0; j < kLdB; ++j) pb[j] = gload_b(j, knext * BK);
-    const float sw0 = wsr[0][kt], sw1 = wsr[1][kt];
+    __builtin_amdgcn_sched_barrier(0);
     // columns 2, 3 are read while columns 0, 1 are multiplied
     read_b(cur, 2);
     read_b(cur, 3);
