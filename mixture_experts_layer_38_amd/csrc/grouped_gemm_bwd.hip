@@ -121,28 +121,33 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
     }
     return r;
   };
+  // k-rows past the end are zero-filled when the data is written to LDS, not
+  // when it arrives, so nothing waits for a load before the step's MFMAs
   auto load_kmajor = [&](const __amdgpu_buffer_rsrc_t& r, const KRows& kr, int ld, uint32_t col,
                          uint4 (&v)[4]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint4 x = bload(r, (uint32_t)kr.row[q] * (uint32_t)ld * 2u + col);
-      v[q] = ((kr.ok >> q) & 1) ? x : make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int q = 0; q < 4; ++q) v[q] = bload(r, (uint32_t)kr.row[q] * (uint32_t)ld * 2u + col);
   };
   KRows kra, krb;  // rows of the next load
+  int oka = 0, okb = 0;  // valid k-rows of the loaded data
   auto load = [&](int k0) __attribute__((always_inline)) {
     if (kAT) {
       load_kmajor(ra, kra, t.lda, acol, sa_);
+      oka = kra.ok;
       kra = krows(t.amap, k0 + BK);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) sa_[j] = bload(ra, aoff[j] + (uint32_t)k0 * 2u);
     }
     load_kmajor(rb, krb, t.ldb, bcol, sb_);
+    okb = krb.ok;
     krb = krows(t.bmap, k0 + BK);
   };
   // 4 k-rows x 8 columns -> 8 LDS rows of 4 k (8 bytes each)
-  auto store_kmajor = [&](uint16_t* base, const uint4 (&v)[4]) __attribute__((always_inline)) {
+  auto store_kmajor = [&](uint16_t* base, const uint4 (&vin)[4], int ok) __attribute__((always_inline)) {
+    uint4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = ((ok >> q) & 1) ? vin[q] : make_uint4(0u, 0u, 0u, 0u);
     const uint32_t w[4][4] = {{v[0].x, v[0].y, v[0].z, v[0].w}, {v[1].x, v[1].y, v[1].z, v[1].w},
                               {v[2].x, v[2].y, v[2].z, v[2].w}, {v[3].x, v[3].y, v[3].z, v[3].w}};
 #pragma unroll
@@ -158,12 +163,12 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
   };
   auto store = [&](int buf) __attribute__((always_inline)) {
     if (kAT) {
-      store_kmajor(&smem[buf][0], sa_);
+      store_kmajor(&smem[buf][0], sa_, oka);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) *reinterpret_cast<uint4*>(&smem[buf][lds_at(r0 + 64 * j, c8 * 8)]) = sa_[j];
     }
-    store_kmajor(&smem[buf][BM * LDK], sb_);
+    store_kmajor(&smem[buf][BM * LDK], sb_, okb);
   };
 
   f32x16 acc[4][2];
@@ -185,8 +190,10 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) load(t.k0 + (kt + 1) * BK);
+    // the next step's operands (the last step reloads its own slice and
+    // writes the idle buffer: no branch, so no wait is forced before the MFMAs)
+    load(t.k0 + (kt + 1 < nk ? kt + 1 : kt) * BK);
+    __builtin_amdgcn_sched_barrier(0);
     const uint16_t* sA = smem[cur];
     const uint16_t* sB = smem[cur] + BM * LDK;
 #pragma unroll
@@ -201,7 +208,8 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
 #pragma unroll
         for (int c = 0; c < 2; ++c) acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[c], acc[i][c], 0, 0, 0);
     }
-    if (more) store(cur ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+    store(cur ^ 1);
     __syncthreads();
   }
 
