@@ -29,7 +29,10 @@
 // activations of group g+1 -- of this item, or the first group of the
 // workgroup's next item -- are requested before group g is multiplied; the
 // activations go through registers into the other half of the LDS ring, with
-// one barrier per group. The problem tables (item prefix, expert row offsets)
+// one barrier per group. The activations are requested before the weights,
+// so the end-of-group wait for them leaves the weights in flight until the
+// next group multiplies them, by which time the group after that is already
+// requested. The problem tables (item prefix, expert row offsets)
 // are cached in LDS, so finding an item's problem costs no global round trips.
 #include <type_traits>
 
@@ -152,16 +155,27 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(ExpertGemmArgs a) {
   float sc[2][kU];
   uint4 pa[kU];  // this thread's activation pieces of the next group
 
+  // The activation pieces are requested first and the weights last: loads
+  // retire in issue order for the wait counter, so the wait for the
+  // activations at the end of a group leaves the weights in flight, and the
+  // following group's request goes out before they are waited for.
   auto load_group = [&](const Item& it, int g, uint4 (&w)[kU][kWv], float (&s)[kU]) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int c = min(g * kU + u, it.nch - 1);  // past the end: a valid chunk, unused
+      const uint4 v = *reinterpret_cast<const uint4*>(it.aptr + (size_t)c * kST_KC);
+      pa[u] = it.aval ? v : make_uint4(0, 0, 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int c = min(g * kU + u, it.nch - 1);
 #pragma unroll
       for (int j = 0; j < kWv; ++j)
         w[u][j] = *reinterpret_cast<const uint4*>(it.wptr + (size_t)c * kST_KC * welt + 16 * j);
       s[u] = kFp8 ? it.sptr[c] : 1.0f;
-      pa[u] = it.aval ? *reinterpret_cast<const uint4*>(it.aptr + (size_t)c * kST_KC) : make_uint4(0, 0, 0, 0);
     }
+    __builtin_amdgcn_sched_barrier(0);
   };
   // activation pieces -> LDS ring half `set`
   auto store_act = [&](int set) __attribute__((always_inline)) {
@@ -210,15 +224,13 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(ExpertGemmArgs a) {
     // park the requested activations in the other ring half
     auto group = [&](int g, auto gs_c) __attribute__((always_inline)) {
       constexpr int GS = decltype(gs_c)::value;
-      bool req = true;
-      if (g + 1 < ngr) {
-        load_group(cur, g + 1, wv[GS ^ 1], sc[GS ^ 1]);
-      } else if (has_next) {
-        nxt = setup_item<kFp8, kMode>(a, s_pre, s_off, next_item);
-        load_group(nxt, 0, wv[GS ^ 1], sc[GS ^ 1]);
-      } else {
-        req = false;
-      }
+      // one unconditional request (a branch around the loads would make the
+      // waits after it drain them): the next group of this item, else the
+      // next item's first group, else this group again (unused)
+      const bool in_item = g + 1 < ngr;
+      if (!in_item && has_next) nxt = setup_item<kFp8, kMode>(a, s_pre, s_off, next_item);
+      const bool req = in_item || has_next;
+      load_group(in_item ? cur : nxt, in_item ? g + 1 : (has_next ? 0 : g), wv[GS ^ 1], sc[GS ^ 1]);
 #pragma unroll
       for (int u = 0; u < kU; ++u)
         if (g * kU + u < cur.nch) chunk(wv[GS][u], sc[GS][u], &s_act[(aset * kU + u) * kASlot]);
