@@ -73,69 +73,76 @@ hipError_t launch_simple_down_f32(const ExpertGemmArgs& a, int TK, hipStream_t s
 
 // out[t] = [x[t]] + S[t] + sum_{k<K} Y[slot_row[t*K+k]], fp32, k in order.
 // One workgroup per token, 8 consecutive columns per thread and step.
+namespace {
+// 8 consecutive values of one row, as loaded (bf16: one 16-byte piece;
+// fp32: two)
+template <bool kBf16>
+struct Raw8 {
+  uint4 u[kBf16 ? 1 : 2];
+};
+template <bool kBf16>
+__device__ __forceinline__ Raw8<kBf16> load8(const void* base, size_t row, int D, int d0) {
+  Raw8<kBf16> r;
+  if (kBf16) {
+    r.u[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + row * D + d0);
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + row * D + d0);
+    r.u[0] = p[0];
+    r.u[1] = p[1];
+  }
+  return r;
+}
+// acc += v, or += -0.0 (which leaves every value, signed zeros included,
+// unchanged) when !use: the load was issued regardless, so no wait sits
+// behind a branch
+template <bool kBf16>
+__device__ __forceinline__ void add8(float (&acc)[8], const Raw8<kBf16>& v, bool use) {
+  if (kBf16) {
+    const uint32_t m = use ? 0xFFFFFFFFu : 0x80008000u, z = use ? 0u : 0x80008000u;
+    const uint32_t w[4] = {(v.u[0].x & m) | z, (v.u[0].y & m) | z, (v.u[0].z & m) | z, (v.u[0].w & m) | z};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[2 * i] += __uint_as_float(w[i] << 16);
+      acc[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
+    }
+  } else {
+    const uint32_t w[8] = {v.u[0].x, v.u[0].y, v.u[0].z, v.u[0].w, v.u[1].x, v.u[1].y, v.u[1].z, v.u[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += __uint_as_float(use ? w[i] : 0x80000000u);
+  }
+}
+}  // namespace
+
 template <bool kYBf16, bool kXBf16, bool kOutBf16>
 __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int t = blockIdx.x;
   int rows[kMaxTopK];
 #pragma unroll
   for (int k = 0; k < kMaxTopK; ++k) rows[k] = (k < a.K) ? a.slot_row[(size_t)t * a.K + k] : 0;
+  const bool has_shared = a.y_shared != nullptr;
+  // a source that is absent reads a valid row instead (never added)
+  const void* sbase = has_shared ? a.y_shared : a.y_routed;
+  const size_t srow = has_shared ? (size_t)t : (size_t)rows[0];
   for (int d0 = threadIdx.x * 8; d0 < a.D; d0 += blockDim.x * 8) {
+    // every load of this step first (the residual, the shared row, up to 8
+    // routed rows), then the adds in the fixed order
+    const Raw8<kXBf16> xv = load8<kXBf16>(a.x, (size_t)t, a.D, d0);
+    const Raw8<kYBf16> sv = load8<kYBf16>(sbase, srow, a.D, d0);
+    Raw8<kYBf16> v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = load8<kYBf16>(a.y_routed, (size_t)rows[k], a.D, d0);
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    if (a.add_residual) {
-      if (kXBf16) {
-        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.x) + (size_t)t * a.D + d0);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    if (a.add_residual) add8<kXBf16>(acc, xv, true);
+    add8<kYBf16>(acc, sv, has_shared);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] = __uint_as_float(w[i] << 16);
-          acc[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-        }
-      } else {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.x) + (size_t)t * a.D + d0);
-        const float4 u = p[0], v = p[1];
-        acc[0] = u.x; acc[1] = u.y; acc[2] = u.z; acc[3] = u.w;
-        acc[4] = v.x; acc[5] = v.y; acc[6] = v.z; acc[7] = v.w;
-      }
-    }
-    auto add_row = [&](const void* base, size_t row) {
-      if (kYBf16) {
-        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + row * a.D + d0);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    for (int k = 0; k < 8; ++k) add8<kYBf16>(acc, v[k], k < a.K);
+    if (a.K > 8) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += __uint_as_float(w[i] << 16);
-          acc[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
-        }
-      } else {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + row * a.D + d0);
-        const float4 u = p[0], v = p[1];
-        acc[0] += u.x; acc[1] += u.y; acc[2] += u.z; acc[3] += u.w;
-        acc[4] += v.x; acc[5] += v.y; acc[6] += v.z; acc[7] += v.w;
-      }
-    };
-    if (a.y_shared) add_row(a.y_shared, (size_t)t);
-    if (kYBf16) {
-      // every row load in flight before the adds, which still run in k order
-      uint4 v[kMaxTopK];
+      for (int k = 8; k < kMaxTopK; ++k) v[k - 8] = load8<kYBf16>(a.y_routed, (size_t)rows[k], a.D, d0);
 #pragma unroll
-      for (int k = 0; k < kMaxTopK; ++k)
-        if (k < a.K)
-          v[k] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.y_routed) + (size_t)rows[k] * a.D + d0);
-#pragma unroll
-      for (int k = 0; k < kMaxTopK; ++k) {
-        if (k < a.K) {
-          const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[2 * i] += __uint_as_float(w[i] << 16);
-            acc[2 * i + 1] += __uint_as_float(w[i] & 0xFFFF0000u);
-          }
-        }
-      }
-    } else {
-      for (int k = 0; k < a.K; ++k) add_row(a.y_routed, (size_t)rows[k]);
+      for (int k = 8; k < kMaxTopK; ++k) add8<kYBf16>(acc, v[k - 8], k < a.K);
     }
     if (kOutBf16) {
       uint32_t w[4];
