@@ -178,17 +178,34 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(DispatchArgs a) {
   }
 }
 
-// Up to 1024 entries (decode-sized batches): the scan and the stable
-// permutation in one workgroup, the 64-entry chunks being its 16 waves and
-// the per-chunk counts living in LDS -- one launch instead of four.
-constexpr int kSmallDispatch = 1024;
+// Up to kSmallDispatch (1024) entries (decode-sized batches): the expert
+// counts, the scan and the stable permutation in one workgroup, the 64-entry
+// chunks being its 16 waves and the per-chunk counts living in LDS -- one
+// launch instead of six (counts zeroed, histogram, scan, chunk counts, chunk
+// scan, placement). The counts are written to a.counts for later readers.
+static_assert(kSmallDispatch == 16 * 64, "one 64-entry chunk per wave of a 1024-thread block");
 
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
   __shared__ int32_t cnt[16][kMaxExperts];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  // offsets and item prefixes, as dispatch_scan_kernel
+  // per-wave (chunk) expert counts
+  for (int e = lane; e < a.E; e += 64) cnt[w][e] = 0;
+  __syncthreads();
+  const int n = a.T * a.K;
+  const int i = tid;
+  int e = i < n ? a.idx[i] : -1;
+  if (e >= a.E) e = -1;  // out-of-range entries are skipped, as in the histogram
+  if (e >= 0) atomicAdd(&cnt[w][e], 1);
+  __syncthreads();
+  // offsets and item prefixes, as dispatch_scan_kernel, on the counts summed
+  // over the chunks
   const int p = tid;
-  const int rows = (p < a.E) ? a.counts[p] : (p == a.E ? a.shared_rows : 0);
+  int ecount = 0;
+  if (p < a.E) {
+    for (int c = 0; c < 16; ++c) ecount += cnt[c][p];
+    a.counts[p] = ecount;
+  }
+  const int rows = (p < a.E) ? ecount : (p == a.E ? a.shared_rows : 0);
   const int c0 = (p < a.E) ? rows : 0;
   const int mblocks = (rows + a.bm - 1) / a.bm;
   const int it1 = (p <= a.E) ? mblocks * (p < a.E ? a.n1_routed : a.n1_shared) : 0;
@@ -210,15 +227,6 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
     a.pre1[p] = tot1;
     a.pre2[p] = tot2;
   }
-  // per-wave (chunk) expert counts
-  for (int e = lane; e < a.E; e += 64) cnt[w][e] = 0;
-  __syncthreads();
-  const int n = a.T * a.K;
-  const int i = tid;
-  int e = i < n ? a.idx[i] : -1;
-  if (e >= a.E) e = -1;  // out-of-range entries are skipped, as in the histogram
-  if (e >= 0) atomicAdd(&cnt[w][e], 1);
-  __syncthreads();
   // per expert: the first row of each chunk's entries
   if (p < a.E) {
     int acc = off;
@@ -247,7 +255,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
 
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   const int n = a.T * a.K;
-  if (n > 0 && n <= kSmallDispatch) {
+  if (small_dispatch(n)) {
     hipLaunchKernelGGL(dispatch_small_kernel, dim3(1), dim3(1024), 0, s, a);
     return hipGetLastError();
   }

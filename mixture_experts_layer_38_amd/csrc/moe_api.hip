@@ -363,6 +363,7 @@ moe_status moe_router_forward(moe_cfg* c, const void* x, int T, const float* gat
   r.rsf = c->p.routed_scaling_factor;
   r.num_cus = c->num_cus;
   r.w_split = c->w_split;
+  r.hist = 1;
   hipError_t e = launch_router(r, s);
   return e == hipSuccess ? MOE_OK : hip_fail(c, e);
 }
@@ -398,8 +399,11 @@ moe_status moe_dispatch_forward(moe_cfg* c, const int32_t* topk_idx, int T, int3
   if (!offsets || (T > 0 && (!topk_idx || !row_token || !slot_row))) return MOE_ERR_INVALID_ARG;
   if (!on_cfg_device(c)) return MOE_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_histogram(topk_idx, c->counts, T * c->p.top_k, c->p.n_routed, s);
-  if (e != hipSuccess) return hip_fail(c, e);
+  hipError_t e = hipSuccess;
+  if (!small_dispatch(T * c->p.top_k)) {  // the one-workgroup dispatch counts the entries itself
+    e = launch_histogram(topk_idx, c->counts, T * c->p.top_k, c->p.n_routed, s);
+    if (e != hipSuccess) return hip_fail(c, e);
+  }
   DispatchArgs d{};
   d.idx = topk_idx; d.gate = nullptr; d.counts = c->counts; d.counts_out = nullptr;
   d.offsets = offsets; d.chunk_base = c->chunk_base; d.row_token = row_token; d.row_gate = nullptr;
@@ -448,6 +452,7 @@ moe_status moe_layer_forward(moe_cfg* c, const void* x, int T, const float* gate
   r.rsf = p.routed_scaling_factor;
   r.num_cus = c->num_cus;
   r.w_split = c->w_split;
+  r.hist = !small_dispatch(T * p.top_k);  // the one-workgroup dispatch counts the entries itself
   if ((e = launch_router(r, s)) != hipSuccess) return hip_fail(c, e);
   mark(c, 1, s);
 
@@ -566,6 +571,7 @@ moe_status moe_layer_backward(moe_cfg* c, const void* x, int T, const float* gat
   r.rsf = p.routed_scaling_factor;
   r.num_cus = c->num_cus;
   r.w_split = c->w_split;
+  r.hist = !small_dispatch(T * p.top_k);  // the one-workgroup dispatch counts the entries itself
   if ((e = launch_router(r, s)) != hipSuccess) return hip_fail(c, e);
   DispatchArgs d{};
   d.idx = c->idx; d.gate = c->gate; d.counts = c->counts; d.counts_out = nullptr;

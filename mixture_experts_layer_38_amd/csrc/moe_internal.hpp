@@ -167,9 +167,14 @@ struct RouterArgs {
   int num_cus;
   int splits;           // set by launch_router
   uint16_t* w_split;    // [3][E][D] bf16 planes of gate_w (bf16 activations), or null
+  int hist;             // 1: also count the selections into counts (else the dispatch does)
 };
 // from this many tokens on, bf16 activations take the bf16x3 logits kernel
 constexpr int kRouterX3MinTokens = 512;
+// Up to this many (token, slot) entries the dispatch runs in one workgroup
+// and derives the expert counts itself (the router's histogram is skipped).
+constexpr int kSmallDispatch = 1024;
+inline bool small_dispatch(int n) { return n > 0 && n <= kSmallDispatch; }
 // number of partial-logit planes launch_router uses for T tokens
 int router_splits(int T, int D, int E, int num_cus);
 hipError_t launch_router(const RouterArgs& a, hipStream_t s);

@@ -433,7 +433,7 @@ hipError_t launch_router(const RouterArgs& a0, hipStream_t s) {
   else
     hipLaunchKernelGGL(router_select_kernel<kMaxExperts / kWave>, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  return launch_histogram(a.idx, a.counts, a.T * a.K, a.E, s);
+  return a.hist ? launch_histogram(a.idx, a.counts, a.T * a.K, a.E, s) : hipSuccess;
 }
 
 }  // namespace moe
