@@ -35,6 +35,14 @@ namespace {
 constexpr int BM = 256, BN = 256, BK = 64, LDK = BK + 8;  // LDS row: 72 bf16 (144 bytes)
 constexpr int kRowsL = BM + BN;
 constexpr int kThreads = 512;
+// The four expert GEMMs hand tiles out in runs of kRunB consecutive tile
+// indices per XCD (block b runs on XCD b % 8; run r goes to XCD r % 8), so
+// the tiles that share operand slices share that XCD's L2.
+constexpr int kRunB = 32;
+__device__ __forceinline__ int run_tile(int bid) {
+  const int slot = bid >> 3;
+  return ((slot / kRunB) * 8 + (bid & 7)) * kRunB + slot % kRunB;
+}
 
 enum : int { kDgradH = 0, kDgradX = 1, kWgradD = 2, kWgradGU = 3, kRouterW = 4, kRouterX = 5 };
 
@@ -301,7 +309,7 @@ template <int kMode>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][kRowsL * LDK];
   float* s_red = reinterpret_cast<float*>(&smem[0][0]);  // epilogue only (8 x BM), after the K loop
-  const int tile = blockIdx.x;
+  const int tile = (kMode <= kWgradGU) ? run_tile(blockIdx.x) : (int)blockIdx.x;
   BwdTile t;
   t.au = nullptr; t.gate = nullptr; t.part = nullptr; t.npart = 0; t.Hp = 0;
   t.amap = nullptr; t.bmap = nullptr;
@@ -367,9 +375,13 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
     const int M = routed ? Mr : Ms, N = routed ? Nr : Ns, Hp = routed ? a.H : a.Hs;
     const int rows = routed ? a.offsets[p + 1] - a.offsets[p] : a.T;
     const int rb = routed ? a.offsets[p] : 0;
-    const int nnt = cdiv(N, BN);
-    t.m0 = (local / nnt) * BM;
-    t.n0 = (local % nnt) * BN;
+    // groups of four m-tiles, column-major inside a group: a run of 32
+    // consecutive tiles covers 4 m-slices x 8 n-slices of the operands
+    const int nmt = cdiv(M, BM), nnt = cdiv(N, BN);
+    const int g0 = (local / (4 * nnt)) * 4, gsz = min(4, nmt - g0);
+    const int idx = local - g0 * nnt;
+    t.m0 = (g0 + idx % gsz) * BM;
+    t.n0 = (idx / gsz) * BN;
     t.M = M;
     t.N = N;
     t.K = rows;
@@ -607,6 +619,8 @@ __global__ __launch_bounds__(256) void planes_sum_kernel(const float* __restrict
 }
 
 int grid_for(size_t n) { return (int)std::min<size_t>((n + 255) / 256, 8192); }
+// blocks covering every tile index below n under the run mapping
+int run_grid(int n) { return cdiv(cdiv(n, kRunB), 8) * 8 * kRunB; }
 
 }  // namespace
 
@@ -628,20 +642,20 @@ hipError_t launch_layer_backward(const BwdArgs& a, hipStream_t s) {
   BwdArgs b = a;
   b.pre = a.pre_h;
   const int tiles_h = (int)(mblk * cdiv(a.H, BN) + mblk_s * cdiv(a.Hs, BN));
-  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kDgradH>, dim3(tiles_h), dim3(kThreads), 0, s, b);
+  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kDgradH>, dim3(run_grid(tiles_h)), dim3(kThreads), 0, s, b);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // router backward needs every dL/dg partial
   hipLaunchKernelGGL(router_bwd_kernel, dim3((a.T + 3) / 4), dim3(256), 0, s, a.logits, a.idx, a.slot_row, a.part,
                      cdiv(a.H, BN), a.T, a.E, a.Ep, a.K, a.score_fn, a.norm, a.rsf, a.dlogit);
   b.pre = a.pre_x;
   const int tiles_x = (int)(mblk * cdiv(a.D, BN) + mblk_s * cdiv(a.D, BN));
-  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kDgradX>, dim3(tiles_x), dim3(kThreads), 0, s, b);
+  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kDgradX>, dim3(run_grid(tiles_x)), dim3(kThreads), 0, s, b);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int tiles_wd = a.E * cdiv(a.D, BM) * cdiv(a.H, BN) + (a.Hs > 0 ? cdiv(a.D, BM) * cdiv(a.Hs, BN) : 0);
-  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kWgradD>, dim3(tiles_wd), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kWgradD>, dim3(run_grid(tiles_wd)), dim3(kThreads), 0, s, a);
   const int tiles_wgu =
       a.E * cdiv(2 * a.H, BM) * cdiv(a.D, BN) + (a.Hs > 0 ? cdiv(2 * a.Hs, BM) * cdiv(a.D, BN) : 0);
-  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kWgradGU>, dim3(tiles_wgu), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kWgradGU>, dim3(run_grid(tiles_wgu)), dim3(kThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int tiles_rw = cdiv(a.Ep, BM) * cdiv(a.D, BN) * a.splits;
   hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kRouterW>, dim3(tiles_rw), dim3(kThreads), 0, s, a);
