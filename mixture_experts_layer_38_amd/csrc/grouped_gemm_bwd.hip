@@ -283,6 +283,42 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
       for (int q = 0; q < 8; ++q) v += s_red[q * BM + tid];
       t.part[(size_t)(t.m0 + tid) * t.npart + t.n0 / BN] = v;
     }
+  } else if (kMode == kDgradX) {
+    // bf16 tile staged through LDS (rows of 264 elements over both buffers),
+    // then written as full 16-byte pieces of each 512-byte row. Rows e, e+1
+    // (e even) of a lane are adjacent rows of one column; an even lane swaps
+    // its row-(e+1) value for its odd neighbour's row-e value (DPP quad
+    // permute 1,0,3,2), so each lane writes two adjacent columns of one row
+    // as one 32-bit word.
+    constexpr int kLdo = BN + 8;
+    static_assert(BM * kLdo <= 2 * kRowsL * LDK, "staging tile fits the two LDS buffers");
+    uint16_t* so = &smem[0][0];
+    const bool odd = lane & 1;
+    __syncthreads();  // every wave is past its last fragment reads
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          const int r = 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          const uint32_t b0 = f32_to_bf16(acc[i][c][e]), b1 = f32_to_bf16(acc[i][c][e + 1]);
+          const uint32_t x = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? b0 : b1), 0xB1, 0xF, 0xF, false);
+          const uint32_t w = odd ? (x | (b1 << 16)) : (b0 | (x << 16));
+          const int col = 64 * wn + 32 * c + lr;
+          *reinterpret_cast<uint32_t*>(&so[(r + (odd ? 1 : 0)) * kLdo + (col & ~1)]) = w;
+        }
+    __syncthreads();
+    const int q = tid & 31;  // 16-byte piece of a row
+    const int n = t.n0 + 8 * q;
+    if (n < t.N) {  // N % 128 == 0: a piece is wholly inside or outside
+#pragma unroll 4
+      for (int r = tid >> 5; r < BM; r += 16) {
+        if (t.m0 + r >= t.M) break;
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(t.c) + (size_t)(t.m0 + r) * t.ldc + n) =
+            *reinterpret_cast<const uint4*>(&so[r * kLdo + 8 * q]);
+      }
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -294,10 +330,7 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
         for (int e = 0; e < 16; ++e) {
           const int m = t.m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
           if (m >= t.M) continue;
-          if (kMode == kDgradX)
-            static_cast<uint16_t*>(t.c)[(size_t)m * t.ldc + n] = f32_to_bf16(acc[i][c][e]);
-          else
-            static_cast<float*>(t.c)[(size_t)m * t.ldc + n] = acc[i][c][e];
+          static_cast<float*>(t.c)[(size_t)m * t.ldc + n] = acc[i][c][e];
         }
       }
   }
