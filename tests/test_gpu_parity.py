@@ -175,6 +175,18 @@ def test_layer_small(cfg, path):
     _check_layer(inp, path=path)
 
 
+@pytest.mark.parametrize("K,path", [(1, "grouped"), (12, "grouped"), (16, "grouped"), (16, "stream")])
+def test_layer_top_k_extremes(K, path):
+    """The smallest and largest accepted top-K (1 and 16; 12 in between):
+    the selection beyond 8 slots, the dispatch at T*K around the
+    one-workgroup limit, and the combine's second group of row loads."""
+    T = 64 if path == "stream" else 300
+    cfg = MI.LayerConfig(f"topk{K}", T=T, D=256, E=64, H=128, G=8, kg=4, K=K, score_fn="sigmoid",
+                         bias="normal", norm=True, rsf=2.5, Hs=128, act="bf16", weight="bf16", bias_std=0.05)
+    inp = MI.make_layer(cfg, DEV)
+    _check_layer(inp, path=path)
+
+
 @pytest.mark.parametrize("path", ["stream", "grouped"])
 def test_layer_fp8_every_code(path):
     """Expert weights drawn uniformly over all 254 finite e4m3 codes (tiny,
