@@ -30,9 +30,12 @@
 // Both operands are staged through two LDS buffers (rows padded to 144 bytes so
 // that the 16-byte fragment reads of consecutive rows hit distinct banks): the
 // weight rows of the next K step, and the token rows of the step after it
-// (two register slots: gathered rows are the slower ones to arrive), are
-// loaded into registers while the current step is multiplied, and the next
-// step is written to the other buffer; one barrier per K step.
+// (two register slots), are loaded into registers while the current step is
+// multiplied, and the next step is written to the other buffer; one barrier
+// per K step. The loads are spread between the MFMAs of the first three
+// substeps (weights first) rather than issued together: a wave whose
+// request cannot enter a full memory queue stalls, and with it the MFMAs
+// behind it in program order.
 // Blocks are mapped so that runs of consecutive tiles land on one XCD and its
 // L2, with runs spread round-robin over the XCDs. Tiles are ordered
 // column-tile major, and an expert's rows are split evenly (in 32-row blocks)
@@ -239,37 +242,45 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
     // the step body has no branch (and the scheduler sees one region).
     const int knext = (kt + 1 < nk ? kt + 1 : kt) * BK;
     const int knext2 = (kt + 2 < nk ? kt + 2 : nk - 1) * BK;
-    // Weight rows of the next step first, token rows of the step after it
-    // last: loads complete in issue order for the wait counter, so waiting
-    // for the weights at the end of this step leaves the token rows in flight.
-#pragma unroll
-    for (int j = 0; j < kLdB; ++j) pb[j] = gload(kLd / 2 + j, knext);
-    if (kW8) pbs = wsrow[knext >> 7];
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < kLd / 2; ++j) pa[S][j] = gload(j, knext2);
-    __builtin_amdgcn_sched_barrier(0);
-    // substeps 0-2: next fragments interleaved with the MFMAs
+    // Weight rows of the next step (spread over substep 0), token rows of
+    // the step after it (spread over substep 1): loads complete in issue
+    // order for the wait counter, so waiting for the weights at the end of
+    // this step leaves the token rows in flight; spreading the requests keeps
+    // the matrix instructions behind them from waiting on a full queue.
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
+      if (s == 0) {
+#pragma unroll
+        for (int j = 0; j < kLdB; ++j) pb[j] = gload(kLd / 2 + j, knext);
+        if (kW8) pbs = wsrow[knext >> 7];
+      } else {
+#pragma unroll
+        for (int j = 0; j < kLd / 4; ++j) pa[S][j] = gload(j, knext2);
+      }
       read_frags(smem[cur], 16 * (s + 1), (s + 1) & 1);
       mfmas(s & 1);
+      constexpr int nv = (kLdB > kLd / 2 ? kLdB : kLd / 2);
 #pragma unroll
       for (int q = 0; q < p1; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (q < nv) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x020, nv > p1 ? nv - p1 : 0, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, nr - p1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, nm - p1, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // substep 2: last fragments
+    // substep 2: last fragments, the second half of the token rows
+#pragma unroll
+    for (int j = kLd / 4; j < kLd / 2; ++j) pa[S][j] = gload(j, knext2);
     read_frags(smem[cur], 48, 1);
     mfmas(0);
 #pragma unroll
     for (int q = 0; q < p1; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (q < kLd / 4) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, nr - p1, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, nm - p1, 0);
