@@ -116,7 +116,18 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
     int row[4];
     int ok;  // bit q: k-row q is inside [k0, k1) (else zero-filled)
   };
-  auto krows = [&](const int32_t* map, int k0) __attribute__((always_inline)) {
+  // The row maps are read through buffer resources, an absent map through
+  // one of zero length (its reads return 0 and are replaced by the identity),
+  // so the reads are unconditional: a branch around them would split the
+  // step's scheduling region.
+  const bool has_amap = t.amap != nullptr, has_bmap = t.bmap != nullptr;
+  const __amdgpu_buffer_rsrc_t rma = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(has_amap ? t.amap : reinterpret_cast<const int32_t*>(t.a)), (short)0,
+      has_amap ? (uint32_t)t.k1 * 4u : 0u, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rmb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(has_bmap ? t.bmap : reinterpret_cast<const int32_t*>(t.b)), (short)0,
+      has_bmap ? (uint32_t)t.k1 * 4u : 0u, 0x00020000);
+  auto krows = [&](const __amdgpu_buffer_rsrc_t& rm, bool has_map, int k0) __attribute__((always_inline)) {
     KRows r;
     r.ok = 0;
 #pragma unroll
@@ -124,7 +135,8 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
       const int k = k0 + 4 * kg + q;
       const bool ok = k < t.k1;
       const int kk = ok ? k : t.k0;
-      r.row[q] = map ? map[kk] : kk;
+      const int v = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, (uint32_t)kk * 4u, 0, 0);
+      r.row[q] = has_map ? v : kk;
       r.ok |= (ok ? 1 : 0) << q;
     }
     return r;
@@ -138,18 +150,20 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
   };
   KRows kra, krb;  // rows of the next load
   int oka = 0, okb = 0;  // valid k-rows of the loaded data
-  auto load = [&](int k0) __attribute__((always_inline)) {
+  auto load_a = [&](int k0) __attribute__((always_inline)) {
     if (kAT) {
       load_kmajor(ra, kra, t.lda, acol, sa_);
       oka = kra.ok;
-      kra = krows(t.amap, k0 + BK);
+      kra = krows(rma, has_amap, k0 + BK);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) sa_[j] = bload(ra, aoff[j] + (uint32_t)k0 * 2u);
     }
+  };
+  auto load_b = [&](int k0) __attribute__((always_inline)) {
     load_kmajor(rb, krb, t.ldb, bcol, sb_);
     okb = krb.ok;
-    krb = krows(t.bmap, k0 + BK);
+    krb = krows(rmb, has_bmap, k0 + BK);
   };
   // 4 k-rows x 8 columns -> 8 LDS rows of 4 k (8 bytes each)
   auto store_kmajor = [&](uint16_t* base, const uint4 (&vin)[4], int ok) __attribute__((always_inline)) {
@@ -190,22 +204,27 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
   const int lr = lane & 31, lk = (lane >> 5) * 8;
   const int nk = (t.k1 - t.k0 + BK - 1) / BK;
   if (nk > 0) {  // an expert without rows: no loads, zero gradient
-    if (kAT) kra = krows(t.amap, t.k0);
-    krb = krows(t.bmap, t.k0);
-    load(t.k0);
+    if (kAT) kra = krows(rma, has_amap, t.k0);
+    krb = krows(rmb, has_bmap, t.k0);
+    load_a(t.k0);
+    load_b(t.k0);
     store(0);
   }
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     // the next step's operands (the last step reloads its own slice and
-    // writes the idle buffer: no branch, so no wait is forced before the MFMAs)
-    load(t.k0 + (kt + 1 < nk ? kt + 1 : kt) * BK);
-    __builtin_amdgcn_sched_barrier(0);
+    // writes the idle buffer: no branch, so no wait is forced before the
+    // MFMAs), A's requests spread between the MFMAs of substep 0 and B's
+    // between those of substep 1: a request that cannot enter a full memory
+    // queue stalls the wave, and the MFMAs behind it with it
+    const int kn = t.k0 + (kt + 1 < nk ? kt + 1 : kt) * BK;
     const uint16_t* sA = smem[cur];
     const uint16_t* sB = smem[cur] + BM * LDK;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 16) {
+      if (kk == 0) load_a(kn);
+      if (kk == 16) load_b(kn);
       bf16x8 fa[4], fb[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(&sA[lds_at(128 * wm + 32 * i + lr, kk + lk)]);
@@ -215,8 +234,15 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int c = 0; c < 2; ++c) acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[c], acc[i][c], 0, 0, 0);
+      if (kk < 32) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
     store(cur ^ 1);
     __syncthreads();
   }
