@@ -211,6 +211,18 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
     store(0);
   }
   __syncthreads();
+  // Fragments are double-buffered across the four 16-wide substeps: the LDS
+  // reads of substep s+1 are issued before the MFMAs of substep s.
+  bf16x8 fa[2][4], fb[2][2];
+  auto read_frags = [&](const uint16_t* sbuf, int kk, int slot) __attribute__((always_inline)) {
+    const uint16_t* sA = sbuf;
+    const uint16_t* sB = sbuf + BM * LDK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[slot][i] = *reinterpret_cast<const bf16x8*>(&sA[lds_at(128 * wm + 32 * i + lr, kk + lk)]);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) fb[slot][c] = *reinterpret_cast<const bf16x8*>(&sB[lds_at(64 * wn + 32 * c + lr, kk + lk)]);
+  };
+  if (nk > 0) read_frags(smem[0], 0, 0);
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     // the next step's operands (the last step reloads its own slice and
@@ -219,32 +231,36 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
     // between those of substep 1: a request that cannot enter a full memory
     // queue stalls the wave, and the MFMAs behind it with it
     const int kn = t.k0 + (kt + 1 < nk ? kt + 1 : kt) * BK;
-    const uint16_t* sA = smem[cur];
-    const uint16_t* sB = smem[cur] + BM * LDK;
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      if (kk == 0) load_a(kn);
-      if (kk == 16) load_b(kn);
-      bf16x8 fa[4], fb[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) fa[i] = *reinterpret_cast<const bf16x8*>(&sA[lds_at(128 * wm + 32 * i + lr, kk + lk)]);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) fb[c] = *reinterpret_cast<const bf16x8*>(&sB[lds_at(64 * wn + 32 * c + lr, kk + lk)]);
+    for (int s = 0; s < 4; ++s) {
+      if (s == 0) load_a(kn);
+      if (s == 1) load_b(kn);
+      if (s < 3) read_frags(smem[cur], 16 * (s + 1), (s + 1) & 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int c = 0; c < 2; ++c) acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[c], acc[i][c], 0, 0, 0);
-      if (kk < 32) {
+        for (int c = 0; c < 2; ++c)
+          acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][c], acc[i][c], 0, 0, 0);
+      if (s < 2) {
+        // (MFMA, LDS read, global load) x 6, then (MFMA, global load) x 2
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if (q < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+      } else if (s == 2) {
+#pragma unroll
+        for (int q = 0; q < 6; ++q) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     store(cur ^ 1);
     __syncthreads();
+    read_frags(smem[cur ^ 1], 0, 0);
   }
 
   // D layout of the 32x32 MFMA: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
