@@ -510,10 +510,10 @@ moe_status moe_layer_forward(moe_cfg* c, const void* x, int T, const float* gate
       mark(c, 3, s);
       if ((e = launch_grouped_down_f8(g2, s)) != hipSuccess) return hip_fail(c, e);
     } else {
-      const int cap = c->num_cus * 2;  // persistent workgroups
-      if ((e = launch_stream_gateup(g1, fp8, std::min(g1.max_items, cap), s)) != hipSuccess) return hip_fail(c, e);
+      // persistent workgroups: as many as fit on the CUs at once
+      if ((e = launch_stream_gateup(g1, fp8, g1.max_items, c->num_cus, s)) != hipSuccess) return hip_fail(c, e);
       mark(c, 3, s);
-      if ((e = launch_stream_down(g2, fp8, std::min(g2.max_items, cap), s)) != hipSuccess) return hip_fail(c, e);
+      if ((e = launch_stream_down(g2, fp8, g2.max_items, c->num_cus, s)) != hipSuccess) return hip_fail(c, e);
     }
   }
 

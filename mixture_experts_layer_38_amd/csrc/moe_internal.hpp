@@ -239,8 +239,8 @@ hipError_t launch_grouped_gateup_f8(const ExpertGemmArgs& a, hipStream_t s);
 hipError_t launch_grouped_down_f8(const ExpertGemmArgs& a, hipStream_t s);
 // x bf16 [rows][cols] -> e4m3 codes [rows][cols] + scales [rows][cols/128]
 hipError_t launch_quant_e4m3(const uint16_t* x, int rows, int cols, uint8_t* q, float* scale, hipStream_t s);
-hipError_t launch_stream_gateup(const ExpertGemmArgs& a, int fp8, int blocks, hipStream_t s);
-hipError_t launch_stream_down(const ExpertGemmArgs& a, int fp8, int blocks, hipStream_t s);
+hipError_t launch_stream_gateup(const ExpertGemmArgs& a, int fp8, int max_items, int num_cus, hipStream_t s);
+hipError_t launch_stream_down(const ExpertGemmArgs& a, int fp8, int max_items, int num_cus, hipStream_t s);
 hipError_t launch_simple_gateup_f32(const ExpertGemmArgs& a, int TK, hipStream_t s);
 hipError_t launch_simple_down_f32(const ExpertGemmArgs& a, int TK, hipStream_t s);
 

@@ -34,6 +34,7 @@
 // next group multiplies them, by which time the group after that is already
 // requested. The problem tables (item prefix, expert row offsets)
 // are cached in LDS, so finding an item's problem costs no global round trips.
+#include <algorithm>
 #include <type_traits>
 
 #include "moe_internal.hpp"
@@ -230,10 +231,28 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(ExpertGemmArgs a) {
       const bool in_item = g + 1 < ngr;
       if (!in_item && has_next) nxt = setup_item<kFp8, kMode>(a, s_pre, s_off, next_item);
       const bool req = in_item || has_next;
-      load_group(in_item ? cur : nxt, in_item ? g + 1 : (has_next ? 0 : g), wv[GS ^ 1], sc[GS ^ 1]);
+      // activations first, then each chunk's weights just before a chunk of
+      // this group is multiplied (requests spread between the MFMAs)
+      const Item& src = in_item ? cur : nxt;
+      const int gl = in_item ? g + 1 : (has_next ? 0 : g);
 #pragma unroll
-      for (int u = 0; u < kU; ++u)
+      for (int u = 0; u < kU; ++u) {
+        const int c = min(gl * kU + u, src.nch - 1);
+        const uint4 v = *reinterpret_cast<const uint4*>(src.aptr + (size_t)c * kST_KC);
+        pa[u] = src.aval ? v : make_uint4(0, 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        {
+          const int c = min(gl * kU + u, src.nch - 1);
+#pragma unroll
+          for (int j = 0; j < kWv; ++j)
+            wv[GS ^ 1][u][j] = *reinterpret_cast<const uint4*>(src.wptr + (size_t)c * kST_KC * welt + 16 * j);
+          sc[GS ^ 1][u] = kFp8 ? src.sptr[c] : 1.0f;
+        }
         if (g * kU + u < cur.nch) chunk(wv[GS][u], sc[GS][u], &s_act[(aset * kU + u) * kASlot]);
+      }
       if (req) store_act(aset ^ 1);
       __syncthreads();
       aset ^= 1;
@@ -273,20 +292,37 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(ExpertGemmArgs a) {
   }
 }
 
-hipError_t launch_stream_gateup(const ExpertGemmArgs& a, int fp8, int blocks, hipStream_t s) {
-  if (fp8)
-    hipLaunchKernelGGL((stream_gemm_kernel<true, 0>), dim3(blocks), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((stream_gemm_kernel<false, 0>), dim3(blocks), dim3(256), 0, s, a);
+// Workgroups of one kernel that fit on a CU at once (registers and LDS
+// decide: the e4m3 kernels fit three, the bf16 ones two); the grid is that
+// many per CU, capped at the item count, so every workgroup is resident from
+// the start and none picks up its first item late.
+template <bool kFp8, int kMode>
+static int resident_per_cu() {
+  static int n = 0;  // the same on every gfx950 device; a racing first call computes the same value
+  if (n == 0) {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, stream_gemm_kernel<kFp8, kMode>, 256, 0) != hipSuccess ||
+        v < 1)
+      v = 1;
+    n = v;
+  }
+  return n;
+}
+
+template <bool kFp8, int kMode>
+static hipError_t launch_stream(const ExpertGemmArgs& a, int max_items, int num_cus, hipStream_t s) {
+  const int blocks = std::min(max_items, resident_per_cu<kFp8, kMode>() * num_cus);
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((stream_gemm_kernel<kFp8, kMode>), dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_stream_down(const ExpertGemmArgs& a, int fp8, int blocks, hipStream_t s) {
-  if (fp8)
-    hipLaunchKernelGGL((stream_gemm_kernel<true, 1>), dim3(blocks), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((stream_gemm_kernel<false, 1>), dim3(blocks), dim3(256), 0, s, a);
-  return hipGetLastError();
+hipError_t launch_stream_gateup(const ExpertGemmArgs& a, int fp8, int max_items, int num_cus, hipStream_t s) {
+  return fp8 ? launch_stream<true, 0>(a, max_items, num_cus, s) : launch_stream<false, 0>(a, max_items, num_cus, s);
+}
+
+hipError_t launch_stream_down(const ExpertGemmArgs& a, int fp8, int max_items, int num_cus, hipStream_t s) {
+  return fp8 ? launch_stream<true, 1>(a, max_items, num_cus, s) : launch_stream<false, 1>(a, max_items, num_cus, s);
 }
 
 }  // namespace moe
