@@ -6,6 +6,8 @@
 // map, softmax, greedy or group-limited greedy top-K) and the selection-only
 // bias of the DeepSeek-V3 basics page (section 1.2): the bias shifts the scores
 // used to choose groups and experts; gates come from the unbiased scores.
+#include <type_traits>
+
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -176,21 +178,19 @@ __global__ __launch_bounds__(256) void router_logits_x3_kernel(const uint16_t* _
     ow[i] = (size_t)(min(e0 + lr + 32 * i, E - 1) - min(e0 + lr, E - 1)) * D;
   }
   const size_t plane = (size_t)E * D;
-  uint4 px[4], pw[12];
-#define X3_LOAD(k0)                                                                             \
-  {                                                                                             \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i) px[i] =                                       \
-        *reinterpret_cast<const uint4*>(gx + ox[i] + (k0));                                     \
-    _Pragma("unroll") for (int j = 0; j < 12; ++j) pw[j] =                                      \
-        *reinterpret_cast<const uint4*>(gw + (j >> 2) * plane + ow[j & 3] + (k0));              \
-  }
-#define X3_STORE(bf)                                                                            \
-  {                                                                                             \
-    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                               \
-        *reinterpret_cast<uint4*>(&sm[bf][0][(lr + 32 * i) * kX3_LD + lc]) = px[i];             \
-    _Pragma("unroll") for (int j = 0; j < 12; ++j)                                              \
-        *reinterpret_cast<uint4*>(&sm[bf][1 + (j >> 2)][(lr + 32 * (j & 3)) * kX3_LD + lc]) = pw[j]; \
-  }
+  // Operands two K steps ahead through two register slots (slot k & 1 holds
+  // step k; one wave per SIMD, so the accumulators can live in AGPRs and the
+  // registers hold both slots); a step's 16 requests are spread over its
+  // four substeps, between the MFMAs, and the fragments are double-buffered.
+  typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;  // a value type: no aggregate copies
+  u32x4 px[2][4], pw[2][12];
+  auto store_tile = [&](int bf, int s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&sm[bf][0][(lr + 32 * i) * kX3_LD + lc]) = px[s][i];
+#pragma unroll
+    for (int j = 0; j < 12; ++j)
+      *reinterpret_cast<u32x4*>(&sm[bf][1 + (j >> 2)][(lr + 32 * (j & 3)) * kX3_LD + lc]) = pw[s][j];
+  };
 
   f32x16 acc[4];
 #pragma unroll
@@ -199,32 +199,76 @@ __global__ __launch_bounds__(256) void router_logits_x3_kernel(const uint16_t* _
     for (int i = 0; i < 16; ++i) acc[m][i] = 0.f;
 
   const int fr = lane & 31, fk = 8 * (lane >> 5);
+  bf16x8 bw[2][3], ax[2][4];
+  auto read_frags = [&](int buf, int ks, int fs) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      bw[fs][p] = *reinterpret_cast<const bf16x8*>(&sm[buf][1 + p][(32 * wave + fr) * kX3_LD + 16 * ks + fk]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      ax[fs][m] = *reinterpret_cast<const bf16x8*>(&sm[buf][0][(32 * m + fr) * kX3_LD + 16 * ks + fk]);
+  };
   if (nsteps > 0) {
-    X3_LOAD(kbeg);
-    X3_STORE(0);
+    const int k1 = kbeg + min(1, nsteps - 1) * kX3_BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) px[0][i] = *reinterpret_cast<const u32x4*>(gx + ox[i] + kbeg);
+#pragma unroll
+    for (int j = 0; j < 12; ++j) pw[0][j] = *reinterpret_cast<const u32x4*>(gw + (j >> 2) * plane + ow[j & 3] + kbeg);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) px[1][i] = *reinterpret_cast<const u32x4*>(gx + ox[i] + k1);
+#pragma unroll
+    for (int j = 0; j < 12; ++j) pw[1][j] = *reinterpret_cast<const u32x4*>(gw + (j >> 2) * plane + ow[j & 3] + k1);
+    store_tile(0, 0);
   }
   __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    // branch-free: the last step reloads its own K slice into the idle buffer
-    X3_LOAD(kbeg + min(st + 1, nsteps - 1) * kX3_BK);
+  if (nsteps > 0) read_frags(0, 0, 0);
+  // one 16-wide substep: its share of the requests for step st + 2 (x rows in
+  // substep 0, a third of the weight planes in each of 1 - 3), the next
+  // substep's fragments, the MFMAs (indices are compile-time constants
+  // throughout, so the operand slots stay in registers)
+  auto substep = [&](auto ks_c, auto s_c, int buf, int kn) __attribute__((always_inline)) {
+    constexpr int KS = decltype(ks_c)::value, S = decltype(s_c)::value;
+    if constexpr (KS == 0) {
 #pragma unroll
-    for (int ks = 0; ks < kX3_BK / 16; ++ks) {
-      bf16x8 bw[3], ax[4];
+      for (int i = 0; i < 4; ++i) px[S][i] = *reinterpret_cast<const u32x4*>(gx + ox[i] + kn);
+    } else {
 #pragma unroll
-      for (int p = 0; p < 3; ++p)
-        bw[p] = *reinterpret_cast<const bf16x8*>(&sm[buf][1 + p][(32 * wave + fr) * kX3_LD + 16 * ks + fk]);
+      for (int j = 4 * (KS - 1); j < 4 * KS; ++j)
+        pw[S][j] = *reinterpret_cast<const u32x4*>(gw + (j >> 2) * plane + ow[j & 3] + kn);
+    }
+    if constexpr (KS < 3) read_frags(buf, KS + 1, (KS + 1) & 1);
+#pragma unroll
+    for (int p = 2; p >= 0; --p)  // smallest terms first
 #pragma unroll
       for (int m = 0; m < 4; ++m)
-        ax[m] = *reinterpret_cast<const bf16x8*>(&sm[buf][0][(32 * m + fr) * kX3_LD + 16 * ks + fk]);
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ax[KS & 1][m], bw[KS & 1][p], acc[m], 0, 0, 0);
 #pragma unroll
-      for (int p = 2; p >= 0; --p)  // smallest terms first
-#pragma unroll
-        for (int m = 0; m < 4; ++m) acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ax[m], bw[p], acc[m], 0, 0, 0);
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if constexpr (KS < 3) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    X3_STORE(buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto step = [&](int st, auto s_c) __attribute__((always_inline)) {
+    constexpr int S = decltype(s_c)::value;  // = st & 1: slot of step st, refilled with step st + 2
+    const int buf = st & 1;
+    // branch-free: the last steps reload the last K slice and write the idle buffer
+    const int kn = kbeg + min(st + 2, nsteps - 1) * kX3_BK;
+    substep(std::integral_constant<int, 0>{}, s_c, buf, kn);
+    substep(std::integral_constant<int, 1>{}, s_c, buf, kn);
+    substep(std::integral_constant<int, 2>{}, s_c, buf, kn);
+    substep(std::integral_constant<int, 3>{}, s_c, buf, kn);
+    store_tile(buf ^ 1, S ^ 1);
     __syncthreads();
+    read_frags(buf ^ 1, 0, 0);
+  };
+  int st = 0;
+  for (; st + 1 < nsteps; st += 2) {
+    step(st, std::integral_constant<int, 0>{});
+    step(st + 1, std::integral_constant<int, 1>{});
   }
+  if (st < nsteps) step(st, std::integral_constant<int, 0>{});
   const int e = e0 + 32 * wave + fr;
   if (e < E) {
 #pragma unroll
@@ -236,8 +280,6 @@ __global__ __launch_bounds__(256) void router_logits_x3_kernel(const uint16_t* _
       }
   }
 }
-#undef X3_LOAD
-#undef X3_STORE
 
 // ---------------------------------------------------------------------------
 // Per-token scoring and selection; one wave per token, expert e = lane + 64*j.
