@@ -43,10 +43,10 @@ GATEUP_COUNTERS = {
     "sources": {"mixture_experts_layer_38_amd/csrc/grouped_gemm.hip":
                 "b06967abb48fbb8bb3023847dcd277aab4f49217368893dfa3a6ce98d2a12d89",
                 "mixture_experts_layer_38_amd/csrc/moe_internal.hpp":
-                "c2cbb7252603f07395f28ffaa0720056db5db2139a3255d195211492576a9bd2"},
+                "5800378b02ef820f8ce78ee45da4b2a3ea5e30c7b0d944f53f36fdd8edce392c"},
     "workload": "v3_prefill",
-    "fetch_kib": 14153719.1, "write_kib": 617808.0,
-    "fetch_scale": 1048576.0 / 524315.0, "write_scale": 1.0,
+    "fetch_kib": 15028031.7, "write_kib": 617808.0,
+    "fetch_scale": 1048576.0 / 524316.0, "write_scale": 1.0,
 }
 
 
