@@ -27,6 +27,9 @@
 //   kRouterX  dx_r     = dlogit gate_w         (T x D, fp32)
 #include <type_traits>
 
+#include <algorithm>
+#include <type_traits>
+
 #include "moe_internal.hpp"
 
 namespace moe {
@@ -72,6 +75,18 @@ __device__ __forceinline__ uint4 bload(const __amdgpu_buffer_rsrc_t& r, uint32_t
 
 __host__ __device__ constexpr int cdiv(int x, int y) { return (x + y - 1) / y; }
 
+// Tile fields are the same in every lane; saying so keeps the buffer
+// descriptors built from them in scalar registers (a descriptor the compiler
+// cannot prove uniform costs a loop over its distinct values at every load).
+template <class T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 // LDS layout: row r holds its 64 k values as eight 16-byte chunks, chunk c at
@@ -81,32 +96,61 @@ __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uin
 __device__ __forceinline__ int lds_at(int r, int k) { return r * LDK + ((((k >> 3) ^ (r >> 4)) & 7) << 3) + (k & 7); }
 }  // namespace
 
-template <int kMode, bool kAT>
-__device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRowsL * LDK], float* s_red) {
+// The tiles of one workgroup, in order: the first is t; with kPersist, next(tn)
+// supplies the following ones (false when none is left). The loader state
+// (buffer resources, row maps, offsets) belongs to the tile being loaded,
+// which during a tile's last K step is already the next tile: that step
+// requests the next tile's first slice instead of nothing, so the first
+// loads of a tile overlap the previous tile's last MFMAs and epilogue.
+template <int kMode, bool kAT, bool kPersist, class Next>
+__device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*smem)[kRowsL * LDK], float* s_red) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(t.a), (short)0,
-                                                                      t.a_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(t.b), (short)0,
-                                                                      t.b_bytes, 0x00020000);
   // natural loader: rows r0 + 64j, 16-byte chunk c8 of the 64-wide K step
   const int c8 = tid & 7, r0 = tid >> 3;
   // k-major loader: k rows 4*kg .. +3 of the step, columns 8*mg .. +7 of the tile
   const int kg = tid >> 5, mg = tid & 31;
 
-  uint32_t aoff[4];
-  if (!kAT) {
+  // loader state of the tile being loaded
+  __amdgpu_buffer_rsrc_t ra, rb, rma, rmb;
+  bool has_amap, has_bmap;
+  uint32_t aoff[4], acol, bcol;
+  int lk0, lk1, llda, lldb;
+  auto init_loader = [&](const BwdTile& L) __attribute__((always_inline)) {
+    ra = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(const_cast<uint16_t*>(L.a)), (short)0, uniform_u32(L.a_bytes),
+                                           0x00020000);
+    rb = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(const_cast<uint16_t*>(L.b)), (short)0, uniform_u32(L.b_bytes),
+                                           0x00020000);
+    if (!kAT) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int m = t.m0 + r0 + 64 * j;
-      m = m < t.M ? m : t.M - 1;
-      const int row = t.amap ? t.amap[m] : m;
-      aoff[j] = ((uint32_t)row * (uint32_t)t.lda + c8 * 8) * 2u;
+      for (int j = 0; j < 4; ++j) {
+        int m = L.m0 + r0 + 64 * j;
+        m = m < L.M ? m : L.M - 1;
+        const int row = L.amap ? L.amap[m] : m;
+        aoff[j] = ((uint32_t)row * (uint32_t)L.lda + c8 * 8) * 2u;
+      }
     }
-  }
-  // k-major operands: byte offset of column 8*mg (rows added per step)
-  const uint32_t acol = (uint32_t)(t.m0 + 8 * mg) * 2u, bcol = (uint32_t)(t.n0 + 8 * mg) * 2u;
+    // k-major operands: byte offset of column 8*mg (rows added per step)
+    acol = (uint32_t)(L.m0 + 8 * mg) * 2u;
+    bcol = (uint32_t)(L.n0 + 8 * mg) * 2u;
+    // The row maps are read through buffer resources, an absent map through
+    // one of zero length (its reads return 0 and are replaced by the
+    // identity), so the reads are unconditional: a branch around them would
+    // split the step's scheduling region.
+    has_amap = L.amap != nullptr;
+    has_bmap = L.bmap != nullptr;
+    rma = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(const_cast<int32_t*>(has_amap ? L.amap : reinterpret_cast<const int32_t*>(L.a))), (short)0,
+        uniform_u32(has_amap ? (uint32_t)L.k1 * 4u : 0u), 0x00020000);
+    rmb = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(const_cast<int32_t*>(has_bmap ? L.bmap : reinterpret_cast<const int32_t*>(L.b))), (short)0,
+        uniform_u32(has_bmap ? (uint32_t)L.k1 * 4u : 0u), 0x00020000);
+    lk0 = (int)uniform_u32((uint32_t)L.k0);
+    lk1 = (int)uniform_u32((uint32_t)L.k1);
+    llda = (int)uniform_u32((uint32_t)L.lda);
+    lldb = (int)uniform_u32((uint32_t)L.ldb);
+  };
 
   uint4 sa_[4], sb_[4];
   // storage rows of this thread's 4 k-rows of a step (through the row map
@@ -116,25 +160,14 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
     int row[4];
     int ok;  // bit q: k-row q is inside [k0, k1) (else zero-filled)
   };
-  // The row maps are read through buffer resources, an absent map through
-  // one of zero length (its reads return 0 and are replaced by the identity),
-  // so the reads are unconditional: a branch around them would split the
-  // step's scheduling region.
-  const bool has_amap = t.amap != nullptr, has_bmap = t.bmap != nullptr;
-  const __amdgpu_buffer_rsrc_t rma = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int32_t*>(has_amap ? t.amap : reinterpret_cast<const int32_t*>(t.a)), (short)0,
-      has_amap ? (uint32_t)t.k1 * 4u : 0u, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rmb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<int32_t*>(has_bmap ? t.bmap : reinterpret_cast<const int32_t*>(t.b)), (short)0,
-      has_bmap ? (uint32_t)t.k1 * 4u : 0u, 0x00020000);
   auto krows = [&](const __amdgpu_buffer_rsrc_t& rm, bool has_map, int k0) __attribute__((always_inline)) {
     KRows r;
     r.ok = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int k = k0 + 4 * kg + q;
-      const bool ok = k < t.k1;
-      const int kk = ok ? k : t.k0;
+      const bool ok = k < lk1;
+      const int kk = ok ? k : lk0;
       const int v = (int)__builtin_amdgcn_raw_buffer_load_b32(rm, (uint32_t)kk * 4u, 0, 0);
       r.row[q] = has_map ? v : kk;
       r.ok |= (ok ? 1 : 0) << q;
@@ -152,7 +185,7 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
   int oka = 0, okb = 0;  // valid k-rows of the loaded data
   auto load_a = [&](int k0) __attribute__((always_inline)) {
     if (kAT) {
-      load_kmajor(ra, kra, t.lda, acol, sa_);
+      load_kmajor(ra, kra, llda, acol, sa_);
       oka = kra.ok;
       kra = krows(rma, has_amap, k0 + BK);
     } else {
@@ -161,7 +194,7 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
     }
   };
   auto load_b = [&](int k0) __attribute__((always_inline)) {
-    load_kmajor(rb, krb, t.ldb, bcol, sb_);
+    load_kmajor(rb, krb, lldb, bcol, sb_);
     okb = krb.ok;
     krb = krows(rmb, has_bmap, k0 + BK);
   };
@@ -194,23 +227,7 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
   };
 
   f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][c][e] = 0.f;
-
   const int lr = lane & 31, lk = (lane >> 5) * 8;
-  const int nk = (t.k1 - t.k0 + BK - 1) / BK;
-  if (nk > 0) {  // an expert without rows: no loads, zero gradient
-    if (kAT) kra = krows(rma, has_amap, t.k0);
-    krb = krows(rmb, has_bmap, t.k0);
-    load_a(t.k0);
-    load_b(t.k0);
-    store(0);
-  }
-  __syncthreads();
   // Fragments are double-buffered across the four 16-wide substeps: the LDS
   // reads of substep s+1 are issued before the MFMAs of substep s.
   bf16x8 fa[2][4], fb[2][2];
@@ -222,46 +239,96 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
 #pragma unroll
     for (int c = 0; c < 2; ++c) fb[slot][c] = *reinterpret_cast<const bf16x8*>(&sB[lds_at(64 * wn + 32 * c + lr, kk + lk)]);
   };
-  if (nk > 0) read_frags(smem[0], 0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    // the next step's operands (the last step reloads its own slice and
-    // writes the idle buffer: no branch, so no wait is forced before the
-    // MFMAs), A's requests spread between the MFMAs of substep 0 and B's
-    // between those of substep 1: a request that cannot enter a full memory
-    // queue stalls the wave, and the MFMAs behind it with it
-    const int kn = t.k0 + (kt + 1 < nk ? kt + 1 : kt) * BK;
+  // the rows of a tile's first step (then one step ahead, inside load_a/load_b)
+  auto first_rows = [&]() __attribute__((always_inline)) {
+    if (kAT) kra = krows(rma, has_amap, lk0);
+    krb = krows(rmb, has_bmap, lk0);
+  };
+
+  // first tile: its first step (a tile without rows loads row 0, zero-filled)
+  init_loader(t);
+  first_rows();
+  load_a(t.k0);
+  load_b(t.k0);
+  store(0);
+  __syncthreads();
+  read_frags(smem[0], 0, 0);
+  int b0 = 0;  // LDS buffer holding the current tile's first step
+  while (true) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s == 0) load_a(kn);
-      if (s == 1) load_b(kn);
-      if (s < 3) read_frags(smem[cur], 16 * (s + 1), (s + 1) & 1);
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
-          acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][c], acc[i][c], 0, 0, 0);
-      if (s < 2) {
-        // (MFMA, LDS read, global load) x 6, then (MFMA, global load) x 2
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          if (q < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        }
-      } else if (s == 2) {
-#pragma unroll
-        for (int q = 0; q < 6; ++q) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int e = 0; e < 16; ++e) acc[i][c][e] = 0.f;
+    const int nk = (t.k1 - t.k0 + BK - 1) / BK;
+    BwdTile tn = t;  // the next tile, found just before the last step (no registers held across the loop)
+    bool more = false;
+    // one K step: the next step's operands are requested (A's between the
+    // MFMAs of substep 0, B's between those of substep 1: a request that
+    // cannot enter a full memory queue stalls the wave, and the MFMAs behind
+    // it with it) and written to the idle buffer after the MFMAs. The last
+    // step requests the next tile's first step (persistent), else its own
+    // slice again (unused): no branch around the loads.
+    auto kstep = [&](int kt, auto last_c) __attribute__((always_inline)) {
+      constexpr bool kLast = decltype(last_c)::value;
+      const int cur = (b0 + kt) & 1;
+      int kn = t.k0 + (kt + 1) * BK;
+      if constexpr (kLast) {
+        if constexpr (kPersist) {
+          init_loader(tn);
+          first_rows();
+          kn = tn.k0;
+        } else {
+          kn = t.k0 + kt * BK;
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        if (s == 0) load_a(kn);
+        if (s == 1) load_b(kn);
+        if (s < 3) read_frags(smem[cur], 16 * (s + 1), (s + 1) & 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+            acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][c], acc[i][c], 0, 0, 0);
+        if (s < 2) {
+          // (MFMA, LDS read, global load) x 6, then (MFMA, global load) x 2
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (q < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          }
+        } else if (s == 2) {
+#pragma unroll
+          for (int q = 0; q < 6; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      store(cur ^ 1);
+      __syncthreads();
+      read_frags(smem[cur ^ 1], 0, 0);
+    };
+    for (int kt = 0; kt + 1 < nk; ++kt) kstep(kt, std::false_type{});
+    if constexpr (kPersist) more = next(tn);
+    if (nk > 0) {
+      kstep(nk - 1, std::true_type{});
+    } else if (kPersist) {
+      // a tile without rows (zero gradient): the next tile's first step now
+      init_loader(tn);
+      first_rows();
+      load_a(tn.k0);
+      load_b(tn.k0);
+      store(b0 ^ 1);
+      __syncthreads();
+      read_frags(smem[b0 ^ 1], 0, 0);
     }
-    store(cur ^ 1);
-    __syncthreads();
-    read_frags(smem[cur ^ 1], 0, 0);
-  }
+    b0 = (b0 + (nk > 0 ? nk : 1)) & 1;
 
   // D layout of the 32x32 MFMA: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
   // column l%32.
@@ -376,6 +443,11 @@ __device__ __forceinline__ void bwd_tile(const BwdTile& t, uint16_t (*smem)[kRow
         }
       }
   }
+    // (the fp32 epilogue above touches no LDS: the next tile's first step,
+    // already in buffer b0, stays intact)
+    if (!more) break;
+    t = tn;
+  }
 }
 
 // One launch per product; tiles enumerate (problem, m tile, n tile) as the
@@ -384,6 +456,7 @@ template <int kMode>
 __global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2][kRowsL * LDK];
   float* s_red = reinterpret_cast<float*>(&smem[0][0]);  // epilogue only (8 x BM), after the K loop
+  auto no_next = [](BwdTile&) { return false; };
   const int tile = (kMode <= kWgradGU) ? run_tile(blockIdx.x) : (int)blockIdx.x;
   BwdTile t;
   t.au = nullptr; t.gate = nullptr; t.part = nullptr; t.npart = 0; t.Hp = 0;
@@ -435,7 +508,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
       t.c = routed ? static_cast<void*>(a.dxr + (size_t)rb * a.D) : static_cast<void*>(a.dxs);
       t.ldc = a.D;
     }
-    bwd_tile<kMode, false>(t, smem, s_red);
+    bwd_tiles<kMode, false, false>(t, no_next, smem, s_red);
   } else if (kMode == kWgradD || kMode == kWgradGU) {
     // every problem (experts, then the shared expert) gets its full weight
     // gradient; experts without rows get zeros
@@ -443,49 +516,67 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
     const int Ms = kMode == kWgradD ? a.D : 2 * a.Hs, Ns = kMode == kWgradD ? a.Hs : a.D;
     const int per_r = cdiv(Mr, BM) * cdiv(Nr, BN), per_s = cdiv(Ms, BM) * cdiv(Ns, BN);
     const int total = a.E * per_r + (a.Hs > 0 ? per_s : 0);
-    if (tile >= total) return;
-    const bool routed = tile < a.E * per_r;
-    const int p = routed ? tile / per_r : a.E;
-    const int local = routed ? tile % per_r : tile - a.E * per_r;
-    const int M = routed ? Mr : Ms, N = routed ? Nr : Ns, Hp = routed ? a.H : a.Hs;
-    const int rows = routed ? a.offsets[p + 1] - a.offsets[p] : a.T;
-    const int rb = routed ? a.offsets[p] : 0;
-    // groups of four m-tiles, column-major inside a group: a run of 32
-    // consecutive tiles covers 4 m-slices x 8 n-slices of the operands
-    const int nmt = cdiv(M, BM), nnt = cdiv(N, BN);
-    const int g0 = (local / (4 * nnt)) * 4, gsz = min(4, nmt - g0);
-    const int idx = local - g0 * nnt;
-    t.m0 = (g0 + idx % gsz) * BM;
-    t.n0 = (idx / gsz) * BN;
-    t.M = M;
-    t.N = N;
-    t.K = rows;
-    t.k0 = 0;
-    t.k1 = rows;
-    if (kMode == kWgradD) {
-      // A[m = d][k = r] = dOut[tok(r)][d]; B[n = h][k = r] = (g h)[r][h]
-      t.a = a.dout;
-      t.amap = routed ? a.row_token + rb : nullptr;
-      t.a_bytes = (uint32_t)((size_t)a.T * a.D * 2);
-      t.lda = a.D;
-      t.b = routed ? a.gh + (size_t)rb * a.H : a.gh_shared;
-      t.b_bytes = (uint32_t)((size_t)(rows > 0 ? rows : 1) * Hp * 2);
-      t.ldb = Hp;
-      t.c = routed ? static_cast<void*>(a.dw_down + (size_t)p * a.D * a.H) : static_cast<void*>(a.dw_down_shared);
-      t.ldc = Hp;
-    } else {
-      // A[m = j][k = r] = [dA | dU][r][j]; B[n = d][k = r] = x[tok(r)][d]
-      t.a = routed ? a.dau + (size_t)rb * 2 * a.H : a.dau_shared;
-      t.a_bytes = (uint32_t)((size_t)(rows > 0 ? rows : 1) * 2 * Hp * 2);
-      t.lda = 2 * Hp;
-      t.b = a.x;
-      t.bmap = routed ? a.row_token + rb : nullptr;
-      t.b_bytes = (uint32_t)((size_t)a.T * a.D * 2);
-      t.ldb = a.D;
-      t.c = routed ? static_cast<void*>(a.dw_gu + (size_t)p * 2 * a.H * a.D) : static_cast<void*>(a.dw_gu_shared);
-      t.ldc = a.D;
-    }
-    bwd_tile<kMode, true>(t, smem, s_red);
+    const BwdTile base = t;
+    auto make = [&](int tile, BwdTile& t) -> bool {
+      if (tile >= total) return false;
+      t = base;
+      const bool routed = tile < a.E * per_r;
+      const int p = routed ? tile / per_r : a.E;
+      const int local = routed ? tile % per_r : tile - a.E * per_r;
+      const int M = routed ? Mr : Ms, N = routed ? Nr : Ns, Hp = routed ? a.H : a.Hs;
+      const int rows = routed ? a.offsets[p + 1] - a.offsets[p] : a.T;
+      const int rb = routed ? a.offsets[p] : 0;
+      // groups of four m-tiles, column-major inside a group: a run of 32
+      // consecutive tiles covers 4 m-slices x 8 n-slices of the operands
+      const int nmt = cdiv(M, BM), nnt = cdiv(N, BN);
+      const int g0 = (local / (4 * nnt)) * 4, gsz = min(4, nmt - g0);
+      const int idx = local - g0 * nnt;
+      t.m0 = (g0 + idx % gsz) * BM;
+      t.n0 = (idx / gsz) * BN;
+      t.M = M;
+      t.N = N;
+      t.K = rows;
+      t.k0 = 0;
+      t.k1 = rows;
+      if (kMode == kWgradD) {
+        // A[m = d][k = r] = dOut[tok(r)][d]; B[n = h][k = r] = (g h)[r][h]
+        t.a = a.dout;
+        t.amap = routed ? a.row_token + rb : nullptr;
+        t.a_bytes = (uint32_t)((size_t)a.T * a.D * 2);
+        t.lda = a.D;
+        t.b = routed ? a.gh + (size_t)rb * a.H : a.gh_shared;
+        t.b_bytes = (uint32_t)((size_t)(rows > 0 ? rows : 1) * Hp * 2);
+        t.ldb = Hp;
+        t.c = routed ? static_cast<void*>(a.dw_down + (size_t)p * a.D * a.H)
+                     : static_cast<void*>(a.dw_down_shared);
+        t.ldc = Hp;
+      } else {
+        // A[m = j][k = r] = [dA | dU][r][j]; B[n = d][k = r] = x[tok(r)][d]
+        t.a = routed ? a.dau + (size_t)rb * 2 * a.H : a.dau_shared;
+        t.a_bytes = (uint32_t)((size_t)(rows > 0 ? rows : 1) * 2 * Hp * 2);
+        t.lda = 2 * Hp;
+        t.b = a.x;
+        t.bmap = routed ? a.row_token + rb : nullptr;
+        t.b_bytes = (uint32_t)((size_t)a.T * a.D * 2);
+        t.ldb = a.D;
+        t.c = routed ? static_cast<void*>(a.dw_gu + (size_t)p * 2 * a.H * a.D)
+                     : static_cast<void*>(a.dw_gu_shared);
+        t.ldc = a.D;
+      }
+      return true;
+    };
+    // A persistent grid (a multiple of 8 workgroups, about one per CU): block b
+    // takes the run-mapped tiles of blocks b, b + G, b + 2G, ... (increasing,
+    // so the first one past the end ends the sequence). Short-K tiles (an
+    // expert's tokens) are many, and the next tile's first loads then overlap
+    // this tile's last MFMAs and its epilogue.
+    int kseq = 0;
+    if (!make(run_tile(blockIdx.x), t)) return;
+    auto next = [&](BwdTile& tn) -> bool {
+      ++kseq;
+      return make(run_tile(blockIdx.x + kseq * gridDim.x), tn);
+    };
+    bwd_tiles<kMode, true, true>(t, next, smem, s_red);
   } else if (kMode == kRouterW) {
     // d gate_w planes: A[m = e][k = t] = dlogit[t][e]; B[n = d][k = t] = x[t][d]; K split over planes
     const int nmt = cdiv(a.Ep, BM), nnt = cdiv(a.D, BN);
@@ -508,7 +599,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
     t.ldb = a.D;
     t.c = a.gw_planes + (size_t)z * a.E * a.D;
     t.ldc = a.D;
-    bwd_tile<kMode, true>(t, smem, s_red);
+    bwd_tiles<kMode, true, false>(t, no_next, smem, s_red);
   } else {
     // dx_r = dlogit gate_w: A = dlogit rows (K = Ep, zero-padded); B[n = d][k = e] = gate_w[e][d]
     const int nnt = cdiv(a.D, BN);
@@ -528,7 +619,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
     t.ldb = a.D;
     t.c = a.dx_router;
     t.ldc = a.D;
-    bwd_tile<kMode, false>(t, smem, s_red);
+    bwd_tiles<kMode, false, false>(t, no_next, smem, s_red);
   }
 }
 
@@ -727,10 +818,18 @@ hipError_t launch_layer_backward(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kDgradX>, dim3(run_grid(tiles_x)), dim3(kThreads), 0, s, b);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int tiles_wd = a.E * cdiv(a.D, BM) * cdiv(a.H, BN) + (a.Hs > 0 ? cdiv(a.D, BM) * cdiv(a.Hs, BN) : 0);
-  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kWgradD>, dim3(run_grid(tiles_wd)), dim3(kThreads), 0, s, a);
+  // the weight gradients: a persistent grid of about one workgroup per CU (a
+  // multiple of 8, the XCD count)
+  int dev = 0, cus = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  const int persist = std::max(8, (cus / 8) * 8);
+  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kWgradD>, dim3(std::min(run_grid(tiles_wd), persist)), dim3(kThreads), 0,
+                     s, a);
   const int tiles_wgu =
       a.E * cdiv(2 * a.H, BM) * cdiv(a.D, BN) + (a.Hs > 0 ? cdiv(2 * a.Hs, BM) * cdiv(a.D, BN) : 0);
-  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kWgradGU>, dim3(run_grid(tiles_wgu)), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kWgradGU>, dim3(std::min(run_grid(tiles_wgu), persist)), dim3(kThreads), 0,
+                     s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int tiles_rw = cdiv(a.Ep, BM) * cdiv(a.D, BN) * a.splits;
   hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kRouterW>, dim3(tiles_rw), dim3(kThreads), 0, s, a);
