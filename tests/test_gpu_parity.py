@@ -382,7 +382,14 @@ def _check_backward(cfg, add_residual=True, with_shared=True, seed=5):
     return layer, inp, d_out, got
 
 
-@pytest.mark.parametrize("cfg", [BWD_SIG, BWD_SOFTMAX, BWD_GROUP], ids=lambda c: c.name)
+# few tokens over many experts: about half the experts get no rows (zero
+# weight gradients), and with ~1000 weight-gradient tiles each workgroup of
+# the persistent weight-gradient grid walks several tiles, empty ones among them
+BWD_SPARSE = MI.LayerConfig("bwd_sparse", T=40, D=1024, E=64, H=512, G=8, kg=3, K=2, score_fn="softmax",
+                            bias="none", norm=True, rsf=1.0, Hs=512, act="bf16", weight="bf16")
+
+
+@pytest.mark.parametrize("cfg", [BWD_SIG, BWD_SOFTMAX, BWD_GROUP, BWD_SPARSE], ids=lambda c: c.name)
 def test_backward_matches_the_oracle(cfg):
     _check_backward(cfg)
 
