@@ -626,12 +626,25 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
 namespace {
 
 // fp32 -> bf16 (RNE), rows of `cols` values into rows of `ldd` (zero padding)
+// dst[r][c] = bf16(src[r][c]) for r < srows, c < cols; 0 elsewhere in the
+// rows x ldd destination. 8 consecutive values per thread (cols and ldd are
+// multiples of 8): two 16-byte loads, one 16-byte store.
 __global__ __launch_bounds__(256) void to_bf16_kernel(const float* __restrict__ src, int rows, int cols, int srows,
                                                      uint16_t* __restrict__ dst, int ldd) {
-  const size_t n = (size_t)rows * ldd;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-    const int r = (int)(i / ldd), c = (int)(i % ldd);
-    dst[i] = (r < srows && c < cols) ? f32_to_bf16(src[(size_t)r * cols + c]) : (uint16_t)0;
+  const int cpr = ldd / 8;  // 8-value pieces per destination row
+  const int n = rows * cpr;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const int r = i / cpr, c = (i - r * cpr) * 8;
+    uint4 o = make_uint4(0u, 0u, 0u, 0u);
+    if (r < srows && c < cols) {
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(src + (size_t)r * cols + c);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + (size_t)r * cols + c + 4);
+      o.x = (uint32_t)f32_to_bf16(v0.x) | ((uint32_t)f32_to_bf16(v0.y) << 16);
+      o.y = (uint32_t)f32_to_bf16(v0.z) | ((uint32_t)f32_to_bf16(v0.w) << 16);
+      o.z = (uint32_t)f32_to_bf16(v1.x) | ((uint32_t)f32_to_bf16(v1.y) << 16);
+      o.w = (uint32_t)f32_to_bf16(v1.z) | ((uint32_t)f32_to_bf16(v1.w) << 16);
+    }
+    *reinterpret_cast<uint4*>(dst + (size_t)r * ldd + c) = o;
   }
 }
 
@@ -726,47 +739,59 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
 }
 
 // dx[t] = [d_out[t]] + dX_shared[t] + sum_k dX_rows[slot(t,k)] + dx_router[t]
+// 8 consecutive columns per thread (D % 128 == 0): every load of a step (the
+// residual, the shared row, up to 8 slot rows, the router part) is issued
+// before the first add, and the adds run in that fixed order; an absent
+// source reads a valid row and adds -0.0 (which changes no value, signed
+// zeros included), so no branch sits around a load.
+__device__ __forceinline__ void add_bf16x8(float (&acc)[8], const uint4 s4, bool use) {
+  const uint32_t m = use ? 0xFFFFFFFFu : 0x80008000u, z = use ? 0u : 0x80008000u;
+  const uint32_t w[4] = {(s4.x & m) | z, (s4.y & m) | z, (s4.z & m) | z, (s4.w & m) | z};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc[2 * q] += __uint_as_float(w[q] << 16);
+    acc[2 * q + 1] += __uint_as_float(w[q] & 0xFFFF0000u);
+  }
+}
+
 __global__ __launch_bounds__(256) void dx_combine_kernel(const float* __restrict__ dout,
                                                          const uint16_t* __restrict__ dxr,
                                                          const uint16_t* __restrict__ dxs,
                                                          const float* __restrict__ dx_router,
                                                          const int32_t* __restrict__ slot_row, int T, int D, int K,
                                                          int add_residual, float* __restrict__ dx) {
-  // 8 consecutive columns per thread (D % 128 == 0): 16-byte bf16 row loads,
-  // four slot rows requested at a time, added in slot order
   const int t = blockIdx.x;
-  const int* sr = slot_row + (size_t)t * K;
+  int rows[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) rows[k] = slot_row[(size_t)t * K + (k < K ? k : 0)];
+  const bool has_shared = dxs != nullptr;
+  const uint16_t* sbase = has_shared ? dxs + (size_t)t * D : dxr + (size_t)rows[0] * D;
   for (int d = 8 * threadIdx.x; d < D; d += 8 * blockDim.x) {
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(dout + (size_t)t * D + d);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(dout + (size_t)t * D + d + 4);
+    const uint4 sv = *reinterpret_cast<const uint4*>(sbase + d);
+    uint4 rk[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) rk[k] = *reinterpret_cast<const uint4*>(dxr + (size_t)rows[k] * D + d);
+    const f32x4 r0 = *reinterpret_cast<const f32x4*>(dx_router + (size_t)t * D + d);
+    const f32x4 r1 = *reinterpret_cast<const f32x4*>(dx_router + (size_t)t * D + d + 4);
     float acc[8];
     if (add_residual) {
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(dout + (size_t)t * D + d);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(dout + (size_t)t * D + d + 4);
-      acc[0] = a0.x; acc[1] = a0.y; acc[2] = a0.z; acc[3] = a0.w; acc[4] = a1.x; acc[5] = a1.y; acc[6] = a1.z;
-      acc[7] = a1.w;
+      acc[0] = a0.x; acc[1] = a0.y; acc[2] = a0.z; acc[3] = a0.w;
+      acc[4] = a1.x; acc[5] = a1.y; acc[6] = a1.z; acc[7] = a1.w;
     } else {
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[q] = 0.f;
     }
-    auto add8 = [&](const uint4 s4) __attribute__((always_inline)) {
-      const uint32_t w[4] = {s4.x, s4.y, s4.z, s4.w};
+    add_bf16x8(acc, sv, has_shared);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += __uint_as_float(w[q] << 16);
-        acc[2 * q + 1] += __uint_as_float(w[q] & 0xFFFF0000u);
-      }
-    };
-    if (dxs) add8(*reinterpret_cast<const uint4*>(dxs + (size_t)t * D + d));
-    for (int k0 = 0; k0 < K; k0 += 4) {
-      uint4 rk[4];
+    for (int k = 0; k < 8; ++k) add_bf16x8(acc, rk[k], k < K);
+    if (K > 8) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        rk[u] = k0 + u < K ? *reinterpret_cast<const uint4*>(dxr + (size_t)sr[k0 + u] * D + d) : make_uint4(0, 0, 0, 0);
+      for (int k = 8; k < kMaxTopK; ++k) rk[k - 8] = *reinterpret_cast<const uint4*>(dxr + (size_t)rows[k] * D + d);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if (k0 + u < K) add8(rk[u]);
+      for (int k = 8; k < kMaxTopK; ++k) add_bf16x8(acc, rk[k - 8], k < K);
     }
-    const f32x4 r0 = *reinterpret_cast<const f32x4*>(dx_router + (size_t)t * D + d);
-    const f32x4 r1 = *reinterpret_cast<const f32x4*>(dx_router + (size_t)t * D + d + 4);
     acc[0] += r0.x; acc[1] += r0.y; acc[2] += r0.z; acc[3] += r0.w;
     acc[4] += r1.x; acc[5] += r1.y; acc[6] += r1.z; acc[7] += r1.w;
     *reinterpret_cast<f32x4*>(dx + (size_t)t * D + d) = f32x4{acc[0], acc[1], acc[2], acc[3]};
@@ -793,10 +818,10 @@ int run_grid(int n) { return cdiv(cdiv(n, kRunB), 8) * 8 * kRunB; }
 hipError_t launch_layer_backward(const BwdArgs& a, hipStream_t s) {
   hipError_t e;
   // dOut and gate_w to bf16 (gate_w rows padded with zeros to Ep)
-  hipLaunchKernelGGL(to_bf16_kernel, dim3(grid_for((size_t)a.T * a.D)), dim3(256), 0, s, a.dout_f32, a.T, a.D, a.T,
-                     a.dout, a.D);
-  hipLaunchKernelGGL(to_bf16_kernel, dim3(grid_for((size_t)a.Ep * a.D)), dim3(256), 0, s, a.gate_w, a.Ep, a.D, a.E,
-                     a.gw_bf16, a.D);
+  hipLaunchKernelGGL(to_bf16_kernel, dim3(grid_for((size_t)a.T * a.D / 8)), dim3(256), 0, s, a.dout_f32, a.T, a.D,
+                     a.T, a.dout, a.D);
+  hipLaunchKernelGGL(to_bf16_kernel, dim3(grid_for((size_t)a.Ep * a.D / 8)), dim3(256), 0, s, a.gate_w, a.Ep, a.D,
+                     a.E, a.gw_bf16, a.D);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // tile prefixes of the two row-grouped products
   hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, a.offsets, a.E, a.Hs > 0 ? a.T : 0,
@@ -838,7 +863,10 @@ hipError_t launch_layer_backward(const BwdArgs& a, hipStream_t s) {
   const int tiles_rx = cdiv(a.T, BM) * cdiv(a.D, BN);
   hipLaunchKernelGGL(grouped_gemm_bwd_kernel<kRouterX>, dim3(tiles_rx), dim3(kThreads), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(dx_combine_kernel, dim3(a.T), dim3(256), 0, s, a.dout_f32, a.dxr, a.Hs > 0 ? a.dxs : nullptr,
+  // threads per token: the 8-column pieces of a row spread evenly over at
+  // most 256 threads (D = 7168: 224 threads x 4 pieces)
+  const int pieces = a.D / 8, iters = (pieces + 255) / 256;
+  hipLaunchKernelGGL(dx_combine_kernel, dim3(a.T), dim3((pieces + iters - 1) / iters), 0, s, a.dout_f32, a.dxr, a.Hs > 0 ? a.dxs : nullptr,
                      a.dx_router, a.slot_row, a.T, a.D, a.K, a.add_residual, a.dx);
   return hipGetLastError();
 }
