@@ -185,6 +185,22 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(ExpertGemmArgs a) {
       *reinterpret_cast<uint4*>(&s_act[(set * kU + u) * kASlot + (tid >> 4) * kALd + (tid & 15) * 8]) = pa[u];
   };
 
+  // Issue priority falls in four steps as this workgroup works through its
+  // items: the workgroups sharing a CU hold equal item counts, and with equal
+  // priority the oldest waves win the issue slots, so the first workgroup
+  // on a CU would finish long before the last and leave the CU short of
+  // requests in flight; a workgroup that is ahead now yields to those behind.
+  const int my_items = (total - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
+  int done = 0;
+  auto set_priority = [&]() __attribute__((always_inline)) {
+    switch (3 - min(3, (4 * done) / my_items)) {
+      case 3: __builtin_amdgcn_s_setprio(3); break;
+      case 2: __builtin_amdgcn_s_setprio(2); break;
+      case 1: __builtin_amdgcn_s_setprio(1); break;
+      default: __builtin_amdgcn_s_setprio(0); break;
+    }
+  };
+  set_priority();
   Item cur = setup_item<kFp8, kMode>(a, s_pre, s_off, item);
   load_group(cur, 0, wv[0], sc[0]);
   store_act(0);
@@ -289,6 +305,8 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(ExpertGemmArgs a) {
     if (!has_next) break;
     item = next_item;
     cur = nxt;
+    ++done;
+    set_priority();
   }
 }
 
