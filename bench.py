@@ -50,11 +50,24 @@ GATEUP_COUNTERS = {
 }
 
 
-def gateup_traffic(cfg):
-    """Calibrated HBM bytes per gate/up launch, or None when the counters do not
-    describe the kernel that was built (or another workload)."""
+# the same two counters for the fp8 decode layer's gate/up streaming kernel
+# (stream_gemm_kernel<true, 0>, decode workload run in the prefill slot:
+# `bench.py --config v3_decode_fp8`; the same 1 GiB copy calibrates FETCH_SIZE)
+DECODE_GATEUP_COUNTERS = {
+    "sources": {"mixture_experts_layer_38_amd/csrc/stream_gemm.hip":
+                "5642dae0c2a36492c0bf56d8786bd828ef913fd48cb64e9e80d1c6d0530da611",
+                "mixture_experts_layer_38_amd/csrc/moe_internal.hpp":
+                "5800378b02ef820f8ce78ee45da4b2a3ea5e30c7b0d944f53f36fdd8edce392c"},
+    "workload": "v3_decode_fp8",
+    "fetch_kib": 1889999.1, "write_kib": 2331.9,
+    "fetch_scale": 1048576.0 / 524315.6, "write_scale": 1.0,
+}
+
+
+def pinned_traffic(c, cfg):
+    """Calibrated HBM bytes per launch from counter figures c, or None when they
+    do not describe the kernel that was built (or another workload)."""
     import hashlib
-    c = GATEUP_COUNTERS
     if cfg.name != c["workload"]:
         return None
     for rel, digest in c["sources"].items():
@@ -62,6 +75,11 @@ def gateup_traffic(cfg):
             if hashlib.sha256(f.read()).hexdigest() != digest:
                 return None
     return round((c["fetch_kib"] * c["fetch_scale"] + c["write_kib"] * c["write_scale"]) * 1024)
+
+
+def gateup_traffic(cfg):
+    """Calibrated HBM bytes per gate/up GEMM launch (prefill), or None."""
+    return pinned_traffic(GATEUP_COUNTERS, cfg)
 
 
 def gateup_algorithmic_bytes(cfg):
@@ -253,6 +271,8 @@ def run_decode(args, torch, M, MI):
                 roofline=dict(bound="hbm", kernel="stream_gemm_kernel<fp8, gate/up + SwiGLU>",
                               achieved=round(gu / (g1 * 1e-3) / 1e9, 1), peak=PEAK_HBM_GBS, unit="GB/s",
                               frac=round(gu / (g1 * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), per_launch_bytes=gu,
+                              traffic=pinned_traffic(DECODE_GATEUP_COUNTERS, cfg),
+                              traffic_unit="HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                               avg_ms=round(g1, 4)))
 
 
