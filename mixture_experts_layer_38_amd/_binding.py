@@ -108,6 +108,17 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _check_tensor(name, t, dtype, shape, device):
+    """Raises ValueError unless t is a contiguous tensor of this dtype and
+    shape on `device` (a bare device pointer carries none of these)."""
+    if not torch.is_tensor(t):
+        raise ValueError(f"{name} must be a tensor, got {type(t).__name__}")
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+
+
 def _stream_handle(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -202,16 +213,53 @@ class MoELayer:
     def _check_x(self, x):
         p = self.params
         want = _TORCH_OF[p.act_dtype]
-        if x.dtype != want or not x.is_cuda or not x.is_contiguous() or x.dim() != 2 or x.shape[1] != p.dim:
+        if (not torch.is_tensor(x) or x.dtype != want or not x.is_cuda or not x.is_contiguous() or x.dim() != 2
+                or x.shape[1] != p.dim):
             raise ValueError(f"x must be a contiguous cuda {want} tensor [T, {p.dim}]")
+
+    def _check_router_inputs(self, x, gate_w, sel_bias):
+        p = self.params
+        _check_tensor("gate_w", gate_w, torch.float32, (p.n_routed, p.dim), x.device)
+        if sel_bias is not None:
+            _check_tensor("sel_bias", sel_bias, torch.float32, (p.n_routed,), x.device)
+
+    def _check_weights(self, x, experts, shared):
+        """Expert and shared weights against the cfg: dtype, shape, device,
+        contiguity (the library receives bare pointers and cannot)."""
+        p = self.params
+        E, D, H, Hs = p.n_routed, p.dim, p.hidden, p.shared_hidden
+        wdt = _TORCH_OF[p.weight_dtype]
+        fp8 = p.weight_dtype == MOE_FP8_E4M3
+        sets = [("experts", experts, (E,), H)]
+        if Hs > 0:
+            if shared is None:
+                raise ValueError("this layer has a shared expert (shared_hidden > 0): pass its weights")
+            sets.append(("shared", shared, (), Hs))
+        for name, w, lead, h in sets:
+            if w is None:
+                raise ValueError(f"{name} weights missing")
+            _check_tensor(f"{name}.gate_up", w.gate_up, wdt, lead + (2 * h, D), x.device)
+            _check_tensor(f"{name}.down", w.down, wdt, lead + (D, h), x.device)
+            if fp8:
+                _check_tensor(f"{name}.gate_up_scale", getattr(w, "gate_up_scale", None), torch.float32,
+                              lead + (2 * h // 128, D // 128), x.device)
+                _check_tensor(f"{name}.down_scale", getattr(w, "down_scale", None), torch.float32,
+                              lead + (D // 128, h // 128), x.device)
 
     def forward(self, x, gate_w, sel_bias, experts, shared, out=None, expert_counts=None, stream=None):
         """out [T, D] (out dtype) and, if given, expert_counts [E] int32 are written."""
         p = self.params
         self._check_x(x)
         T = x.shape[0]
+        self._check_router_inputs(x, gate_w, sel_bias)
+        self._check_weights(x, experts, shared)
+        if p.shared_hidden == 0:
+            shared = None
         if out is None:
             out = torch.empty((T, p.dim), dtype=_TORCH_OF[p.out_dtype], device=x.device)
+        _check_tensor("out", out, _TORCH_OF[p.out_dtype], (T, p.dim), x.device)
+        if expert_counts is not None:
+            _check_tensor("expert_counts", expert_counts, torch.int32, (p.n_routed,), x.device)
         ew, sw = _weights(experts), _weights(shared)
         st = self.lib.moe_layer_forward(self.handle, _ptr(x), T, _ptr(gate_w), _ptr(sel_bias),
                                         ctypes.byref(ew), None if sw is None else ctypes.byref(sw), _ptr(out),
@@ -229,8 +277,11 @@ class MoELayer:
         self._check_x(x)
         T = x.shape[0]
         dev = x.device
-        if d_out.dtype != torch.float32 or not d_out.is_contiguous() or tuple(d_out.shape) != (T, p.dim):
-            raise ValueError("d_out must be a contiguous float32 tensor [T, D]")
+        _check_tensor("d_out", d_out, torch.float32, (T, p.dim), dev)
+        self._check_router_inputs(x, gate_w, sel_bias)
+        self._check_weights(x, experts, shared)
+        if p.shared_hidden == 0:
+            shared = None
         f32 = dict(dtype=torch.float32, device=dev)
         g = dict(dx=torch.empty((T, p.dim), **f32), d_gate_w=torch.empty((p.n_routed, p.dim), **f32),
                  d_gate_up=torch.empty((p.n_routed, 2 * p.hidden, p.dim), **f32),
@@ -254,6 +305,7 @@ class MoELayer:
         """(topk_idx [T, K] int32, topk_gate [T, K] fp32, expert_counts [E] int32)."""
         p = self.params
         self._check_x(x)
+        self._check_router_inputs(x, gate_w, sel_bias)
         T = x.shape[0]
         idx = torch.empty((T, p.top_k), dtype=torch.int32, device=x.device)
         gate = torch.empty((T, p.top_k), dtype=torch.float32, device=x.device)
@@ -266,24 +318,33 @@ class MoELayer:
     def dispatch(self, topk_idx, stream=None):
         """(offsets [E+1], row_token [T*K], slot_row [T*K]), all int32."""
         p = self.params
+        if not torch.is_tensor(topk_idx) or topk_idx.dim() != 2:
+            raise ValueError(f"topk_idx must be an int32 cuda tensor [T, {p.top_k}]")
         T = topk_idx.shape[0]
         dev = topk_idx.device
+        _check_tensor("topk_idx", topk_idx, torch.int32, (T, p.top_k), dev)
         offsets = torch.empty((p.n_routed + 1,), dtype=torch.int32, device=dev)
         row_token = torch.empty((max(T * p.top_k, 1),), dtype=torch.int32, device=dev)
         slot_row = torch.empty((max(T * p.top_k, 1),), dtype=torch.int32, device=dev)
-        st = self.lib.moe_dispatch_forward(self.handle, _ptr(topk_idx.contiguous()), T, _ptr(offsets),
+        st = self.lib.moe_dispatch_forward(self.handle, _ptr(topk_idx), T, _ptr(offsets),
                                            _ptr(row_token), _ptr(slot_row), _stream_handle(stream))
         self._check(st, "moe_dispatch_forward")
         return offsets, row_token[:T * p.top_k], slot_row[:T * p.top_k]
 
 
+def _check_counts(expert_counts):
+    if not torch.is_tensor(expert_counts) or expert_counts.dim() != 1 or not expert_counts.is_cuda:
+        raise ValueError("expert_counts must be a 1-d int32 cuda tensor [E]")
+    _check_tensor("expert_counts", expert_counts, torch.int32, (expert_counts.shape[0],), expert_counts.device)
+    return expert_counts.shape[0]
+
+
 def bias_update(expert_counts, sel_bias, gamma: float, stream=None):
     """moe_bias_update: sel_bias [E] fp32 (device, updated in place) from
     expert_counts [E] int32 (device)."""
-    E = expert_counts.shape[0]
-    if sel_bias.dtype != torch.float32 or not sel_bias.is_contiguous() or sel_bias.shape[0] != E:
-        raise ValueError("sel_bias must be a contiguous float32 tensor of E elements")
-    st = load_library().moe_bias_update(_ptr(expert_counts.to(torch.int32).contiguous()), E, float(gamma),
+    E = _check_counts(expert_counts)
+    _check_tensor("sel_bias", sel_bias, torch.float32, (E,), expert_counts.device)
+    st = load_library().moe_bias_update(_ptr(expert_counts), E, float(gamma),
                                         _ptr(sel_bias), _stream_handle(stream))
     if st != MOE_OK:
         raise MoEError(st, "moe_bias_update")
@@ -293,10 +354,9 @@ def bias_update(expert_counts, sel_bias, gamma: float, stream=None):
 def load_stats(expert_counts, stream=None):
     """moe_load_stats: tensor [3] fp32 = (std of load, mean (load - 1/E)^2,
     max violation) from expert_counts [E] int32 (device)."""
-    E = expert_counts.shape[0]
+    E = _check_counts(expert_counts)
     stats = torch.empty((3,), dtype=torch.float32, device=expert_counts.device)
-    st = load_library().moe_load_stats(_ptr(expert_counts.to(torch.int32).contiguous()), E, _ptr(stats),
-                                       _stream_handle(stream))
+    st = load_library().moe_load_stats(_ptr(expert_counts), E, _ptr(stats), _stream_handle(stream))
     if st != MOE_OK:
         raise MoEError(st, "moe_load_stats")
     return stats

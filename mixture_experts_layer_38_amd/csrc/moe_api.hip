@@ -51,6 +51,7 @@ struct moe_cfg {
   float* gw_planes;
   int32_t* pre_h;
   int32_t* pre_x;
+  size_t logit_rows;  // rows of the partial-logit planes region ([logit_rows][E] fp32)
   int last_hip_error;
   // stage timing
   bool timing;
@@ -211,8 +212,10 @@ moe_status moe_cfg_create(const moe_params* p, moe_cfg** out) {
   const size_t act = (p->weight_dtype == MOE_F32) ? 4 : 2;  // h and y element size
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + std::max<size_t>(bytes, 1)); return o; };
-  // partial-logit planes: router_splits(T) * T <= 64 * CUs + T for every T
+  // partial-logit planes: the router uses at most 64 * CUs / T + 1 planes of
+  // T rows (checked again before each launch)
   const size_t lg = (size_t)64 * c->num_cus + Tm;
+  c->logit_rows = lg;
   const size_t o_logits = take(lg * E * 4), o_idx = take(Tm * K * 4), o_gate = take(Tm * K * 4);
   const size_t o_wsplit = (p->act_dtype == MOE_BF16) ? take(3 * E * D * 2) : 0;
   const size_t o_counts = take(E * 4), o_offsets = take((E + 1) * 4), o_chunk = take(((Tm * K + kDispatchChunk - 1) / kDispatchChunk + 1) * E * 4);
@@ -363,6 +366,7 @@ moe_status moe_router_forward(moe_cfg* c, const void* x, int T, const float* gat
   r.rsf = c->p.routed_scaling_factor;
   r.num_cus = c->num_cus;
   r.w_split = c->w_split;
+  r.logit_rows = c->logit_rows;
   r.hist = 1;
   hipError_t e = launch_router(r, s);
   return e == hipSuccess ? MOE_OK : hip_fail(c, e);
@@ -452,6 +456,7 @@ moe_status moe_layer_forward(moe_cfg* c, const void* x, int T, const float* gate
   r.rsf = p.routed_scaling_factor;
   r.num_cus = c->num_cus;
   r.w_split = c->w_split;
+  r.logit_rows = c->logit_rows;
   r.hist = !small_dispatch(T * p.top_k);  // the one-workgroup dispatch counts the entries itself
   if ((e = launch_router(r, s)) != hipSuccess) return hip_fail(c, e);
   mark(c, 1, s);
@@ -571,6 +576,7 @@ moe_status moe_layer_backward(moe_cfg* c, const void* x, int T, const float* gat
   r.rsf = p.routed_scaling_factor;
   r.num_cus = c->num_cus;
   r.w_split = c->w_split;
+  r.logit_rows = c->logit_rows;
   r.hist = !small_dispatch(T * p.top_k);  // the one-workgroup dispatch counts the entries itself
   if ((e = launch_router(r, s)) != hipSuccess) return hip_fail(c, e);
   DispatchArgs d{};

@@ -166,6 +166,7 @@ struct RouterArgs {
   float rsf;
   int num_cus;
   int splits;           // set by launch_router
+  size_t logit_rows;    // rows of E floats the partial-logit planes may use (splits * T of them)
   uint16_t* w_split;    // [3][E][D] bf16 planes of gate_w (bf16 activations), or null
   int hist;             // 1: also count the selections into counts (else the dispatch does)
 };

@@ -412,19 +412,23 @@ __global__ __launch_bounds__(256) void reduce_planes_kernel(float* __restrict__ 
   logits[i] = v;
 }
 
-// K splits of the fp32 kernel: about one workgroup per CU; at most
-// 64*num_cus/T + 1 planes, which the partial-logit workspace holds
-int router_splits(int T, int D, int E, int num_cus) {
+// Width (a multiple of 32) of each K split of the fp32 kernel: about one
+// workgroup per CU. kc >= D / sp, so there are at most sp planes, and
+// sp <= ceil(num_cus / tiles) <= 64 * num_cus / T + 1 (tiles >= T / 64).
+static int router_kc(int T, int D, int E, int num_cus) {
   const int tiles = ((T + 63) / 64) * ((E + 63) / 64);
   int sp = (num_cus + tiles - 1) / tiles;
   sp = sp < 1 ? 1 : (sp > D / 32 ? D / 32 : sp);
-  const int kc = ((D / sp + 31) / 32) * 32;
+  return ((D + sp - 1) / sp + 31) / 32 * 32;
+}
+
+int router_splits(int T, int D, int E, int num_cus) {
+  const int kc = router_kc(T, D, E, num_cus);
   return (D + kc - 1) / kc;
 }
 
-// K splits of the bf16x3 kernel: about one workgroup per CU, and never more
-// than 32*num_cus/T + 1 planes (the partial-logit workspace holds
-// 64*num_cus + T rows).
+// Width (a multiple of kX3_BK) of each K split of the bf16x3 kernel: about
+// one workgroup per CU, at most sp <= 32 * num_cus / T + 1 planes.
 static int router_x3_kc(int T, int D, int E, int num_cus) {
   const int tiles = ((T + kX3_BT - 1) / kX3_BT) * ((E + kX3_BE - 1) / kX3_BE);
   int sp = (num_cus + tiles - 1) / tiles;
@@ -432,7 +436,7 @@ static int router_x3_kc(int T, int D, int E, int num_cus) {
   sp = sp > cap ? cap : sp;
   sp = sp > D / kX3_BK ? D / kX3_BK : sp;
   sp = sp < 1 ? 1 : sp;
-  return ((D / sp + kX3_BK - 1) / kX3_BK) * kX3_BK;
+  return ((D + sp - 1) / sp + kX3_BK - 1) / kX3_BK * kX3_BK;
 }
 
 hipError_t launch_router(const RouterArgs& a0, hipStream_t s) {
@@ -441,6 +445,7 @@ hipError_t launch_router(const RouterArgs& a0, hipStream_t s) {
   if (a.act_bf16 && a.w_split && a.T >= kRouterX3MinTokens) {
     const int kc = router_x3_kc(a.T, a.D, a.E, a.num_cus);
     a.splits = (a.D + kc - 1) / kc;
+    if ((size_t)a.splits * a.T > a.logit_rows) return hipErrorInvalidValue;
     const size_t n4 = (size_t)a.E * a.D / 4;
     hipLaunchKernelGGL(split_gate_w_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, a.gate_w,
                        a.w_split, n4);
@@ -451,9 +456,9 @@ hipError_t launch_router(const RouterArgs& a0, hipStream_t s) {
     hipLaunchKernelGGL(router_logits_x3_kernel, g, dim3(256), 0, s, static_cast<const uint16_t*>(a.x),
                        a.w_split, a.logits, a.T, a.D, a.E, kc, n_et, n_tiles);
   } else {
-    const int sp0 = router_splits(a.T, a.D, a.E, a.num_cus);
-    const int kc = ((a.D / sp0 + 31) / 32) * 32;
+    const int kc = router_kc(a.T, a.D, a.E, a.num_cus);
     a.splits = (a.D + kc - 1) / kc;
+    if ((size_t)a.splits * a.T > a.logit_rows) return hipErrorInvalidValue;
     dim3 g1((a.T + 63) / 64, (a.E + 63) / 64, a.splits);
     if (a.act_bf16)
       hipLaunchKernelGGL(router_logits_kernel<true>, g1, dim3(256), 0, s, a.x, a.gate_w, a.logits,

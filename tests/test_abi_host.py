@@ -3,6 +3,7 @@ header declares, and rejects invalid layers before touching any device."""
 import ctypes
 
 import pytest
+import torch
 
 import mixture_experts_layer_38_amd as M
 
@@ -124,3 +125,15 @@ def test_quantizer_entry_point_rejects_bad_arguments():
     assert lib.moe_quantize_e4m3_1x128(b, 2, 128, None, b, None) == bad
     assert lib.moe_quantize_e4m3_1x128(b, 2, 128, b, None, None) == bad
     assert lib.moe_quantize_e4m3_1x128(None, 0, 128, None, None, None) == M.MOE_OK
+
+
+def test_binding_tensor_check():
+    """The binding's tensor check (CPU tensors stand in for device ones)."""
+    from mixture_experts_layer_38_amd._binding import _check_tensor
+    cpu = torch.device("cpu")
+    t = torch.zeros((4, 8), dtype=torch.float32)
+    _check_tensor("t", t, torch.float32, (4, 8), cpu)
+    for args in ((t, torch.bfloat16, (4, 8)), (t, torch.float32, (4, 9)), (t.t(), torch.float32, (8, 4)),
+                 (None, torch.float32, (4, 8)), (t.numpy(), torch.float32, (4, 8))):
+        with pytest.raises(ValueError):
+            _check_tensor("t", args[0], args[1], args[2], cpu)

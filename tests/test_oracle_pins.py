@@ -144,6 +144,44 @@ def test_e4m3_act_ffn_within_the_quantisation_error():
     assert np.allclose(out, quant * (1 + r["gate"].sum(axis=1, keepdims=True)), rtol=1e-12, atol=1e-12)
 
 
+def test_e4m3_act_ffn_hand_worked_example():
+    """Each quantisation step of the e4m3-activation FFN on its own, worked by
+    hand (D = hidden = 128, one block each):
+
+    * u = [448, 12.4, 0, ...]: the block maximum is 448, so the scale is 1,
+      and 12.4 becomes the e4m3 value 12 (between 8 and 16 the format steps
+      by 1); gate rows 0 and 1 read u[1], so both gate pre-activations are
+      12, not 12.4;
+    * up row 0 is 1/448 and up row 1 is 16.5/448^2 on u[0] = 448: up values
+      1 and 16.5/448;
+    * h = [s, s*16.5/448, 0, ...] with s = SiLU(12) = 12 / (1 + e^-12): the
+      block maximum s maps to 448 (scale s/448), and h[1] / scale = 16.5
+      becomes the e4m3 value 16 (between 16 and 32 the format steps by 2);
+    * the down projection picks h[0] and h[1] into outputs 0 and 1.
+
+    So out = [s, 16 s / 448, 0, ...] up to the float32 roundings of h and of
+    the scales (a few 2^-24). Skipping the quantisation of u gives
+    SiLU(12.4) in out[0] (3 % off); skipping that of h gives 16.5 s / 448 in
+    out[1] (3 % off); rounding h to bfloat16 before quantising it gives 12.0
+    in out[0] (5e-6 off)."""
+    D = h = 128
+    u = np.zeros((1, D))
+    u[0, 0], u[0, 1] = 448.0, 12.4
+    u = u.astype(np.float32).astype(np.float64)
+    wg = np.zeros((h, D))
+    wg[0, 1] = wg[1, 1] = 1.0
+    wu = np.zeros((h, D))
+    wu[0, 0] = 1.0 / 448.0
+    wu[1, 0] = 16.5 / 448.0 ** 2
+    wd = np.zeros((D, h))
+    wd[0, 0] = wd[1, 1] = 1.0
+    got = O.swiglu_ffn_e4m3_act(u, wg, wu, wd)[0]
+    s = 12.0 / (1.0 + math.exp(-12.0))
+    want = np.zeros(D)
+    want[0], want[1] = s, 16.0 * s / 448.0
+    assert np.allclose(got, want, rtol=1e-6, atol=0.0), (got[:2], want[:2])
+
+
 # ----------------------------------------------------------------------------
 # router
 # ----------------------------------------------------------------------------
@@ -685,6 +723,30 @@ def test_pins_catch_planted_bugs(monkeypatch):
     with pytest.raises(AssertionError):
         test_quantize_act_closed_forms()
     monkeypatch.setattr(O, "quantize_act_1x128", good_q)
+
+    good_ffn8 = O.swiglu_ffn_e4m3_act
+
+    def qdq(v):
+        return O.dequant_act_1x128(*O.quantize_act_1x128(np.asarray(v).astype(np.float32)))
+
+    def u_not_quantised(uu, g, up, dn):  # only h quantised
+        hh = O.silu(uu @ g.T) * (uu @ up.T)
+        return qdq(hh) @ dn.T
+
+    def h_not_quantised(uu, g, up, dn):  # only u quantised
+        uq = qdq(uu)
+        return (O.silu(uq @ g.T) * (uq @ up.T)) @ dn.T
+
+    def h_via_bf16(uu, g, up, dn):  # h rounded to bfloat16 before its quantisation
+        uq = qdq(uu)
+        hh = torch.from_numpy(O.silu(uq @ g.T) * (uq @ up.T)).to(torch.bfloat16).double().numpy()
+        return qdq(hh) @ dn.T
+    for bad in (u_not_quantised, h_not_quantised, h_via_bf16):
+        monkeypatch.setattr(O, "swiglu_ffn_e4m3_act", bad)
+        with pytest.raises(AssertionError):
+            test_e4m3_act_ffn_hand_worked_example()
+    monkeypatch.setattr(O, "swiglu_ffn_e4m3_act", good_ffn8)
+    test_e4m3_act_ffn_hand_worked_example()
 
     good_sg = O.silu_grad
     monkeypatch.setattr(O, "silu_grad", lambda z: 1.0 / (1.0 + np.exp(-z)))  # sigma(z) for SiLU'(z)
