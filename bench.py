@@ -213,6 +213,57 @@ def run_prefill(args, torch, M, MI):
     return res
 
 
+def run_config(args, torch, M, MI, name):
+    """One of the other workloads: W warm-ups, then K steps timed end to end
+    (HIP events on the library's stream, no per-stage events), then an equal
+    pass with per-stage events for the gate/up kernel's roofline."""
+    cfg = MI.CONFIGS[name]
+    inp = MI.make_layer(cfg, "cuda")
+    layer = M.MoELayer.from_config(cfg)
+    out = torch.empty((cfg.T, cfg.D), dtype=torch.float32, device="cuda")
+    counts = torch.empty((cfg.E,), dtype=torch.int32, device="cuda")
+
+    def step():
+        layer.forward(inp.x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared, out=out, expert_counts=counts)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.steps):
+        step()
+    b.record()
+    b.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    layer.set_stage_timing(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    stages, calls = layer.stage_times()
+    layer.set_stage_timing(False)
+    stage_avg = {k: v / max(calls, 1) for k, v in stages.items()}
+    flop = mfma_flops(cfg)
+    res = dict(T=cfg.T, ms_per_step=round(ms, 4), routed_tokens_per_s=round(cfg.T / (ms * 1e-3), 1),
+               assignments_per_s=round(cfg.T * cfg.K / (ms * 1e-3), 1),
+               stages_ms={k: round(v, 4) for k, v in stage_avg.items()})
+    if cfg.weight == "f32":
+        # the tiny fp32 layer: seven launches of a few microseconds each
+        res["bound"] = "launch latency"
+        res["expert_flop"] = flop
+    else:
+        g1 = stage_avg["gate_up_gemm"]
+        res["mfma_frac"] = round(flop / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4)
+        res["roofline"] = dict(bound="mfma", kernel="grouped_gemm_bf16_kernel<0> (gate/up + SwiGLU)",
+                               achieved=round(gateup_flops(cfg) / (g1 * 1e-3) / 1e12, 2), peak=PEAK_BF16_TFLOPS,
+                               unit="TFLOP/s", frac=round(gateup_flops(cfg) / (g1 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                               per_launch_flop=gateup_flops(cfg), avg_ms=round(g1, 4))
+    log(f"{name}: {ms:.4f} ms/step, stages {res['stages_ms']}")
+    del layer, inp, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def decode_bytes(cfg, n_touched):
     E, D, H, Hs = cfg.E, cfg.D, cfg.H, cfg.Hs
     per_expert = 3 * H * D + 4 * ((2 * H // 128) * (D // 128) + (D // 128) * (H // 128))
@@ -276,32 +327,60 @@ def run_decode(args, torch, M, MI):
                               avg_ms=round(g1, 4)))
 
 
-def cpu_baseline(res, n_sample):
-    """The CPU oracle, as it stands, on the first n_sample tokens of the same
-    workload (routing and output of those tokens)."""
+def cpu_baseline(res, n_experts):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload,
+    timed in two stages with every weight decoded before the clock starts:
+    routing (O.route) over all T tokens, and the expert FFN (O.swiglu_ffn,
+    the oracle's per-expert evaluation) for every token routed to n_experts
+    seeded experts plus the shared expert on as many tokens. The stage times
+    per token are then combined into routed tokens/s: a token needs its
+    routing, K routed expert FFNs and the shared FFN."""
     import numpy as np
 
     from oracle import adapter as A
     from oracle import moe_oracle as O
     cfg, inp = res["cfg"], res["inp"]
-    tokens = np.arange(n_sample)
-    # inputs handed over before the clock starts
-    x = A.decode_tensor(inp.x[:n_sample])
+    u = A.decode_tensor(inp.x)
     gw = A.decode_tensor(inp.gate_w)
     bias = None if inp.sel_bias is None else A.decode_tensor(inp.sel_bias)
+    p = A.router_params(cfg)
     t0 = time.perf_counter()
-    out, R = O.layer_forward(A.router_params(cfg), x, gw, bias, A.routed_expert_fn(inp.experts),
-                             A.shared_expert_fn(inp.shared), add_residual=cfg.add_residual)
-    dt = time.perf_counter() - t0
+    R = O.route(u, gw, bias, p)
+    t_route = time.perf_counter() - t0
+    idx = R["idx"]
+    used = np.nonzero(np.bincount(idx.ravel(), minlength=cfg.E))[0]
+    experts = np.sort(np.random.default_rng(0).choice(used, size=min(n_experts, len(used)), replace=False))
+    fn = A.routed_expert_fn(inp.experts)
+    weights = {int(e): fn(int(e)) for e in experts}  # decoded before the clock
+    rows = {e: u[np.nonzero((idx == e).any(axis=1))[0]] for e in weights}
+    pairs = sum(len(r) for r in rows.values())
+    t0 = time.perf_counter()
+    for e, w in weights.items():
+        O.swiglu_ffn(rows[e], *w)
+    t_routed = time.perf_counter() - t0
+    t_shared, n_sh = 0.0, 0
+    if inp.shared is not None:
+        sw = A.shared_expert_fn(inp.shared)()
+        n_sh = min(cfg.T, max(1, pairs // cfg.K))
+        t0 = time.perf_counter()
+        O.swiglu_ffn(u[:n_sh], *sw)
+        t_shared = time.perf_counter() - t0
+    per_tok_route = t_route / cfg.T
+    per_tok_ffn = cfg.K * t_routed / pairs + (t_shared / n_sh if n_sh else 0.0)
     try:
         from threadpoolctl import threadpool_info
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count() or 1
-    return dict(value=round(n_sample / dt, 4), unit="routed tokens/s", cores=int(cores), kind="oracle",
-                sample=f"first {n_sample} tokens of {cfg.name} (routing + shared + {cfg.K} routed expert FFNs "
-                       f"each, float64, expert weights decoded per touched expert); {dt:.1f} s",
-                seconds=round(dt, 2), touched_experts=int(len(np.unique(R['idx']))))
+    return dict(value=round(1.0 / (per_tok_route + per_tok_ffn), 4), unit="routed tokens/s", cores=int(cores),
+                kind="oracle",
+                sample=(f"{cfg.name}: routing of all {cfg.T} tokens ({t_route:.1f} s); routed FFNs of the "
+                        f"{pairs} (token, expert) pairs of {len(weights)} seeded experts ({t_routed:.1f} s) and "
+                        f"the shared FFN of {n_sh} tokens ({t_shared:.1f} s), float64, weights decoded before "
+                        f"the clock; value = 1 / (routing + K routed FFNs + shared FFN) per token"),
+                routing_tokens_per_s=round(1.0 / per_tok_route, 1),
+                ffn_tokens_per_s=round(1.0 / per_tok_ffn, 4),
+                seconds=round(t_route + t_routed + t_shared, 2))
 
 
 def main():
@@ -314,7 +393,10 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
-    ap.add_argument("--cpu-sample", type=int, default=40)
+    ap.add_argument("--cpu-experts", type=int, default=6,
+                    help="experts whose routed FFNs the CPU baseline times")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the tiny, group-limited and V2-shaped workloads")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run one plain 1 GiB device-to-device copy first (a known-size reference "
                          "for hardware byte counters)")
@@ -369,12 +451,15 @@ def main():
     if "backward" in res:
         line["backward"] = res["backward"]
     if not args.no_cpu_baseline:
-        log(f"timing the CPU oracle on {args.cpu_sample} tokens")
-        line["cpu_baseline"] = cpu_baseline(res, args.cpu_sample)
+        log(f"timing the CPU oracle (routing of every token, FFNs of {args.cpu_experts} experts)")
+        line["cpu_baseline"] = cpu_baseline(res, args.cpu_experts)
+        log(f"cpu baseline: {line['cpu_baseline']}")
     del res
     torch.cuda.empty_cache()
     if not args.no_decode:
         line["decode"] = run_decode(args, torch, M, MI)
+    if not args.no_other_configs:
+        line["configs"] = {n: run_config(args, torch, M, MI, n) for n in ("tiny_f32", "group_bf16", "v2_prefill")}
     print(json.dumps(line), flush=True)
 
 

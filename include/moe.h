@@ -232,6 +232,38 @@ moe_status moe_quantize_e4m3_1x128(const void* x, int rows, int cols, uint8_t* c
 moe_status moe_bias_update(const int32_t* expert_counts, int E, float gamma, float* sel_bias, void* stream);
 moe_status moe_load_stats(const int32_t* expert_counts, int E, float* stats, void* stream);
 
+/* Score column sums for the importance statistic (the load-balance code in the
+ * DeepSeekMoE + MLA notes, page 3, sums every token's scores per expert).
+ * With score_sum set (device memory, [E] fp32), every later
+ * moe_layer_forward and moe_router_forward on this cfg also writes
+ *   score_sum[e] = sum over the call's T tokens of s[t][e]
+ * (s = the unbiased softmax or sigmoid scores of all E experts, fp32; summed
+ * in token order over chunks of 256 tokens, the chunks added in order in
+ * double, so repeated calls give identical bits; T == 0 writes zeros). It adds
+ * a write of the T x E scores and two small launches to the router stage.
+ * NULL turns it off (the default). The pointer is used by calls on the cfg's
+ * stream until it is replaced. MOE_ERR_INVALID_ARG for a NULL cfg. */
+moe_status moe_cfg_set_score_sums(moe_cfg* cfg, float* score_sum);
+
+/* The balance statistics of that code, expert- and device-level, in one
+ * small launch (no cfg; stream-ordered). Inputs in device memory:
+ *   expert_counts [E] int32 >= 0, score_sum [E] fp32 >= 0 (as written above).
+ * load_e = counts_e / sum(counts), importance_e = score_sum_e / sum(score_sum);
+ * devices own contiguous runs of E / n_devices experts (the placement of one
+ * expert group per device), device load and importance are the sums over their
+ * experts, renormalised to sum 1. Written to stats [9] fp32 (device memory):
+ *   [0] std of load (n-1 denominator)    [1] mean_e (load_e - 1/E)^2
+ *   [2] max_e counts_e / (sum/E) - 1      [3] std of importance
+ *   [4] mean_e (importance_e - 1/E)^2     [5] std of device load
+ *   [6] mean_d (dev_load_d - 1/n_devices)^2
+ *   [7] std of device importance          [8] mean_d (dev_imp_d - 1/n_devices)^2
+ * The losses are the page's loss_load / loss_importance terms before their
+ * weights alpha. Statistics of a quantity whose total is 0 are 0; a std over
+ * one value is 0. MOE_ERR_INVALID_ARG (nothing launched) for a NULL pointer, E
+ * outside [1, 512], or n_devices outside [1, E] or not dividing E. */
+moe_status moe_balance_stats(const int32_t* expert_counts, const float* score_sum, int E, int n_devices,
+                             float* stats, void* stream);
+
 /* Stage timing (observability): when enabled, moe_layer_forward records HIP
  * events on its stream around each stage -- 0 router, 1 dispatch, 2 gate/up
  * GEMM, 3 down GEMM, 4 combine -- for up to MOE_TIMING_CALLS calls.

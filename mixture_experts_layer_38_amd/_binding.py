@@ -80,13 +80,15 @@ def load_library() -> ctypes.CDLL:
     lib.moe_bias_update.argtypes = [vp, ctypes.c_int, ctypes.c_float, vp, vp]
     lib.moe_load_stats.argtypes = [vp, ctypes.c_int, vp, vp]
     lib.moe_quantize_e4m3_1x128.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+    lib.moe_cfg_set_score_sums.argtypes = [vp, vp]
+    lib.moe_balance_stats.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, vp]
     lib.moe_layer_backward.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.POINTER(MoeWeights),
                                        ctypes.POINTER(MoeWeights), vp, vp, vp, ctypes.POINTER(MoeWeightGrads),
                                        ctypes.POINTER(MoeWeightGrads), vp]
     for f in ("moe_cfg_create", "moe_cfg_destroy", "moe_layer_forward", "moe_router_forward",
               "moe_dispatch_forward", "moe_cfg_last_hip_error", "moe_cfg_set_stage_timing",
               "moe_cfg_stage_times", "moe_bias_update", "moe_load_stats", "moe_quantize_e4m3_1x128",
-              "moe_layer_backward"):
+              "moe_layer_backward", "moe_cfg_set_score_sums", "moe_balance_stats"):
         getattr(lib, f).restype = ctypes.c_int
     del i32p
     _lib = lib
@@ -205,6 +207,17 @@ class MoELayer:
         calls = ctypes.c_int()
         self._check(self.lib.moe_cfg_stage_times(self.handle, ms, ctypes.byref(calls)), "moe_cfg_stage_times")
         return dict(zip(self.STAGES, list(ms))), calls.value
+
+    def set_score_sums(self, score_sum):
+        """moe_cfg_set_score_sums: later forward / router calls also write the
+        column sums of the scores into score_sum ([E] fp32 cuda tensor, kept
+        alive by the layer); None turns it off."""
+        if score_sum is not None:
+            _check_tensor("score_sum", score_sum, torch.float32, (self.params.n_routed,), score_sum.device)
+            if not score_sum.is_cuda:
+                raise ValueError("score_sum must be a cuda tensor")
+        self._score_sum = score_sum
+        self._check(self.lib.moe_cfg_set_score_sums(self.handle, _ptr(score_sum)), "moe_cfg_set_score_sums")
 
     def _check(self, st, what):
         if st != MOE_OK:
@@ -359,6 +372,23 @@ def load_stats(expert_counts, stream=None):
     st = load_library().moe_load_stats(_ptr(expert_counts), E, _ptr(stats), _stream_handle(stream))
     if st != MOE_OK:
         raise MoEError(st, "moe_load_stats")
+    return stats
+
+
+BALANCE_STATS = ("load_std", "load_loss", "max_violation", "importance_std", "importance_loss",
+                 "device_load_std", "device_load_loss", "device_importance_std", "device_importance_loss")
+
+
+def balance_stats(expert_counts, score_sum, n_devices: int = 1, stream=None):
+    """moe_balance_stats: tensor [9] fp32 (names in BALANCE_STATS) from
+    expert_counts [E] int32 and score_sum [E] fp32 (device)."""
+    E = _check_counts(expert_counts)
+    _check_tensor("score_sum", score_sum, torch.float32, (E,), expert_counts.device)
+    stats = torch.empty((len(BALANCE_STATS),), dtype=torch.float32, device=expert_counts.device)
+    st = load_library().moe_balance_stats(_ptr(expert_counts), _ptr(score_sum), E, int(n_devices), _ptr(stats),
+                                          _stream_handle(stream))
+    if st != MOE_OK:
+        raise MoEError(st, "moe_balance_stats")
     return stats
 
 

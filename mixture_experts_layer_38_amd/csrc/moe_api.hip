@@ -52,6 +52,8 @@ struct moe_cfg {
   int32_t* pre_h;
   int32_t* pre_x;
   size_t logit_rows;  // rows of the partial-logit planes region ([logit_rows][E] fp32)
+  float* score_part;  // [score_part_rows(max_tokens)][E] partial score column sums
+  float* score_sum;   // caller's [E] buffer for the score column sums, or null
   int last_hip_error;
   // stage timing
   bool timing;
@@ -167,16 +169,7 @@ __global__ void zero_counts_kernel(int32_t* p, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0;
 }
 
-__global__ void zero_f32_kernel(float* p, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    p[i] = 0.f;
-}
-
-hipError_t zero_f32(float* p, size_t n, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(zero_f32_kernel, dim3((unsigned)std::min<size_t>((n + 255) / 256, 16384)), dim3(256), 0, s, p, n);
-  return hipGetLastError();
-}
+hipError_t zero_f32(float* p, size_t n, hipStream_t s) { return launch_zero_f32(p, n, s); }
 
 }  // namespace
 
@@ -217,6 +210,7 @@ moe_status moe_cfg_create(const moe_params* p, moe_cfg** out) {
   const size_t lg = (size_t)64 * c->num_cus + Tm;
   c->logit_rows = lg;
   const size_t o_logits = take(lg * E * 4), o_idx = take(Tm * K * 4), o_gate = take(Tm * K * 4);
+  const size_t o_spart = take((size_t)score_part_rows((int)Tm) * E * 4);
   const size_t o_wsplit = (p->act_dtype == MOE_BF16) ? take(3 * E * D * 2) : 0;
   const size_t o_counts = take(E * 4), o_offsets = take((E + 1) * 4), o_chunk = take(((Tm * K + kDispatchChunk - 1) / kDispatchChunk + 1) * E * 4);
   const size_t o_pre1 = take((E + 2) * 4), o_pre2 = take((E + 2) * 4);
@@ -245,6 +239,7 @@ moe_status moe_cfg_create(const moe_params* p, moe_cfg** out) {
     return MOE_ERR_OOM;
   }
   c->logits = (float*)(c->ws + o_logits);
+  c->score_part = (float*)(c->ws + o_spart);
   c->w_split = (p->act_dtype == MOE_BF16) ? (uint16_t*)(c->ws + o_wsplit) : nullptr;
   c->idx = (int32_t*)(c->ws + o_idx);
   c->gate = (float*)(c->ws + o_gate);
@@ -356,6 +351,7 @@ moe_status moe_router_forward(moe_cfg* c, const void* x, int T, const float* gat
   if (T == 0) {
     hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(256), 0, s, counts, c->p.n_routed);
     hipError_t e = hipGetLastError();
+    if (e == hipSuccess && c->score_sum) e = zero_f32(c->score_sum, c->p.n_routed, s);
     return e == hipSuccess ? MOE_OK : hip_fail(c, e);
   }
   RouterArgs r{};
@@ -367,6 +363,8 @@ moe_status moe_router_forward(moe_cfg* c, const void* x, int T, const float* gat
   r.num_cus = c->num_cus;
   r.w_split = c->w_split;
   r.logit_rows = c->logit_rows;
+  r.score_sum = c->score_sum;
+  r.score_part = c->score_part;
   r.hist = 1;
   hipError_t e = launch_router(r, s);
   return e == hipSuccess ? MOE_OK : hip_fail(c, e);
@@ -393,6 +391,20 @@ moe_status moe_bias_update(const int32_t* expert_counts, int E, float gamma, flo
 moe_status moe_load_stats(const int32_t* expert_counts, int E, float* stats, void* stream) {
   if (!expert_counts || !stats || E < 1 || E > kMaxExperts) return MOE_ERR_INVALID_ARG;
   return launch_balance(expert_counts, E, 0.f, nullptr, stats, (hipStream_t)stream) == hipSuccess
+             ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_cfg_set_score_sums(moe_cfg* c, float* score_sum) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  c->score_sum = score_sum;
+  return MOE_OK;
+}
+
+moe_status moe_balance_stats(const int32_t* expert_counts, const float* score_sum, int E, int n_devices,
+                             float* stats, void* stream) {
+  if (!expert_counts || !score_sum || !stats || E < 1 || E > kMaxExperts) return MOE_ERR_INVALID_ARG;
+  if (n_devices < 1 || n_devices > E || E % n_devices != 0) return MOE_ERR_INVALID_ARG;
+  return launch_balance_stats(expert_counts, score_sum, E, n_devices, stats, (hipStream_t)stream) == hipSuccess
              ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -432,6 +444,10 @@ moe_status moe_layer_forward(moe_cfg* c, const void* x, int T, const float* gate
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return hip_fail(c, e);
     }
+    if (c->score_sum) {
+      hipError_t e = zero_f32(c->score_sum, p.n_routed, s);
+      if (e != hipSuccess) return hip_fail(c, e);
+    }
     return MOE_OK;
   }
   if (!x || !gate_w || !out || !expert_w || !expert_w->gate_up || !expert_w->down) return MOE_ERR_INVALID_ARG;
@@ -457,6 +473,8 @@ moe_status moe_layer_forward(moe_cfg* c, const void* x, int T, const float* gate
   r.num_cus = c->num_cus;
   r.w_split = c->w_split;
   r.logit_rows = c->logit_rows;
+  r.score_sum = c->score_sum;
+  r.score_part = c->score_part;
   r.hist = !small_dispatch(T * p.top_k);  // the one-workgroup dispatch counts the entries itself
   if ((e = launch_router(r, s)) != hipSuccess) return hip_fail(c, e);
   mark(c, 1, s);

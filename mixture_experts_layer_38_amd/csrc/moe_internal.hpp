@@ -169,7 +169,11 @@ struct RouterArgs {
   size_t logit_rows;    // rows of E floats the partial-logit planes may use (splits * T of them)
   uint16_t* w_split;    // [3][E][D] bf16 planes of gate_w (bf16 activations), or null
   int hist;             // 1: also count the selections into counts (else the dispatch does)
+  float* score_sum;     // [E] column sums of the scores over the T tokens, or null
+  float* score_part;    // [score_part_rows(T)][E] partial sums (when score_sum is set)
 };
+// rows of partial score sums launch_router needs for T tokens
+int score_part_rows(int T);
 // from this many tokens on, bf16 activations take the bf16x3 logits kernel
 constexpr int kRouterX3MinTokens = 512;
 // Up to this many (token, slot) entries the dispatch runs in one workgroup
@@ -311,5 +315,10 @@ hipError_t launch_layer_backward(const BwdArgs& a, hipStream_t s);
 
 // one workgroup: bias update (bias != null) and/or load statistics (stats != null)
 hipError_t launch_balance(const int32_t* counts, int E, float gamma, float* bias, float* stats, hipStream_t s);
+// one workgroup: load and importance statistics, expert- and device-level
+hipError_t launch_balance_stats(const int32_t* counts, const float* score_sum, int E, int n_devices, float* stats,
+                                hipStream_t s);
+// dst[0..n) = 0 (a fill kernel, so that the call can sit in a captured graph)
+hipError_t launch_zero_f32(float* dst, size_t n, hipStream_t s);
 
 }  // namespace moe

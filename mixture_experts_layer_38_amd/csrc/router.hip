@@ -291,7 +291,7 @@ __global__ __launch_bounds__(256) void router_select_kernel(RouterArgs a) {
   const int t = blockIdx.x * 4 + wave;
   if (t >= a.T) return;
   const int E = a.E;
-  const float* lrow = a.logits + (size_t)t * E;
+  float* lrow = a.logits + (size_t)t * E;
   float s[kVPL], z[kVPL];
   float lmax = -INFINITY;
 #pragma unroll
@@ -321,6 +321,12 @@ __global__ __launch_bounds__(256) void router_select_kernel(RouterArgs a) {
   for (int j = 0; j < kVPL; ++j) {
     const int e = lane + kWave * j;
     z[j] = s[j] + ((a.bias != nullptr && e < E) ? a.bias[e] : 0.f);
+  }
+  // the scores replace the token's logits when their column sums are wanted
+  if (a.score_sum != nullptr) {
+#pragma unroll
+    for (int j = 0; j < kVPL; ++j)
+      if (lane + kWave * j < E) lrow[lane + kWave * j] = s[j];
   }
 
   // allowed[j]: expert lane+64j may be chosen
@@ -394,6 +400,39 @@ __global__ __launch_bounds__(256) void router_select_kernel(RouterArgs a) {
     a.gate[(size_t)t * a.K + lane] = g;
   }
 }
+
+// Column sums of the scores (the importance statistic of the load-balance
+// code in the DeepSeekMoE + MLA notes, page 3): part[c][e] = sum of s[t][e]
+// over the kScoreChunk tokens of chunk c, in token order (each of the four
+// waves sums a quarter of the chunk, the quarters are added in order); then
+// score_sum[e] = sum over the chunks in order, in double.
+constexpr int kScoreChunk = 256;
+
+__global__ __launch_bounds__(256) void score_part_kernel(const float* __restrict__ scores, int T, int E,
+                                                         float* __restrict__ part) {
+  __shared__ float q[4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  const int t0 = blockIdx.y * kScoreChunk + wave * (kScoreChunk / 4);
+  const int t1 = min(T, t0 + kScoreChunk / 4);
+  float acc = 0.f;
+  if (e < E)
+    for (int t = t0; t < t1; ++t) acc += scores[(size_t)t * E + e];
+  q[wave][lane] = acc;
+  __syncthreads();
+  if (wave == 0 && e < E) part[(size_t)blockIdx.y * E + e] = ((q[0][lane] + q[1][lane]) + q[2][lane]) + q[3][lane];
+}
+
+__global__ __launch_bounds__(512) void score_sum_kernel(const float* __restrict__ part, int chunks, int E,
+                                                        float* __restrict__ score_sum) {
+  const int e = threadIdx.x;
+  if (e >= E) return;
+  double acc = 0.0;
+  for (int c = 0; c < chunks; ++c) acc += (double)part[(size_t)c * E + e];
+  score_sum[e] = (float)acc;
+}
+
+int score_part_rows(int T) { return (T + kScoreChunk - 1) / kScoreChunk; }
 
 // plane 0 += planes 1 .. splits-1, in plane order (one thread per logit);
 // eight planes are loaded at a time, then added in order
@@ -480,6 +519,14 @@ hipError_t launch_router(const RouterArgs& a0, hipStream_t s) {
   else
     hipLaunchKernelGGL(router_select_kernel<kMaxExperts / kWave>, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (a.score_sum != nullptr) {
+    const int chunks = score_part_rows(a.T);
+    hipLaunchKernelGGL(score_part_kernel, dim3((a.E + 63) / 64, chunks), dim3(256), 0, s, a.logits, a.T, a.E,
+                       a.score_part);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(score_sum_kernel, dim3(1), dim3(512), 0, s, a.score_part, chunks, a.E, a.score_sum);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   return a.hist ? launch_histogram(a.idx, a.counts, a.T * a.K, a.E, s) : hipSuccess;
 }
 

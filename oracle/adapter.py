@@ -14,15 +14,24 @@ from . import moe_oracle as O
 
 
 def decode_tensor(t: torch.Tensor, scale: torch.Tensor | None = None) -> np.ndarray:
+    """Exact float64 values of a stored tensor. Large bf16 and e4m3 tensors
+    (expert weights) are widened by torch's conversions, which equal the
+    oracle's own decoders on every code (pinned over all 65536 bf16 and all
+    256 e4m3 codes) and run on every host core; small ones go through the
+    oracle's decoders themselves."""
     t = t.detach().cpu()
+    big = t.numel() >= (1 << 20)
     if t.dtype == torch.float32:
         return O.decode_f32(t.numpy())
     if t.dtype == torch.bfloat16:
-        return O.decode_bf16(t.view(torch.int16).numpy())
+        return t.to(torch.float64).numpy() if big else O.decode_bf16(t.view(torch.int16).numpy())
     if t.dtype == torch.uint8:
         if scale is None:
             raise ValueError("e4m3 codes need their block scales")
-        return O.dequant_e4m3_blocks(t.numpy(), scale.detach().cpu().numpy())
+        sc = scale.detach().cpu().numpy()
+        if big:
+            return O.apply_block_scales(t.contiguous().view(torch.float8_e4m3fn).to(torch.float64).numpy(), sc)
+        return O.dequant_e4m3_blocks(t.numpy(), sc)
     raise TypeError(t.dtype)
 
 

@@ -99,7 +99,13 @@ def dequant_e4m3_blocks(codes, scale, block: int = 128) -> np.ndarray:
     if _E4M3_TABLE is None:
         _E4M3_TABLE = decode_e4m3(np.arange(256))
     c = np.asarray(codes)
-    q = _E4M3_TABLE[c.astype(np.intp)]
+    return apply_block_scales(_E4M3_TABLE[c.astype(np.intp)], scale, block)
+
+
+def apply_block_scales(q, scale, block: int = 128) -> np.ndarray:
+    """w[r, c] = q[r, c] * scale[r // block, c // block], in float64, for
+    decoded e4m3 values q [..., R, C] and float32 scales [..., R/block, C/block]."""
+    q = np.asarray(q, np.float64)
     s = np.asarray(scale, dtype=np.float32).astype(np.float64)
     *lead, R, C = q.shape
     qb = q.reshape(*lead, R // block, block, C // block, block)
@@ -516,3 +522,48 @@ def load_stats(counts) -> dict:
         "load_loss": float(((load - 1.0 / E) ** 2).mean()),
         "max_violation": float(c.max() / mean - 1.0),
     }
+
+
+def score_sums(scores) -> np.ndarray:
+    """S_e = sum over the tokens of s[t, e] (the column sums the importance
+    statistic normalises), in float64."""
+    return np.asarray(scores, np.float64).sum(axis=0)
+
+
+def balance_stats(counts, score_sum, n_devices: int = 1) -> dict:
+    """The statistics of the load-balance code in the "DeepSeekMoE + MLA"
+    notes (page 3, expert- and device-level balance): load_e = c_e / sum(c)
+    and importance_e = S_e / sum(S) (S the column sums of the scores); their
+    standard deviations over the experts (n-1 denominator, as torch's std)
+    and the loss terms mean((x - 1/E)^2); the same for devices, each owning a
+    contiguous run of E / n_devices experts, whose load and importance are the
+    sums over their experts renormalised to sum 1. Readings: the page's 1e-9
+    in each denominator only guards an empty batch, so the normalisation is
+    exact here and every statistic of a quantity whose total is 0 is 0; the
+    standard deviation of a single value is 0. max_violation as in
+    load_stats."""
+    c = np.asarray(counts, dtype=np.float64)
+    S = np.asarray(score_sum, dtype=np.float64)
+    E = c.shape[0]
+    if n_devices < 1 or E % n_devices:
+        raise ValueError("n_devices must divide E")
+
+    def spread(x):
+        n = x.shape[0]
+        std = float(np.sqrt(((x - x.mean()) ** 2).sum() / (n - 1))) if n > 1 else 0.0
+        return std, float(((x - 1.0 / n) ** 2).mean())
+
+    def normalise(x):
+        return x / x.sum()
+
+    out = {}
+    for name, v in (("load", c), ("importance", S)):
+        keys = (f"{name}_std", f"{name}_loss", f"device_{name}_std", f"device_{name}_loss")
+        if v.sum() == 0:
+            out.update({k: 0.0 for k in keys})
+            continue
+        x = normalise(v)
+        dev = normalise(x.reshape(n_devices, E // n_devices).sum(axis=1))
+        (out[keys[0]], out[keys[1]]), (out[keys[2]], out[keys[3]]) = spread(x), spread(dev)
+    out["max_violation"] = float(c.max() / (c.sum() / E) - 1.0) if c.sum() > 0 else 0.0
+    return out

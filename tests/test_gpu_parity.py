@@ -747,3 +747,45 @@ def test_binding_rejects_mismatched_tensors():
     # the good call still runs
     layer.forward(**good)
     torch.cuda.synchronize()
+
+
+def test_score_sums_and_balance_stats_match_the_oracle():
+    """Score column sums written by the forward (sigmoid with bias, and
+    softmax with groups) within 1e-5 relative of the oracle's fp64 sums, bit
+    identical on a repeat and on the router entry point, zero for T = 0; the
+    balance statistics on the GPU's own counts and sums against the oracle's
+    at 1e-6 relative, and on the oracle's counts and sums at 1e-4."""
+    for cfg in (SMALL_SIG, BWD_GROUP):
+        inp = MI.make_layer(cfg, DEV)
+        layer = M.MoELayer.from_config(cfg)
+        S = torch.full((cfg.E,), -1.0, device=DEV)
+        layer.set_score_sums(S)
+        counts = torch.empty(cfg.E, dtype=torch.int32, device=DEV)
+        layer.forward(inp.x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared, expert_counts=counts)
+        torch.cuda.synchronize()
+        s1 = S.clone()
+        R = A.route_inputs(inp)
+        ref = O.score_sums(R["scores"])
+        got = s1.cpu().numpy().astype(np.float64)
+        assert np.max(np.abs(got - ref) / ref) <= 1e-5, np.max(np.abs(got - ref) / ref)
+        S.fill_(-1.0)
+        layer.router(inp.x, inp.gate_w, inp.sel_bias)
+        torch.cuda.synchronize()
+        assert torch.equal(S, s1)
+        for nd in (1, 4, cfg.E):
+            st = M.balance_stats(counts, S, n_devices=nd).cpu().numpy()
+            mine = O.balance_stats(counts.cpu().numpy(), S.cpu().numpy(), n_devices=nd)
+            full = O.balance_stats(R["counts"], ref, n_devices=nd)
+            for i, k in enumerate(M.BALANCE_STATS):
+                assert abs(st[i] - mine[k]) <= 1e-6 * max(abs(mine[k]), 1e-6), (cfg.name, nd, k, st[i], mine[k])
+                if not near_tie_mask(R).any():  # else a near-tie token may move one count
+                    assert abs(st[i] - full[k]) <= 1e-4 * max(abs(full[k]), 1e-6), (cfg.name, nd, k, st[i], full[k])
+        layer.forward(inp.x[:0], inp.gate_w, inp.sel_bias, inp.experts, inp.shared)
+        torch.cuda.synchronize()
+        assert not S.any()
+        assert not M.balance_stats(torch.zeros(cfg.E, dtype=torch.int32, device=DEV), S, 2).any()
+        layer.set_score_sums(None)
+    with pytest.raises(ValueError):
+        M.balance_stats(counts, S[:-1])
+    with pytest.raises(M.MoEError):
+        M.balance_stats(counts, S, n_devices=5)  # does not divide E

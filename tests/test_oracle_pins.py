@@ -540,6 +540,62 @@ def test_load_stats_closed_forms():
     assert math.isclose(st["max_violation"], c.max() * 64 / c.sum() - 1, rel_tol=1e-12)
 
 
+def test_balance_stats_closed_forms():
+    """Expert- and device-level balance statistics (load and importance) on
+    cases worked by hand."""
+    E = 8
+    z = O.balance_stats(np.full(E, 5), np.full(E, 2.5), n_devices=4)
+    assert all(v == 0.0 for v in z.values()), z
+    # every assignment and all the score mass on expert 3 (device 1 of 4)
+    one = O.balance_stats(np.eye(E, dtype=np.int64)[3] * 40, np.eye(E)[3] * 7.0, n_devices=4)
+    for name in ("load", "importance"):
+        assert math.isclose(one[f"{name}_std"], 1 / math.sqrt(E), rel_tol=1e-12)
+        assert math.isclose(one[f"{name}_loss"], (E - 1) / E ** 2, rel_tol=1e-12)
+        assert math.isclose(one[f"device_{name}_std"], 1 / math.sqrt(4), rel_tol=1e-12)
+        assert math.isclose(one[f"device_{name}_loss"], 3 / 16, rel_tol=1e-12)
+    assert math.isclose(one["max_violation"], E - 1, rel_tol=1e-12)
+    # half the experts at twice the mean, half empty: deviations +-1/E
+    half = O.balance_stats(np.array([2, 2, 2, 2, 0, 0, 0, 0]) * 9, np.array([2, 0] * 4, np.float64), n_devices=2)
+    assert math.isclose(half["load_std"], math.sqrt(1 / (E * (E - 1))), rel_tol=1e-12)
+    assert math.isclose(half["load_loss"], 1 / E ** 2, rel_tol=1e-12)
+    assert math.isclose(half["importance_loss"], 1 / E ** 2, rel_tol=1e-12)
+    # devices own contiguous runs: the load sits on device 0 ([1, 0]), while
+    # the importance alternates and is even across the two devices
+    assert math.isclose(half["device_load_std"], math.sqrt(0.5), rel_tol=1e-12)
+    assert math.isclose(half["device_load_loss"], 0.25, rel_tol=1e-12)
+    assert half["device_importance_std"] == 0.0 and half["device_importance_loss"] == 0.0
+    # empty batch: all zero; one device: device statistics zero; E devices: the expert ones
+    assert all(v == 0.0 for v in O.balance_stats(np.zeros(E, np.int64), np.zeros(E)).values())
+    c = RNG.integers(0, 50, size=64)
+    S = RNG.random(64) * 30
+    st1 = O.balance_stats(c, S, n_devices=1)
+    assert st1["device_load_std"] == st1["device_load_loss"] == st1["device_importance_loss"] == 0.0
+    stE = O.balance_stats(c, S, n_devices=64)
+    for name in ("load", "importance"):
+        assert math.isclose(stE[f"device_{name}_std"], stE[f"{name}_std"], rel_tol=1e-12)
+        assert math.isclose(stE[f"device_{name}_loss"], stE[f"{name}_loss"], rel_tol=1e-12)
+    # torch's n-1 std; scale invariance; the count statistics equal load_stats
+    imp = torch.tensor(S, dtype=torch.float64) / S.sum()
+    assert math.isclose(st1["importance_std"], float(imp.std()), rel_tol=1e-12)
+    st3 = O.balance_stats(c * 3, S * 0.5, n_devices=1)
+    assert all(math.isclose(st3[k], st1[k], rel_tol=1e-12, abs_tol=1e-15) for k in st1)
+    ls = O.load_stats(c)
+    assert all(math.isclose(st1[k], ls[k], rel_tol=1e-12) for k in ls)
+
+
+def test_score_sums_of_softmax_add_up_to_the_tokens():
+    """Softmax scores of each token sum to 1, so the column sums add up to T;
+    a token's sigmoid scores each lie in (0, 1)."""
+    u = RNG.standard_normal((37, 16))
+    w = RNG.standard_normal((12, 16))
+    S = O.score_sums(O.affinity(O.router_logits(u, w), "softmax"))
+    assert math.isclose(S.sum(), 37.0, rel_tol=1e-12)
+    S2 = O.score_sums(O.affinity(O.router_logits(u, w), "sigmoid"))
+    assert np.all((S2 > 0) & (S2 < 37))
+    one = O.score_sums(O.affinity(O.router_logits(u[:1], w), "sigmoid"))
+    assert np.allclose(one, 1 / (1 + np.exp(-(u[0] @ w.T))), rtol=1e-14)
+
+
 # ----------------------------------------------------------------------------
 # backward: the chain rule against central finite differences
 # ----------------------------------------------------------------------------
@@ -747,6 +803,27 @@ def test_pins_catch_planted_bugs(monkeypatch):
             test_e4m3_act_ffn_hand_worked_example()
     monkeypatch.setattr(O, "swiglu_ffn_e4m3_act", good_ffn8)
     test_e4m3_act_ffn_hand_worked_example()
+
+    good_bs = O.balance_stats
+
+    def strided_devices(counts, score_sum, n_devices=1):  # device d owns experts e with e % n == d
+        c = np.asarray(counts)
+        S = np.asarray(score_sum, np.float64)
+        E = c.shape[0]
+        perm = np.arange(E).reshape(E // n_devices, n_devices).T.ravel()
+        return good_bs(c[perm], S[perm], n_devices)
+
+    def population_std(counts, score_sum, n_devices=1):  # n instead of n-1
+        st = good_bs(counts, score_sum, n_devices)
+        E = len(counts)
+        for k in ("load_std", "importance_std"):
+            st[k] *= math.sqrt((E - 1) / E)
+        return st
+    for bad in (strided_devices, population_std):
+        monkeypatch.setattr(O, "balance_stats", bad)
+        with pytest.raises(AssertionError):
+            test_balance_stats_closed_forms()
+    monkeypatch.setattr(O, "balance_stats", good_bs)
 
     good_sg = O.silu_grad
     monkeypatch.setattr(O, "silu_grad", lambda z: 1.0 / (1.0 + np.exp(-z)))  # sigma(z) for SiLU'(z)
