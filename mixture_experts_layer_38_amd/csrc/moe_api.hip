@@ -171,6 +171,210 @@ __global__ void zero_counts_kernel(int32_t* p, int n) {
 
 hipError_t zero_f32(float* p, size_t n, hipStream_t s) { return launch_zero_f32(p, n, s); }
 
+// Workspace layout for c->p (max_tokens tokens) on a part with c->num_cus
+// CUs: returns its size in bytes and, when base is given, points the cfg's
+// buffers into it.
+size_t layout_workspace(moe_cfg* c, char* base) {
+  const moe_params* p = &c->p;
+  const size_t Tm = (size_t)p->max_tokens, E = p->n_routed, K = p->top_k, D = p->dim;
+  const size_t H = p->hidden, Hs = p->shared_hidden;
+  const size_t act = (p->weight_dtype == MOE_F32) ? 4 : 2;  // h and y element size
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + std::max<size_t>(bytes, 1)); return o; };
+  // partial-logit planes: the router uses at most 64 * CUs / T + 1 planes of
+  // T rows (checked again before each launch)
+  const size_t lg = (size_t)64 * c->num_cus + Tm;
+  const size_t o_logits = take(lg * E * 4), o_idx = take(Tm * K * 4), o_gate = take(Tm * K * 4);
+  const size_t o_spart = take((size_t)score_part_rows((int)Tm) * E * 4);
+  // the bf16x3 router planes of gate_w are used from kRouterX3MinTokens tokens on
+  const bool wsplit = p->act_dtype == MOE_BF16 && Tm >= (size_t)kRouterX3MinTokens;
+  const size_t o_wsplit = wsplit ? take(3 * E * D * 2) : 0;
+  const size_t o_counts = take(E * 4), o_offsets = take((E + 1) * 4), o_chunk = take(((Tm * K + kDispatchChunk - 1) / kDispatchChunk + 1) * E * 4);
+  const size_t o_pre1 = take((E + 2) * 4), o_pre2 = take((E + 2) * 4);
+  const size_t o_rt = take(Tm * K * 4), o_rg = take(Tm * K * 4), o_sr = take(Tm * K * 4);
+  const size_t o_hr = take(Tm * K * H * act), o_hs = take(Tm * Hs * act);
+  const size_t o_yr = take(Tm * K * D * act), o_ys = take(Tm * D * act);
+  const bool aq = p->act_quant == MOE_ACT_QUANT_E4M3_1X128;
+  const size_t o_xq = aq ? take(Tm * D) : 0, o_xs = aq ? take(Tm * (D / 128) * 4) : 0;
+  const size_t o_hsr = aq ? take(Tm * K * (H / 128) * 4) : 0, o_hss = aq ? take(Tm * (Hs / 128) * 4) : 0;
+  const bool bw = p->backward != 0;
+  const size_t Ep = (E + 63) / 64 * 64;
+  // d gate_w: K (tokens) split so that about one 256 x 256 tile per CU runs
+  const int rw_tiles = (int)((Ep + 255) / 256) * (int)((D + 255) / 256);
+  const int splits = bw ? std::max(1, std::min(32, (c->num_cus + rw_tiles - 1) / std::max(rw_tiles, 1))) : 0;
+  const size_t o_dout = bw ? take(Tm * D * 2) : 0, o_gw = bw ? take(Ep * D * 2) : 0;
+  const size_t o_au = bw ? take(Tm * K * 2 * H * 2) : 0, o_aus = bw ? take(Tm * 2 * Hs * 2) : 0;
+  const size_t o_dau = bw ? take(Tm * K * 2 * H * 2) : 0, o_daus = bw ? take(Tm * 2 * Hs * 2) : 0;
+  const size_t o_part = bw ? take(Tm * K * (H / 128) * 4) : 0, o_parts = bw ? take(Tm * (Hs / 128) * 4) : 0;
+  const size_t o_dlog = bw ? take(Tm * Ep * 2) : 0, o_dxr = bw ? take(Tm * D * 4) : 0;
+  const size_t o_planes = bw ? take((size_t)splits * E * D * 4) : 0;
+  const size_t o_preh = bw ? take((E + 2) * 4) : 0, o_prex = bw ? take((E + 2) * 4) : 0;
+  if (!base) return off;
+  c->logit_rows = lg;
+  c->logits = (float*)(base + o_logits);
+  c->score_part = (float*)(base + o_spart);
+  c->w_split = wsplit ? (uint16_t*)(base + o_wsplit) : nullptr;
+  c->idx = (int32_t*)(base + o_idx);
+  c->gate = (float*)(base + o_gate);
+  c->counts = (int32_t*)(base + o_counts);
+  c->offsets = (int32_t*)(base + o_offsets);
+  c->chunk_base = (int32_t*)(base + o_chunk);
+  c->pre1 = (int32_t*)(base + o_pre1);
+  c->pre2 = (int32_t*)(base + o_pre2);
+  c->row_token = (int32_t*)(base + o_rt);
+  c->row_gate = (float*)(base + o_rg);
+  c->slot_row = (int32_t*)(base + o_sr);
+  c->h_routed = base + o_hr;
+  c->h_shared = base + o_hs;
+  c->y_routed = base + o_yr;
+  c->y_shared = base + o_ys;
+  if (bw) {
+    c->Ep = (int)Ep;
+    c->bwd_splits = splits;
+    c->dout_bf = (uint16_t*)(base + o_dout);
+    c->gw_bf = (uint16_t*)(base + o_gw);
+    c->au = (uint16_t*)(base + o_au);
+    c->au_shared = (uint16_t*)(base + o_aus);
+    c->dau = (uint16_t*)(base + o_dau);
+    c->dau_shared = (uint16_t*)(base + o_daus);
+    c->part = (float*)(base + o_part);
+    c->part_shared = (float*)(base + o_parts);
+    c->dlogit = (uint16_t*)(base + o_dlog);
+    c->dx_router = (float*)(base + o_dxr);
+    c->gw_planes = (float*)(base + o_planes);
+    c->pre_h = (int32_t*)(base + o_preh);
+    c->pre_x = (int32_t*)(base + o_prex);
+  }
+  if (aq) {
+    c->xq = (uint8_t*)(base + o_xq);
+    c->xs = (float*)(base + o_xs);
+    c->hs_routed = (float*)(base + o_hsr);
+    c->hs_shared = (float*)(base + o_hss);
+  }
+  return off;
+}
+
+// The layer forward on the cfg's workspace (arguments checked by the caller
+// for T and the device; the rest here).
+moe_status forward_impl(moe_cfg* c, const void* x, int T, const float* gate_w, const float* sel_bias,
+                             const moe_weights* expert_w, const moe_weights* shared_w, void* out,
+                             int32_t* expert_counts, void* stream) {
+  const moe_params& p = c->p;
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) {
+    if (expert_counts) {
+      hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(256), 0, s, expert_counts, p.n_routed);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return hip_fail(c, e);
+    }
+    if (c->score_sum) {
+      hipError_t e = zero_f32(c->score_sum, p.n_routed, s);
+      if (e != hipSuccess) return hip_fail(c, e);
+    }
+    return MOE_OK;
+  }
+  if (!x || !gate_w || !out || !expert_w || !expert_w->gate_up || !expert_w->down) return MOE_ERR_INVALID_ARG;
+  const bool fp8 = p.weight_dtype == MOE_FP8_E4M3;
+  if (fp8 && (!expert_w->gate_up_scale || !expert_w->down_scale)) return MOE_ERR_INVALID_ARG;
+  const bool has_shared = p.shared_hidden > 0;
+  if (has_shared) {
+    if (!shared_w || !shared_w->gate_up || !shared_w->down) return MOE_ERR_INVALID_ARG;
+    if (fp8 && (!shared_w->gate_up_scale || !shared_w->down_scale)) return MOE_ERR_INVALID_ARG;
+  }
+
+  const Path path = choose_path(p, T);
+  hipError_t e;
+
+  // 1. router
+  mark(c, 0, s);
+  RouterArgs r{};
+  r.x = x; r.gate_w = gate_w; r.bias = sel_bias; r.logits = c->logits;
+  r.idx = c->idx; r.gate = c->gate; r.counts = c->counts;
+  r.T = T; r.D = p.dim; r.E = p.n_routed; r.G = p.n_group; r.kg = p.topk_group; r.K = p.top_k;
+  r.act_bf16 = p.act_dtype == MOE_BF16; r.score_fn = p.score_fn; r.norm = p.norm_topk;
+  r.rsf = p.routed_scaling_factor;
+  r.num_cus = c->num_cus;
+  r.w_split = c->w_split;
+  r.logit_rows = c->logit_rows;
+  r.score_sum = c->score_sum;
+  r.score_part = c->score_part;
+  r.hist = !small_dispatch(T * p.top_k);  // the one-workgroup dispatch counts the entries itself
+  if ((e = launch_router(r, s)) != hipSuccess) return hip_fail(c, e);
+  mark(c, 1, s);
+
+  // 2. dispatch
+  DispatchArgs d{};
+  d.idx = c->idx; d.gate = c->gate; d.counts = c->counts; d.counts_out = expert_counts;
+  d.offsets = c->offsets; d.chunk_base = c->chunk_base; d.row_token = c->row_token; d.row_gate = c->row_gate;
+  d.slot_row = c->slot_row; d.pre1 = c->pre1; d.pre2 = c->pre2;
+  d.T = T; d.K = p.top_k; d.E = p.n_routed;
+  fill_dispatch_geometry(p, path, T, &d);
+  if ((e = launch_dispatch(d, s)) != hipSuccess) return hip_fail(c, e);
+  mark(c, 2, s);
+
+  // 3./4. expert GEMMs
+  const int TK = T * p.top_k;
+  ExpertGemmArgs g{};
+  g.offsets = c->offsets; g.row_token = c->row_token; g.row_gate = c->row_gate;
+  g.E = p.n_routed; g.T = has_shared ? T : 0; g.D = p.dim; g.H = p.hidden; g.Hs = p.shared_hidden;
+  g.x_rows = T;
+  ExpertGemmArgs g1 = g, g2 = g;
+  g1.pre = c->pre1;
+  g1.a = x; g1.w = expert_w->gate_up; g1.w_scale = expert_w->gate_up_scale;
+  g1.w_shared = has_shared ? shared_w->gate_up : nullptr;
+  g1.w_shared_scale = has_shared ? shared_w->gate_up_scale : nullptr;
+  g1.c = c->h_routed; g1.c_shared = c->h_shared;
+  g2.pre = c->pre2;
+  g2.a = c->h_routed; g2.a_shared = c->h_shared; g2.w = expert_w->down; g2.w_scale = expert_w->down_scale;
+  g2.w_shared = has_shared ? shared_w->down : nullptr;
+  g2.w_shared_scale = has_shared ? shared_w->down_scale : nullptr;
+  g2.c = c->y_routed; g2.c_shared = c->y_shared;
+
+  if (path == Path::kF32) {
+    if ((e = launch_simple_gateup_f32(g1, TK, s)) != hipSuccess) return hip_fail(c, e);
+    mark(c, 3, s);
+    if ((e = launch_simple_down_f32(g2, TK, s)) != hipSuccess) return hip_fail(c, e);
+  } else {
+    // upper bounds on the item counts the dispatch can produce
+    const long mblk = (long)(TK + d.bm - 1) / d.bm + p.n_routed;
+    const long mblk_s = has_shared ? (T + d.bm - 1) / d.bm : 0;
+    g1.max_items = (int)(mblk * d.n1_routed + mblk_s * d.n1_shared);
+    g2.max_items = (int)(mblk * d.n2_routed + mblk_s * d.n2_shared);
+    if (path == Path::kGrouped) {
+      if ((e = launch_grouped_gateup(g1, fp8, s)) != hipSuccess) return hip_fail(c, e);
+      mark(c, 3, s);
+      if ((e = launch_grouped_down(g2, fp8, s)) != hipSuccess) return hip_fail(c, e);
+    } else if (path == Path::kGroupedF8) {
+      // token rows to e4m3 (counted in the gate/up stage), then both GEMMs on
+      // codes + block scales; the gate/up GEMM writes h as codes + scales
+      if ((e = launch_quant_e4m3(static_cast<const uint16_t*>(x), T, p.dim, c->xq, c->xs, s)) != hipSuccess)
+        return hip_fail(c, e);
+      g1.a = c->xq; g1.a_scale = c->xs;
+      g1.c_scale = c->hs_routed; g1.c_shared_scale = c->hs_shared;
+      g2.a_scale = c->hs_routed; g2.a_shared_scale = c->hs_shared;
+      if ((e = launch_grouped_gateup_f8(g1, s)) != hipSuccess) return hip_fail(c, e);
+      mark(c, 3, s);
+      if ((e = launch_grouped_down_f8(g2, s)) != hipSuccess) return hip_fail(c, e);
+    } else {
+      // persistent workgroups: as many as fit on the CUs at once
+      if ((e = launch_stream_gateup(g1, fp8, g1.max_items, c->num_cus, s)) != hipSuccess) return hip_fail(c, e);
+      mark(c, 3, s);
+      if ((e = launch_stream_down(g2, fp8, g2.max_items, c->num_cus, s)) != hipSuccess) return hip_fail(c, e);
+    }
+  }
+
+  // 5. combine
+  mark(c, 4, s);
+  CombineArgs cb{};
+  cb.x = x; cb.y_routed = c->y_routed; cb.y_shared = has_shared ? c->y_shared : nullptr;
+  cb.slot_row = c->slot_row; cb.out = out; cb.T = T; cb.D = p.dim; cb.K = p.top_k;
+  cb.act_bf16 = p.act_dtype == MOE_BF16; cb.y_bf16 = p.weight_dtype != MOE_F32;
+  cb.out_bf16 = p.out_dtype == MOE_BF16; cb.add_residual = p.add_residual;
+  if ((e = launch_combine(cb, s)) != hipSuccess) return hip_fail(c, e);
+  mark(c, 5, s);
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -199,85 +403,13 @@ moe_status moe_cfg_create(const moe_params* p, moe_cfg** out) {
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, c->device) != hipSuccess) { delete c; return MOE_ERR_HIP; }
   c->num_cus = prop.multiProcessorCount;
-
-  const size_t Tm = (size_t)p->max_tokens, E = p->n_routed, K = p->top_k, D = p->dim;
-  const size_t H = p->hidden, Hs = p->shared_hidden;
-  const size_t act = (p->weight_dtype == MOE_F32) ? 4 : 2;  // h and y element size
-  size_t off = 0;
-  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + std::max<size_t>(bytes, 1)); return o; };
-  // partial-logit planes: the router uses at most 64 * CUs / T + 1 planes of
-  // T rows (checked again before each launch)
-  const size_t lg = (size_t)64 * c->num_cus + Tm;
-  c->logit_rows = lg;
-  const size_t o_logits = take(lg * E * 4), o_idx = take(Tm * K * 4), o_gate = take(Tm * K * 4);
-  const size_t o_spart = take((size_t)score_part_rows((int)Tm) * E * 4);
-  const size_t o_wsplit = (p->act_dtype == MOE_BF16) ? take(3 * E * D * 2) : 0;
-  const size_t o_counts = take(E * 4), o_offsets = take((E + 1) * 4), o_chunk = take(((Tm * K + kDispatchChunk - 1) / kDispatchChunk + 1) * E * 4);
-  const size_t o_pre1 = take((E + 2) * 4), o_pre2 = take((E + 2) * 4);
-  const size_t o_rt = take(Tm * K * 4), o_rg = take(Tm * K * 4), o_sr = take(Tm * K * 4);
-  const size_t o_hr = take(Tm * K * H * act), o_hs = take(Tm * Hs * act);
-  const size_t o_yr = take(Tm * K * D * act), o_ys = take(Tm * D * act);
-  const bool aq = p->act_quant == MOE_ACT_QUANT_E4M3_1X128;
-  const size_t o_xq = aq ? take(Tm * D) : 0, o_xs = aq ? take(Tm * (D / 128) * 4) : 0;
-  const size_t o_hsr = aq ? take(Tm * K * (H / 128) * 4) : 0, o_hss = aq ? take(Tm * (Hs / 128) * 4) : 0;
-  const bool bw = p->backward != 0;
-  const size_t Ep = (E + 63) / 64 * 64;
-  // d gate_w: K (tokens) split so that about one 256 x 256 tile per CU runs
-  const int rw_tiles = (int)((Ep + 255) / 256) * (int)((D + 255) / 256);
-  const int splits = bw ? std::max(1, std::min(32, (c->num_cus + rw_tiles - 1) / std::max(rw_tiles, 1))) : 0;
-  const size_t o_dout = bw ? take(Tm * D * 2) : 0, o_gw = bw ? take(Ep * D * 2) : 0;
-  const size_t o_au = bw ? take(Tm * K * 2 * H * 2) : 0, o_aus = bw ? take(Tm * 2 * Hs * 2) : 0;
-  const size_t o_dau = bw ? take(Tm * K * 2 * H * 2) : 0, o_daus = bw ? take(Tm * 2 * Hs * 2) : 0;
-  const size_t o_part = bw ? take(Tm * K * (H / 128) * 4) : 0, o_parts = bw ? take(Tm * (Hs / 128) * 4) : 0;
-  const size_t o_dlog = bw ? take(Tm * Ep * 2) : 0, o_dxr = bw ? take(Tm * D * 4) : 0;
-  const size_t o_planes = bw ? take((size_t)splits * E * D * 4) : 0;
-  const size_t o_preh = bw ? take((E + 2) * 4) : 0, o_prex = bw ? take((E + 2) * 4) : 0;
-  c->ws_bytes = off;
+  c->ws_bytes = layout_workspace(c, nullptr);
   if (hipMalloc((void**)&c->ws, c->ws_bytes) != hipSuccess) {
     (void)hipGetLastError();
     delete c;
     return MOE_ERR_OOM;
   }
-  c->logits = (float*)(c->ws + o_logits);
-  c->score_part = (float*)(c->ws + o_spart);
-  c->w_split = (p->act_dtype == MOE_BF16) ? (uint16_t*)(c->ws + o_wsplit) : nullptr;
-  c->idx = (int32_t*)(c->ws + o_idx);
-  c->gate = (float*)(c->ws + o_gate);
-  c->counts = (int32_t*)(c->ws + o_counts);
-  c->offsets = (int32_t*)(c->ws + o_offsets);
-  c->chunk_base = (int32_t*)(c->ws + o_chunk);
-  c->pre1 = (int32_t*)(c->ws + o_pre1);
-  c->pre2 = (int32_t*)(c->ws + o_pre2);
-  c->row_token = (int32_t*)(c->ws + o_rt);
-  c->row_gate = (float*)(c->ws + o_rg);
-  c->slot_row = (int32_t*)(c->ws + o_sr);
-  c->h_routed = c->ws + o_hr;
-  c->h_shared = c->ws + o_hs;
-  c->y_routed = c->ws + o_yr;
-  c->y_shared = c->ws + o_ys;
-  if (bw) {
-    c->Ep = (int)Ep;
-    c->bwd_splits = splits;
-    c->dout_bf = (uint16_t*)(c->ws + o_dout);
-    c->gw_bf = (uint16_t*)(c->ws + o_gw);
-    c->au = (uint16_t*)(c->ws + o_au);
-    c->au_shared = (uint16_t*)(c->ws + o_aus);
-    c->dau = (uint16_t*)(c->ws + o_dau);
-    c->dau_shared = (uint16_t*)(c->ws + o_daus);
-    c->part = (float*)(c->ws + o_part);
-    c->part_shared = (float*)(c->ws + o_parts);
-    c->dlogit = (uint16_t*)(c->ws + o_dlog);
-    c->dx_router = (float*)(c->ws + o_dxr);
-    c->gw_planes = (float*)(c->ws + o_planes);
-    c->pre_h = (int32_t*)(c->ws + o_preh);
-    c->pre_x = (int32_t*)(c->ws + o_prex);
-  }
-  if (aq) {
-    c->xq = (uint8_t*)(c->ws + o_xq);
-    c->xs = (float*)(c->ws + o_xs);
-    c->hs_routed = (float*)(c->ws + o_hsr);
-    c->hs_shared = (float*)(c->ws + o_hss);
-  }
+  layout_workspace(c, c->ws);
   *out = c;
   return MOE_OK;
 }
@@ -434,122 +566,9 @@ moe_status moe_layer_forward(moe_cfg* c, const void* x, int T, const float* gate
                              const moe_weights* expert_w, const moe_weights* shared_w, void* out,
                              int32_t* expert_counts, void* stream) {
   if (!c) return MOE_ERR_INVALID_ARG;
-  const moe_params& p = c->p;
-  if (T < 0 || T > p.max_tokens) return MOE_ERR_INVALID_ARG;
+  if (T < 0 || T > c->p.max_tokens) return MOE_ERR_INVALID_ARG;
   if (!on_cfg_device(c)) return MOE_ERR_INVALID_ARG;
-  hipStream_t s = (hipStream_t)stream;
-  if (T == 0) {
-    if (expert_counts) {
-      hipLaunchKernelGGL(zero_counts_kernel, dim3(1), dim3(256), 0, s, expert_counts, p.n_routed);
-      hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return hip_fail(c, e);
-    }
-    if (c->score_sum) {
-      hipError_t e = zero_f32(c->score_sum, p.n_routed, s);
-      if (e != hipSuccess) return hip_fail(c, e);
-    }
-    return MOE_OK;
-  }
-  if (!x || !gate_w || !out || !expert_w || !expert_w->gate_up || !expert_w->down) return MOE_ERR_INVALID_ARG;
-  const bool fp8 = p.weight_dtype == MOE_FP8_E4M3;
-  if (fp8 && (!expert_w->gate_up_scale || !expert_w->down_scale)) return MOE_ERR_INVALID_ARG;
-  const bool has_shared = p.shared_hidden > 0;
-  if (has_shared) {
-    if (!shared_w || !shared_w->gate_up || !shared_w->down) return MOE_ERR_INVALID_ARG;
-    if (fp8 && (!shared_w->gate_up_scale || !shared_w->down_scale)) return MOE_ERR_INVALID_ARG;
-  }
-
-  const Path path = choose_path(p, T);
-  hipError_t e;
-
-  // 1. router
-  mark(c, 0, s);
-  RouterArgs r{};
-  r.x = x; r.gate_w = gate_w; r.bias = sel_bias; r.logits = c->logits;
-  r.idx = c->idx; r.gate = c->gate; r.counts = c->counts;
-  r.T = T; r.D = p.dim; r.E = p.n_routed; r.G = p.n_group; r.kg = p.topk_group; r.K = p.top_k;
-  r.act_bf16 = p.act_dtype == MOE_BF16; r.score_fn = p.score_fn; r.norm = p.norm_topk;
-  r.rsf = p.routed_scaling_factor;
-  r.num_cus = c->num_cus;
-  r.w_split = c->w_split;
-  r.logit_rows = c->logit_rows;
-  r.score_sum = c->score_sum;
-  r.score_part = c->score_part;
-  r.hist = !small_dispatch(T * p.top_k);  // the one-workgroup dispatch counts the entries itself
-  if ((e = launch_router(r, s)) != hipSuccess) return hip_fail(c, e);
-  mark(c, 1, s);
-
-  // 2. dispatch
-  DispatchArgs d{};
-  d.idx = c->idx; d.gate = c->gate; d.counts = c->counts; d.counts_out = expert_counts;
-  d.offsets = c->offsets; d.chunk_base = c->chunk_base; d.row_token = c->row_token; d.row_gate = c->row_gate;
-  d.slot_row = c->slot_row; d.pre1 = c->pre1; d.pre2 = c->pre2;
-  d.T = T; d.K = p.top_k; d.E = p.n_routed;
-  fill_dispatch_geometry(p, path, T, &d);
-  if ((e = launch_dispatch(d, s)) != hipSuccess) return hip_fail(c, e);
-  mark(c, 2, s);
-
-  // 3./4. expert GEMMs
-  const int TK = T * p.top_k;
-  ExpertGemmArgs g{};
-  g.offsets = c->offsets; g.row_token = c->row_token; g.row_gate = c->row_gate;
-  g.E = p.n_routed; g.T = has_shared ? T : 0; g.D = p.dim; g.H = p.hidden; g.Hs = p.shared_hidden;
-  g.x_rows = T;
-  ExpertGemmArgs g1 = g, g2 = g;
-  g1.pre = c->pre1;
-  g1.a = x; g1.w = expert_w->gate_up; g1.w_scale = expert_w->gate_up_scale;
-  g1.w_shared = has_shared ? shared_w->gate_up : nullptr;
-  g1.w_shared_scale = has_shared ? shared_w->gate_up_scale : nullptr;
-  g1.c = c->h_routed; g1.c_shared = c->h_shared;
-  g2.pre = c->pre2;
-  g2.a = c->h_routed; g2.a_shared = c->h_shared; g2.w = expert_w->down; g2.w_scale = expert_w->down_scale;
-  g2.w_shared = has_shared ? shared_w->down : nullptr;
-  g2.w_shared_scale = has_shared ? shared_w->down_scale : nullptr;
-  g2.c = c->y_routed; g2.c_shared = c->y_shared;
-
-  if (path == Path::kF32) {
-    if ((e = launch_simple_gateup_f32(g1, TK, s)) != hipSuccess) return hip_fail(c, e);
-    mark(c, 3, s);
-    if ((e = launch_simple_down_f32(g2, TK, s)) != hipSuccess) return hip_fail(c, e);
-  } else {
-    // upper bounds on the item counts the dispatch can produce
-    const long mblk = (long)(TK + d.bm - 1) / d.bm + p.n_routed;
-    const long mblk_s = has_shared ? (T + d.bm - 1) / d.bm : 0;
-    g1.max_items = (int)(mblk * d.n1_routed + mblk_s * d.n1_shared);
-    g2.max_items = (int)(mblk * d.n2_routed + mblk_s * d.n2_shared);
-    if (path == Path::kGrouped) {
-      if ((e = launch_grouped_gateup(g1, fp8, s)) != hipSuccess) return hip_fail(c, e);
-      mark(c, 3, s);
-      if ((e = launch_grouped_down(g2, fp8, s)) != hipSuccess) return hip_fail(c, e);
-    } else if (path == Path::kGroupedF8) {
-      // token rows to e4m3 (counted in the gate/up stage), then both GEMMs on
-      // codes + block scales; the gate/up GEMM writes h as codes + scales
-      if ((e = launch_quant_e4m3(static_cast<const uint16_t*>(x), T, p.dim, c->xq, c->xs, s)) != hipSuccess)
-        return hip_fail(c, e);
-      g1.a = c->xq; g1.a_scale = c->xs;
-      g1.c_scale = c->hs_routed; g1.c_shared_scale = c->hs_shared;
-      g2.a_scale = c->hs_routed; g2.a_shared_scale = c->hs_shared;
-      if ((e = launch_grouped_gateup_f8(g1, s)) != hipSuccess) return hip_fail(c, e);
-      mark(c, 3, s);
-      if ((e = launch_grouped_down_f8(g2, s)) != hipSuccess) return hip_fail(c, e);
-    } else {
-      // persistent workgroups: as many as fit on the CUs at once
-      if ((e = launch_stream_gateup(g1, fp8, g1.max_items, c->num_cus, s)) != hipSuccess) return hip_fail(c, e);
-      mark(c, 3, s);
-      if ((e = launch_stream_down(g2, fp8, g2.max_items, c->num_cus, s)) != hipSuccess) return hip_fail(c, e);
-    }
-  }
-
-  // 5. combine
-  mark(c, 4, s);
-  CombineArgs cb{};
-  cb.x = x; cb.y_routed = c->y_routed; cb.y_shared = has_shared ? c->y_shared : nullptr;
-  cb.slot_row = c->slot_row; cb.out = out; cb.T = T; cb.D = p.dim; cb.K = p.top_k;
-  cb.act_bf16 = p.act_dtype == MOE_BF16; cb.y_bf16 = p.weight_dtype != MOE_F32;
-  cb.out_bf16 = p.out_dtype == MOE_BF16; cb.add_residual = p.add_residual;
-  if ((e = launch_combine(cb, s)) != hipSuccess) return hip_fail(c, e);
-  mark(c, 5, s);
-  return MOE_OK;
+  return forward_impl(c, x, T, gate_w, sel_bias, expert_w, shared_w, out, expert_counts, stream);
 }
 
 moe_status moe_layer_backward(moe_cfg* c, const void* x, int T, const float* gate_w, const float* sel_bias,
