@@ -42,7 +42,9 @@ typedef enum {
   MOE_ERR_INVALID_ARG = -1, /* bad pointer, size or parameter combination */
   MOE_ERR_UNSUPPORTED = -2, /* valid layer, but a shape/dtype this build does not run */
   MOE_ERR_OOM = -3,         /* workspace allocation failed */
-  MOE_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+  MOE_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+  MOE_ERR_SCRATCH = -5      /* moe_layer_forward_noalloc: the call needs more
+                               workspace than its fixed scratch array holds */
 } moe_status;
 
 typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score_fn;
@@ -135,6 +137,31 @@ moe_status moe_layer_forward(moe_cfg* cfg, const void* x, int T, const float* ga
                              const float* sel_bias, const moe_weights* expert_w,
                              const moe_weights* shared_w, void* out, int32_t* expert_counts,
                              void* stream);
+
+/* The layer forward without any device allocation, for callers that cannot
+ * allocate: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, semantics and results (the same kernels)
+ * as moe_layer_forward on a cfg created from *params, with two differences:
+ *  - there is no cfg: *params (host memory, read during the call) describes
+ *    the layer; its max_tokens and backward fields are ignored;
+ *  - the workspace is a fixed array of 64 MiB in device memory, one per GPU,
+ *    loaded with the library's code and held until the process ends. The
+ *    call needs the workspace a cfg with max_tokens = T would allocate
+ *    (moe_cfg_workspace_bytes); above 64 MiB it returns MOE_ERR_SCRATCH and
+ *    launches nothing (the V3 decode shape, D = 7168, E = 256, H = 2048,
+ *    K = 8, fits up to T = 256 tokens).
+ * Every call on one GPU uses that GPU's one array and leaves its contents
+ * behind (nothing in it needs to start at zero: each call writes what it
+ * reads): calls that overlap on one GPU race, so keep them on one stream or
+ * synchronise them. The first call on each device looks up the array's
+ * device address (hipGetSymbolAddress) and the device's CU count; later calls
+ * make no runtime query beyond hipGetDevice. No hipMalloc, hipFree or other
+ * allocating call is made. Score sums (moe_cfg_set_score_sums) and stage
+ * timing belong to a cfg and are not available here. */
+moe_status moe_layer_forward_noalloc(const moe_params* params, const void* x, int T, const float* gate_w,
+                                     const float* sel_bias, const moe_weights* expert_w,
+                                     const moe_weights* shared_w, void* out, int32_t* expert_counts,
+                                     void* stream);
 
 /* Gradients of a layer (the back-propagation step of the training data flow
  * in the "Transformer block" article, which updates experts and router):

@@ -16,7 +16,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe.h")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_OOM, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_OOM, MOE_ERR_HIP, MOE_ERR_SCRATCH = 0, -1, -2, -3, -4, -5
 MOE_SCORE_SOFTMAX, MOE_SCORE_SIGMOID = 0, 1
 MOE_F32, MOE_BF16, MOE_FP8_E4M3 = 0, 1, 2
 MOE_PATH_AUTO, MOE_PATH_GROUPED, MOE_PATH_STREAM = 0, 1, 2
@@ -81,6 +81,8 @@ def load_library() -> ctypes.CDLL:
     lib.moe_load_stats.argtypes = [vp, ctypes.c_int, vp, vp]
     lib.moe_quantize_e4m3_1x128.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp, vp]
     lib.moe_cfg_set_score_sums.argtypes = [vp, vp]
+    lib.moe_layer_forward_noalloc.argtypes = [ctypes.POINTER(MoeParams), vp, ctypes.c_int, vp, vp,
+                                              ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeWeights), vp, vp, vp]
     lib.moe_balance_stats.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, vp]
     lib.moe_layer_backward.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.POINTER(MoeWeights),
                                        ctypes.POINTER(MoeWeights), vp, vp, vp, ctypes.POINTER(MoeWeightGrads),
@@ -88,7 +90,8 @@ def load_library() -> ctypes.CDLL:
     for f in ("moe_cfg_create", "moe_cfg_destroy", "moe_layer_forward", "moe_router_forward",
               "moe_dispatch_forward", "moe_cfg_last_hip_error", "moe_cfg_set_stage_timing",
               "moe_cfg_stage_times", "moe_bias_update", "moe_load_stats", "moe_quantize_e4m3_1x128",
-              "moe_layer_backward", "moe_cfg_set_score_sums", "moe_balance_stats"):
+              "moe_layer_backward", "moe_cfg_set_score_sums", "moe_balance_stats",
+              "moe_layer_forward_noalloc"):
         getattr(lib, f).restype = ctypes.c_int
     del i32p
     _lib = lib
@@ -99,7 +102,7 @@ def declared_functions() -> list[str]:
     """Names of the functions include/moe.h declares."""
     text = open(HEADER_PATH).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def status_string(status: int) -> str:
@@ -373,6 +376,34 @@ def load_stats(expert_counts, stream=None):
     if st != MOE_OK:
         raise MoEError(st, "moe_load_stats")
     return stats
+
+
+def layer_forward_noalloc(params: MoeParams, x, gate_w, sel_bias, experts, shared, out=None,
+                          expert_counts=None, stream=None):
+    """moe_layer_forward_noalloc: the layer forward on the library's fixed
+    per-GPU scratch array (no cfg, no device allocation by the library).
+    The tensors are checked against params as for MoELayer.forward; out is
+    allocated here by torch when not given."""
+    chk = MoELayer.__new__(MoELayer)  # the checks only, without a cfg
+    chk.params = params
+    chk._check_x(x)
+    T = x.shape[0]
+    chk._check_router_inputs(x, gate_w, sel_bias)
+    chk._check_weights(x, experts, shared)
+    if params.shared_hidden == 0:
+        shared = None
+    if out is None:
+        out = torch.empty((T, params.dim), dtype=_TORCH_OF[params.out_dtype], device=x.device)
+    _check_tensor("out", out, _TORCH_OF[params.out_dtype], (T, params.dim), x.device)
+    if expert_counts is not None:
+        _check_tensor("expert_counts", expert_counts, torch.int32, (params.n_routed,), x.device)
+    ew, sw = _weights(experts), _weights(shared)
+    st = load_library().moe_layer_forward_noalloc(ctypes.byref(params), _ptr(x), T, _ptr(gate_w), _ptr(sel_bias),
+                                                  ctypes.byref(ew), None if sw is None else ctypes.byref(sw),
+                                                  _ptr(out), _ptr(expert_counts), _stream_handle(stream))
+    if st != MOE_OK:
+        raise MoEError(st, "moe_layer_forward_noalloc")
+    return out
 
 
 BALANCE_STATS = ("load_std", "load_loss", "max_violation", "importance_std", "importance_loss",

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 
 #include "moe_internal.hpp"
@@ -254,6 +255,36 @@ size_t layout_workspace(moe_cfg* c, char* base) {
   return off;
 }
 
+// The no-allocation forward's workspace: one array per GPU, loaded with the
+// code object and held until the process ends. Host code never passes its
+// name to a kernel (on the host it is only a stand-in); the device address
+// comes from hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxScratchDevices = 64;
+static __device__ __align__(256) char scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxScratchDevices];
+int g_scratch_cus[kMaxScratchDevices];
+
+// the current device's scratch address and CU count (set up on its first use)
+moe_status scratch_of_current_device(int* dev, char** ptr, int* cus) {
+  if (hipGetDevice(dev) != hipSuccess) return MOE_ERR_HIP;
+  if (*dev < 0 || *dev >= kMaxScratchDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[*dev]) {
+    void* p = nullptr;
+    int n = 0;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MOE_ERR_HIP;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, *dev) != hipSuccess || n <= 0)
+      return MOE_ERR_HIP;
+    g_scratch_cus[*dev] = n;
+    g_scratch_ptr[*dev] = static_cast<char*>(p);
+  }
+  *ptr = g_scratch_ptr[*dev];
+  *cus = g_scratch_cus[*dev];
+  return MOE_OK;
+}
+
 // The layer forward on the cfg's workspace (arguments checked by the caller
 // for T and the device; the rest here).
 moe_status forward_impl(moe_cfg* c, const void* x, int T, const float* gate_w, const float* sel_bias,
@@ -386,6 +417,7 @@ const char* moe_status_string(moe_status s) {
     case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case MOE_ERR_OOM: return "out of device memory";
     case MOE_ERR_HIP: return "HIP runtime error";
+    case MOE_ERR_SCRATCH: return "input needs more than the no-allocation scratch holds";
   }
   return "unknown status";
 }
@@ -569,6 +601,29 @@ moe_status moe_layer_forward(moe_cfg* c, const void* x, int T, const float* gate
   if (T < 0 || T > c->p.max_tokens) return MOE_ERR_INVALID_ARG;
   if (!on_cfg_device(c)) return MOE_ERR_INVALID_ARG;
   return forward_impl(c, x, T, gate_w, sel_bias, expert_w, shared_w, out, expert_counts, stream);
+}
+
+moe_status moe_layer_forward_noalloc(const moe_params* params, const void* x, int T, const float* gate_w,
+                                     const float* sel_bias, const moe_weights* expert_w,
+                                     const moe_weights* shared_w, void* out, int32_t* expert_counts,
+                                     void* stream) {
+  if (!params || T < 0) return MOE_ERR_INVALID_ARG;
+  // a cfg on the stack: the layer as given, sized for exactly T tokens, no
+  // backward workspace, its buffers in this device's scratch array
+  moe_cfg c;
+  memset(&c, 0, sizeof(c));
+  c.p = *params;
+  c.p.max_tokens = T;
+  c.p.backward = 0;
+  moe_status st = validate(&c.p);
+  if (st != MOE_OK) return st;
+  char* base = nullptr;
+  if ((st = scratch_of_current_device(&c.device, &base, &c.num_cus)) != MOE_OK) return st;
+  c.ws_bytes = layout_workspace(&c, nullptr);
+  if (c.ws_bytes > kScratchBytes) return MOE_ERR_SCRATCH;
+  c.ws = base;
+  layout_workspace(&c, base);
+  return forward_impl(&c, x, T, gate_w, sel_bias, expert_w, shared_w, out, expert_counts, stream);
 }
 
 moe_status moe_layer_backward(moe_cfg* c, const void* x, int T, const float* gate_w, const float* sel_bias,

@@ -1,0 +1,82 @@
+"""The no-allocation forward (moe_layer_forward_noalloc) against the cfg
+forward (moe_layer_forward) through the C ABI: identical outputs and expert
+counts on two calls in a row, the second with fewer tokens, on the weight-
+streaming path (fp8 decode shape and a small fp8 layer) and on the grouped
+path (a bf16 layer past 256 tokens, then below); a call that needs more than
+the fixed scratch array is refused without touching the output."""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_layer_38_amd as M
+import moe_inputs as MI
+from oracle import adapter as A
+from tests.parity import TOL, layer_error, near_tie_mask
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+SMALL_FP8 = MI.LayerConfig("small_fp8", T=77, D=256, E=16, H=256, G=4, kg=2, K=4, score_fn="sigmoid",
+                           bias="normal", norm=True, rsf=2.5, Hs=256, act="bf16", weight="fp8", bias_std=0.05)
+GROUPED_BF16 = MI.LayerConfig("grouped_bf16", T=400, D=384, E=32, H=256, G=8, kg=4, K=6, score_fn="sigmoid",
+                              bias="normal", norm=True, rsf=2.5, Hs=128, act="bf16", weight="bf16", bias_std=0.05)
+
+
+def _params(cfg, T):
+    return M.make_params(dim=cfg.D, n_routed=cfg.E, hidden=cfg.H, shared_hidden=cfg.Hs, top_k=cfg.K,
+                         n_group=cfg.G, topk_group=cfg.kg, score_fn=cfg.score_fn, norm_topk=cfg.norm,
+                         routed_scaling_factor=cfg.rsf, act=cfg.act, weight=cfg.weight, out=cfg.out,
+                         add_residual=cfg.add_residual, max_tokens=T)
+
+
+def _both(inp, T, layer):
+    cfg = inp.cfg
+    x = inp.x[:T].contiguous()
+    c_ref = torch.full((cfg.E,), -1, dtype=torch.int32, device=DEV)
+    ref = layer.forward(x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared, expert_counts=c_ref)
+    c_na = torch.full((cfg.E,), -7, dtype=torch.int32, device=DEV)
+    out = torch.full((T, cfg.D), float("nan"), device=DEV)
+    M.layer_forward_noalloc(_params(cfg, 0), x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared, out=out,
+                            expert_counts=c_na)
+    torch.cuda.synchronize()
+    return ref, c_ref, out, c_na
+
+
+@pytest.mark.parametrize("name,Ts", [("v3_decode_fp8", (64, 16)), ("small_fp8", (77, 30)),
+                                     ("grouped_bf16", (400, 150))])
+def test_noalloc_matches_the_cfg_forward(name, Ts):
+    cfg = {"small_fp8": SMALL_FP8, "grouped_bf16": GROUPED_BF16}.get(name) or MI.CONFIGS[name]
+    inp = MI.make_layer(cfg, DEV)
+    layer = M.MoELayer.from_config(cfg)
+    R = A.route_inputs(inp)
+    for T in Ts:  # the second call has fewer tokens and reuses the scratch array
+        ref, c_ref, out, c_na = _both(inp, T, layer)
+        assert torch.equal(out, ref), (name, T)
+        assert torch.equal(c_na, c_ref), (name, T)
+        # and the cfg forward is itself within the layer's bound of the oracle
+        tok = np.arange(min(T, 32))
+        want, _ = A.run_layer(inp, tokens=tok, routing=R)
+        err = layer_error(ref[:len(tok)], want, A.decode_tensor(inp.x)[tok], cfg.add_residual,
+                          exclude=near_tie_mask(R)[tok])
+        assert err["max"] <= TOL[cfg.weight], (name, T, err)
+        print(f"{name} T={T}: no-allocation forward identical to the cfg forward; oracle err {err}")
+
+
+def test_noalloc_refuses_what_the_scratch_cannot_hold():
+    cfg = GROUPED_BF16
+    T = 16384  # y rows alone need T*K*D*2 = 72 MiB at this shape
+    inp = MI.make_layer(cfg, DEV)
+    x = torch.zeros((T, cfg.D), dtype=torch.bfloat16, device=DEV)
+    out = torch.full((T, cfg.D), 5.0, device=DEV)
+    with pytest.raises(M.MoEError) as ei:
+        M.layer_forward_noalloc(_params(cfg, 0), x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared, out=out)
+    assert ei.value.status == M.MOE_ERR_SCRATCH
+    torch.cuda.synchronize()
+    assert bool((out == 5.0).all())
+    # T = 0 is a no-op that zeroes the counts
+    counts = torch.full((cfg.E,), 3, dtype=torch.int32, device=DEV)
+    M.layer_forward_noalloc(_params(cfg, 0), x[:0], inp.gate_w, inp.sel_bias, inp.experts, inp.shared,
+                            out=out[:0], expert_counts=counts)
+    torch.cuda.synchronize()
+    assert not counts.any()
