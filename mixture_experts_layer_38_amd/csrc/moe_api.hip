@@ -147,8 +147,10 @@ void fill_dispatch_geometry(const moe_params& p, Path path, int T, DispatchArgs*
     d->n1_shared = p.shared_hidden / kST_N1;
     d->n2_routed = d->n2_shared = p.dim / kST_N2;
   } else {
-    d->bm = 1;
-    d->n1_routed = d->n1_shared = d->n2_routed = d->n2_shared = 0;
+    d->bm = kF32_BM;
+    d->n1_routed = (p.hidden + 31) / 32;
+    d->n1_shared = (p.shared_hidden + 31) / 32;
+    d->n2_routed = d->n2_shared = (p.dim + 63) / 64;
   }
 }
 
@@ -361,16 +363,16 @@ moe_status forward_impl(moe_cfg* c, const void* x, int T, const float* gate_w, c
   g2.w_shared_scale = has_shared ? shared_w->down_scale : nullptr;
   g2.c = c->y_routed; g2.c_shared = c->y_shared;
 
+  // upper bounds on the item counts the dispatch can produce
+  const long mblk = (long)(TK + d.bm - 1) / d.bm + p.n_routed;
+  const long mblk_s = has_shared ? (T + d.bm - 1) / d.bm : 0;
+  g1.max_items = (int)(mblk * d.n1_routed + mblk_s * d.n1_shared);
+  g2.max_items = (int)(mblk * d.n2_routed + mblk_s * d.n2_shared);
   if (path == Path::kF32) {
     if ((e = launch_simple_gateup_f32(g1, TK, s)) != hipSuccess) return hip_fail(c, e);
     mark(c, 3, s);
     if ((e = launch_simple_down_f32(g2, TK, s)) != hipSuccess) return hip_fail(c, e);
   } else {
-    // upper bounds on the item counts the dispatch can produce
-    const long mblk = (long)(TK + d.bm - 1) / d.bm + p.n_routed;
-    const long mblk_s = has_shared ? (T + d.bm - 1) / d.bm : 0;
-    g1.max_items = (int)(mblk * d.n1_routed + mblk_s * d.n1_shared);
-    g2.max_items = (int)(mblk * d.n2_routed + mblk_s * d.n2_shared);
     if (path == Path::kGrouped) {
       if ((e = launch_grouped_gateup(g1, fp8, s)) != hipSuccess) return hip_fail(c, e);
       mark(c, 3, s);

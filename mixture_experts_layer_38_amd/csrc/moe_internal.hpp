@@ -31,6 +31,9 @@ constexpr int kF8_BM = 128;   // rows (tokens) per tile
 constexpr int kF8_BK = 128;   // K step = one scale block (elements = bytes)
 constexpr int kActBlock = 128;  // activation quantisation block (1 x 128)
 constexpr int kDispatchChunk = 128;  // (token, slot) entries per wave in the stable permutation
+// fp32 layers: rows per work item of the grouped fp32 GEMMs (gate/up items
+// cover 32 hidden units, down items 64 output columns)
+constexpr int kF32_BM = 64;
 // Weight-streaming path (small token counts): token rows and columns per workgroup item.
 constexpr int kST_BM = 16;
 constexpr int kST_N1 = 32;    // hidden columns per gate/up item (32 gate + 32 up rows)

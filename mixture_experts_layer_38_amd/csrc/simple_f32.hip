@@ -1,9 +1,15 @@
 // fp32 expert FFNs and the combine.
 //
-// The fp32 layer (fp32 activations and weights) is tiny in every workload it
-// serves, so its expert GEMMs are plain per-output dot products in fp32, one
-// thread per output element; each row of the expert-contiguous buffer is one
-// (token, expert) pair, or one token of the shared expert.
+// The fp32 layer (fp32 activations and weights): grouped LDS-tiled GEMMs in
+// fp32 FMAs, one launch per GEMM over every problem (routed expert e, or the
+// shared expert), work items from the dispatch's item prefix like the bf16
+// path. A work item is 64 rows (expert-contiguous rows, i.e. (token, expert)
+// pairs, or tokens of the shared expert) x 64 weight rows: for gate/up, 32
+// W_gate rows and the matching 32 W_up rows, so h = SiLU(gate) * up is formed
+// in registers; for down, 64 output columns, times the row's gate. K steps of
+// 32 staged through LDS with coalesced loads (consecutive threads read
+// consecutive elements of a row); each thread accumulates 4 rows x 4 columns
+// in k order.
 //
 // The combine is the gate-weighted sum of the page-1 MoE forward plus the
 // shared expert and the residual; it runs for every dtype.
@@ -13,61 +19,121 @@ namespace moe {
 
 __device__ __forceinline__ float silu_precise(float z) { return z / (1.0f + expf(-z)); }
 
-__global__ __launch_bounds__(64) void gateup_f32_kernel(ExpertGemmArgs a, int TK) {
-  const int r = blockIdx.y;
-  const bool routed = r < TK;
-  const int p = routed ? find_problem(a.offsets, a.E - 1, r) : a.E;
-  const int Hp = routed ? a.H : a.Hs;
-  const int j = blockIdx.x * 64 + threadIdx.x;
-  if (j >= Hp) return;
-  const int tok = routed ? a.row_token[r] : r - TK;
-  const float* x = static_cast<const float*>(a.a) + (size_t)tok * a.D;
-  const float* W = routed ? static_cast<const float*>(a.w) + (size_t)p * 2 * Hp * a.D
-                          : static_cast<const float*>(a.w_shared);
-  const float* wg = W + (size_t)j * a.D;
-  const float* wu = W + (size_t)(Hp + j) * a.D;
-  float g = 0.f, u = 0.f;
-  for (int d = 0; d < a.D; ++d) {
-    g = fmaf(x[d], wg[d], g);
-    u = fmaf(x[d], wu[d], u);
-  }
-  float* h = routed ? static_cast<float*>(a.c) + (size_t)r * Hp
-                    : static_cast<float*>(a.c_shared) + (size_t)(r - TK) * Hp;
-  h[j] = silu_precise(g) * u;
+namespace {
+constexpr int kF32_BK = 32, kF32_LD = kF32_BK + 1;
 }
 
-__global__ __launch_bounds__(64) void down_f32_kernel(ExpertGemmArgs a, int TK) {
-  const int r = blockIdx.y;
-  const bool routed = r < TK;
-  const int p = routed ? find_problem(a.offsets, a.E - 1, r) : a.E;
+// kMode 0: gate/up + SwiGLU -> h; 1: down x gate -> y
+template <int kMode>
+__global__ __launch_bounds__(256) void grouped_f32_kernel(ExpertGemmArgs a) {
+  __shared__ float sA[kF32_BM * kF32_LD];
+  __shared__ float sB[64 * kF32_LD];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int tile = blockIdx.x;
+  if (tile >= a.pre[a.E + 1]) return;
+  const int p = find_problem(a.pre, a.E, tile);
+  const bool routed = p < a.E;
+  const int rows = routed ? a.offsets[p + 1] - a.offsets[p] : a.T;
+  const int row_base = routed ? a.offsets[p] : 0;
   const int Hp = routed ? a.H : a.Hs;
-  const int n = blockIdx.x * 64 + threadIdx.x;
-  if (n >= a.D) return;
-  const float* h = routed ? static_cast<const float*>(a.a) + (size_t)r * Hp
-                          : static_cast<const float*>(a.a_shared) + (size_t)(r - TK) * Hp;
-  const float* W = routed ? static_cast<const float*>(a.w) + (size_t)p * a.D * Hp
-                          : static_cast<const float*>(a.w_shared);
-  const float* wd = W + (size_t)n * Hp;
-  float acc = 0.f;
-  for (int j = 0; j < Hp; ++j) acc = fmaf(h[j], wd[j], acc);
-  if (routed)
-    static_cast<float*>(a.c)[(size_t)r * a.D + n] = a.row_gate[r] * acc;
-  else
-    static_cast<float*>(a.c_shared)[(size_t)(r - TK) * a.D + n] = acc;
+  const int ncols = kMode == 0 ? (Hp + 31) / 32 : (a.D + 63) / 64;
+  const int local = tile - a.pre[p];
+  const int m0 = (local / ncols) * kF32_BM, nt = local % ncols;
+  const int vrows = min(kF32_BM, rows - m0);
+  const int K = kMode == 0 ? a.D : Hp;
+  // A rows: gathered token rows of x (gate/up) or this problem's h rows (down)
+  const float* arow[8];
+  // B rows: W_gate / W_up rows nt*32 + c (gate/up) or W_down rows nt*64 + c (down)
+  const float* W = kMode == 0
+      ? (routed ? static_cast<const float*>(a.w) + (size_t)p * 2 * Hp * a.D : static_cast<const float*>(a.w_shared))
+      : (routed ? static_cast<const float*>(a.w) + (size_t)p * a.D * Hp : static_cast<const float*>(a.w_shared));
+  const float* brow[8];
+  bool bval[8], aval[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int r = (tid >> 5) + 8 * q;  // row of the 64-row tile this thread stages
+    aval[q] = r < vrows;
+    const int rr = aval[q] ? m0 + r : m0;
+    if (kMode == 0) {
+      const int tok = routed ? a.row_token[row_base + rr] : rr;
+      arow[q] = static_cast<const float*>(a.a) + (size_t)tok * a.D;
+      const int c = nt * 32 + (r & 31);
+      bval[q] = c < Hp;
+      brow[q] = W + (size_t)((r < 32 ? 0 : Hp) + (bval[q] ? c : 0)) * a.D;
+    } else {
+      arow[q] = routed ? static_cast<const float*>(a.a) + (size_t)(row_base + rr) * Hp
+                       : static_cast<const float*>(a.a_shared) + (size_t)rr * Hp;
+      const int c = nt * 64 + r;
+      bval[q] = c < a.D;
+      brow[q] = W + (size_t)(bval[q] ? c : 0) * Hp;
+    }
+  }
+  const int kc = tid & 31;  // the thread's element of each staged 32-wide row piece
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int k0 = 0; k0 < K; k0 += kF32_BK) {
+    const int k = k0 + kc;
+    const bool kin = k < K;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int r = (tid >> 5) + 8 * q;
+      sA[r * kF32_LD + kc] = (aval[q] && kin) ? arow[q][k] : 0.f;
+      sB[r * kF32_LD + kc] = (bval[q] && kin) ? brow[q][k] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < kF32_BK; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = sA[(ty + 16 * i) * kF32_LD + kk];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = sB[(tx + 16 * j) * kF32_LD + kk];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = ty + 16 * i;
+    if (r >= vrows) continue;
+    if (kMode == 0) {
+      float* h = routed ? static_cast<float*>(a.c) + (size_t)(row_base + m0 + r) * Hp
+                        : static_cast<float*>(a.c_shared) + (size_t)(m0 + r) * Hp;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int c = nt * 32 + tx + 16 * j;  // columns j (gate) and j + 2 (up) of the tile
+        if (c < Hp) h[c] = silu_precise(acc[i][j]) * acc[i][j + 2];
+      }
+    } else {
+      const float g = routed ? a.row_gate[row_base + m0 + r] : 1.0f;
+      float* y = routed ? static_cast<float*>(a.c) + (size_t)(row_base + m0 + r) * a.D
+                        : static_cast<float*>(a.c_shared) + (size_t)(m0 + r) * a.D;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = nt * 64 + tx + 16 * j;
+        if (c < a.D) y[c] = g * acc[i][j];
+      }
+    }
+  }
 }
 
 hipError_t launch_simple_gateup_f32(const ExpertGemmArgs& a, int TK, hipStream_t s) {
-  const int rows = TK + (a.Hs > 0 ? a.T : 0);
-  if (rows == 0) return hipSuccess;
-  const int hmax = a.H > a.Hs ? a.H : a.Hs;
-  hipLaunchKernelGGL(gateup_f32_kernel, dim3((hmax + 63) / 64, rows), dim3(64), 0, s, a, TK);
+  (void)TK;
+  if (a.max_items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(grouped_f32_kernel<0>, dim3(a.max_items), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_simple_down_f32(const ExpertGemmArgs& a, int TK, hipStream_t s) {
-  const int rows = TK + (a.Hs > 0 ? a.T : 0);
-  if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(down_f32_kernel, dim3((a.D + 63) / 64, rows), dim3(64), 0, s, a, TK);
+  (void)TK;
+  if (a.max_items <= 0) return hipSuccess;
+  hipLaunchKernelGGL(grouped_f32_kernel<1>, dim3(a.max_items), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
