@@ -304,6 +304,20 @@ moe_status moe_balance_stats(const int32_t* expert_counts, const float* score_su
 moe_status moe_cfg_set_stage_timing(moe_cfg* cfg, int enable);
 moe_status moe_cfg_stage_times(moe_cfg* cfg, double* ms, int* calls);
 
+/* Debug builds (the library compiled with MOE_DEBUG, built as
+ * libmoe_mi355x_debug.so): every index a kernel reads from memory (gathered
+ * token rows, slot -> row maps, expert indices, dispatch placements) is
+ * checked against its buffer; a violation is recorded -- the first one's
+ * check site and offending value -- and the index replaced by 0, so the
+ * access stays inside the buffer instead of faulting. moe_debug_status
+ * synchronises the device, writes that site (0 = no violation since the last
+ * call) and value, and clears the record. Sites: 1 grouped-GEMM token row,
+ * 2 grouped-GEMM tile row, 3 e4m3-GEMM token row, 4 streaming-GEMM token row,
+ * 5 fp32-GEMM token row, 6 combine slot row, 7 backward expert index,
+ * 8 backward slot row, 9 dispatch placement. Release builds return
+ * MOE_ERR_UNSUPPORTED (site and value 0); MOE_ERR_INVALID_ARG for NULL. */
+moe_status moe_debug_status(int* site, int* value);
+
 /* HIP error code behind the last MOE_ERR_HIP on this cfg (0 if none). */
 int moe_cfg_last_hip_error(const moe_cfg* cfg);
 

@@ -13,7 +13,9 @@ import re
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
+# MOE_MI355X_DEBUG=1 loads the bounds-checked debug build instead
+LIB_PATH = os.path.join(_PKG, "libmoe_mi355x_debug.so" if os.environ.get("MOE_MI355X_DEBUG") == "1"
+                        else "libmoe_mi355x.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe.h")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_OOM, MOE_ERR_HIP, MOE_ERR_SCRATCH = 0, -1, -2, -3, -4, -5
@@ -81,6 +83,7 @@ def load_library() -> ctypes.CDLL:
     lib.moe_load_stats.argtypes = [vp, ctypes.c_int, vp, vp]
     lib.moe_quantize_e4m3_1x128.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp, vp, vp]
     lib.moe_cfg_set_score_sums.argtypes = [vp, vp]
+    lib.moe_debug_status.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
     lib.moe_layer_forward_noalloc.argtypes = [ctypes.POINTER(MoeParams), vp, ctypes.c_int, vp, vp,
                                               ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeWeights), vp, vp, vp]
     lib.moe_balance_stats.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, vp]
@@ -91,7 +94,7 @@ def load_library() -> ctypes.CDLL:
               "moe_dispatch_forward", "moe_cfg_last_hip_error", "moe_cfg_set_stage_timing",
               "moe_cfg_stage_times", "moe_bias_update", "moe_load_stats", "moe_quantize_e4m3_1x128",
               "moe_layer_backward", "moe_cfg_set_score_sums", "moe_balance_stats",
-              "moe_layer_forward_noalloc"):
+              "moe_layer_forward_noalloc", "moe_debug_status"):
         getattr(lib, f).restype = ctypes.c_int
     del i32p
     _lib = lib
@@ -376,6 +379,16 @@ def load_stats(expert_counts, stream=None):
     if st != MOE_OK:
         raise MoEError(st, "moe_load_stats")
     return stats
+
+
+def debug_status():
+    """moe_debug_status: (site, value) of the first bounds violation since the
+    last call (0, 0 when none); the library must be the debug build."""
+    site, value = ctypes.c_int(), ctypes.c_int()
+    st = load_library().moe_debug_status(ctypes.byref(site), ctypes.byref(value))
+    if st != MOE_OK:
+        raise MoEError(st, "moe_debug_status")
+    return site.value, value.value
 
 
 def layer_forward_noalloc(params: MoeParams, x, gate_w, sel_bias, experts, shared, out=None,

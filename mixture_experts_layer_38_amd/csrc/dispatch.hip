@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void dispatch_permute_kernel(DispatchArgs a) {
     }
     const int base = e >= 0 ? run[w][e] : 0;
     if (e >= 0) {
-      const int r = base + __popcll(mine & ((1ull << lane) - 1ull));
+      const int r = dcheck(base + __popcll(mine & ((1ull << lane) - 1ull)), a.T * a.K, kSiteDispatchRow);
       a.row_token[r] = i / a.K;
       if (a.row_gate) a.row_gate[r] = a.gate[i];
       a.slot_row[i] = r;
@@ -246,7 +246,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
     todo &= ~m;
   }
   if (e >= 0) {
-    const int r = cnt[w][e] + __popcll(mine & ((1ull << lane) - 1ull));
+    const int r = dcheck(cnt[w][e] + __popcll(mine & ((1ull << lane) - 1ull)), a.T * a.K, kSiteDispatchRow);
     a.row_token[r] = i / a.K;
     if (a.row_gate) a.row_gate[r] = a.gate[i];
     a.slot_row[i] = r;
@@ -270,5 +270,7 @@ hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(dispatch_permute_kernel, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
+
+MOE_DEBUG_READER(debug_read_dispatch)
 
 }  // namespace moe

@@ -98,7 +98,7 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
   for (int j = 0; j < kLd / 2; ++j) {
     const int m = r0 + 64 * j;
     const int mm = t.m0 + (m < t.vrows ? m : 0);
-    const int row = (kMode != 1 && t.tok != nullptr) ? t.tok[mm] : mm;
+    const int row = (kMode != 1 && t.tok != nullptr) ? dcheck(t.tok[mm], (int)(t.a_bytes / (2u * t.lda)), kSiteGroupedTok) : mm;
     voff[j] = ((uint32_t)row * (uint32_t)t.lda + c8 * 8) * 2u;
   }
   // Weight (B) rows: one VGPR offset for the thread's first row, the other
@@ -441,6 +441,7 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
     t.nt = idx / gsz;
   }
   t.K = (kMode != 1) ? a.D : t.Hp;
+  t.m0 = dcheck(t.m0, rows, kSiteGroupedRows);
   t.vrows = min(rows - t.m0, rpt);
   if (kMode != 1) {
     t.a_rows = static_cast<const uint16_t*>(a.a);
@@ -526,5 +527,7 @@ hipError_t launch_grouped_down(const ExpertGemmArgs& a, int fp8, hipStream_t s) 
     hipLaunchKernelGGL((grouped_gemm_bf16_kernel<1, false>), dim3(blocks), dim3(512), 0, s, a);
   return hipGetLastError();
 }
+
+MOE_DEBUG_READER(debug_read_grouped)
 
 }  // namespace moe

@@ -708,9 +708,9 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const float* __restrict
   float ss = 0.f, dg = 0.f;
   int ek = -1;
   if (lane < K) {
-    ek = idx[(size_t)t * K + lane];
+    ek = dcheck(idx[(size_t)t * K + lane], E, kSiteBwdExpert);
     ss = score(ek);
-    const float* pr = part + (size_t)slot_row[(size_t)t * K + lane] * npart;
+    const float* pr = part + (size_t)dcheck(slot_row[(size_t)t * K + lane], T * K, kSiteBwdRow) * npart;
     for (int j = 0; j < npart; ++j) dg += pr[j];
   }
   float ds = rsf * dg;
@@ -763,7 +763,7 @@ __global__ __launch_bounds__(256) void dx_combine_kernel(const float* __restrict
   const int t = blockIdx.x;
   int rows[kMaxTopK];
 #pragma unroll
-  for (int k = 0; k < kMaxTopK; ++k) rows[k] = slot_row[(size_t)t * K + (k < K ? k : 0)];
+  for (int k = 0; k < kMaxTopK; ++k) rows[k] = dcheck(slot_row[(size_t)t * K + (k < K ? k : 0)], T * K, kSiteBwdRow);
   const bool has_shared = dxs != nullptr;
   const uint16_t* sbase = has_shared ? dxs + (size_t)t * D : dxr + (size_t)rows[0] * D;
   for (int d = 8 * threadIdx.x; d < D; d += 8 * blockDim.x) {
@@ -870,5 +870,7 @@ hipError_t launch_layer_backward(const BwdArgs& a, hipStream_t s) {
                      a.dx_router, a.slot_row, a.T, a.D, a.K, a.add_residual, a.dx);
   return hipGetLastError();
 }
+
+MOE_DEBUG_READER(debug_read_bwd)
 
 }  // namespace moe

@@ -97,7 +97,7 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
   for (int j = 0; j < kLdA; ++j) {
     const int m = r0 + 64 * j;
     const int mm = t.m0 + (m < t.vrows ? m : 0);
-    const int row = (kMode == 0 && t.tok != nullptr) ? t.tok[mm] : mm;
+    const int row = (kMode == 0 && t.tok != nullptr) ? dcheck(t.tok[mm], (int)(t.a_bytes / (uint32_t)t.lda), kSiteF8Tok) : mm;
     voa[j] = (uint32_t)row * (uint32_t)t.lda + c16 * 16;
   }
   // B rows r0 + 64*j: one VGPR offset for row r0, the other rows' distance
@@ -117,7 +117,7 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
   {
     const int m = tid & (BM - 1);
     const int mm = t.m0 + (m < t.vrows ? m : 0);
-    const int row = (kMode == 0 && t.tok != nullptr) ? t.tok[mm] : mm;
+    const int row = (kMode == 0 && t.tok != nullptr) ? dcheck(t.tok[mm], (int)(t.a_bytes / (uint32_t)t.lda), kSiteF8Tok) : mm;
     asrow = t.a_scale + (size_t)row * t.a_sld;
   }
   // weight scales: gate/up, one 128-row block of W_gate and one of W_up;
@@ -443,5 +443,7 @@ hipError_t launch_grouped_down_f8(const ExpertGemmArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((grouped_gemm_f8_kernel<1>), dim3(blocks), dim3(512), 0, s, a);
   return hipGetLastError();
 }
+
+MOE_DEBUG_READER(debug_read_f8)
 
 }  // namespace moe

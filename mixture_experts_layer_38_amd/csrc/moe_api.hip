@@ -560,6 +560,28 @@ moe_status moe_load_stats(const int32_t* expert_counts, int E, float* stats, voi
              ? MOE_OK : MOE_ERR_HIP;
 }
 
+moe_status moe_debug_status(int* site, int* value) {
+  if (!site || !value) return MOE_ERR_INVALID_ARG;
+  *site = 0;
+  *value = 0;
+#ifdef MOE_DEBUG
+  if (hipDeviceSynchronize() != hipSuccess) return MOE_ERR_HIP;
+  hipError_t (*readers[])(unsigned long long*) = {debug_read_dispatch, debug_read_grouped, debug_read_f8,
+                                                   debug_read_stream, debug_read_f32, debug_read_bwd};
+  for (auto rd : readers) {
+    unsigned long long w = 0;
+    if (rd(&w) != hipSuccess) return MOE_ERR_HIP;
+    if (w != 0 && *site == 0) {
+      *site = (int)(w >> 32);
+      *value = (int)(uint32_t)w;
+    }
+  }
+  return MOE_OK;
+#else
+  return MOE_ERR_UNSUPPORTED;
+#endif
+}
+
 moe_status moe_cfg_set_score_sums(moe_cfg* c, float* score_sum) {
   if (!c) return MOE_ERR_INVALID_ARG;
   c->score_sum = score_sum;

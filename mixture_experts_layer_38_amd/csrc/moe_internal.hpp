@@ -139,6 +139,47 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return (a + b) + (c + d);
 }
 
+// Bounds checks of the debug build (compiled with MOE_DEBUG): an index read
+// from memory that lies outside [0, n) is recorded -- the first violation's
+// site code and value, in a word of device memory that moe_debug_status reads
+// and clears -- and replaced by 0, so the access that follows stays inside
+// its buffer. Device code is not linked across translation units, so each
+// unit holds its own word and its own reader. Release builds compile the
+// checks away.
+#ifdef MOE_DEBUG
+static __device__ unsigned long long moe_debug_word;
+__device__ __forceinline__ int dcheck(int v, int n, int site) {
+  if ((unsigned)v >= (unsigned)n) {
+    atomicCAS(&moe_debug_word, 0ull, ((unsigned long long)(unsigned)site << 32) | (unsigned)v);
+    return 0;
+  }
+  return v;
+}
+#define MOE_DEBUG_READER(name)                                                              \
+  hipError_t name(unsigned long long* w) {                                                  \
+    hipError_t e = hipMemcpyFromSymbol(w, HIP_SYMBOL(moe_debug_word), sizeof(*w), 0,        \
+                                       hipMemcpyDeviceToHost);                              \
+    if (e != hipSuccess) return e;                                                          \
+    const unsigned long long z = 0;                                                         \
+    return hipMemcpyToSymbol(HIP_SYMBOL(moe_debug_word), &z, sizeof(z), 0, hipMemcpyHostToDevice); \
+  }
+#else
+__device__ __forceinline__ int dcheck(int v, int, int) { return v; }
+#define MOE_DEBUG_READER(name)
+#endif
+// debug check sites (the code moe_debug_status reports)
+enum DebugSite {
+  kSiteGroupedTok = 1,     // gathered token row of a grouped GEMM tile
+  kSiteGroupedRows = 2,    // a tile's first row inside its problem
+  kSiteF8Tok = 3,          // gathered token row, e4m3-activation GEMM
+  kSiteStreamTok = 4,      // gathered token row, streaming GEMM
+  kSiteF32Tok = 5,         // gathered token row, fp32 GEMM
+  kSiteCombineRow = 6,     // slot -> row of the combine
+  kSiteBwdExpert = 7,      // expert index read by the router backward
+  kSiteBwdRow = 8,         // slot -> row in the backward
+  kSiteDispatchRow = 9,    // row a dispatch entry is placed at
+};
+
 // problem p in [0, E]: routed expert p (< E) or the shared expert (== E).
 // Largest p with pre[p] <= i, for a non-decreasing pre[0..E+1].
 __device__ __forceinline__ int find_problem(const int32_t* pre, int E, int i) {
@@ -315,6 +356,16 @@ struct BwdArgs {
   float* dw_down_shared;    // [D][Hs]
 };
 hipError_t launch_layer_backward(const BwdArgs& a, hipStream_t s);
+
+#ifdef MOE_DEBUG
+// readers of each translation unit's debug word (value, then cleared)
+hipError_t debug_read_dispatch(unsigned long long* w);
+hipError_t debug_read_grouped(unsigned long long* w);
+hipError_t debug_read_f8(unsigned long long* w);
+hipError_t debug_read_stream(unsigned long long* w);
+hipError_t debug_read_f32(unsigned long long* w);
+hipError_t debug_read_bwd(unsigned long long* w);
+#endif
 
 // one workgroup: bias update (bias != null) and/or load statistics (stats != null)
 hipError_t launch_balance(const int32_t* counts, int E, float gamma, float* bias, float* stats, hipStream_t s);

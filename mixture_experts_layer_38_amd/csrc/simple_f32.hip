@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void grouped_f32_kernel(ExpertGemmArgs a) {
     aval[q] = r < vrows;
     const int rr = aval[q] ? m0 + r : m0;
     if (kMode == 0) {
-      const int tok = routed ? a.row_token[row_base + rr] : rr;
+      const int tok = routed ? dcheck(a.row_token[row_base + rr], a.x_rows, kSiteF32Tok) : rr;
       arow[q] = static_cast<const float*>(a.a) + (size_t)tok * a.D;
       const int c = nt * 32 + (r & 31);
       bval[q] = c < Hp;
@@ -184,7 +184,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const int t = blockIdx.x;
   int rows[kMaxTopK];
 #pragma unroll
-  for (int k = 0; k < kMaxTopK; ++k) rows[k] = (k < a.K) ? a.slot_row[(size_t)t * a.K + k] : 0;
+  for (int k = 0; k < kMaxTopK; ++k)
+    rows[k] = (k < a.K) ? dcheck(a.slot_row[(size_t)t * a.K + k], a.T * a.K, kSiteCombineRow) : 0;
   const bool has_shared = a.y_shared != nullptr;
   // a source that is absent reads a valid row instead (never added)
   const void* sbase = has_shared ? a.y_shared : a.y_routed;
@@ -244,5 +245,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   }
   return hipGetLastError();
 }
+
+MOE_DEBUG_READER(debug_read_f32)
 
 }  // namespace moe

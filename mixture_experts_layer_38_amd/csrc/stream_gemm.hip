@@ -113,7 +113,7 @@ __device__ __forceinline__ Item setup_item(const ExpertGemmArgs& a, const int32_
   it.aval = arow < it.nrows;
   const int mm = m0 + (it.aval ? arow : 0);  // in-bounds row for masked threads
   if (kMode == 0) {
-    const int tok = routed ? a.row_token[row_base + mm] : mm;
+    const int tok = routed ? dcheck(a.row_token[row_base + mm], a.x_rows, kSiteStreamTok) : mm;
     it.aptr = static_cast<const uint16_t*>(a.a) + (size_t)tok * a.D + (tid & 15) * 8;
   } else {
     it.aptr = routed ? static_cast<const uint16_t*>(a.a) + (size_t)(row_base + mm) * a.H + (tid & 15) * 8
@@ -342,5 +342,7 @@ hipError_t launch_stream_gateup(const ExpertGemmArgs& a, int fp8, int max_items,
 hipError_t launch_stream_down(const ExpertGemmArgs& a, int fp8, int max_items, int num_cus, hipStream_t s) {
   return fp8 ? launch_stream<true, 1>(a, max_items, num_cus, s) : launch_stream<false, 1>(a, max_items, num_cus, s);
 }
+
+MOE_DEBUG_READER(debug_read_stream)
 
 }  // namespace moe

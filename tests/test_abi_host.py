@@ -137,3 +137,22 @@ def test_binding_tensor_check():
                  (None, torch.float32, (4, 8)), (t.numpy(), torch.float32, (4, 8))):
         with pytest.raises(ValueError):
             _check_tensor("t", args[0], args[1], args[2], cpu)
+
+
+def test_debug_build_exports_every_declared_function():
+    """The bounds-checked debug library (built beside the release one) loads
+    and exports the same functions; the release library's debug query says
+    it is not a debug build."""
+    import os
+    from mixture_experts_layer_38_amd import _binding as B
+    from mixture_experts_layer_38_amd import build as Bd
+    assert os.path.exists(Bd.LIB_DEBUG), "run the build first (release and debug)"
+    dbg = ctypes.CDLL(Bd.LIB_DEBUG)
+    for n in M.declared_functions():
+        assert hasattr(dbg, n), n
+    lib = M.load_library()
+    site, value = ctypes.c_int(7), ctypes.c_int(7)
+    if B.LIB_PATH.endswith("libmoe_mi355x.so"):
+        assert lib.moe_debug_status(ctypes.byref(site), ctypes.byref(value)) == M.MOE_ERR_UNSUPPORTED
+        assert site.value == 0 and value.value == 0
+    assert lib.moe_debug_status(None, ctypes.byref(value)) == M.MOE_ERR_INVALID_ARG

@@ -711,6 +711,47 @@ def test_layer_v3_decode_fp8(layers):
     _check_layer(inp)
 
 
+def test_debug_build_matches_and_reports_no_violation():
+    """The bounds-checked debug library gives bit-identical results on every
+    kernel family (grouped and streaming bf16, e4m3 weights, e4m3
+    activations, fp32, the backward pass) and records no out-of-range
+    index."""
+    from mixture_experts_layer_38_amd import _binding as B
+    from mixture_experts_layer_38_amd import build as Bd
+
+    cases = [(SMALL_SIG, "grouped"), (SMALL_SIG, "stream"), (SMALL_FP8, "stream"), (SMALL_FP8, "grouped"),
+             (SMALL_W8A8, "auto"), (SMALL_F32, "auto")]
+    inputs = [MI.make_layer(c, DEV) for c, _ in cases]
+    bw_inp = MI.make_layer(BWD_SIG, DEV)
+    d_out = torch.randn((BWD_SIG.T, BWD_SIG.D), generator=torch.Generator().manual_seed(5)).to(DEV)
+
+    def run_all():
+        outs = []
+        for (cfg, path), inp in zip(cases, inputs):
+            layer = M.MoELayer.from_config(cfg, path=path)
+            counts = torch.empty(cfg.E, dtype=torch.int32, device=DEV)
+            outs.append((layer.forward(inp.x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared,
+                                       expert_counts=counts), counts))
+        layer = M.MoELayer.from_config(BWD_SIG, backward=True)
+        g = layer.backward(bw_inp.x, bw_inp.gate_w, bw_inp.sel_bias, bw_inp.experts, bw_inp.shared, d_out)
+        torch.cuda.synchronize()
+        return outs, g
+
+    ref_outs, ref_g = run_all()
+    saved = (B.LIB_PATH, B._lib)
+    try:
+        B.LIB_PATH, B._lib = Bd.LIB_DEBUG, None
+        B.load_library()
+        assert M.debug_status() == (0, 0)
+        outs, g = run_all()
+        assert M.debug_status() == (0, 0)
+    finally:
+        B.LIB_PATH, B._lib = saved
+    for (o, c), (ro, rc) in zip(outs, ref_outs):
+        assert torch.equal(o, ro) and torch.equal(c, rc)
+    for k in ("dx", "d_gate_w", "d_gate_up", "d_down"):
+        assert torch.equal(g[k], ref_g[k]), k
+
 def test_binding_rejects_mismatched_tensors():
     """The binding checks every tensor against the cfg before the library
     sees a bare pointer: wrong dtype, shape, device or layout raise."""
