@@ -8,8 +8,9 @@
 // W_gate rows and the matching 32 W_up rows, so h = SiLU(gate) * up is formed
 // in registers; for down, 64 output columns, times the row's gate. K steps of
 // 32 staged through LDS with coalesced loads (consecutive threads read
-// consecutive elements of a row); each thread accumulates 4 rows x 4 columns
-// in k order.
+// consecutive elements of a row), the next step's loads in flight while the
+// current one is multiplied; each thread accumulates 4 rows x 4 columns in k
+// order.
 //
 // The combine is the gate-weighted sum of the page-1 MoE forward plus the
 // shared expert and the residual; it runs for every dtype.
@@ -74,16 +75,28 @@ __global__ __launch_bounds__(256) void grouped_f32_kernel(ExpertGemmArgs a) {
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-  for (int k0 = 0; k0 < K; k0 += kF32_BK) {
+  // the next K slice is loaded into registers while the current one is
+  // multiplied from LDS
+  float va[8], vb[8];
+  auto load_slice = [&](int k0) __attribute__((always_inline)) {
     const int k = k0 + kc;
     const bool kin = k < K;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
+      va[q] = (aval[q] && kin) ? arow[q][k] : 0.f;
+      vb[q] = (bval[q] && kin) ? brow[q][k] : 0.f;
+    }
+  };
+  load_slice(0);
+  for (int k0 = 0; k0 < K; k0 += kF32_BK) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
       const int r = (tid >> 5) + 8 * q;
-      sA[r * kF32_LD + kc] = (aval[q] && kin) ? arow[q][k] : 0.f;
-      sB[r * kF32_LD + kc] = (bval[q] && kin) ? brow[q][k] : 0.f;
+      sA[r * kF32_LD + kc] = va[q];
+      sB[r * kF32_LD + kc] = vb[q];
     }
     __syncthreads();
+    if (k0 + kF32_BK < K) load_slice(k0 + kF32_BK);
 #pragma unroll 8
     for (int kk = 0; kk < kF32_BK; ++kk) {
       float av[4], bv[4];

@@ -437,6 +437,16 @@ def _rel(a, b):
     return float(np.abs(a - b).max() / max(np.abs(b).max(), 1e-30))
 
 
+def _rel_rows(a, b, floor=1e-2):
+    """Per-row error of a matrix: max over rows of max|a - b| / max|b| within
+    the row (rows whose reference is below floor x the matrix maximum are
+    measured against that floor instead)."""
+    a = a.detach().float().cpu().numpy().astype(np.float64) if torch.is_tensor(a) else a
+    a, b = a.reshape(a.shape[0], -1), np.asarray(b).reshape(b.shape[0], -1)
+    den = np.maximum(np.abs(b).max(axis=1), floor * max(np.abs(b).max(), 1e-30))
+    return float((np.abs(a - b).max(axis=1) / den).max())
+
+
 def _check_backward(cfg, add_residual=True, with_shared=True, seed=5):
     inp = MI.make_layer(cfg, DEV)
     over = {} if with_shared else {"shared_hidden": 0}
@@ -457,20 +467,20 @@ def _check_backward(cfg, add_residual=True, with_shared=True, seed=5):
     tol = TOL["bf16"]
     dx = got["dx"].cpu().numpy().astype(np.float64)
     e_dx = np.abs(dx - ref["dx"]).max(axis=1) / np.maximum(np.abs(ref["dx"]).max(axis=1), 1e-30)
-    errs = {"dx": float(e_dx.max()), "d_gate_w": _rel(got["d_gate_w"], ref["d_gate_w"])}
+    errs = {"dx": float(e_dx.max()), "d_gate_w": _rel_rows(got["d_gate_w"], ref["d_gate_w"])}
     worst_w = 0.0
     for e in range(cfg.E):
         if e not in ref["d_routed"]:
             assert not got["d_gate_up"][e].any() and not got["d_down"][e].any(), f"unused expert {e} not zero"
             continue
         dwg, dwu, dwd = ref["d_routed"][e]
-        worst_w = max(worst_w, _rel(got["d_gate_up"][e], np.concatenate([dwg, dwu], 0)),
-                      _rel(got["d_down"][e], dwd))
+        worst_w = max(worst_w, _rel_rows(got["d_gate_up"][e], np.concatenate([dwg, dwu], 0)),
+                      _rel_rows(got["d_down"][e], dwd))
     errs["d_experts"] = worst_w
     if with_shared:
         dwg, dwu, dwd = ref["d_shared"]
-        errs["d_shared"] = max(_rel(got["d_shared_gate_up"], np.concatenate([dwg, dwu], 0)),
-                               _rel(got["d_shared_down"], dwd))
+        errs["d_shared"] = max(_rel_rows(got["d_shared_gate_up"], np.concatenate([dwg, dwu], 0)),
+                               _rel_rows(got["d_shared_down"], dwd))
     print(f"{cfg.name} backward errors {errs}")
     for k, v in errs.items():
         assert v <= tol, (k, v)
@@ -508,12 +518,12 @@ def test_backward_routed_only_and_repeatable():
     ref = O.layer_backward(A.router_params(cfg), A.decode_tensor(inp.x)[:1], A.decode_tensor(inp.gate_w), bias,
                            A.routed_expert_fn(inp.experts), d1.cpu().numpy().astype(np.float64), None,
                            add_residual=False)
-    assert _rel(gt["dx"], ref["dx"]) <= TOL["bf16"] and _rel(gt["d_gate_w"], ref["d_gate_w"]) <= TOL["bf16"]
+    assert _rel(gt["dx"], ref["dx"]) <= TOL["bf16"] and _rel_rows(gt["d_gate_w"], ref["d_gate_w"]) <= TOL["bf16"]
     for e in range(cfg.E):
         if e in ref["d_routed"]:
             dwg, dwu, dwd = ref["d_routed"][e]
-            assert _rel(gt["d_gate_up"][e], np.concatenate([dwg, dwu], 0)) <= TOL["bf16"]
-            assert _rel(gt["d_down"][e], dwd) <= TOL["bf16"]
+            assert _rel_rows(gt["d_gate_up"][e], np.concatenate([dwg, dwu], 0)) <= TOL["bf16"]
+            assert _rel_rows(gt["d_down"][e], dwd) <= TOL["bf16"]
         else:
             assert not gt["d_gate_up"][e].any() and not gt["d_down"][e].any()
 
@@ -698,7 +708,7 @@ def test_backward_v3_prefill_sampled(layers):
     e_w = 0.0
     for e in experts:
         dwg, dwu, dwd = ref["d_routed"][e]
-        e_w = max(e_w, _rel(got["d_gate_up"][e], np.concatenate([dwg, dwu], 0)), _rel(got["d_down"][e], dwd))
+        e_w = max(e_w, _rel_rows(got["d_gate_up"][e], np.concatenate([dwg, dwu], 0)), _rel_rows(got["d_down"][e], dwd))
     print(f"v3 backward: dx err {e_dx} over {len(tokens)} tokens, expert grads err {e_w} "
           f"(experts {experts}, rows {load[experts].tolist()}), near-tie tokens {int(near.sum())}")
     assert e_dx <= TOL["bf16"] and e_w <= TOL["bf16"]
