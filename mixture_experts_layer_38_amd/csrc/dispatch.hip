@@ -67,9 +67,9 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(DispatchArgs a) {
   const int p = threadIdx.x;  // problem: routed expert p < E, shared expert p == E
   const int rows = (p < a.E) ? a.counts[p] : (p == a.E ? a.shared_rows : 0);
   const int cnt = (p < a.E) ? rows : 0;
-  const int mblocks = (rows + a.bm - 1) / a.bm;
-  const int it1 = (p <= a.E) ? mblocks * (p < a.E ? a.n1_routed : a.n1_shared) : 0;
-  const int it2 = (p <= a.E) ? mblocks * (p < a.E ? a.n2_routed : a.n2_shared) : 0;
+  const int mb1 = (rows + a.bm1 - 1) / a.bm1, mb2 = (rows + a.bm2 - 1) / a.bm2;
+  const int it1 = (p <= a.E) ? mb1 * (p < a.E ? a.n1_routed : a.n1_shared) : 0;
+  const int it2 = (p <= a.E) ? mb2 * (p < a.E ? a.n2_routed : a.n2_shared) : 0;
   int tot0, tot1, tot2;
   const int off = block_exclusive_scan(cnt, &tot0);
   const int o1 = block_exclusive_scan(it1, &tot1);
@@ -207,9 +207,9 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(DispatchArgs a) {
   }
   const int rows = (p < a.E) ? ecount : (p == a.E ? a.shared_rows : 0);
   const int c0 = (p < a.E) ? rows : 0;
-  const int mblocks = (rows + a.bm - 1) / a.bm;
-  const int it1 = (p <= a.E) ? mblocks * (p < a.E ? a.n1_routed : a.n1_shared) : 0;
-  const int it2 = (p <= a.E) ? mblocks * (p < a.E ? a.n2_routed : a.n2_shared) : 0;
+  const int mb1 = (rows + a.bm1 - 1) / a.bm1, mb2 = (rows + a.bm2 - 1) / a.bm2;
+  const int it1 = (p <= a.E) ? mb1 * (p < a.E ? a.n1_routed : a.n1_shared) : 0;
+  const int it2 = (p <= a.E) ? mb2 * (p < a.E ? a.n2_routed : a.n2_shared) : 0;
   int tot0, tot1, tot2;
   const int off = block_exclusive_scan(c0, &tot0);
   const int o1 = block_exclusive_scan(it1, &tot1);

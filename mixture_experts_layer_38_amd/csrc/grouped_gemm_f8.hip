@@ -18,18 +18,27 @@
 // Token rows are gathered (codes and their scales) through the dispatch's
 // row -> token map. Down GEMM: Y[row] = g_row * (h[row] W_down^T), bf16.
 //
-// Tile 128 x 256, 8 waves (two per SIMD) as 2 x 4, each wave 64 x 64 = 4 x 4
-// blocks of 16 x 16 (64 fp32 accumulators per lane); a wave's four 16-row
-// blocks are interleaved with the other row-wave's (blocks wm + 2i), and the
-// tile body is instantiated per count of valid row blocks. Operands are
-// staged through two LDS buffers (rows padded to 144 bytes): the weight rows
-// of the next K step and the token rows (and their scales) of the step after
-// it are loaded into registers while the current step is multiplied; the
-// second pair of column blocks is read from LDS behind the first pair's
-// MFMAs, and the next step's tile is written behind the second pair's; one
-// barrier per step. Tile order and the even split of an expert's rows over
-// its row tiles follow the bf16 grouped GEMMs (runs of 32 tiles per XCD,
+// Both GEMMs: 8 waves (two per SIMD) as 2 x 4, each wave owns 64 columns
+// (4 blocks of 16) and the row blocks wm + 2i of the tile, interleaved with
+// the other row-wave's; the tile body is instantiated per count of valid row
+// blocks. Operands are staged through two LDS buffers (rows padded to 144
+// bytes), the next K step's operands are loaded into registers while the
+// current one is multiplied and written to the idle buffer behind its MFMAs;
+// one barrier per step. Tile order and the even split of an expert's rows
+// over its row tiles follow the bf16 grouped GEMMs (runs of 32 tiles per XCD,
 // column-tile major).
+//
+// The two GEMMs differ in tile height. Gate/up tiles are 128 x 256 (4 row
+// blocks per wave): all fragments of a step are held in registers, the token
+// rows are loaded two steps ahead, and the second pair of column blocks is
+// read behind the first pair's MFMAs. Down tiles are 256 x 256 (8 row blocks
+// per wave), which halves the weight bytes streamed per output: the four
+// column fragments are held for the step while the row fragments (and their
+// scales) stream through two register slots one row block ahead; the row
+// block count is rounded up to an even number (a block past the valid rows
+// multiplies a copy of a valid row and is never stored). The gate/up GEMM
+// keeps the shorter tile: its extra scale work per MFMA (two weight scales)
+// and its h-quantisation epilogue leave no registers for the taller one.
 #include <type_traits>
 
 #include "moe_internal.hpp"
@@ -37,15 +46,17 @@
 namespace moe {
 
 namespace {
-constexpr int BM = kF8_BM, BN = 256, BK = kF8_BK, LDB = BK + 16;  // LDS row stride in bytes
-constexpr int kRowsL = BM + BN;                                   // LDS rows per buffer: A then B
-constexpr int kBufBytes = kRowsL * LDB;
+constexpr int BM1 = kF8_BM1, BM2 = kF8_BM2;  // tile rows: gate/up, down
+constexpr int BN = 256, BK = kF8_BK, LDB = BK + 16;  // LDS row stride in bytes
+// bytes of one LDS operand buffer: A rows then B rows
+constexpr int buf_bytes(int bm) { return (bm + BN) * LDB; }
+constexpr int kBuf1 = buf_bytes(BM1), kBuf2 = buf_bytes(BM2);
 constexpr int kRun = 32;
-constexpr int kLdA = 2, kLdB = 4;  // 16-byte global loads per thread per K step
-constexpr int kHLd = BK + 4;       // gate/up epilogue: fp32 h staging row (floats)
-constexpr int kYLd = BN + 8;       // down epilogue: bf16 y staging row (elements)
-static_assert(BM * kHLd * 4 <= 2 * kBufBytes, "h staging fits the operand buffers");
-static_assert(BM * kYLd * 2 <= 2 * kBufBytes, "y staging fits the operand buffers");
+constexpr int kLdB = 4;        // 16-byte weight loads per thread per K step
+constexpr int kHLd = BK + 4;   // gate/up epilogue: fp32 h staging row (floats)
+constexpr int kYLd = BN + 8;   // down epilogue: bf16 y staging row (elements)
+static_assert(BM1 * kHLd * 4 <= 2 * kBuf1, "h staging fits the operand buffers");
+static_assert(BM2 * kYLd * 2 <= 2 * kBuf2, "y staging fits the operand buffers");
 
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 
@@ -75,67 +86,52 @@ __device__ __forceinline__ f32x4 mfma_f8(const i32x8& a, const i32x8& b, const f
   // format 0 = e4m3 for both operands; E8M0 scale 127 = 2^0
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
+
+// source row of the tile's A row m (m < BM): rows past the valid ones read
+// the tile's first row instead (loaded, never stored), so every load is
+// unconditional; gate/up routed rows go through the row -> token map
+__device__ __forceinline__ int a_source_row(const TileF8& t, int m) {
+  const int mm = t.m0 + (m < t.vrows ? m : 0);
+  return t.tok != nullptr ? dcheck(t.tok[mm], (int)(t.a_bytes / (uint32_t)t.lda), kSiteF8Tok) : mm;
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
 }  // namespace
 
-template <int kMode, int NRB>
-__device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kBufBytes], float (*s_asc)[512],
-                                             float* s_gate) {
+// Gate/up + SwiGLU + h quantisation, 128-row tiles: the tile's 128 hidden
+// columns are W_gate rows nt*128 .. +127 and the same W_up rows.
+template <int NRB>
+__device__ __forceinline__ void gateup_body_f8(const TileF8& t, uint8_t (*smem)[kBuf1], float (*s_asc)[512]) {
+  constexpr int BM = BM1, kLdA = 2;  // A rows r0 and r0 + 64
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 2, wn = wave & 3;
   const int c16 = tid & 7, r0 = tid >> 3;
 
   // loader: 16-byte pieces; A rows r0 and r0 + 64 (128 bytes = one K step
-  // each), B rows r0 + 64*j. Rows past the valid ones read a valid row
-  // instead (never stored), so every load is unconditional.
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(t.a_rows), (short)0, t.a_bytes, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(t.w), (short)0, t.w_bytes, 0x00020000);
+  // each), B rows r0 + 64*j
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(t.a_rows, t.a_bytes);
+  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(t.w, t.w_bytes);
   uint32_t voa[kLdA];
 #pragma unroll
-  for (int j = 0; j < kLdA; ++j) {
-    const int m = r0 + 64 * j;
-    const int mm = t.m0 + (m < t.vrows ? m : 0);
-    const int row = (kMode == 0 && t.tok != nullptr) ? dcheck(t.tok[mm], (int)(t.a_bytes / (uint32_t)t.lda), kSiteF8Tok) : mm;
-    voa[j] = (uint32_t)row * (uint32_t)t.lda + c16 * 16;
-  }
+  for (int j = 0; j < kLdA; ++j) voa[j] = (uint32_t)a_source_row(t, r0 + 64 * j) * (uint32_t)t.lda + c16 * 16;
   // B rows r0 + 64*j: one VGPR offset for row r0, the other rows' distance
-  // (uniform) in the scalar offset (gate/up: W_gate rows nt*128 + r0 +
-  // {0, 64}, then the same W_up rows; down rows past D read row nt*256 + r0)
-  const uint32_t vob = (uint32_t)((kMode == 0) ? t.nt * 128 + r0 : t.nt * BN + r0) * (uint32_t)t.K + c16 * 16;
+  // (uniform) in the scalar offset: W_gate rows nt*128 + r0 + {0, 64}, then
+  // the same W_up rows
+  const uint32_t vob = (uint32_t)(t.nt * 128 + r0) * (uint32_t)t.K + c16 * 16;
   uint32_t bd[kLdB];
 #pragma unroll
-  for (int j = 0; j < kLdB; ++j) {
-    int dr = (kMode == 0) ? (j & 1) * 64 + (j >> 1) * t.Hp : 64 * j;
-    if (kMode == 1 && t.nt * BN + 64 * j >= t.D) dr = 0;
-    bd[j] = (uint32_t)dr * (uint32_t)t.K;
-  }
+  for (int j = 0; j < kLdB; ++j) bd[j] = (uint32_t)((j & 1) * 64 + (j >> 1) * t.Hp) * (uint32_t)t.K;
   // row scales: thread tid stages the scale of A row tid % 128 (threads
   // past 128 write a copy that is never read, so the K loop has no branch)
-  const float* asrow;
-  {
-    const int m = tid & (BM - 1);
-    const int mm = t.m0 + (m < t.vrows ? m : 0);
-    const int row = (kMode == 0 && t.tok != nullptr) ? dcheck(t.tok[mm], (int)(t.a_bytes / (uint32_t)t.lda), kSiteF8Tok) : mm;
-    asrow = t.a_scale + (size_t)row * t.a_sld;
-  }
-  // weight scales: gate/up, one 128-row block of W_gate and one of W_up;
-  // down, the 128-row block of W_down holding this wave's 64 columns
-  // (read through vector loads one K step ahead: a scalar load in the loop
-  // would make every LDS wait after it wait for the scalar load too)
-  uint32_t wso[2];
-  if (kMode == 0) {
-    wso[0] = (uint32_t)(t.nt * t.a_sld) * 4u;
-    wso[1] = (uint32_t)((t.Hp / 128 + t.nt) * t.a_sld) * 4u;
-  } else {
-    int cb = (t.nt * BN + 64 * wn) >> 7;
-    if (cb * 128 >= t.D) cb = 0;
-    wso[0] = wso[1] = (uint32_t)(cb * t.a_sld) * 4u;
-  }
-  const uint32_t ws_bytes = (uint32_t)(((kMode == 0) ? 2 * t.Hp : t.D) / 128 * t.a_sld) * 4u;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(t.ws), (short)0,
-                                                                      ws_bytes, 0x00020000);
+  const float* asrow = t.a_scale + (size_t)a_source_row(t, tid & (BM - 1)) * t.a_sld;
+  // weight scales: one 128-row block of W_gate and one of W_up (read
+  // through vector loads one K step ahead: a scalar load in the loop would
+  // make every LDS wait after it wait for the scalar load too)
+  const uint32_t wso[2] = {(uint32_t)(t.nt * t.a_sld) * 4u, (uint32_t)((t.Hp / 128 + t.nt) * t.a_sld) * 4u};
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(t.ws, (uint32_t)(2 * t.Hp / 128 * t.a_sld) * 4u);
   auto load_ws = [&](int c, int kb) __attribute__((always_inline)) {
     return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 0u, wso[c] + 4u * kb, 0));
   };
@@ -148,8 +144,7 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
   };
 
   // 16 x 16 output blocks: row block i (rows 16*(wm + 2i) ..), column block
-  // c (gate/up: c < 2 the wave's two W_gate blocks, c >= 2 the matching W_up
-  // blocks; down: 64*wn + 16c)
+  // c: c < 2 the wave's two W_gate blocks, c >= 2 the matching W_up blocks
   constexpr int NA = NRB > 0 ? NRB : 1;
   f32x4 acc[NA][4];
 #pragma unroll
@@ -158,10 +153,8 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
     for (int c = 0; c < 4; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
   int bcol[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) bcol[c] = (kMode == 0) ? 128 * (c >> 1) + 32 * wn + 16 * (c & 1) : 64 * wn + 16 * c;
+  for (int c = 0; c < 4; ++c) bcol[c] = 128 * (c >> 1) + 32 * wn + 16 * (c & 1);
   const int lr = lane & 15, lk = (lane >> 4) * 32;
-
-  if (kMode == 1 && tid < BM) s_gate[tid] = (t.gate != nullptr && tid < t.vrows) ? t.gate[t.m0 + tid] : 1.0f;
 
   const int nk = t.K / BK;
   uint4 pa[2][kLdA], pb[kLdB];
@@ -249,7 +242,7 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
 #pragma unroll
     for (int c = 2; c < 4; ++c)
 #pragma unroll
-      for (int i = 0; i < NRB; ++i) block(i, c, kMode == 0 ? sw1 : sw0);
+      for (int i = 0; i < NRB; ++i) block(i, c, sw1);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     read_a(cur ^ 1);
@@ -266,7 +259,7 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
 
   // D layout of the 16x16 MFMA: element j of lane l is row 4*(l/16) + j,
   // column l%16.
-  if (kMode == 0) {
+  {
     // h tile (128 x 128 fp32) into LDS, then each row's block is quantised:
     // four lanes per row, 32 columns each
     float* sh = reinterpret_cast<float*>(&smem[0][0]);
@@ -304,8 +297,162 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
       *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
       if (q == 0) t.c_scale[(size_t)(t.m0 + r) * t.c_sld + t.nt] = s;
     }
-  } else {
-    // y tile (128 x 256 bf16) staged through LDS, then written as 16-byte
+  }
+}
+
+// Down + gate scale, 256-row tiles: Y[row] = g_row * (h[row] W_down^T), the
+// tile's 256 columns W_down rows nt*256 .. +255. NRB is even.
+template <int NRB>
+__device__ __forceinline__ void down_body_f8(const TileF8& t, uint8_t (*smem)[kBuf2], float (*s_asc)[512],
+                                             float* s_gate) {
+  static_assert(NRB % 2 == 0, "row blocks stream through two register slots");
+  constexpr int BM = BM2, kLdA = 4;  // A rows r0 + 64*j
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2, wn = wave & 3;
+  const int c16 = tid & 7, r0 = tid >> 3;
+
+  // loader: 16-byte pieces of rows r0 + 64*j (128 bytes = one K step each)
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(t.a_rows, t.a_bytes);
+  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(t.w, t.w_bytes);
+  uint32_t voa[kLdA];
+#pragma unroll
+  for (int j = 0; j < kLdA; ++j) voa[j] = (uint32_t)a_source_row(t, r0 + 64 * j) * (uint32_t)t.lda + c16 * 16;
+  // B rows nt*256 + r0 + 64*j: one VGPR offset for row r0, the other rows'
+  // distance (uniform) in the scalar offset; rows past D read row nt*256 + r0
+  const uint32_t vob = (uint32_t)(t.nt * BN + r0) * (uint32_t)t.K + c16 * 16;
+  uint32_t bd[kLdB];
+#pragma unroll
+  for (int j = 0; j < kLdB; ++j) bd[j] = (t.nt * BN + 64 * j >= t.D) ? 0u : (uint32_t)(64 * j) * (uint32_t)t.K;
+  // row scales: thread tid stages the scale of A row tid % 256 (threads
+  // past 256 write a copy that is never read, so the K loop has no branch)
+  const float* asrow = t.a_scale + (size_t)a_source_row(t, tid & (BM - 1)) * t.a_sld;
+  // weight scale: the 128-row block of W_down holding this wave's 64
+  // columns (vector loads one K step ahead)
+  int cb = (t.nt * BN + 64 * wn) >> 7;
+  if (cb * 128 >= t.D) cb = 0;
+  const uint32_t wso = (uint32_t)(cb * t.a_sld) * 4u;
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(t.ws, (uint32_t)(t.D / 128 * t.a_sld) * 4u);
+  auto load_ws = [&](int kb) __attribute__((always_inline)) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, 0u, wso + 4u * kb, 0));
+  };
+  auto gload_a = [&](int j, int k0) __attribute__((always_inline)) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ra, voa[j], k0, 0));
+  };
+  auto gload_b = [&](int j, int k0) __attribute__((always_inline)) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, vob, k0 + bd[j], 0));
+  };
+
+  // 16 x 16 output blocks: row block i (rows 16*(wm + 2i) ..), column block
+  // c (columns 64*wn + 16c ..)
+  constexpr int NA = NRB > 0 ? NRB : 1;
+  f32x4 acc[NA][4];
+#pragma unroll
+  for (int i = 0; i < NA; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[i][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int bcol[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) bcol[c] = 64 * wn + 16 * c;
+  const int lr = lane & 15, lk = (lane >> 4) * 32;
+
+  if (tid < BM) s_gate[tid] = (t.gate != nullptr && tid < t.vrows) ? t.gate[t.m0 + tid] : 1.0f;
+
+  const int nk = t.K / BK;
+  uint4 pa[kLdA], pb[kLdB];
+  float pas;
+#pragma unroll
+  for (int j = 0; j < kLdA; ++j) pa[j] = gload_a(j, 0);
+  pas = asrow[0];
+#pragma unroll
+  for (int j = 0; j < kLdB; ++j) pb[j] = gload_b(j, 0);
+  float swc = load_ws(0);  // weight scale of the step being multiplied
+
+  auto store_a = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kLdA; ++j) *reinterpret_cast<uint4*>(&smem[buf][(r0 + 64 * j) * LDB + c16 * 16]) = pa[j];
+    s_asc[buf][tid] = pas;
+  };
+  auto store_b = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kLdB; ++j)
+      *reinterpret_cast<uint4*>(&smem[buf][(BM + r0 + 64 * j) * LDB + c16 * 16]) = pb[j];
+  };
+  store_a(0);
+  store_b(0);
+  __syncthreads();
+
+  // fragments: lane l holds row (or column) l % 16, K bytes 32*(l/16) .. +31;
+  // the four B fragments are held for the whole step, the A fragments (and
+  // the four row scales of each) stream through two slots, one row block
+  // ahead of its MFMAs
+  i32x8 fa[2], fb[4];
+  f32x4 sa[2];
+  auto read_a = [&](int buf, int i, int slot) __attribute__((always_inline)) {
+    fa[slot] = lds_frag(&smem[buf][(16 * (wm + 2 * i) + lr) * LDB + lk]);
+    // scales of this lane's rows 16*(wm + 2i) + 4*(l/16) + 0..3
+    sa[slot] = *reinterpret_cast<const f32x4*>(&s_asc[buf][16 * (wm + 2 * i) + 4 * (lane >> 4)]);
+  };
+  auto read_b = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) fb[c] = lds_frag(&smem[buf][(BM + bcol[c] + lr) * LDB + lk]);
+  };
+  // row block i: four MFMAs on slot `slot`, each partial sum added to the
+  // accumulators times (row scale x weight scale)
+  auto block = [&](int i, int slot, float sw) __attribute__((always_inline)) {
+    f32x4 s0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s0[e] = sa[slot][e] * sw;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 p = mfma_f8(fa[slot], fb[c], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[i][c][e] = __builtin_fmaf(p[e], s0[e], acc[i][c][e]);
+    }
+  };
+  read_b(0);
+  if (NRB > 0) read_a(0, 0, 0);
+
+  auto kstep = [&](int kt) __attribute__((always_inline)) {
+    const int cur = kt & 1;
+    const int knext = kt + 1 < nk ? kt + 1 : kt;  // the last step reloads its own slice: no branch
+    // weights (and their scales) first, token rows after: loads complete in
+    // issue order for the wait counter
+#pragma unroll
+    for (int j = 0; j < kLdB; ++j) pb[j] = gload_b(j, knext * BK);
+    const float sw = swc;
+    swc = load_ws(knext);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kLdA; ++j) pa[j] = gload_a(j, knext * BK);
+    pas = asrow[knext];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NRB; ++i) {
+      if (i + 1 < NRB) read_a(cur, i + 1, (i + 1) & 1);
+      // the next step's tile goes to the idle buffer behind the second half
+      // of this step's row blocks
+      if (i == (NRB > 2 ? NRB - 2 : NRB / 2)) {
+        store_a(cur ^ 1);
+        store_b(cur ^ 1);
+      }
+      block(i, i & 1, sw);
+    }
+    if (NRB == 0) {
+      store_a(cur ^ 1);
+      store_b(cur ^ 1);
+    }
+    __syncthreads();
+    read_b(cur ^ 1);
+    if (NRB > 0) read_a(cur ^ 1, 0, 0);
+  };
+  for (int kt = 0; kt < nk; ++kt) kstep(kt);
+  __syncthreads();  // the fragment reads issued after the last step are done
+
+  // D layout of the 16x16 MFMA: element j of lane l is row 4*(l/16) + j,
+  // column l%16.
+  {
+    // y tile (256 x 256 bf16) staged through LDS, then written as 16-byte
     // pieces of each row. Rows e, e+1 (e even) of a lane are adjacent rows of
     // one column; an even lane swaps its row-(e+1) value for its odd
     // neighbour's row-e value (DPP quad permute 1,0,3,2), so each lane writes
@@ -344,8 +491,9 @@ __device__ __forceinline__ void tile_body_f8(const TileF8& t, uint8_t (*smem)[kB
 // kMode 0: gate/up + SwiGLU + h quantisation, 1: down + gate scale
 template <int kMode>
 __global__ __launch_bounds__(512) void grouped_gemm_f8_kernel(ExpertGemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][kBufBytes];
-  __shared__ __attribute__((aligned(16))) float s_asc[2][512];  // row scales (entries 0..127 used)
+  constexpr int BM = kMode == 0 ? BM1 : BM2;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2][buf_bytes(BM)];
+  __shared__ __attribute__((aligned(16))) float s_asc[2][512];  // row scales (entries 0..BM-1 used)
   __shared__ int32_t s_pre[kMaxExperts + 2];
   __shared__ int32_t s_off[kMaxExperts + 1];
   __shared__ float s_gate[BM];
@@ -413,13 +561,24 @@ __global__ __launch_bounds__(512) void grouped_gemm_f8_kernel(ExpertGemmArgs a) 
   const int wm = (threadIdx.x >> 6) >> 2;
   int nrb = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) nrb += (16 * (wm + 2 * i) < t.vrows) ? 1 : 0;
-  switch (nrb) {
-    case 4: tile_body_f8<kMode, 4>(t, smem, s_asc, s_gate); break;
-    case 3: tile_body_f8<kMode, 3>(t, smem, s_asc, s_gate); break;
-    case 2: tile_body_f8<kMode, 2>(t, smem, s_asc, s_gate); break;
-    case 1: tile_body_f8<kMode, 1>(t, smem, s_asc, s_gate); break;
-    default: tile_body_f8<kMode, 0>(t, smem, s_asc, s_gate); break;
+  for (int i = 0; i < BM / 32; ++i) nrb += (16 * (wm + 2 * i) < t.vrows) ? 1 : 0;
+  if constexpr (kMode == 0) {
+    switch (nrb) {
+      case 4: gateup_body_f8<4>(t, smem, s_asc); break;
+      case 3: gateup_body_f8<3>(t, smem, s_asc); break;
+      case 2: gateup_body_f8<2>(t, smem, s_asc); break;
+      case 1: gateup_body_f8<1>(t, smem, s_asc); break;
+      default: gateup_body_f8<0>(t, smem, s_asc); break;
+    }
+  } else {
+    // rounded up to an even count: five instantiations, not nine
+    switch ((nrb + 1) & ~1) {
+      case 8: down_body_f8<8>(t, smem, s_asc, s_gate); break;
+      case 6: down_body_f8<6>(t, smem, s_asc, s_gate); break;
+      case 4: down_body_f8<4>(t, smem, s_asc, s_gate); break;
+      case 2: down_body_f8<2>(t, smem, s_asc, s_gate); break;
+      default: down_body_f8<0>(t, smem, s_asc, s_gate); break;
+    }
   }
 }
 

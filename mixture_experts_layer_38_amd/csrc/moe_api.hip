@@ -132,22 +132,23 @@ bool on_cfg_device(const moe_cfg* c) {
 void fill_dispatch_geometry(const moe_params& p, Path path, int T, DispatchArgs* d) {
   d->shared_rows = p.shared_hidden > 0 ? T : 0;
   if (path == Path::kGrouped) {
-    d->bm = kGB_BM;
+    d->bm1 = d->bm2 = kGB_BM;
     d->n1_routed = p.hidden / kG1_BNH;
     d->n1_shared = p.shared_hidden / kG1_BNH;
     d->n2_routed = d->n2_shared = (p.dim + kG2_BN - 1) / kG2_BN;
   } else if (path == Path::kGroupedF8) {
-    d->bm = kF8_BM;
+    d->bm1 = kF8_BM1;
+    d->bm2 = kF8_BM2;
     d->n1_routed = p.hidden / kG1_BNH;
     d->n1_shared = p.shared_hidden / kG1_BNH;
     d->n2_routed = d->n2_shared = (p.dim + kG2_BN - 1) / kG2_BN;
   } else if (path == Path::kStream) {
-    d->bm = kST_BM;
+    d->bm1 = d->bm2 = kST_BM;
     d->n1_routed = p.hidden / kST_N1;
     d->n1_shared = p.shared_hidden / kST_N1;
     d->n2_routed = d->n2_shared = p.dim / kST_N2;
   } else {
-    d->bm = kF32_BM;
+    d->bm1 = d->bm2 = kF32_BM;
     d->n1_routed = (p.hidden + 31) / 32;
     d->n1_shared = (p.shared_hidden + 31) / 32;
     d->n2_routed = d->n2_shared = (p.dim + 63) / 64;
@@ -364,10 +365,10 @@ moe_status forward_impl(moe_cfg* c, const void* x, int T, const float* gate_w, c
   g2.c = c->y_routed; g2.c_shared = c->y_shared;
 
   // upper bounds on the item counts the dispatch can produce
-  const long mblk = (long)(TK + d.bm - 1) / d.bm + p.n_routed;
-  const long mblk_s = has_shared ? (T + d.bm - 1) / d.bm : 0;
-  g1.max_items = (int)(mblk * d.n1_routed + mblk_s * d.n1_shared);
-  g2.max_items = (int)(mblk * d.n2_routed + mblk_s * d.n2_shared);
+  auto row_blocks = [&](int bm) { return (long)(TK + bm - 1) / bm + p.n_routed; };
+  auto row_blocks_s = [&](int bm) { return has_shared ? (long)(T + bm - 1) / bm : 0L; };
+  g1.max_items = (int)(row_blocks(d.bm1) * d.n1_routed + row_blocks_s(d.bm1) * d.n1_shared);
+  g2.max_items = (int)(row_blocks(d.bm2) * d.n2_routed + row_blocks_s(d.bm2) * d.n2_shared);
   if (path == Path::kF32) {
     if ((e = launch_simple_gateup_f32(g1, TK, s)) != hipSuccess) return hip_fail(c, e);
     mark(c, 3, s);
@@ -711,8 +712,8 @@ moe_status moe_layer_backward(moe_cfg* c, const void* x, int T, const float* gat
   g.x_rows = T;
   g.a = x; g.w = expert_w->gate_up; g.w_shared = has_shared ? shared_w->gate_up : nullptr;
   g.c = c->au; g.c_shared = c->au_shared; g.c2 = c->h_routed; g.c2_shared = c->h_shared;
-  const long mblk = (long)(TK + d.bm - 1) / d.bm + p.n_routed;
-  const long mblk_s = has_shared ? (T + d.bm - 1) / d.bm : 0;
+  const long mblk = (long)(TK + d.bm1 - 1) / d.bm1 + p.n_routed;
+  const long mblk_s = has_shared ? (T + d.bm1 - 1) / d.bm1 : 0;
   g.max_items = (int)(mblk * d.n1_routed + mblk_s * d.n1_shared);
   if ((e = launch_grouped_recompute(g, s)) != hipSuccess) return hip_fail(c, e);
 

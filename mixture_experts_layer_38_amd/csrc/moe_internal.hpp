@@ -27,7 +27,8 @@ constexpr int kG1_BNH = 128;  // hidden columns per gate/up tile (128 gate + 128
 constexpr int kG2_BN = 256;   // output columns per down tile
 constexpr int kGB_BK = 64;    // K step
 // Grouped GEMMs on e4m3 activations and weights (fp8 matrix cores).
-constexpr int kF8_BM = 128;   // rows (tokens) per tile
+constexpr int kF8_BM1 = 128;  // rows (tokens) per gate/up tile
+constexpr int kF8_BM2 = 256;  // rows (h rows) per down tile
 constexpr int kF8_BK = 128;   // K step = one scale block (elements = bytes)
 constexpr int kActBlock = 128;  // activation quantisation block (1 x 128)
 constexpr int kDispatchChunk = 128;  // (token, slot) entries per wave in the stable permutation
@@ -242,7 +243,7 @@ struct DispatchArgs {
   int32_t* pre2;          // [E+2] item prefix, down GEMM
   int T, K, E;
   int shared_rows;        // rows of the shared problem (T, or 0 without shared expert)
-  int bm;                 // rows per item
+  int bm1, bm2;           // rows per item, gate/up and down GEMMs
   int n1_routed, n1_shared;  // column items per row block, gate/up GEMM
   int n2_routed, n2_shared;  // column items per row block, down GEMM
 };
