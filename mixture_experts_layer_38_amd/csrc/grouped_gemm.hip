@@ -80,7 +80,8 @@ struct Tile {
 
 template <int kMode, int NRB, bool kW8>
 __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows * LDW], float* s_gate) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: no VGPR held across the K loop
   const int wm = wave >> 2, wn = wave & 3;
   const int c8 = tid & 7, r0 = tid >> 3;
 
@@ -413,15 +414,17 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
   for (int i = threadIdx.x; i < a.E + 2; i += blockDim.x) s_pre[i] = a.pre[i];
   for (int i = threadIdx.x; i < a.E + 1; i += blockDim.x) s_off[i] = a.offsets[i];
   __syncthreads();
-  const int p = find_problem(s_pre, a.E, tile);
+  // workgroup-uniform values, made scalar: read from LDS they would sit in
+  // VGPRs, and so would every pointer built from them
+  const int p = __builtin_amdgcn_readfirstlane(find_problem(s_pre, a.E, tile));
   const bool routed = p < a.E;
-  const int rows = routed ? s_off[p + 1] - s_off[p] : a.T;
-  const int row_base = routed ? s_off[p] : 0;
+  const int rows = __builtin_amdgcn_readfirstlane(routed ? s_off[p + 1] - s_off[p] : a.T);
+  const int row_base = __builtin_amdgcn_readfirstlane(routed ? s_off[p] : 0);
   constexpr size_t kWB = kW8 ? 1 : 2;  // bytes per weight
   Tile t;
   t.Hp = routed ? a.H : a.Hs;
   t.D = a.D;
-  const int local = tile - s_pre[p];
+  const int local = __builtin_amdgcn_readfirstlane(tile - s_pre[p]);
   // an expert's rows are split evenly (in 32-row blocks) over its row tiles,
   // so the tiles that share a weight slice run at the same pace
   const int nmt = (rows + BM - 1) / BM;
