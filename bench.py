@@ -41,12 +41,12 @@ def log(msg):
 # Valid only for the kernel sources with these hashes; otherwise reported null.
 GATEUP_COUNTERS = {
     "sources": {"mixture_experts_layer_38_amd/csrc/grouped_gemm.hip":
-                "b06967abb48fbb8bb3023847dcd277aab4f49217368893dfa3a6ce98d2a12d89",
+                "9b41129c9cb70104a4eae2b41fc9f48a740ea5e0da1d456d7a15e452693a7a6e",
                 "mixture_experts_layer_38_amd/csrc/moe_internal.hpp":
-                "5800378b02ef820f8ce78ee45da4b2a3ea5e30c7b0d944f53f36fdd8edce392c"},
+                "c221dddc2a5591347d4ff0b878e360d3ef875983f160a301cbf11238ea8d01ac"},
     "workload": "v3_prefill",
-    "fetch_kib": 15028031.7, "write_kib": 617808.0,
-    "fetch_scale": 1048576.0 / 524316.0, "write_scale": 1.0,
+    "fetch_kib": 13817708.0, "write_kib": 589824.0,
+    "fetch_scale": 1048576.0 / 524315.9, "write_scale": 1.0,
 }
 
 
@@ -55,12 +55,12 @@ GATEUP_COUNTERS = {
 # `bench.py --config v3_decode_fp8`; the same 1 GiB copy calibrates FETCH_SIZE)
 DECODE_GATEUP_COUNTERS = {
     "sources": {"mixture_experts_layer_38_amd/csrc/stream_gemm.hip":
-                "5642dae0c2a36492c0bf56d8786bd828ef913fd48cb64e9e80d1c6d0530da611",
+                "83b1f26397b50ce0e3081863c2a07c2c2afaad8512bcf89977af074417837ac9",
                 "mixture_experts_layer_38_amd/csrc/moe_internal.hpp":
-                "5800378b02ef820f8ce78ee45da4b2a3ea5e30c7b0d944f53f36fdd8edce392c"},
+                "c221dddc2a5591347d4ff0b878e360d3ef875983f160a301cbf11238ea8d01ac"},
     "workload": "v3_decode_fp8",
-    "fetch_kib": 1889999.1, "write_kib": 2331.9,
-    "fetch_scale": 1048576.0 / 524315.6, "write_scale": 1.0,
+    "fetch_kib": 1887508.9, "write_kib": 2335.0,
+    "fetch_scale": 1048576.0 / 524314.5, "write_scale": 1.0,
 }
 
 
