@@ -25,8 +25,9 @@
 // while the other waits. A wave's four 32-row blocks are interleaved with the
 // other row-wave's (blocks wm, wm+2, wm+4, wm+6), so a ragged tile splits its
 // valid rows evenly; the tile body is instantiated per count of valid row
-// blocks, so blocks with no valid row cost no MFMA and the K loop stays
-// branch-free.
+// blocks (and of 64-row groups of token rows to load), so blocks with no
+// valid row cost no MFMA, groups with no valid row no load or LDS write, and
+// the K loop stays branch-free.
 // Both operands are staged through two LDS buffers (rows padded to 144 bytes so
 // that the 16-byte fragment reads of consecutive rows hit distinct banks): the
 // weight rows of the next K step, and the token rows of the step after it
@@ -78,7 +79,7 @@ struct Tile {
 };
 }  // namespace
 
-template <int kMode, int NRB, bool kW8>
+template <int kMode, int NRB, int NLA, bool kW8>
 __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows * LDW], float* s_gate) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: no VGPR held across the K loop
@@ -161,12 +162,12 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
   uint4 pa[2][kLd / 2], pb[kLdB];
   float pbs = 1.0f;  // e4m3: block scale of the staged weight slice
 #pragma unroll
-  for (int j = 0; j < kLd / 2; ++j) pa[0][j] = gload(j, 0);
+  for (int j = 0; j < NLA; ++j) pa[0][j] = gload(j, 0);
 #pragma unroll
   for (int j = 0; j < kLdB; ++j) pb[j] = gload(kLd / 2 + j, 0);
   if (kW8) pbs = wsrow[0];
 #pragma unroll
-  for (int j = 0; j < kLd / 2; ++j) pa[1][j] = gload(j, (nk > 1 ? 1 : 0) * BK);
+  for (int j = 0; j < NLA; ++j) pa[1][j] = gload(j, (nk > 1 ? 1 : 0) * BK);
 
   // Fragments are double-buffered across the four 16-wide substeps of a K
   // step: the LDS reads of substep kk+1 are issued before the MFMAs of
@@ -198,7 +199,7 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
   // work.
   auto store_a = [&](int buf, const uint4 (&v)[kLd / 2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < kLd / 2; ++j) *reinterpret_cast<uint4*>(&smem[buf][(r0 + 64 * j) * LDW + c8 * 8]) = v[j];
+    for (int j = 0; j < NLA; ++j) *reinterpret_cast<uint4*>(&smem[buf][(r0 + 64 * j) * LDW + c8 * 8]) = v[j];
   };
   auto store_b = [&](int buf) __attribute__((always_inline)) {
     if (kW8) {
@@ -227,13 +228,14 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
     }
   };
 #pragma unroll
-  for (int j = 0; j < kLd / 2; ++j) *reinterpret_cast<uint4*>(&smem[0][(r0 + 64 * j) * LDW + c8 * 8]) = pa[0][j];
+  for (int j = 0; j < NLA; ++j) *reinterpret_cast<uint4*>(&smem[0][(r0 + 64 * j) * LDW + c8 * 8]) = pa[0][j];
   store_b(0);
   __syncthreads();
   // instruction counts per substep, for the interleave below
   constexpr int nr = kNC + NRB, nm = kNC * NRB, nw = kLd / 2;
   constexpr int p1 = nr < nm ? nr : nm;              // (MFMA, LDS read) pairs
-  constexpr int p4 = 2 * nw < nm ? 2 * nw : nm;      // last substep: (MFMA, LDS write) pairs
+  constexpr int nwr = NLA + kLd / 2;                 // LDS writes of the last substep (A, then B)
+  constexpr int p4 = nwr < nm ? nwr : nm;            // last substep: (MFMA, LDS write) pairs
 
   read_frags(smem[0], 0, 0);
   auto kstep = [&](int kt, auto s_c) __attribute__((always_inline)) {
@@ -256,7 +258,7 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
         if (kW8) pbs = wsrow[knext >> 7];
       } else {
 #pragma unroll
-        for (int j = 0; j < kLd / 4; ++j) pa[S][j] = gload(j, knext2);
+        for (int j = 0; j < (NLA < kLd / 4 ? NLA : kLd / 4); ++j) pa[S][j] = gload(j, knext2);
       }
       read_frags(smem[cur], 16 * (s + 1), (s + 1) & 1);
       mfmas(s & 1);
@@ -274,7 +276,7 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
     }
     // substep 2: last fragments, the second half of the token rows
 #pragma unroll
-    for (int j = kLd / 4; j < kLd / 2; ++j) pa[S][j] = gload(j, knext2);
+    for (int j = kLd / 4; j < NLA; ++j) pa[S][j] = gload(j, knext2);
     read_frags(smem[cur], 48, 1);
     mfmas(0);
 #pragma unroll
@@ -295,7 +297,7 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x200, 2 * nw - p4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, nwr - p4, 0);
     __builtin_amdgcn_sched_group_barrier(0x008, nm - p4, 0);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
@@ -484,17 +486,24 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
     t.w_bytes = (uint32_t)((size_t)a.D * t.Hp * kWB);
   }
 
-  // valid 32-row blocks of this wave: wm + 2*i for i < nrb
-  const int wm = (threadIdx.x >> 6) >> 2;
+  // valid 32-row blocks of this wave: wm + 2*i for i < nrb; the tile's
+  // token rows are loaded in nla groups of 64 (rows past the last group are
+  // neither loaded nor written to LDS: no fragment read reaches them). The
+  // first row-wave has nrb == nla, the second nla or nla - 1.
+  const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >> 2;
   int nrb = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) nrb += (32 * (wm + 2 * i) < t.vrows) ? 1 : 0;
-  switch (nrb) {
-    case 4: tile_body<kMode, 4, kW8>(t, smem, s_gate); break;
-    case 3: tile_body<kMode, 3, kW8>(t, smem, s_gate); break;
-    case 2: tile_body<kMode, 2, kW8>(t, smem, s_gate); break;
-    case 1: tile_body<kMode, 1, kW8>(t, smem, s_gate); break;
-    default: tile_body<kMode, 0, kW8>(t, smem, s_gate); break;
+  const int nla = min(4, max(1, (t.vrows + 63) / 64));
+  switch (nrb * 8 + nla) {
+    case 4 * 8 + 4: tile_body<kMode, 4, 4, kW8>(t, smem, s_gate); break;
+    case 3 * 8 + 4: tile_body<kMode, 3, 4, kW8>(t, smem, s_gate); break;
+    case 3 * 8 + 3: tile_body<kMode, 3, 3, kW8>(t, smem, s_gate); break;
+    case 2 * 8 + 3: tile_body<kMode, 2, 3, kW8>(t, smem, s_gate); break;
+    case 2 * 8 + 2: tile_body<kMode, 2, 2, kW8>(t, smem, s_gate); break;
+    case 1 * 8 + 2: tile_body<kMode, 1, 2, kW8>(t, smem, s_gate); break;
+    case 1 * 8 + 1: tile_body<kMode, 1, 1, kW8>(t, smem, s_gate); break;
+    default: tile_body<kMode, 0, 1, kW8>(t, smem, s_gate); break;
   }
 }
 
