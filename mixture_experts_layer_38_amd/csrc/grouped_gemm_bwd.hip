@@ -88,6 +88,7 @@ __device__ __forceinline__ T* uniform_ptr(T* p) {
 __device__ __forceinline__ uint32_t uniform_u32(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 // LDS layout: row r holds its 64 k values as eight 16-byte chunks, chunk c at
 // position c ^ ((r >> 4) & 7) (rows padded to 144 bytes). With this swizzle
@@ -102,7 +103,7 @@ __device__ __forceinline__ int lds_at(int r, int k) { return r * LDK + ((((k >> 
 // which during a tile's last K step is already the next tile: that step
 // requests the next tile's first slice instead of nothing, so the first
 // loads of a tile overlap the previous tile's last MFMAs and epilogue.
-template <int kMode, bool kAT, bool kPersist, class Next>
+template <int kMode, bool kAT, bool kPersist, int NRB, class Next>
 __device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*smem)[kRowsL * LDK], float* s_red) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -226,7 +227,10 @@ __device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*sme
     store_kmajor(&smem[buf][BM * LDK], sb_, okb);
   };
 
-  f32x16 acc[4][2];
+  // this wave's valid 32-row blocks (rows 128 wm + 32 i, i < NRB): blocks
+  // past a ragged tile's last row cost no MFMA
+  constexpr int NA = NRB > 0 ? NRB : 1;
+  f32x16 acc[NA][2];
   const int lr = lane & 31, lk = (lane >> 5) * 8;
   // Fragments are double-buffered across the four 16-wide substeps: the LDS
   // reads of substep s+1 are issued before the MFMAs of substep s.
@@ -235,7 +239,7 @@ __device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*sme
     const uint16_t* sA = sbuf;
     const uint16_t* sB = sbuf + BM * LDK;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[slot][i] = *reinterpret_cast<const bf16x8*>(&sA[lds_at(128 * wm + 32 * i + lr, kk + lk)]);
+    for (int i = 0; i < NRB; ++i) fa[slot][i] = *reinterpret_cast<const bf16x8*>(&sA[lds_at(128 * wm + 32 * i + lr, kk + lk)]);
 #pragma unroll
     for (int c = 0; c < 2; ++c) fb[slot][c] = *reinterpret_cast<const bf16x8*>(&sB[lds_at(64 * wn + 32 * c + lr, kk + lk)]);
   };
@@ -256,7 +260,7 @@ __device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*sme
   int b0 = 0;  // LDS buffer holding the current tile's first step
   while (true) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NA; ++i)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -289,7 +293,7 @@ __device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*sme
         if (s == 1) load_b(kn);
         if (s < 3) read_frags(smem[cur], 16 * (s + 1), (s + 1) & 1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < NRB; ++i)
 #pragma unroll
           for (int c = 0; c < 2; ++c)
             acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][c], acc[i][c], 0, 0, 0);
@@ -334,62 +338,114 @@ __device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*sme
   // column l%32.
   if (kMode == kDgradH) {
     // dH = g * acc; [dA | dU] = dH * u * SiLU'(a) | dH * SiLU(a); the row's
-    // partial dL/dg = sum over this tile's columns of acc * SiLU(a) * u
-    uint16_t* dau = static_cast<uint16_t*>(t.c);
-    float rs[4][16];
+    // partial dL/dg = sum over this tile's columns of acc * SiLU(a) * u.
+    // One half of the tile's rows (those of one row-wave) at a time: its a
+    // and u rows and gates are staged in LDS with 16-byte loads (LDS row r:
+    // the tile's 256 a values, then its 256 u values), the half's waves
+    // replace a and u by dA and dU there, and the rows leave as 16-byte
+    // pieces (element-wise global accesses here would make every element
+    // wait for its own loads).
+    constexpr int kLdh = 2 * BN + 8;  // LDS row: a, then u (bf16)
+    constexpr int kHalf = BM / 2;
+    static_assert(kHalf * kLdh * 2 + kHalf * 4 + 8 * BM * 4 <= 2 * kRowsL * LDK * 2,
+                  "a, u, gates and the row sums fit the operand buffers");
+    uint16_t* sAU = &smem[0][0];
+    float* sG = reinterpret_cast<float*>(sAU + kHalf * kLdh);
+    float* sR = sG + kHalf;  // [8][BM] row partial sums (column wave, lane half)
+    // a thread moves 16-byte piece pc = tid % 64 of rows tid / 64 + 8j: one
+    // VGPR offset (its column; pieces past N get an offset past the buffer,
+    // which reads 0 and writes nothing), the row in the scalar offset; a
+    // wave's 64 lanes cover one row, so the row test is uniform
+    const int pc = tid & 63, rw = tid >> 6;
+    const uint32_t vcol = (t.n0 + 8 * (pc & 31) < t.N)
+                              ? (uint32_t)((pc >= 32 ? t.Hp : 0) + t.n0 + 8 * (pc & 31)) * 2u
+                              : 0x80000000u;
+    const __amdgpu_buffer_rsrc_t rau = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(const_cast<uint16_t*>(t.au)), (short)0, uniform_u32((uint32_t)((size_t)t.M * 2 * t.Hp * 2)),
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t rdau = __builtin_amdgcn_make_buffer_rsrc(
+        uniform_ptr(static_cast<uint16_t*>(t.c)), (short)0, uniform_u32((uint32_t)((size_t)t.M * t.ldc * 2)),
+        0x00020000);
+    __syncthreads();  // every wave is past its last fragment reads
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {
+      const int mh = t.m0 + kHalf * h;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int b = 0; b < 2; ++b) {
+        uint4 v[8];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = t.m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        float sum = 0.f;
-        if (m < t.M) {
-          const float g = t.gate ? t.gate[m] : 1.0f;
+        for (int j = 0; j < 8; ++j) {
+          const int m = mh + rw + 8 * (8 * b + j);
+          v[j] = make_uint4(0u, 0u, 0u, 0u);
+          if (m < t.M)
+            v[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rau, vcol, (uint32_t)m * (uint32_t)(2 * t.Hp) * 2u, 0));
+        }
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int n = t.n0 + 64 * wn + 32 * c + lr;
-            if (n >= t.N) continue;
-            const float av = bf16f(t.au[(size_t)m * 2 * t.Hp + n]);
-            const float uv = bf16f(t.au[(size_t)m * 2 * t.Hp + t.Hp + n]);
-            const float sg = 1.0f / (1.0f + __expf(-av));
-            const float sl = av * sg;
-            const float dh = g * acc[i][c][e];
-            dau[(size_t)m * t.ldc + n] = f32_to_bf16(dh * uv * sg * (1.0f + av * (1.0f - sg)));
-            dau[(size_t)m * t.ldc + t.Hp + n] = f32_to_bf16(dh * sl);
-            sum += acc[i][c][e] * sl * uv;
+        for (int j = 0; j < 8; ++j)
+          *reinterpret_cast<uint4*>(sAU + (rw + 8 * (8 * b + j)) * kLdh + 8 * pc) = v[j];
+      }
+      if (tid < kHalf) sG[tid] = (t.gate != nullptr && mh + tid < t.M) ? t.gate[mh + tid] : 1.0f;
+      __syncthreads();
+      if (wm == h) {
+        // this lane's rows 32i + 8(e/4) + 4(l/32) + e%4 of the half, columns
+        // 64wn + 32c + l%32; offsets from two per-lane bases (rows below and
+        // from 64), so every access has an immediate offset
+        const int lim = t.M - mh - 4 * (lane >> 5);  // row offsets ro < lim are valid rows
+        uint16_t* lb0 = sAU + (4 * (lane >> 5)) * kLdh + 64 * wn + lr;
+        uint16_t* lb1 = lb0 + 64 * kLdh;
+        const float* gb = sG + 4 * (lane >> 5);
+        float* rb = sR + (wn * 2 + ((lane >> 4) & 1)) * BM + kHalf * h + 4 * (lane >> 5);
+        const bool col_ok[2] = {t.n0 + 64 * wn + lr < t.N, t.n0 + 64 * wn + 32 + lr < t.N};
+#pragma unroll
+        for (int i = 0; i < NRB; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int ro = 32 * i + 8 * (e >> 2) + (e & 3);  // row offset from the lane's base row
+            uint16_t* ep = (i < 2 ? lb0 : lb1) + (32 * (i & 1) + 8 * (e >> 2) + (e & 3)) * kLdh;
+            float sum = 0.f;
+            if (ro < lim) {
+              const float g = gb[ro];
+#pragma unroll
+              for (int c = 0; c < 2; ++c) {
+                if (!col_ok[c]) continue;
+                const float av = bf16f(ep[32 * c]);
+                const float uv = bf16f(ep[BN + 32 * c]);
+                const float sg = 1.0f / (1.0f + __expf(-av));
+                const float sl = av * sg;
+                const float dh = g * acc[i][c][e];
+                ep[32 * c] = (uint16_t)f32_to_bf16(dh * uv * sg * (1.0f + av * (1.0f - sg)));
+                ep[BN + 32 * c] = (uint16_t)f32_to_bf16(dh * sl);
+                sum += acc[i][c][e] * sl * uv;
+              }
+            }
+            // sum over the 32 lanes of a row group: 16-lane rows by DPP, then
+            // the two rows and the four column waves through LDS, in a fixed
+            // order
+            float v = sum;
+            v += __uint_as_float(dpp_u32<0xB1>(__float_as_uint(v)));
+            v += __uint_as_float(dpp_u32<0x4E>(__float_as_uint(v)));
+            v += __uint_as_float(dpp_u32<0x141>(__float_as_uint(v)));
+            v += __uint_as_float(dpp_u32<0x140>(__float_as_uint(v)));
+            if ((lane & 15) == 0) rb[ro] = v;
           }
-        }
-        rs[i][e] = sum;
       }
-    // sum over the 32 lanes of a row group: 16-lane rows by DPP, then the two
-    // rows and the four column waves through LDS, in a fixed order
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float v = rs[i][e];
-        v += __uint_as_float(dpp_u32<0xB1>(__float_as_uint(v)));
-        v += __uint_as_float(dpp_u32<0x4E>(__float_as_uint(v)));
-        v += __uint_as_float(dpp_u32<0x141>(__float_as_uint(v)));
-        v += __uint_as_float(dpp_u32<0x140>(__float_as_uint(v)));
-        rs[i][e] = v;
+      __syncthreads();
+      // dA and dU rows of this half, 16-byte pieces
+#pragma unroll 4
+      for (int j = 0; j < 16; ++j) {
+        const int m = mh + rw + 8 * j;
+        if (m < t.M)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(v4u, *reinterpret_cast<const uint4*>(sAU + (rw + 8 * j) * kLdh + 8 * pc)), rdau,
+              vcol, (uint32_t)m * (uint32_t)t.ldc * 2u, 0);
       }
-    // s_red[wn][half of 32][row]: lanes 0, 16 (rows of lane group 0), 32, 48
-    if ((lane & 15) == 0) {
-      const int half = (lane >> 4) & 1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int r = 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          s_red[(wn * 2 + half) * BM + r] = rs[i][e];
-        }
+      __syncthreads();
     }
-    __syncthreads();
     if (tid < BM && t.m0 + tid < t.M) {
       float v = 0.f;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v += s_red[q * BM + tid];
+      for (int q = 0; q < 8; ++q) v += sR[q * BM + tid];
       t.part[(size_t)(t.m0 + tid) * t.npart + t.n0 / BN] = v;
     }
   } else if (kMode == kDgradX) {
@@ -405,7 +461,7 @@ __device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*sme
     const bool odd = lane & 1;
     __syncthreads();  // every wave is past its last fragment reads
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NRB; ++i)
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
@@ -430,7 +486,7 @@ __device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*sme
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NRB; ++i)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int n = t.n0 + 64 * wn + 32 * c + lr;
@@ -508,7 +564,16 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
       t.c = routed ? static_cast<void*>(a.dxr + (size_t)rb * a.D) : static_cast<void*>(a.dxs);
       t.ldc = a.D;
     }
-    bwd_tiles<kMode, false, false>(t, no_next, smem, s_red);
+    // valid 32-row blocks of this wave (rows 128 wm + 32 i)
+    const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >> 2;
+    const int vr = min(BM, t.M - t.m0) - 128 * wm;
+    switch (vr <= 0 ? 0 : min(4, (vr + 31) / 32)) {
+      case 4: bwd_tiles<kMode, false, false, 4>(t, no_next, smem, s_red); break;
+      case 3: bwd_tiles<kMode, false, false, 3>(t, no_next, smem, s_red); break;
+      case 2: bwd_tiles<kMode, false, false, 2>(t, no_next, smem, s_red); break;
+      case 1: bwd_tiles<kMode, false, false, 1>(t, no_next, smem, s_red); break;
+      default: bwd_tiles<kMode, false, false, 0>(t, no_next, smem, s_red); break;
+    }
   } else if (kMode == kWgradD || kMode == kWgradGU) {
     // every problem (experts, then the shared expert) gets its full weight
     // gradient; experts without rows get zeros
@@ -576,7 +641,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
       ++kseq;
       return make(run_tile(blockIdx.x + kseq * gridDim.x), tn);
     };
-    bwd_tiles<kMode, true, true>(t, next, smem, s_red);
+    bwd_tiles<kMode, true, true, 4>(t, next, smem, s_red);
   } else if (kMode == kRouterW) {
     // d gate_w planes: A[m = e][k = t] = dlogit[t][e]; B[n = d][k = t] = x[t][d]; K split over planes
     const int nmt = cdiv(a.Ep, BM), nnt = cdiv(a.D, BN);
@@ -599,7 +664,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
     t.ldb = a.D;
     t.c = a.gw_planes + (size_t)z * a.E * a.D;
     t.ldc = a.D;
-    bwd_tiles<kMode, true, false>(t, no_next, smem, s_red);
+    bwd_tiles<kMode, true, false, 4>(t, no_next, smem, s_red);
   } else {
     // dx_r = dlogit gate_w: A = dlogit rows (K = Ep, zero-padded); B[n = d][k = e] = gate_w[e][d]
     const int nnt = cdiv(a.D, BN);
@@ -619,7 +684,7 @@ __global__ __launch_bounds__(kThreads) void grouped_gemm_bwd_kernel(BwdArgs a) {
     t.ldb = a.D;
     t.c = a.dx_router;
     t.ldc = a.D;
-    bwd_tiles<kMode, false, false>(t, no_next, smem, s_red);
+    bwd_tiles<kMode, false, false, 4>(t, no_next, smem, s_red);
   }
 }
 
