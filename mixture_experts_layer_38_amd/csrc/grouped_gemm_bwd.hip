@@ -7,15 +7,17 @@
 // Every product is one grouped bf16 MFMA GEMM C[m][n] = sum_k A[m][k] B[n][k]
 // (fp32 accumulation) over 256 x 256 tiles, K step 64, 8 waves (two per SIMD)
 // of 128 x 64 (4 x 2 blocks of v_mfma_f32_32x32x16_bf16), operands staged
-// through two LDS buffers in [row][k] layout. The right operand is always stored k-major
+// through two LDS buffers. The right operand is always stored k-major
 // (B[n][k] = stored[k][n]: the weights read "the other way" than the
-// forward, or activations summed over rows for the weight gradients) and is
-// transposed while it is staged: a thread loads 4 k-rows x 8 consecutive n
-// (four 16-byte loads) and writes 8 rows of 4 k (v_perm_b32 pairs, 8-byte LDS
-// stores). The left operand is either natural (k contiguous, 16-byte chunks)
-// or k-major and transposed the same way. k-major operands past the valid
-// K (an expert's ragged row count) are zero-filled, so the weight gradients
-// of experts with few rows come out exact.
+// forward, or activations summed over rows for the weight gradients) and
+// keeps that layout in LDS: a thread loads 4 k-rows x 8 consecutive n (four
+// 16-byte loads) and writes them as they are; the MFMA fragments (8
+// consecutive k of one column) are then read with gfx950's transposing LDS
+// read, two per fragment. The left operand is either natural (k contiguous,
+// [row][k] in LDS, 16-byte chunks) or k-major and staged the same way as
+// the right one. k-major operands past the valid K (an expert's ragged row
+// count) are zero-filled, so the weight gradients of experts with few rows
+// come out exact.
 //
 //   kDgradH   dH   = dOut[tok] W_down          (rows x H; epilogue: SwiGLU
 //                                                backward -> [dA | dU], and
@@ -89,12 +91,32 @@ __device__ __forceinline__ uint32_t uniform_u32(uint32_t v) { return __builtin_a
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef short v4s8 __attribute__((ext_vector_type(8)));
 
 // LDS layout: row r holds its 64 k values as eight 16-byte chunks, chunk c at
 // position c ^ ((r >> 4) & 7) (rows padded to 144 bytes). With this swizzle
 // the fragment reads (16 rows x one chunk per 16 lanes) and the transposed
 // 8-byte stores (rows 8 apart, 4 k each) both fall on distinct banks.
 __device__ __forceinline__ int lds_at(int r, int k) { return r * LDK + ((((k >> 3) ^ (r >> 4)) & 7) << 3) + (k & 7); }
+
+// k-major operands (stored with k-rows in memory) keep that layout in LDS:
+// row k holds the tile's 256 m (or n) values, rows 576 bytes apart (16 banks
+// of offset per row). An MFMA fragment (8 consecutive k of one column) is
+// read with two transposing reads (ds_read_b64_tr_b16): in each group of 16
+// lanes, lane s names 4 values of row k0 + s/4 at column c0 + 4(s%4), and
+// receives column c0 + s at rows k0 .. k0 + 3.
+constexpr int KLD = BM + 32;
+static_assert(BK * KLD == BM * LDK, "a k-major operand fills the same LDS as a natural one");
+typedef short v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 lds_frag_tr(const uint16_t* base, int c0, int kk, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int k0 = kk + 8 * (g >> 1), col = c0 + 16 * (g & 1) + 4 * (s & 3);
+  const uint16_t* p0 = base + (k0 + (s >> 2)) * KLD + col;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s __attribute__((address_space(3)))*)p0);
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s __attribute__((address_space(3)))*)(p0 + 4 * KLD));
+  const v4s8 u = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, u);
+}
 }  // namespace
 
 // The tiles of one workgroup, in order: the first is t; with kPersist, next(tn)
@@ -199,23 +221,11 @@ __device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*sme
     okb = krb.ok;
     krb = krows(rmb, has_bmap, k0 + BK);
   };
-  // 4 k-rows x 8 columns -> 8 LDS rows of 4 k (8 bytes each)
+  // 4 k-rows x 8 columns -> rows 4kg + q of the k-major LDS layout
   auto store_kmajor = [&](uint16_t* base, const uint4 (&vin)[4], int ok) __attribute__((always_inline)) {
-    uint4 v[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = ((ok >> q) & 1) ? vin[q] : make_uint4(0u, 0u, 0u, 0u);
-    const uint32_t w[4][4] = {{v[0].x, v[0].y, v[0].z, v[0].w}, {v[1].x, v[1].y, v[1].z, v[1].w},
-                              {v[2].x, v[2].y, v[2].z, v[2].w}, {v[3].x, v[3].y, v[3].z, v[3].w}};
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      // dword p of each k-row holds columns 2p (low half) and 2p+1 (high half)
-      const uint32_t lo01 = __builtin_amdgcn_perm(w[1][p], w[0][p], 0x05040100u);
-      const uint32_t lo23 = __builtin_amdgcn_perm(w[3][p], w[2][p], 0x05040100u);
-      const uint32_t hi01 = __builtin_amdgcn_perm(w[1][p], w[0][p], 0x07060302u);
-      const uint32_t hi23 = __builtin_amdgcn_perm(w[3][p], w[2][p], 0x07060302u);
-      *reinterpret_cast<uint2*>(&base[lds_at(8 * mg + 2 * p, 4 * kg)]) = make_uint2(lo01, lo23);
-      *reinterpret_cast<uint2*>(&base[lds_at(8 * mg + 2 * p + 1, 4 * kg)]) = make_uint2(hi01, hi23);
-    }
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint4*>(&base[(4 * kg + q) * KLD + 8 * mg]) = ((ok >> q) & 1) ? vin[q] : make_uint4(0u, 0u, 0u, 0u);
   };
   auto store = [&](int buf) __attribute__((always_inline)) {
     if (kAT) {
@@ -239,9 +249,11 @@ __device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*sme
     const uint16_t* sA = sbuf;
     const uint16_t* sB = sbuf + BM * LDK;
 #pragma unroll
-    for (int i = 0; i < NRB; ++i) fa[slot][i] = *reinterpret_cast<const bf16x8*>(&sA[lds_at(128 * wm + 32 * i + lr, kk + lk)]);
+    for (int i = 0; i < NRB; ++i)
+      fa[slot][i] = kAT ? lds_frag_tr(sA, 128 * wm + 32 * i, kk, lane)
+                        : *reinterpret_cast<const bf16x8*>(&sA[lds_at(128 * wm + 32 * i + lr, kk + lk)]);
 #pragma unroll
-    for (int c = 0; c < 2; ++c) fb[slot][c] = *reinterpret_cast<const bf16x8*>(&sB[lds_at(64 * wn + 32 * c + lr, kk + lk)]);
+    for (int c = 0; c < 2; ++c) fb[slot][c] = lds_frag_tr(sB, 64 * wn + 32 * c, kk, lane);
   };
   // the rows of a tile's first step (then one step ahead, inside load_a/load_b)
   auto first_rows = [&]() __attribute__((always_inline)) {
