@@ -455,8 +455,8 @@ def _rel_rows(a, b, floor=0.25):
     return float((np.abs(a - b).max(axis=1) / den).max())
 
 
-def _check_backward(cfg, add_residual=True, with_shared=True, seed=5):
-    inp = MI.make_layer(cfg, DEV)
+def _check_backward(cfg, add_residual=True, with_shared=True, seed=5, inp=None):
+    inp = MI.make_layer(cfg, DEV) if inp is None else inp
     over = {} if with_shared else {"shared_hidden": 0}
     layer = M.MoELayer.from_config(cfg, backward=True, add_residual=add_residual, **over)
     g = torch.Generator().manual_seed(seed)
@@ -541,6 +541,54 @@ def test_backward_routed_only_and_repeatable():
 
 SKEWED = MI.LayerConfig("skewed", T=1100, D=256, E=16, H=128, G=4, kg=2, K=3, score_fn="sigmoid",
                         bias="normal", norm=True, rsf=2.5, Hs=128, act="bf16", weight="bf16", bias_std=0.05)
+
+
+# Every row count a tile body distinguishes: one expert per token (K = 1),
+# the expert of each token forced through x and gate_w (gate_w[e] is the
+# e-th unit vector, x carries 4.0 in the column of its expert and 0 in the
+# other expert columns), so expert e holds exactly ROW_SWEEP[e] rows: 1 row,
+# both sides of every 16-, 32- and 64-row boundary up to two 256-row tiles,
+# and an expert with no rows. Each product's kernels then run tiles and items
+# with every count of valid row blocks and of row groups to load.
+ROW_SWEEP = [1, 15, 16, 17, 31, 32, 33, 63, 64, 65, 95, 127, 128, 129, 191, 192, 193, 255, 256, 257, 300, 511, 512,
+             513, 700, 0]
+SWEEP_BF16 = MI.LayerConfig("row_sweep_bf16", T=sum(ROW_SWEEP), D=256, E=len(ROW_SWEEP), H=256, G=1, kg=1, K=1,
+                            score_fn="softmax", bias="none", norm=False, rsf=1.0, Hs=256, act="bf16",
+                            weight="bf16")
+
+
+def _forced_routing(inp, counts, seed=11):
+    cfg = inp.cfg
+    expert = np.repeat(np.arange(len(counts)), counts)
+    np.random.default_rng(seed).shuffle(expert)  # an expert's tokens spread over the batch
+    e_t = torch.as_tensor(expert, device=DEV)
+    x = inp.x.clone()
+    x[:, :cfg.E] = 0
+    x[torch.arange(cfg.T, device=DEV), e_t] = 4.0
+    gw = torch.zeros((cfg.E, cfg.D), dtype=torch.float32, device=DEV)
+    gw[torch.arange(cfg.E), torch.arange(cfg.E)] = 1.0
+    return dataclasses.replace(inp, x=x, gate_w=gw)
+
+
+@pytest.mark.parametrize("cfg,path", [(SWEEP_BF16, "grouped"), (SWEEP_BF16, "stream"),
+                                      (SWEEP_BF16.with_(name="row_sweep_fp8", weight="fp8"), "grouped"),
+                                      (SWEEP_BF16.with_(name="row_sweep_w8a8", weight="fp8", act_quant=True), "auto"),
+                                      (SWEEP_BF16.with_(name="row_sweep_f32", act="f32", weight="f32"), "auto")],
+                         ids=["bf16-grouped", "bf16-stream", "fp8-grouped", "w8a8", "f32"])
+def test_layer_every_tile_row_count(cfg, path):
+    inp = _forced_routing(MI.make_layer(cfg, DEV), ROW_SWEEP)
+    R = A.route_inputs(inp)
+    assert np.array_equal(np.bincount(R["idx"].ravel(), minlength=cfg.E), ROW_SWEEP)
+    _check_layer(inp, path=path, R=R)
+
+
+def test_backward_every_tile_row_count():
+    """The backward's grouped products on the same forced routing: every
+    count of valid row blocks in the data-gradient tiles, expert row counts
+    on both sides of the 64-row K steps of the weight gradients, and an
+    expert without rows (zero weight gradient)."""
+    inp = _forced_routing(MI.make_layer(SWEEP_BF16, DEV), ROW_SWEEP)
+    _check_backward(SWEEP_BF16, inp=inp)
 
 
 @pytest.mark.parametrize("path", ["grouped", "stream"])
