@@ -507,7 +507,7 @@ __device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*sme
         for (int e = 0; e < 16; ++e) {
           const int m = t.m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
           if (m >= t.M) continue;
-          static_cast<float*>(t.c)[(size_t)m * t.ldc + n] = acc[i][c][e];
+          __builtin_nontemporal_store(acc[i][c][e], static_cast<float*>(t.c) + (size_t)m * t.ldc + n);
         }
       }
   }
