@@ -35,8 +35,8 @@ def log(msg):
 
 # HBM traffic of one gate/up GEMM launch on the V3 prefill workload, from two
 # rocprofv3 --pmc runs of this bench (FETCH_SIZE, then WRITE_SIZE; KiB per
-# dispatch, mean of 3 dispatches), each scaled by what the same counter reads
-# for the bench's 1 GiB device-to-device copy probe (FETCH_SIZE 524315.4 KiB
+# dispatch, mean of 3 dispatches on each of two boxes), each scaled by what the same counter reads
+# for the bench's 1 GiB device-to-device copy probe (FETCH_SIZE 524315.7 KiB
 # for 1048576 KiB read; WRITE_SIZE 1048576 KiB for 1048576 KiB written).
 # Valid only for the kernel sources with these hashes; otherwise reported null.
 GATEUP_COUNTERS = {
@@ -45,8 +45,8 @@ GATEUP_COUNTERS = {
                 "mixture_experts_layer_38_amd/csrc/moe_internal.hpp":
                 "c221dddc2a5591347d4ff0b878e360d3ef875983f160a301cbf11238ea8d01ac"},
     "workload": "v3_prefill",
-    "fetch_kib": 15809611.1, "write_kib": 589824.0,
-    "fetch_scale": 1048576.0 / 524315.4, "write_scale": 1.0,
+    "fetch_kib": 15951172.1, "write_kib": 589824.0,
+    "fetch_scale": 1048576.0 / 524315.7, "write_scale": 1.0,
 }
 
 
