@@ -304,11 +304,19 @@ __device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*sme
         if (s == 0) load_a(kn);
         if (s == 1) load_b(kn);
         if (s < 3) read_frags(smem[cur], 16 * (s + 1), (s + 1) & 1);
+        if (s == 3) store(cur ^ 1);  // the next step's operands, behind this substep's MFMAs
 #pragma unroll
         for (int i = 0; i < NRB; ++i)
 #pragma unroll
           for (int c = 0; c < 2; ++c)
             acc[i][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][c], acc[i][c], 0, 0, 0);
+        if (s == 3) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+          }
+        }
         if (s < 2) {
           // (MFMA, LDS read, global load) x 6, then (MFMA, global load) x 2
 #pragma unroll
@@ -326,7 +334,6 @@ __device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*sme
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      store(cur ^ 1);
       __syncthreads();
       read_frags(smem[cur ^ 1], 0, 0);
     };
