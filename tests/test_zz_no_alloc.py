@@ -2,7 +2,8 @@
 forward (moe_layer_forward) through the C ABI: identical outputs and expert
 counts on two calls in a row, the second with fewer tokens, on the weight-
 streaming path (fp8 decode shape and a small fp8 layer) and on the grouped
-path (a bf16 layer past 256 tokens, then below); a call that needs more than
+path (a bf16 layer past 256 tokens, then below) and on the e4m3-activation
+path; a call that needs more than
 the fixed scratch array is refused without touching the output."""
 import numpy as np
 import pytest
@@ -21,13 +22,17 @@ SMALL_FP8 = MI.LayerConfig("small_fp8", T=77, D=256, E=16, H=256, G=4, kg=2, K=4
                            bias="normal", norm=True, rsf=2.5, Hs=256, act="bf16", weight="fp8", bias_std=0.05)
 GROUPED_BF16 = MI.LayerConfig("grouped_bf16", T=400, D=384, E=32, H=256, G=8, kg=4, K=6, score_fn="sigmoid",
                               bias="normal", norm=True, rsf=2.5, Hs=128, act="bf16", weight="bf16", bias_std=0.05)
+# e4m3 activations and weights on the fp8 matrix cores (128-row gate/up
+# tiles, 256-row down tiles)
+W8A8 = MI.LayerConfig("w8a8", T=300, D=384, E=16, H=128, G=4, kg=2, K=3, score_fn="sigmoid", bias="normal",
+                      norm=True, rsf=2.5, Hs=384, act="bf16", weight="fp8", bias_std=0.05, act_quant=True)
 
 
 def _params(cfg, T):
     return M.make_params(dim=cfg.D, n_routed=cfg.E, hidden=cfg.H, shared_hidden=cfg.Hs, top_k=cfg.K,
                          n_group=cfg.G, topk_group=cfg.kg, score_fn=cfg.score_fn, norm_topk=cfg.norm,
                          routed_scaling_factor=cfg.rsf, act=cfg.act, weight=cfg.weight, out=cfg.out,
-                         add_residual=cfg.add_residual, max_tokens=T)
+                         add_residual=cfg.add_residual, max_tokens=T, act_quant=cfg.act_quant)
 
 
 def _both(inp, T, layer):
@@ -44,9 +49,9 @@ def _both(inp, T, layer):
 
 
 @pytest.mark.parametrize("name,Ts", [("v3_decode_fp8", (64, 16)), ("small_fp8", (77, 30)),
-                                     ("grouped_bf16", (400, 150))])
+                                     ("grouped_bf16", (400, 150)), ("w8a8", (300, 90))])
 def test_noalloc_matches_the_cfg_forward(name, Ts):
-    cfg = {"small_fp8": SMALL_FP8, "grouped_bf16": GROUPED_BF16}.get(name) or MI.CONFIGS[name]
+    cfg = {"small_fp8": SMALL_FP8, "grouped_bf16": GROUPED_BF16, "w8a8": W8A8}.get(name) or MI.CONFIGS[name]
     inp = MI.make_layer(cfg, DEV)
     layer = M.MoELayer.from_config(cfg)
     R = A.route_inputs(inp)
