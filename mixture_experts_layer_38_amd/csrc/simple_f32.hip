@@ -203,7 +203,8 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   // a source that is absent reads a valid row instead (never added)
   const void* sbase = has_shared ? a.y_shared : a.y_routed;
   const size_t srow = has_shared ? (size_t)t : (size_t)rows[0];
-  for (int d0 = threadIdx.x * 8; d0 < a.D; d0 += blockDim.x * 8) {
+  // blockIdx.y: this workgroup's share of the row (several per token when tokens are few)
+  for (int d0 = (blockIdx.y * blockDim.x + threadIdx.x) * 8; d0 < a.D; d0 += gridDim.y * blockDim.x * 8) {
     // every load of this step first (the residual, the shared row, up to 8
     // routed rows), then the adds in the fixed order
     const Raw8<kXBf16> xv = load8<kXBf16>(a.x, (size_t)t, a.D, d0);
@@ -243,9 +244,12 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
   const int code = (a.y_bf16 ? 4 : 0) | (a.act_bf16 ? 2 : 0) | (a.out_bf16 ? 1 : 0);
   // threads per token: the 8-column chunks of a row spread evenly over at
-  // most 256 threads (D = 7168: 224 threads x 4 chunks)
+  // most 256 threads (D = 7168: 224 threads x 4 chunks); with fewer tokens
+  // than CUs, a row is split over several workgroups so that every thread
+  // takes one chunk and the row loads of all tokens are in flight at once
   const int chunks = (a.D + 7) / 8, iters = (chunks + 255) / 256;
-  dim3 g(a.T), b((chunks + iters - 1) / iters);
+  const int split = (a.T < 256) ? iters : 1;
+  dim3 g(a.T, split), b((chunks + iters - 1) / iters);
   switch (code) {
     case 0: hipLaunchKernelGGL((combine_kernel<false, false, false>), g, b, 0, s, a); break;
     case 1: hipLaunchKernelGGL((combine_kernel<false, false, true>), g, b, 0, s, a); break;
