@@ -21,7 +21,7 @@ namespace moe {
 // dot products unchanged).
 // ---------------------------------------------------------------------------
 // For few tokens the reduction over D is split across blockIdx.z (kc columns
-// each); every split writes its own partial logits plane, and the select
+// each); every split writes its own partial logits plane, and the selection
 // kernel adds the planes in a fixed order, so the result does not depend on
 // scheduling.
 template <bool kBf16X>
@@ -43,60 +43,72 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
 
   const int lr = tid >> 2, lc = (tid & 3) * 8;  // loader: row, 8 columns
   const int rr = lane & 15, q = lane >> 4;
-  for (int k0 = kbeg; k0 < kend; k0 += BK) {
-    float va[8], vb[8];
-    const int t = t0 + lr;
-    if (t < T) {
+  const int lt = t0 + lr, le = e0 + lr;  // this thread's loader token and expert
+  // The loads of kPre K steps are issued together, then the steps are
+  // multiplied one after another: a split of a few steps (the small-batch
+  // case) waits for memory once, not once per step.
+  constexpr int kPre = 4;
+  for (int kb = kbeg; kb < kend; kb += kPre * BK) {
+    uint4 ra[kPre][2], rb[kPre][2];  // raw x (bf16: ra[u][0] only) and gate_w pieces
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int k0 = kb + u * BK;
+      ra[u][0] = ra[u][1] = rb[u][0] = rb[u][1] = make_uint4(0, 0, 0, 0);
+      if (k0 < kend) {
+        if (lt < T) {
+          if (kBf16X) {
+            ra[u][0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xv) + (size_t)lt * D + k0 + lc);
+          } else {
+            const uint4* src = reinterpret_cast<const uint4*>(static_cast<const float*>(xv) + (size_t)lt * D + k0 + lc);
+            ra[u][0] = src[0];
+            ra[u][1] = src[1];
+          }
+        }
+        if (le < E) {
+          const uint4* src = reinterpret_cast<const uint4*>(w + (size_t)le * D + k0 + lc);
+          rb[u][0] = src[0];
+          rb[u][1] = src[1];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      if (kb + u * BK >= kend) break;  // uniform over the workgroup
+      float va[8];
       if (kBf16X) {
-        const uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(xv) +
-                                                         (size_t)t * D + k0 + lc);
-        const uint32_t p[4] = {u.x, u.y, u.z, u.w};
+        const uint32_t p[4] = {ra[u][0].x, ra[u][0].y, ra[u][0].z, ra[u][0].w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           va[2 * i] = __uint_as_float(p[i] << 16);
           va[2 * i + 1] = __uint_as_float(p[i] & 0xFFFF0000u);
         }
       } else {
-        const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(xv) +
-                                                            (size_t)t * D + k0 + lc);
-        const float4 a = src[0], b = src[1];
-        va[0] = a.x; va[1] = a.y; va[2] = a.z; va[3] = a.w;
-        va[4] = b.x; va[5] = b.y; va[6] = b.z; va[7] = b.w;
+        const uint32_t p[8] = {ra[u][0].x, ra[u][0].y, ra[u][0].z, ra[u][0].w,
+                               ra[u][1].x, ra[u][1].y, ra[u][1].z, ra[u][1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) va[i] = __uint_as_float(p[i]);
       }
-    } else {
+      float4* da = reinterpret_cast<float4*>(&sA[lr * LD + lc]);
+      da[0] = make_float4(va[0], va[1], va[2], va[3]);
+      da[1] = make_float4(va[4], va[5], va[6], va[7]);
+      uint4* db = reinterpret_cast<uint4*>(&sB[lr * LD + lc]);
+      db[0] = rb[u][0];
+      db[1] = rb[u][1];
+      __syncthreads();
 #pragma unroll
-      for (int i = 0; i < 8; ++i) va[i] = 0.f;
-    }
-    const int e = e0 + lr;
-    if (e < E) {
-      const float4* src = reinterpret_cast<const float4*>(w + (size_t)e * D + k0 + lc);
-      const float4 a = src[0], b = src[1];
-      vb[0] = a.x; vb[1] = a.y; vb[2] = a.z; vb[3] = a.w;
-      vb[4] = b.x; vb[5] = b.y; vb[6] = b.z; vb[7] = b.w;
-    } else {
+      for (int kk = 0; kk < BK; kk += 16) {
+        const float4 a = *reinterpret_cast<const float4*>(&sA[(16 * wave + rr) * LD + kk + 4 * q]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) vb[i] = 0.f;
-    }
-    float4* da = reinterpret_cast<float4*>(&sA[lr * LD + lc]);
-    da[0] = make_float4(va[0], va[1], va[2], va[3]);
-    da[1] = make_float4(va[4], va[5], va[6], va[7]);
-    float4* db = reinterpret_cast<float4*>(&sB[lr * LD + lc]);
-    db[0] = make_float4(vb[0], vb[1], vb[2], vb[3]);
-    db[1] = make_float4(vb[4], vb[5], vb[6], vb[7]);
-    __syncthreads();
-#pragma unroll
-    for (int kc = 0; kc < BK; kc += 16) {
-      const float4 a = *reinterpret_cast<const float4*>(&sA[(16 * wave + rr) * LD + kc + 4 * q]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 b = *reinterpret_cast<const float4*>(&sB[(16 * j + rr) * LD + kc + 4 * q]);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc[j], 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          const float4 b = *reinterpret_cast<const float4*>(&sB[(16 * j + rr) * LD + kk + 4 * q]);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x, b.x, acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y, b.y, acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z, b.z, acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w, b.w, acc[j], 0, 0, 0);
+        }
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
   // D layout of the 16x16 MFMA: element i of lane l is row 4*(l/16)+i, column l%16
 #pragma unroll
@@ -285,19 +297,18 @@ __global__ __launch_bounds__(256) void router_logits_x3_kernel(const uint16_t* _
 // Per-token scoring and selection; one wave per token, expert e = lane + 64*j.
 // ---------------------------------------------------------------------------
 // kVPL values per lane: experts lane, lane+64, ... (E <= 64*kVPL)
+// Token t's selection by one wave: `lin` holds its E logits (global memory
+// or LDS); its scores replace its logits in the global row `lrow` when their
+// column sums are wanted.
 template <int kVPL>
-__global__ __launch_bounds__(256) void router_select_kernel(RouterArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= a.T) return;
+__device__ __forceinline__ void select_token(const RouterArgs& a, int t, const float* lin, float* lrow, int lane) {
   const int E = a.E;
-  float* lrow = a.logits + (size_t)t * E;
   float s[kVPL], z[kVPL];
   float lmax = -INFINITY;
 #pragma unroll
   for (int j = 0; j < kVPL; ++j) {
     const int e = lane + kWave * j;
-    s[j] = (e < E) ? lrow[e] : -INFINITY;
+    s[j] = (e < E) ? lin[e] : -INFINITY;
     lmax = fmaxf(lmax, s[j]);
   }
   if (a.score_fn == MOE_SCORE_SOFTMAX) {
@@ -401,6 +412,53 @@ __global__ __launch_bounds__(256) void router_select_kernel(RouterArgs a) {
   }
 }
 
+template <int kVPL>
+__global__ __launch_bounds__(256) void router_select_kernel(RouterArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= a.T) return;
+  float* lrow = a.logits + (size_t)t * a.E;
+  select_token<kVPL>(a, t, lrow, lrow, lane);
+}
+
+// Several partial-logit planes: the token's planes are added in plane order
+// (plane 0, then 1, 2, ...; the loads of 32 planes are issued at a time),
+// the sums go to LDS and to plane 0, and one wave selects from LDS.
+// kTPW = 1 (at most one token per CU): one token per workgroup, its E sums
+// spread over the 256 threads, wave 0 selects. kTPW = 4: a token per wave,
+// lane l adds the planes of experts l, l+64, ... and the wave selects; each
+// lane reads back only the sums it wrote, so no barrier is needed.
+template <int kVPL, int kTPW>
+__global__ __launch_bounds__(256) void router_reduce_select_kernel(RouterArgs a) {
+  __shared__ float sl[kTPW][kVPL * kWave];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = (kTPW == 1) ? (int)blockIdx.x : (int)blockIdx.x * 4 + wave;
+  if (t >= a.T) return;  // kTPW = 4 only: whole waves
+  const size_t n = (size_t)a.T * a.E;
+  float* lrow = a.logits + (size_t)t * a.E;
+  const int e_first = (kTPW == 1) ? (int)threadIdx.x : lane;
+  const int e_step = (kTPW == 1) ? 256 : kWave;
+  float* srow = sl[kTPW == 1 ? 0 : wave];
+  for (int e = e_first; e < a.E; e += e_step) {
+    float v = lrow[e];
+    for (int sp = 1; sp < a.splits; sp += 32) {
+      float tv[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) tv[u] = (sp + u < a.splits) ? lrow[(size_t)(sp + u) * n + e] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 32; ++u)
+        if (sp + u < a.splits) v += tv[u];
+    }
+    srow[e] = v;
+    if (a.score_sum == nullptr) lrow[e] = v;  // else the scores go there
+  }
+  if (kTPW == 1) {
+    __syncthreads();
+    if (wave != 0) return;
+  }
+  select_token<kVPL>(a, t, srow, lrow, lane);
+}
+
 // Column sums of the scores (the importance statistic of the load-balance
 // code in the DeepSeekMoE + MLA notes, page 3): part[c][e] = sum of s[t][e]
 // over the kScoreChunk tokens of chunk c, in token order (each of the four
@@ -433,24 +491,6 @@ __global__ __launch_bounds__(512) void score_sum_kernel(const float* __restrict_
 }
 
 int score_part_rows(int T) { return (T + kScoreChunk - 1) / kScoreChunk; }
-
-// plane 0 += planes 1 .. splits-1, in plane order (one thread per logit);
-// 32 planes are loaded at a time (one round trip for most shapes), then
-// added in order
-__global__ __launch_bounds__(256) void reduce_planes_kernel(float* __restrict__ logits, int n, int splits) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  float v = logits[i];
-  for (int sp = 1; sp < splits; sp += 32) {
-    float t[32];
-#pragma unroll
-    for (int u = 0; u < 32; ++u) t[u] = (sp + u < splits) ? logits[(size_t)(sp + u) * n + i] : 0.f;
-#pragma unroll
-    for (int u = 0; u < 32; ++u)
-      if (sp + u < splits) v += t[u];
-  }
-  logits[i] = v;
-}
 
 // Width (a multiple of 32) of each K split of the fp32 kernel: about one
 // workgroup per CU. kc >= D / sp, so there are at most sp planes, and
@@ -508,17 +548,31 @@ hipError_t launch_router(const RouterArgs& a0, hipStream_t s) {
                          a.T, a.D, a.E, kc);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (a.splits > 1) {
-    const int n = a.T * a.E;
-    hipLaunchKernelGGL(reduce_planes_kernel, dim3((n + 255) / 256), dim3(256), 0, s, a.logits, n, a.splits);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+  if (a.splits > 1 && a.T <= a.num_cus) {  // add the planes and select: one token per workgroup
+    const dim3 g((unsigned)a.T);
+    if (a.E <= 2 * kWave)
+      hipLaunchKernelGGL((router_reduce_select_kernel<2, 1>), g, dim3(256), 0, s, a);
+    else if (a.E <= 4 * kWave)
+      hipLaunchKernelGGL((router_reduce_select_kernel<4, 1>), g, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((router_reduce_select_kernel<kMaxExperts / kWave, 1>), g, dim3(256), 0, s, a);
+  } else if (a.splits > 1) {  // ... one token per wave
+    const dim3 g((unsigned)((a.T + 3) / 4));
+    if (a.E <= 2 * kWave)
+      hipLaunchKernelGGL((router_reduce_select_kernel<2, 4>), g, dim3(256), 0, s, a);
+    else if (a.E <= 4 * kWave)
+      hipLaunchKernelGGL((router_reduce_select_kernel<4, 4>), g, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((router_reduce_select_kernel<kMaxExperts / kWave, 4>), g, dim3(256), 0, s, a);
+  } else {
+    const dim3 g((unsigned)((a.T + 3) / 4));
+    if (a.E <= 2 * kWave)
+      hipLaunchKernelGGL(router_select_kernel<2>, g, dim3(256), 0, s, a);
+    else if (a.E <= 4 * kWave)
+      hipLaunchKernelGGL(router_select_kernel<4>, g, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(router_select_kernel<kMaxExperts / kWave>, g, dim3(256), 0, s, a);
   }
-  if (a.E <= 2 * kWave)
-    hipLaunchKernelGGL(router_select_kernel<2>, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
-  else if (a.E <= 4 * kWave)
-    hipLaunchKernelGGL(router_select_kernel<4>, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(router_select_kernel<kMaxExperts / kWave>, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (a.score_sum != nullptr) {
     const int chunks = score_part_rows(a.T);
