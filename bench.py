@@ -166,16 +166,21 @@ def run_prefill(args, torch, M, MI):
         step()
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} done")
-    layer.set_stage_timing(True)
-    torch.cuda.synchronize()
+    # the timed steps run without per-stage events (each event between two
+    # stages leaves a gap of about 5 us between their kernels) ...
     t0 = time.perf_counter()
     for i in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    # ... and an equal pass with them gives the per-stage split
+    layer.set_stage_timing(True)
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
     stages, calls = layer.stage_times()
     layer.set_stage_timing(False)
-    ms = (t1 - t0) * 1e3 / args.steps
     stage_avg = {k: v / max(calls, 1) for k, v in stages.items()}
     log(f"{args.steps} steps: {ms:.3f} ms/step; stages {stage_avg}")
     # load balance between steps on this step's counts (bias update + statistics)

@@ -572,9 +572,10 @@ def _forced_routing(inp, counts, seed=11):
 
 @pytest.mark.parametrize("cfg,path", [(SWEEP_BF16, "grouped"), (SWEEP_BF16, "stream"),
                                       (SWEEP_BF16.with_(name="row_sweep_fp8", weight="fp8"), "grouped"),
+                                      (SWEEP_BF16.with_(name="row_sweep_fp8", weight="fp8"), "stream"),
                                       (SWEEP_BF16.with_(name="row_sweep_w8a8", weight="fp8", act_quant=True), "auto"),
                                       (SWEEP_BF16.with_(name="row_sweep_f32", act="f32", weight="f32"), "auto")],
-                         ids=["bf16-grouped", "bf16-stream", "fp8-grouped", "w8a8", "f32"])
+                         ids=["bf16-grouped", "bf16-stream", "fp8-grouped", "fp8-stream", "w8a8", "f32"])
 def test_layer_every_tile_row_count(cfg, path):
     inp = _forced_routing(MI.make_layer(cfg, DEV), ROW_SWEEP)
     R = A.route_inputs(inp)
