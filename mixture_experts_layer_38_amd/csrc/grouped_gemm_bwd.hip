@@ -504,22 +504,45 @@ __device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*sme
       }
     }
   } else {
+    // fp32 weight gradient: each wave stages one 32 x 64 block at a time in
+    // its own part of the LDS buffer its last K step was read from (the next
+    // tile's first step is in buffer b0), reads it back as 16-byte row
+    // pieces and writes those (N % 128 == 0: a piece is wholly inside or
+    // outside). The block's values leave in a quarter of the store
+    // instructions that one 4-byte store per value takes. Only the wave's own
+    // lanes share its part, so wavefront fences order the writes and the
+    // reads; the barrier after the loop keeps the next tile's first writes to
+    // this buffer behind every wave's last reads.
+    constexpr int kLdw = 64 + 4;  // staged row: 64 fp32, 4 of padding
+    static_assert(8 * 32 * kLdw * 4 <= kRowsL * LDK * 2, "eight 32 x 64 fp32 blocks fit one operand buffer");
+    float* sw = reinterpret_cast<float*>(&smem[b0 ^ 1][0]) + wave * (32 * kLdw);
+    // the lane index taken afresh here, made opaque so that nothing derived
+    // from it is hoisted to live across the K loop
+    int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    asm volatile("" : "+v"(ln));
+    const int pr = ln >> 4, pq = ln & 15;  // read-back: rows pr + 4j, 16-byte piece pq
+    const int n = t.n0 + 64 * wn + 4 * pq;
+    float* swl = sw + (4 * (ln >> 5)) * kLdw + (ln & 31);  // this lane's first staged value
 #pragma unroll
-    for (int i = 0; i < NRB; ++i)
+    for (int i = 0; i < NRB; ++i) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int n = t.n0 + 64 * wn + 32 * c + lr;
-        if (n >= t.N) continue;
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int m = t.m0 + 128 * wm + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-          if (m >= t.M) continue;
-          __builtin_nontemporal_store(acc[i][c][e], static_cast<float*>(t.c) + (size_t)m * t.ldc + n);
-        }
+        for (int e = 0; e < 16; ++e) swl[(8 * (e >> 2) + (e & 3)) * kLdw + 32 * c] = acc[i][c][e];
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = pr + 4 * j;
+        const int m = t.m0 + 128 * wm + 32 * i + r;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(&sw[r * kLdw + 4 * pq]);
+        if (m < t.M && n < t.N)
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(static_cast<float*>(t.c) + (size_t)m * t.ldc + n));
+        // at most four pieces in registers; after the last, the next block's writes follow these reads
+        if (j == 3 || j == 7) __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       }
+    }
+    __syncthreads();
   }
-    // (the fp32 epilogue above touches no LDS: the next tile's first step,
-    // already in buffer b0, stays intact)
     if (!more) break;
     t = tn;
   }
