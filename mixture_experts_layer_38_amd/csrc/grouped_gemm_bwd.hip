@@ -284,10 +284,13 @@ __device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*sme
     // MFMAs of substep 0, B's between those of substep 1: a request that
     // cannot enter a full memory queue stalls the wave, and the MFMAs behind
     // it with it) and written to the idle buffer after the MFMAs. The last
-    // step requests the next tile's first step (persistent), else its own
-    // slice again (unused): no branch around the loads.
+    // step requests the next tile's first step (persistent); the last step
+    // of a workgroup's only tile requests and stages nothing (decided at
+    // compile time: no branch around the loads; the epilogue that follows
+    // starts with a barrier of its own).
     auto kstep = [&](int kt, auto last_c) __attribute__((always_inline)) {
       constexpr bool kLast = decltype(last_c)::value;
+      constexpr bool kIdle = kLast && !kPersist;
       const int cur = (b0 + kt) & 1;
       int kn = t.k0 + (kt + 1) * BK;
       if constexpr (kLast) {
@@ -295,16 +298,14 @@ __device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*sme
           init_loader(tn);
           first_rows();
           kn = tn.k0;
-        } else {
-          kn = t.k0 + kt * BK;
         }
       }
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        if (s == 0) load_a(kn);
-        if (s == 1) load_b(kn);
+        if (s == 0 && !kIdle) load_a(kn);
+        if (s == 1 && !kIdle) load_b(kn);
         if (s < 3) read_frags(smem[cur], 16 * (s + 1), (s + 1) & 1);
-        if (s == 3) store(cur ^ 1);  // the next step's operands, behind this substep's MFMAs
+        if (s == 3 && !kIdle) store(cur ^ 1);  // the next step's operands, behind this substep's MFMAs
 #pragma unroll
         for (int i = 0; i < NRB; ++i)
 #pragma unroll
@@ -334,8 +335,10 @@ __device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*sme
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      __syncthreads();
-      read_frags(smem[cur ^ 1], 0, 0);
+      if constexpr (!kIdle) {
+        __syncthreads();
+        read_frags(smem[cur ^ 1], 0, 0);
+      }
     };
     for (int kt = 0; kt + 1 < nk; ++kt) kstep(kt, std::false_type{});
     if constexpr (kPersist) more = next(tn);
@@ -515,6 +518,7 @@ __device__ __forceinline__ void bwd_tiles(BwdTile t, Next&& next, uint16_t (*sme
     // this buffer behind every wave's last reads.
     constexpr int kLdw = 64 + 4;  // staged row: 64 fp32, 4 of padding
     static_assert(8 * 32 * kLdw * 4 <= kRowsL * LDK * 2, "eight 32 x 64 fp32 blocks fit one operand buffer");
+    if constexpr (!kPersist) __syncthreads();  // every wave is past its last fragment reads
     float* sw = reinterpret_cast<float*>(&smem[b0 ^ 1][0]) + wave * (32 * kLdw);
     // the lane index taken afresh here, made opaque so that nothing derived
     // from it is hoisted to live across the K loop
