@@ -143,8 +143,10 @@ def test_generator_is_device_agnostic():
 
 
 def test_router_small_all_score_functions():
+    # ROUTER_E384 at 100 tokens: split-K planes added by the selection kernel
+    # with one token per workgroup and eight values per lane
     for cfg in (SMALL_BF16, SMALL_SIG, SMALL_F32, MI.CONFIGS["tiny_f32"], ROUTER_X3, ROUTER_X3_SOFTMAX,
-                ROUTER_E384):
+                ROUTER_E384, ROUTER_E384.with_(name="router_e384_few", T=100)):
         inp = MI.make_layer(cfg, DEV)
         layer = M.MoELayer.from_config(cfg)
         idx, gate, counts = layer.router(inp.x, inp.gate_w, inp.sel_bias)
