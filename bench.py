@@ -133,12 +133,47 @@ def run_backward(args, torch, M, cfg, inp):
     ms = ev0.elapsed_time(ev1) / n
     flop = backward_flops(cfg)
     log(f"backward: {ms:.3f} ms/step ({n} steps)")
-    del g, layer
+    # a training step whose forward keeps the gate/up products ([a | u] and
+    # g * h, from the same accumulators as h): the training forward, then the
+    # backward that reads them instead of recomputing them
+    out = torch.empty((cfg.T, cfg.D), dtype=torch.float32, device="cuda")
+    args_f = (inp.x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared)
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        e1.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def train_step():
+        layer.forward(*args_f, out=out, train=True)
+        return layer.backward(*args_f, d_out, saved=True)
+
+    for _ in range(2):
+        g = train_step()
+    torch.cuda.synchronize()
+    step_ms = timed(train_step)
+    fwd_ms = timed(lambda: layer.forward(*args_f, out=out, train=True))
+    bwd_ms = timed(lambda: layer.backward(*args_f, d_out, saved=True))
+    flop_saved = flop - gateup_flops(cfg)
+    saved_bytes = 2 * (cfg.T * cfg.K * 3 * cfg.H + cfg.T * 3 * cfg.Hs)
+    log(f"training step with saved gate/up products: {step_ms:.3f} ms (forward {fwd_ms:.3f}, backward {bwd_ms:.3f})")
+    del g, layer, out
     torch.cuda.empty_cache()
     return {"ms": round(ms, 4), "steps": n, "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
             "mfma_flop": flop, "achieved_tflops": round(flop / (ms * 1e-3) / 1e12, 2),
             "frac_of_bf16_peak": round(flop / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
-            "gradients": "fp32 (x, gate_w, every expert, shared expert)"}
+            "gradients": "fp32 (x, gate_w, every expert, shared expert)",
+            "recompute": "the gate/up products ([a | u], g * h) recomputed inside the backward",
+            "saved_products": {
+                "train_step_ms": round(step_ms, 4), "forward_train_ms": round(fwd_ms, 4),
+                "backward_ms": round(bwd_ms, 4), "backward_mfma_flop": flop_saved,
+                "backward_frac_of_bf16_peak": round(flop_saved / (bwd_ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12), 4),
+                "saved_bytes": saved_bytes,
+                "what": "forward keeps [a | u] and g * h (bf16); backward reads them instead of recomputing"}}
 
 
 def gen_progress(cfg, torch):

@@ -197,6 +197,33 @@ moe_status moe_layer_backward(moe_cfg* cfg, const void* x, int T, const float* g
                               float* dx, float* d_gate_w, const moe_weight_grads* d_expert_w,
                               const moe_weight_grads* d_shared_w, void* stream);
 
+/* The forward of a training step (same arguments as moe_layer_forward): the
+ * output of moe_layer_forward on the grouped path, bit for bit (the expert
+ * GEMMs take that path whatever T is), and, left in the cfg's workspace, what the
+ * backward pass needs from the gate/up products: the pre-activations
+ * [a | u] and g * SiLU(a) * u of every routed row and of the shared expert,
+ * from the same fp32 accumulators as h, so moe_layer_backward_saved can skip
+ * their recompute. The cfg must have been created with backward = 1, BF16 x
+ * and BF16 weights (else MOE_ERR_UNSUPPORTED). The saved values stay valid
+ * until the next moe_layer_forward_train or moe_layer_backward on this cfg. */
+moe_status moe_layer_forward_train(moe_cfg* cfg, const void* x, int T, const float* gate_w,
+                                   const float* sel_bias, const moe_weights* expert_w,
+                                   const moe_weights* shared_w, void* out, int32_t* expert_counts,
+                                   void* stream);
+
+/* moe_layer_backward (same arguments, outputs and results) that reads [a | u]
+ * and g * h left by the last moe_layer_forward_train on this cfg instead of
+ * recomputing them (the routing is still recomputed). That forward must have
+ * had the same T (else MOE_ERR_INVALID_ARG, nothing launched) and the same x,
+ * gate_w, sel_bias and weights, which is not checked: with other inputs the
+ * gradients are those of a mixture of the two. On the stream order: the
+ * forward must be ordered before this call (same stream, or synchronised). */
+moe_status moe_layer_backward_saved(moe_cfg* cfg, const void* x, int T, const float* gate_w,
+                                    const float* sel_bias, const moe_weights* expert_w,
+                                    const moe_weights* shared_w, const float* d_out, float* dx,
+                                    float* d_gate_w, const moe_weight_grads* d_expert_w,
+                                    const moe_weight_grads* d_shared_w, void* stream);
+
 /* The router alone (the MoEGate forward plus the selection bias):
  *   topk_idx [T][K] int32, listed by descending z then ascending index
  *   topk_gate [T][K] fp32 gate values in the same order

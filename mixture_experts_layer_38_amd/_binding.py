@@ -90,11 +90,14 @@ def load_library() -> ctypes.CDLL:
     lib.moe_layer_backward.argtypes = [vp, vp, ctypes.c_int, vp, vp, ctypes.POINTER(MoeWeights),
                                        ctypes.POINTER(MoeWeights), vp, vp, vp, ctypes.POINTER(MoeWeightGrads),
                                        ctypes.POINTER(MoeWeightGrads), vp]
+    lib.moe_layer_forward_train.argtypes = lib.moe_layer_forward.argtypes
+    lib.moe_layer_backward_saved.argtypes = lib.moe_layer_backward.argtypes
     for f in ("moe_cfg_create", "moe_cfg_destroy", "moe_layer_forward", "moe_router_forward",
               "moe_dispatch_forward", "moe_cfg_last_hip_error", "moe_cfg_set_stage_timing",
               "moe_cfg_stage_times", "moe_bias_update", "moe_load_stats", "moe_quantize_e4m3_1x128",
               "moe_layer_backward", "moe_cfg_set_score_sums", "moe_balance_stats",
-              "moe_layer_forward_noalloc", "moe_debug_status"):
+              "moe_layer_forward_noalloc", "moe_debug_status", "moe_layer_forward_train",
+              "moe_layer_backward_saved"):
         getattr(lib, f).restype = ctypes.c_int
     del i32p
     _lib = lib
@@ -265,8 +268,12 @@ class MoELayer:
                 _check_tensor(f"{name}.down_scale", getattr(w, "down_scale", None), torch.float32,
                               lead + (D // 128, h // 128), x.device)
 
-    def forward(self, x, gate_w, sel_bias, experts, shared, out=None, expert_counts=None, stream=None):
-        """out [T, D] (out dtype) and, if given, expert_counts [E] int32 are written."""
+    def forward(self, x, gate_w, sel_bias, experts, shared, out=None, expert_counts=None, stream=None,
+                train=False):
+        """out [T, D] (out dtype) and, if given, expert_counts [E] int32 are written.
+        train=True: the forward of a training step (moe_layer_forward_train; the
+        cfg needs backward=True), which also keeps what backward(saved=True)
+        reads."""
         p = self.params
         self._check_x(x)
         T = x.shape[0]
@@ -280,18 +287,21 @@ class MoELayer:
         if expert_counts is not None:
             _check_tensor("expert_counts", expert_counts, torch.int32, (p.n_routed,), x.device)
         ew, sw = _weights(experts), _weights(shared)
-        st = self.lib.moe_layer_forward(self.handle, _ptr(x), T, _ptr(gate_w), _ptr(sel_bias),
-                                        ctypes.byref(ew), None if sw is None else ctypes.byref(sw), _ptr(out),
-                                        _ptr(expert_counts), _stream_handle(stream))
-        self._check(st, "moe_layer_forward")
+        fn, name = ((self.lib.moe_layer_forward_train, "moe_layer_forward_train") if train
+                    else (self.lib.moe_layer_forward, "moe_layer_forward"))
+        st = fn(self.handle, _ptr(x), T, _ptr(gate_w), _ptr(sel_bias), ctypes.byref(ew),
+                None if sw is None else ctypes.byref(sw), _ptr(out), _ptr(expert_counts), _stream_handle(stream))
+        self._check(st, name)
         return out
 
-    def backward(self, x, gate_w, sel_bias, experts, shared, d_out, stream=None):
+    def backward(self, x, gate_w, sel_bias, experts, shared, d_out, stream=None, saved=False):
         """Gradients of sum(d_out * forward(...)) (moe_layer_backward); the cfg
         needs backward=True. Returns dict(dx [T, D], d_gate_w [E, D],
         d_gate_up [E, 2H, D], d_down [E, D, H], d_shared_gate_up [2Hs, D],
         d_shared_down [D, Hs]) of fp32 tensors (shared ones None without a
-        shared expert)."""
+        shared expert). saved=True: moe_layer_backward_saved, which reads the
+        gate/up products left by the last forward(train=True) on the same
+        inputs instead of recomputing them."""
         p = self.params
         self._check_x(x)
         T = x.shape[0]
@@ -313,11 +323,12 @@ class MoELayer:
             g["d_shared_down"] = torch.empty((p.dim, p.shared_hidden), **f32)
             dsg = MoeWeightGrads(g["d_shared_gate_up"].data_ptr(), g["d_shared_down"].data_ptr())
         ew, sw = _weights(experts), _weights(shared)
-        st = self.lib.moe_layer_backward(self.handle, _ptr(x), T, _ptr(gate_w), _ptr(sel_bias), ctypes.byref(ew),
-                                         None if sw is None else ctypes.byref(sw), _ptr(d_out), _ptr(g["dx"]),
-                                         _ptr(g["d_gate_w"]), ctypes.byref(dg),
-                                         None if dsg is None else ctypes.byref(dsg), _stream_handle(stream))
-        self._check(st, "moe_layer_backward")
+        fn, name = ((self.lib.moe_layer_backward_saved, "moe_layer_backward_saved") if saved
+                    else (self.lib.moe_layer_backward, "moe_layer_backward"))
+        st = fn(self.handle, _ptr(x), T, _ptr(gate_w), _ptr(sel_bias), ctypes.byref(ew),
+                None if sw is None else ctypes.byref(sw), _ptr(d_out), _ptr(g["dx"]), _ptr(g["d_gate_w"]),
+                ctypes.byref(dg), None if dsg is None else ctypes.byref(dsg), _stream_handle(stream))
+        self._check(st, name)
         return g
 
     def router(self, x, gate_w, sel_bias, stream=None):

@@ -66,7 +66,8 @@ struct Tile {
   const float* ws;         // e4m3: the problem's 128x128 block scales, [rows/128][K/128]
   int kbn;                 // e4m3: K/128
   uint16_t* c;             // output rows of this problem (row 0 = row_base)
-  uint16_t* c2;            // recompute mode: g * h rows of this problem
+  uint16_t* c2;            // recompute mode: g * h rows; training mode: [a | u] rows
+  uint16_t* c3;            // training mode: g * h rows
   const float* gate;       // GEMM2 routed: gates at row_base; null = 1
   uint32_t a_bytes;        // extent of a_rows (buffer range)
   uint32_t w_bytes;        // extent of w
@@ -353,6 +354,15 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
     store_tile128([&](int i, int e, int) { return acc[i][1][e]; }, t.c + t.Hp + t.nt * 128, t.ldc);
     store_tile128([&](int i, int e, int m) { return s_gate[m] * silu_fast(acc[i][0][e]) * acc[i][1][e]; },
                   t.c2 + t.nt * 128, t.Hp);
+  } else if (kMode == 3) {
+    // forward of a training step: h as in mode 0, and from the same
+    // accumulators what the backward pass would recompute (mode 2)
+    store_tile128([&](int i, int e, int) { return silu_fast(acc[i][0][e]) * acc[i][1][e]; },
+                  t.c + t.nt * 128, t.Hp);
+    store_tile128([&](int i, int e, int) { return acc[i][0][e]; }, t.c2 + t.nt * 128, 2 * t.Hp);
+    store_tile128([&](int i, int e, int) { return acc[i][1][e]; }, t.c2 + t.Hp + t.nt * 128, 2 * t.Hp);
+    store_tile128([&](int i, int e, int m) { return s_gate[m] * silu_fast(acc[i][0][e]) * acc[i][1][e]; },
+                  t.c3 + t.nt * 128, t.Hp);
   } else {
     // y tile (256 x 256): staged through LDS, then written as full 16-byte
     // pieces of each row (the tile's rows are 512 contiguous bytes of y).
@@ -393,7 +403,8 @@ __device__ __forceinline__ void tile_body(const Tile& t, uint16_t (*smem)[kRows 
 }
 
 // kMode 0: gate/up + SwiGLU, 1: down + gate scale, 2: gate/up pre-activations
-// and g * h for the backward pass; kW8: e4m3 weights with
+// and g * h for the backward pass, 3: mode 0's h together with mode 2's
+// outputs (the forward of a training step); kW8: e4m3 weights with
 // 128x128 block scales, widened to bf16 (times the scale) as they are staged
 template <int kMode, bool kW8>
 __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a) {
@@ -456,10 +467,17 @@ __global__ __launch_bounds__(512) void grouped_gemm_bf16_kernel(ExpertGemmArgs a
                  : static_cast<const char*>(a.w_shared);
     t.kbn = a.D / 128;
     t.ws = kW8 ? (routed ? a.w_scale + (size_t)p * (2 * t.Hp / 128) * t.kbn : a.w_shared_scale) : nullptr;
+    t.c3 = nullptr;
     if (kMode == 2) {
       t.c = routed ? static_cast<uint16_t*>(a.c) + (size_t)row_base * 2 * a.H : static_cast<uint16_t*>(a.c_shared);
       t.c2 = routed ? static_cast<uint16_t*>(a.c2) + (size_t)row_base * a.H : static_cast<uint16_t*>(a.c2_shared);
       t.ldc = 2 * t.Hp;
+      t.gate = routed ? a.row_gate + row_base : nullptr;
+    } else if (kMode == 3) {
+      t.c = routed ? static_cast<uint16_t*>(a.c) + (size_t)row_base * a.H : static_cast<uint16_t*>(a.c_shared);
+      t.c2 = routed ? static_cast<uint16_t*>(a.c2) + (size_t)row_base * 2 * a.H : static_cast<uint16_t*>(a.c2_shared);
+      t.c3 = routed ? static_cast<uint16_t*>(a.c3) + (size_t)row_base * a.H : static_cast<uint16_t*>(a.c3_shared);
+      t.ldc = t.Hp;
       t.gate = routed ? a.row_gate + row_base : nullptr;
     } else {
       t.c = routed ? static_cast<uint16_t*>(a.c) + (size_t)row_base * a.H : static_cast<uint16_t*>(a.c_shared);
@@ -527,6 +545,13 @@ hipError_t launch_grouped_recompute(const ExpertGemmArgs& a, hipStream_t s) {
   const int blocks = grouped_blocks(a.max_items, kRun);
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL((grouped_gemm_bf16_kernel<2, false>), dim3(blocks), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_gateup_train(const ExpertGemmArgs& a, hipStream_t s) {
+  const int blocks = grouped_blocks(a.max_items, kRun);
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((grouped_gemm_bf16_kernel<3, false>), dim3(blocks), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

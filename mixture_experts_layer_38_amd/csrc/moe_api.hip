@@ -43,6 +43,9 @@ struct moe_cfg {
   uint16_t* gw_bf;
   uint16_t* au;
   uint16_t* au_shared;
+  uint16_t* gh;          // g * h rows (routed), read by dW_down
+  uint16_t* gh_shared;
+  int saved_T;           // tokens of the last training forward whose [a | u], g * h are in au, gh; -1: none
   uint16_t* dau;
   uint16_t* dau_shared;
   float* part;
@@ -208,6 +211,7 @@ size_t layout_workspace(moe_cfg* c, char* base) {
   const int splits = bw ? std::max(1, std::min(32, (c->num_cus + rw_tiles - 1) / std::max(rw_tiles, 1))) : 0;
   const size_t o_dout = bw ? take(Tm * D * 2) : 0, o_gw = bw ? take(Ep * D * 2) : 0;
   const size_t o_au = bw ? take(Tm * K * 2 * H * 2) : 0, o_aus = bw ? take(Tm * 2 * Hs * 2) : 0;
+  const size_t o_gh = bw ? take(Tm * K * H * 2) : 0, o_ghs = bw ? take(Tm * Hs * 2) : 0;
   const size_t o_dau = bw ? take(Tm * K * 2 * H * 2) : 0, o_daus = bw ? take(Tm * 2 * Hs * 2) : 0;
   const size_t o_part = bw ? take(Tm * K * (H / 128) * 4) : 0, o_parts = bw ? take(Tm * (Hs / 128) * 4) : 0;
   const size_t o_dlog = bw ? take(Tm * Ep * 2) : 0, o_dxr = bw ? take(Tm * D * 4) : 0;
@@ -239,6 +243,8 @@ size_t layout_workspace(moe_cfg* c, char* base) {
     c->gw_bf = (uint16_t*)(base + o_gw);
     c->au = (uint16_t*)(base + o_au);
     c->au_shared = (uint16_t*)(base + o_aus);
+    c->gh = (uint16_t*)(base + o_gh);
+    c->gh_shared = (uint16_t*)(base + o_ghs);
     c->dau = (uint16_t*)(base + o_dau);
     c->dau_shared = (uint16_t*)(base + o_daus);
     c->part = (float*)(base + o_part);
@@ -292,7 +298,7 @@ moe_status scratch_of_current_device(int* dev, char** ptr, int* cus) {
 // for T and the device; the rest here).
 moe_status forward_impl(moe_cfg* c, const void* x, int T, const float* gate_w, const float* sel_bias,
                              const moe_weights* expert_w, const moe_weights* shared_w, void* out,
-                             int32_t* expert_counts, void* stream) {
+                             int32_t* expert_counts, void* stream, bool train = false) {
   const moe_params& p = c->p;
   hipStream_t s = (hipStream_t)stream;
   if (T == 0) {
@@ -316,7 +322,9 @@ moe_status forward_impl(moe_cfg* c, const void* x, int T, const float* gate_w, c
     if (fp8 && (!shared_w->gate_up_scale || !shared_w->down_scale)) return MOE_ERR_INVALID_ARG;
   }
 
-  const Path path = choose_path(p, T);
+  // a training forward takes the grouped path: its gate/up GEMM also leaves
+  // [a | u] and g * h for the backward pass
+  const Path path = train ? Path::kGrouped : choose_path(p, T);
   hipError_t e;
 
   // 1. router
@@ -374,7 +382,12 @@ moe_status forward_impl(moe_cfg* c, const void* x, int T, const float* gate_w, c
     mark(c, 3, s);
     if ((e = launch_simple_down_f32(g2, TK, s)) != hipSuccess) return hip_fail(c, e);
   } else {
-    if (path == Path::kGrouped) {
+    if (path == Path::kGrouped && train) {
+      g1.c2 = c->au; g1.c2_shared = c->au_shared; g1.c3 = c->gh; g1.c3_shared = c->gh_shared;
+      if ((e = launch_grouped_gateup_train(g1, s)) != hipSuccess) return hip_fail(c, e);
+      mark(c, 3, s);
+      if ((e = launch_grouped_down(g2, fp8, s)) != hipSuccess) return hip_fail(c, e);
+    } else if (path == Path::kGrouped) {
       if ((e = launch_grouped_gateup(g1, fp8, s)) != hipSuccess) return hip_fail(c, e);
       mark(c, 3, s);
       if ((e = launch_grouped_down(g2, fp8, s)) != hipSuccess) return hip_fail(c, e);
@@ -434,6 +447,7 @@ moe_status moe_cfg_create(const moe_params* p, moe_cfg** out) {
   if (!c) return MOE_ERR_OOM;
   memset(c, 0, sizeof(*c));
   c->p = *p;
+  c->saved_T = -1;
   if (hipGetDevice(&c->device) != hipSuccess) { delete c; return MOE_ERR_HIP; }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, c->device) != hipSuccess) { delete c; return MOE_ERR_HIP; }
@@ -628,6 +642,19 @@ moe_status moe_layer_forward(moe_cfg* c, const void* x, int T, const float* gate
   return forward_impl(c, x, T, gate_w, sel_bias, expert_w, shared_w, out, expert_counts, stream);
 }
 
+moe_status moe_layer_forward_train(moe_cfg* c, const void* x, int T, const float* gate_w, const float* sel_bias,
+                                   const moe_weights* expert_w, const moe_weights* shared_w, void* out,
+                                   int32_t* expert_counts, void* stream) {
+  if (!c) return MOE_ERR_INVALID_ARG;
+  if (!c->p.backward) return MOE_ERR_UNSUPPORTED;
+  if (T < 0 || T > c->p.max_tokens) return MOE_ERR_INVALID_ARG;
+  if (!on_cfg_device(c)) return MOE_ERR_INVALID_ARG;
+  c->saved_T = -1;
+  const moe_status st = forward_impl(c, x, T, gate_w, sel_bias, expert_w, shared_w, out, expert_counts, stream, true);
+  if (st == MOE_OK) c->saved_T = T;
+  return st;
+}
+
 moe_status moe_layer_forward_noalloc(const moe_params* params, const void* x, int T, const float* gate_w,
                                      const float* sel_bias, const moe_weights* expert_w,
                                      const moe_weights* shared_w, void* out, int32_t* expert_counts,
@@ -651,14 +678,17 @@ moe_status moe_layer_forward_noalloc(const moe_params* params, const void* x, in
   return forward_impl(&c, x, T, gate_w, sel_bias, expert_w, shared_w, out, expert_counts, stream);
 }
 
-moe_status moe_layer_backward(moe_cfg* c, const void* x, int T, const float* gate_w, const float* sel_bias,
-                              const moe_weights* expert_w, const moe_weights* shared_w, const float* d_out,
-                              float* dx, float* d_gate_w, const moe_weight_grads* d_expert_w,
-                              const moe_weight_grads* d_shared_w, void* stream) {
+// recompute: the gate/up products are recomputed (moe_layer_backward), else
+// read from the last training forward (moe_layer_backward_saved)
+static moe_status backward_impl(moe_cfg* c, const void* x, int T, const float* gate_w, const float* sel_bias,
+                         const moe_weights* expert_w, const moe_weights* shared_w, const float* d_out, float* dx,
+                         float* d_gate_w, const moe_weight_grads* d_expert_w, const moe_weight_grads* d_shared_w,
+                         void* stream, bool recompute) {
   if (!c) return MOE_ERR_INVALID_ARG;
   const moe_params& p = c->p;
   if (!p.backward) return MOE_ERR_UNSUPPORTED;
   if (T < 0 || T > p.max_tokens) return MOE_ERR_INVALID_ARG;
+  if (!recompute && c->saved_T != T) return MOE_ERR_INVALID_ARG;
   if (!on_cfg_device(c)) return MOE_ERR_INVALID_ARG;
   const bool has_shared = p.shared_hidden > 0;
   if (!gate_w || !d_gate_w || !expert_w || !expert_w->gate_up || !expert_w->down || !d_expert_w ||
@@ -704,18 +734,21 @@ moe_status moe_layer_backward(moe_cfg* c, const void* x, int T, const float* gat
   fill_dispatch_geometry(p, Path::kGrouped, T, &d);
   if ((e = launch_dispatch(d, s)) != hipSuccess) return hip_fail(c, e);
 
-  // gate/up recompute: [a | u] and g * h
-  const int TK = T * p.top_k;
-  ExpertGemmArgs g{};
-  g.offsets = c->offsets; g.row_token = c->row_token; g.row_gate = c->row_gate; g.pre = c->pre1;
-  g.E = p.n_routed; g.T = has_shared ? T : 0; g.D = p.dim; g.H = p.hidden; g.Hs = p.shared_hidden;
-  g.x_rows = T;
-  g.a = x; g.w = expert_w->gate_up; g.w_shared = has_shared ? shared_w->gate_up : nullptr;
-  g.c = c->au; g.c_shared = c->au_shared; g.c2 = c->h_routed; g.c2_shared = c->h_shared;
-  const long mblk = (long)(TK + d.bm1 - 1) / d.bm1 + p.n_routed;
-  const long mblk_s = has_shared ? (T + d.bm1 - 1) / d.bm1 : 0;
-  g.max_items = (int)(mblk * d.n1_routed + mblk_s * d.n1_shared);
-  if ((e = launch_grouped_recompute(g, s)) != hipSuccess) return hip_fail(c, e);
+  // gate/up recompute: [a | u] and g * h (a training forward left them otherwise)
+  if (recompute) {
+    c->saved_T = -1;  // au and gh now hold this call's values
+    const int TK = T * p.top_k;
+    ExpertGemmArgs g{};
+    g.offsets = c->offsets; g.row_token = c->row_token; g.row_gate = c->row_gate; g.pre = c->pre1;
+    g.E = p.n_routed; g.T = has_shared ? T : 0; g.D = p.dim; g.H = p.hidden; g.Hs = p.shared_hidden;
+    g.x_rows = T;
+    g.a = x; g.w = expert_w->gate_up; g.w_shared = has_shared ? shared_w->gate_up : nullptr;
+    g.c = c->au; g.c_shared = c->au_shared; g.c2 = c->gh; g.c2_shared = c->gh_shared;
+    const long mblk = (long)(TK + d.bm1 - 1) / d.bm1 + p.n_routed;
+    const long mblk_s = has_shared ? (T + d.bm1 - 1) / d.bm1 : 0;
+    g.max_items = (int)(mblk * d.n1_routed + mblk_s * d.n1_shared);
+    if ((e = launch_grouped_recompute(g, s)) != hipSuccess) return hip_fail(c, e);
+  }
 
   BwdArgs b{};
   b.E = p.n_routed; b.T = T; b.D = p.dim; b.H = p.hidden; b.Hs = p.shared_hidden; b.K = p.top_k;
@@ -730,7 +763,7 @@ moe_status moe_layer_backward(moe_cfg* c, const void* x, int T, const float* gat
   b.w_down_shared = has_shared ? static_cast<const uint16_t*>(shared_w->down) : nullptr;
   b.dout = c->dout_bf; b.gw_bf16 = c->gw_bf;
   b.au = c->au; b.au_shared = c->au_shared;
-  b.gh = static_cast<const uint16_t*>(c->h_routed); b.gh_shared = static_cast<const uint16_t*>(c->h_shared);
+  b.gh = c->gh; b.gh_shared = c->gh_shared;
   b.dau = c->dau; b.dau_shared = c->dau_shared; b.part = c->part; b.part_shared = c->part_shared;
   b.dxr = static_cast<uint16_t*>(c->y_routed); b.dxs = static_cast<uint16_t*>(c->y_shared);
   b.dlogit = c->dlogit; b.dx_router = c->dx_router; b.gw_planes = c->gw_planes;
@@ -739,6 +772,22 @@ moe_status moe_layer_backward(moe_cfg* c, const void* x, int T, const float* gat
   b.dw_down_shared = has_shared ? d_shared_w->down : nullptr;
   if ((e = launch_layer_backward(b, s)) != hipSuccess) return hip_fail(c, e);
   return MOE_OK;
+}
+
+moe_status moe_layer_backward(moe_cfg* c, const void* x, int T, const float* gate_w, const float* sel_bias,
+                              const moe_weights* expert_w, const moe_weights* shared_w, const float* d_out,
+                              float* dx, float* d_gate_w, const moe_weight_grads* d_expert_w,
+                              const moe_weight_grads* d_shared_w, void* stream) {
+  return backward_impl(c, x, T, gate_w, sel_bias, expert_w, shared_w, d_out, dx, d_gate_w, d_expert_w, d_shared_w,
+                       stream, true);
+}
+
+moe_status moe_layer_backward_saved(moe_cfg* c, const void* x, int T, const float* gate_w, const float* sel_bias,
+                                    const moe_weights* expert_w, const moe_weights* shared_w, const float* d_out,
+                                    float* dx, float* d_gate_w, const moe_weight_grads* d_expert_w,
+                                    const moe_weight_grads* d_shared_w, void* stream) {
+  return backward_impl(c, x, T, gate_w, sel_bias, expert_w, shared_w, d_out, dx, d_gate_w, d_expert_w, d_shared_w,
+                       stream, false);
 }
 
 }  // extern "C"

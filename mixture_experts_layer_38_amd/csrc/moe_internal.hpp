@@ -274,15 +274,20 @@ struct ExpertGemmArgs {
   float* c_scale;               // GEMM1: h routed scales
   float* c_shared_scale;        // GEMM1: h shared scales
   // backward recompute (gate/up mode 2): c, c_shared receive [a | u] rows,
-  // c2, c2_shared receive g * h rows
+  // c2, c2_shared receive g * h rows; training forward (mode 3): c, c_shared
+  // receive h, c2, c2_shared [a | u] and c3, c3_shared g * h
   void* c2;
   void* c2_shared;
+  void* c3;
+  void* c3_shared;
 };
 // grouped (prefill) GEMMs; fp8: e4m3 weights with 128x128 block scales
 hipError_t launch_grouped_gateup(const ExpertGemmArgs& a, int fp8, hipStream_t s);
 hipError_t launch_grouped_down(const ExpertGemmArgs& a, int fp8, hipStream_t s);
 // gate/up GEMM that writes the pre-activations [a | u] and g * h (bf16) for the backward pass
 hipError_t launch_grouped_recompute(const ExpertGemmArgs& a, hipStream_t s);
+// the gate/up GEMM of a training forward (bf16): h, [a | u] and g * h
+hipError_t launch_grouped_gateup_train(const ExpertGemmArgs& a, hipStream_t s);
 // grouped GEMMs on e4m3 activations (1x128 block scales) and e4m3 weights
 // (128x128 block scales), fp8 MFMA; the gate/up GEMM writes h as e4m3 + scales
 hipError_t launch_grouped_gateup_f8(const ExpertGemmArgs& a, hipStream_t s);

@@ -594,6 +594,62 @@ def test_backward_every_tile_row_count():
     _check_backward(SWEEP_BF16, inp=inp)
 
 
+def _train_step_matches(cfg, inp, seed=6):
+    """The forward of a training step against the grouped-path forward, and
+    the backward that reads its saved gate/up products against the one that
+    recomputes them: both bit for bit (the same tile bodies and epilogue
+    expressions produce h, [a | u] and g * h)."""
+    layer = M.MoELayer.from_config(cfg, backward=True, path="grouped")
+    out0 = layer.forward(inp.x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared)
+    out1 = layer.forward(inp.x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared, train=True)
+    d_out = torch.randn((cfg.T, cfg.D), generator=torch.Generator().manual_seed(seed)).to(DEV)
+    g_saved = layer.backward(inp.x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared, d_out, saved=True)
+    g_rec = layer.backward(inp.x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared, d_out)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1)
+    for k, v in g_rec.items():
+        if v is None:
+            assert g_saved[k] is None, k
+        else:
+            assert torch.equal(v, g_saved[k]), k
+    del layer
+
+
+@pytest.mark.parametrize("name", ["small_sigmoid", "skewed", "row_sweep"])
+def test_training_forward_and_saved_backward(name):
+    """Ragged and skewed expert row counts (the row sweep: every count of
+    valid row blocks, an expert without rows), with a shared expert."""
+    if name == "row_sweep":
+        inp = _forced_routing(MI.make_layer(SWEEP_BF16, DEV), ROW_SWEEP)
+    else:
+        inp = MI.make_layer({"small_sigmoid": SMALL_SIG, "skewed": SKEWED}[name], DEV)
+    _train_step_matches(inp.cfg, inp)
+
+
+def test_saved_backward_needs_its_training_forward():
+    """No training forward yet, a different token count, or a recomputing
+    backward in between: the saved backward refuses and launches nothing."""
+    cfg = SMALL_SIG
+    inp = MI.make_layer(cfg, DEV)
+    layer = M.MoELayer.from_config(cfg, backward=True)
+    d_out = torch.randn((cfg.T, cfg.D), generator=torch.Generator().manual_seed(2)).to(DEV)
+    args = (inp.x, inp.gate_w, inp.sel_bias, inp.experts, inp.shared)
+    with pytest.raises(M.MoEError):
+        layer.backward(*args, d_out, saved=True)
+    layer.forward(*args, train=True)
+    with pytest.raises(M.MoEError):
+        layer.backward(inp.x[:100].contiguous(), *args[1:], d_out[:100].contiguous(), saved=True)
+    layer.backward(*args, d_out, saved=True)
+    layer.backward(*args, d_out)
+    with pytest.raises(M.MoEError):
+        layer.backward(*args, d_out, saved=True)
+    # a layer without the backward workspace has no training forward
+    plain = M.MoELayer.from_config(cfg)
+    with pytest.raises(M.MoEError):
+        plain.forward(*args, train=True)
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("path", ["grouped", "stream"])
 def test_layer_skewed_routing(path):
     """A +10 selection bias on experts 1, 2 (group 0) and 6 (group 1) sends
@@ -739,6 +795,14 @@ def test_layer_v3_prefill_w8a8(layers):
     inp = layers("v3_prefill_w8a8")
     _quant_parity(inp.x.cpu(), rows=_sample(inp.cfg.T, 64, seed=3))
     _check_full_size(inp, 16)
+
+
+@pytest.mark.timeout(900)
+def test_training_step_v3_prefill(layers):
+    """The training forward and the saved backward at the V3 prefill shape,
+    bit for bit against the grouped forward and the recomputing backward."""
+    _train_step_matches(MI.CONFIGS["v3_prefill"], layers("v3_prefill"))
+    torch.cuda.empty_cache()
 
 
 def test_backward_v3_prefill_sampled(layers):
