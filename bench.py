@@ -41,12 +41,12 @@ def log(msg):
 # Valid only for the kernel sources with these hashes; otherwise reported null.
 GATEUP_COUNTERS = {
     "sources": {"mixture_experts_layer_38_amd/csrc/grouped_gemm.hip":
-                "8da05a645d096cd245a7ad7a390841ab518df3530392bb3426b2dc9d9f74098d",
+                "53380366932379c1cfb8fb77270e07d4365b3e3562d5e59ee849be5b42cb3642",
                 "mixture_experts_layer_38_amd/csrc/moe_internal.hpp":
-                "c221dddc2a5591347d4ff0b878e360d3ef875983f160a301cbf11238ea8d01ac"},
+                "d8bec0ef68504479c6f90c9ed087ca29354afba77a4f08124880edeb162eec8d"},
     "workload": "v3_prefill",
-    "fetch_kib": 15951172.1, "write_kib": 589824.0,
-    "fetch_scale": 1048576.0 / 524315.7, "write_scale": 1.0,
+    "fetch_kib": 15954495.3, "write_kib": 589824.0,
+    "fetch_scale": 1048576.0 / 524317.1, "write_scale": 1.0,
 }
 
 
@@ -57,10 +57,10 @@ DECODE_GATEUP_COUNTERS = {
     "sources": {"mixture_experts_layer_38_amd/csrc/stream_gemm.hip":
                 "83b1f26397b50ce0e3081863c2a07c2c2afaad8512bcf89977af074417837ac9",
                 "mixture_experts_layer_38_amd/csrc/moe_internal.hpp":
-                "c221dddc2a5591347d4ff0b878e360d3ef875983f160a301cbf11238ea8d01ac"},
+                "d8bec0ef68504479c6f90c9ed087ca29354afba77a4f08124880edeb162eec8d"},
     "workload": "v3_decode_fp8",
-    "fetch_kib": 1887508.9, "write_kib": 2335.0,
-    "fetch_scale": 1048576.0 / 524314.5, "write_scale": 1.0,
+    "fetch_kib": 1886165.5, "write_kib": 2333.9,
+    "fetch_scale": 1048576.0 / 524316.8, "write_scale": 1.0,
 }
 
 
