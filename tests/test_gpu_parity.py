@@ -615,14 +615,17 @@ def _train_step_matches(cfg, inp, seed=6):
     del layer
 
 
-@pytest.mark.parametrize("name", ["small_sigmoid", "skewed", "row_sweep"])
+@pytest.mark.parametrize("name", ["small_sigmoid", "skewed", "row_sweep", "no_shared"])
 def test_training_forward_and_saved_backward(name):
     """Ragged and skewed expert row counts (the row sweep: every count of
-    valid row blocks, an expert without rows), with a shared expert."""
+    valid row blocks, an expert without rows), with a shared expert, and a
+    layer without one."""
     if name == "row_sweep":
         inp = _forced_routing(MI.make_layer(SWEEP_BF16, DEV), ROW_SWEEP)
     else:
-        inp = MI.make_layer({"small_sigmoid": SMALL_SIG, "skewed": SKEWED}[name], DEV)
+        cfg = {"small_sigmoid": SMALL_SIG, "skewed": SKEWED,
+               "no_shared": SMALL_SIG.with_(name="small_sigmoid_no_shared", Hs=0)}[name]
+        inp = MI.make_layer(cfg, DEV)
     _train_step_matches(inp.cfg, inp)
 
 
