@@ -853,8 +853,8 @@ def test_layer_v3_decode_fp8(layers):
 def test_debug_build_matches_and_reports_no_violation():
     """The bounds-checked debug library gives bit-identical results on every
     kernel family (grouped and streaming bf16, e4m3 weights, e4m3
-    activations, fp32, the backward pass) and records no out-of-range
-    index."""
+    activations, fp32, the backward pass, the training forward and the saved
+    backward) and records no out-of-range index."""
     from mixture_experts_layer_38_amd import _binding as B
     from mixture_experts_layer_38_amd import build as Bd
 
@@ -873,6 +873,13 @@ def test_debug_build_matches_and_reports_no_violation():
                                        expert_counts=counts), counts))
         layer = M.MoELayer.from_config(BWD_SIG, backward=True)
         g = layer.backward(bw_inp.x, bw_inp.gate_w, bw_inp.sel_bias, bw_inp.experts, bw_inp.shared, d_out)
+        # the training forward (gate/up mode 3) and the backward that reads what it kept
+        counts = torch.empty(BWD_SIG.E, dtype=torch.int32, device=DEV)
+        outs.append((layer.forward(bw_inp.x, bw_inp.gate_w, bw_inp.sel_bias, bw_inp.experts, bw_inp.shared,
+                                   expert_counts=counts, train=True), counts))
+        g_saved = layer.backward(bw_inp.x, bw_inp.gate_w, bw_inp.sel_bias, bw_inp.experts, bw_inp.shared, d_out,
+                                 saved=True)
+        g.update({"saved_" + k: v for k, v in g_saved.items()})
         torch.cuda.synchronize()
         return outs, g
 
@@ -888,7 +895,8 @@ def test_debug_build_matches_and_reports_no_violation():
         B.LIB_PATH, B._lib = saved
     for (o, c), (ro, rc) in zip(outs, ref_outs):
         assert torch.equal(o, ro) and torch.equal(c, rc)
-    for k in ("dx", "d_gate_w", "d_gate_up", "d_down"):
+    for k in ("dx", "d_gate_w", "d_gate_up", "d_down", "saved_dx", "saved_d_gate_w", "saved_d_gate_up",
+              "saved_d_down"):
         assert torch.equal(g[k], ref_g[k]), k
 
 def test_binding_rejects_mismatched_tensors():
