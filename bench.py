@@ -35,9 +35,10 @@ def log(msg):
 
 # HBM traffic of one gate/up GEMM launch on the V3 prefill workload, from two
 # rocprofv3 --pmc runs of this bench (FETCH_SIZE, then WRITE_SIZE; KiB per
-# dispatch, mean of 3 dispatches on each of two boxes), each scaled by what the same counter reads
-# for the bench's 1 GiB device-to-device copy probe (FETCH_SIZE 524315.7 KiB
-# for 1048576 KiB read; WRITE_SIZE 1048576 KiB for 1048576 KiB written).
+# dispatch, mean of the dispatches after the first, cold one), each scaled by
+# what the same counter reads for the bench's 1 GiB device-to-device copy probe
+# (FETCH_SIZE 524317.1 KiB for 1048576 KiB read; WRITE_SIZE 1048576 KiB for
+# 1048576 KiB written).
 # Valid only for the kernel sources with these hashes; otherwise reported null.
 GATEUP_COUNTERS = {
     "sources": {"mixture_experts_layer_38_amd/csrc/grouped_gemm.hip":

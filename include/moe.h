@@ -40,7 +40,7 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = -1, /* bad pointer, size or parameter combination */
-  MOE_ERR_UNSUPPORTED = -2, /* valid layer, but a shape/dtype this build does not run */
+  MOE_ERR_UNSUPPORTED = -2, /* valid layer, but a shape/dtype the library does not run */
   MOE_ERR_OOM = -3,         /* workspace allocation failed */
   MOE_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
   MOE_ERR_SCRATCH = -5      /* moe_layer_forward_noalloc: the call needs more
@@ -110,7 +110,7 @@ typedef struct moe_cfg moe_cfg;
 /* Validates *p and allocates the workspace for up to p->max_tokens tokens on
  * the current HIP device. Returns MOE_ERR_INVALID_ARG for an invalid layer
  * (E % G != 0, topk_group > G, K > topk_group*E/G, ...), MOE_ERR_UNSUPPORTED
- * for a dtype/shape this build does not run (bf16/fp8 weights need D, H, Hs
+ * for a dtype/shape the library does not run (bf16/fp8 weights need D, H, Hs
  * multiples of 128 and max_tokens*D*2, max_tokens*max(H,Hs)*2 and
  * 2*max(H,Hs)*D*2 below 2^32 bytes; f32 needs D % 32 == 0), MOE_ERR_OOM if
  * the workspace does not fit. On success *out owns the workspace until

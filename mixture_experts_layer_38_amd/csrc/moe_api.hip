@@ -86,7 +86,7 @@ moe_status validate(const moe_params* p) {
   if (p->act_quant != MOE_ACT_QUANT_NONE && p->act_quant != MOE_ACT_QUANT_E4M3_1X128) return MOE_ERR_INVALID_ARG;
   if (p->backward != 0 && p->backward != 1) return MOE_ERR_INVALID_ARG;
   if (!(p->routed_scaling_factor == p->routed_scaling_factor)) return MOE_ERR_INVALID_ARG;  // NaN
-  // dtype combinations this build runs
+  // dtype combinations the library runs
   const bool f32 = p->act_dtype == MOE_F32 && p->weight_dtype == MOE_F32;
   const bool bf = p->act_dtype == MOE_BF16 && p->weight_dtype == MOE_BF16;
   const bool fp8 = p->act_dtype == MOE_BF16 && p->weight_dtype == MOE_FP8_E4M3;
