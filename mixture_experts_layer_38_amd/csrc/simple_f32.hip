@@ -205,9 +205,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
   const size_t srow = has_shared ? (size_t)t : (size_t)rows[0];
   // blockIdx.y: this workgroup's share of the row (several per token when tokens are few)
   for (int d0 = (blockIdx.y * blockDim.x + threadIdx.x) * 8; d0 < a.D; d0 += gridDim.y * blockDim.x * 8) {
-    // every load of this step first (the residual, the shared row, up to 8
-    // routed rows), then the adds in the fixed order
-    const Raw8<kXBf16> xv = load8<kXBf16>(a.x, (size_t)t, a.D, d0);
+    // every load of this step first (the residual if it is added, the shared
+    // row, up to 8 routed rows), then the adds in the fixed order
+    Raw8<kXBf16> xv{};
+    if (a.add_residual) xv = load8<kXBf16>(a.x, (size_t)t, a.D, d0);
     const Raw8<kYBf16> sv = load8<kYBf16>(sbase, srow, a.D, d0);
     Raw8<kYBf16> v[8];
 #pragma unroll
