@@ -56,7 +56,7 @@ GATEUP_COUNTERS = {
 # `bench.py --config v3_decode_fp8`; the same 1 GiB copy calibrates FETCH_SIZE)
 DECODE_GATEUP_COUNTERS = {
     "sources": {"mixture_experts_layer_38_amd/csrc/stream_gemm.hip":
-                "83b1f26397b50ce0e3081863c2a07c2c2afaad8512bcf89977af074417837ac9",
+                "436bdb7bf91f52ede5b7b688aa79451d50c94c5663e94423126d4087dbd8d83d",
                 "mixture_experts_layer_38_amd/csrc/moe_internal.hpp":
                 "d8bec0ef68504479c6f90c9ed087ca29354afba77a4f08124880edeb162eec8d"},
     "workload": "v3_decode_fp8",

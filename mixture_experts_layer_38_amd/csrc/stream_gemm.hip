@@ -8,8 +8,10 @@
 // four waves streams its own 16 weight rows straight from HBM into MFMA
 // operands; the activation rows are shared by the four waves through a small
 // LDS ring. An expert with more than 16 rows in the call gets one item per 16
-// rows; those items are adjacent, so they run together and share the weight
-// lines through L2.
+// rows; the items of one weight slice lie one row block of items apart in the
+// item order (32 gate/up or 112 down items at the V3 sizes, multiples of 8),
+// so on a grid that is a multiple of 8 workgroups they run in the same round
+// on the same XCD and share the weight lines through its L2.
 //
 // v_mfma_f32_16x16x32_bf16: lane l supplies A[token l%16][8 k] and
 // B[8 k][weight row l%16] for k-group l/16. Within a 128-wide K chunk, lane
