@@ -8,10 +8,13 @@
 // four waves streams its own 16 weight rows straight from HBM into MFMA
 // operands; the activation rows are shared by the four waves through a small
 // LDS ring. An expert with more than 16 rows in the call gets one item per 16
-// rows; the items of one weight slice lie one row block of items apart in the
-// item order (32 gate/up or 112 down items at the V3 sizes, multiples of 8),
-// so on a grid that is a multiple of 8 workgroups they run in the same round
-// on the same XCD and share the weight lines through its L2.
+// rows. Inside a problem the items go column-major (the row blocks of one
+// weight slice are consecutive), and the item list is cut into one
+// contiguous stretch per XCD (workgroup b runs on XCD b % 8): the XCD's
+// workgroups walk their stretch in rounds of consecutive items, so the items
+// that read one weight slice run side by side on one XCD and share its lines
+// through that L2, and a row block's activations (the down GEMM's h rows,
+// read by every item of the block) are fetched into one L2, not eight.
 //
 // v_mfma_f32_16x16x32_bf16: lane l supplies A[token l%16][8 k] and
 // B[8 k][weight row l%16] for k-group l/16. Within a 128-wide K chunk, lane
@@ -62,6 +65,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 namespace {
 
 constexpr int kU = 4;               // chunks per group
+constexpr int kXcds = 8;            // XCDs of the part; workgroup b runs on XCD b % 8
 constexpr int kALd = kST_KC + 8;    // LDS row length of an activation chunk (bf16), padded
 constexpr int kASlot = 16 * kALd;   // one chunk of 16 activation rows
 
@@ -89,10 +93,11 @@ __device__ __forceinline__ Item setup_item(const ExpertGemmArgs& a, const int32_
   const int rows = routed ? s_off[p + 1] - s_off[p] : a.T;
   const int row_base = routed ? s_off[p] : 0;
   const int Hp = routed ? a.H : a.Hs;
-  const int ncols = (kMode == 0) ? Hp / kST_N1 : a.D / kST_N2;
   const int local = item - s_pre[p];
-  const int m0 = (local / ncols) * kST_BM;
-  const int nb = local % ncols;
+  // column-major: consecutive items are the row blocks of one weight slice
+  const int nmb = (rows + kST_BM - 1) / kST_BM;  // >= 1: p owns this item
+  const int nb = local / nmb;
+  const int m0 = (local % nmb) * kST_BM;
   it.nrows = min(rows - m0, kST_BM);
   const int K = (kMode == 0) ? a.D : Hp;
   it.nch = K / kST_KC;
@@ -149,8 +154,16 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(ExpertGemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int rr = lane & 15, q = lane >> 4;
   const int total = s_pre[a.E + 1];
-  int item = blockIdx.x;
-  if (item >= total) return;  // uniform over the workgroup
+  // XCD x (workgroups x, x + nx, ...) owns items [beg, end), one nx-th of
+  // the list; its gx workgroups take them in rounds of gx consecutive items
+  // (a grid that is not a multiple of the XCD count walks one stretch)
+  const int nx = (gridDim.x % kXcds == 0) ? kXcds : 1;
+  const int gx = (int)gridDim.x / nx;
+  const int chunk = (total + nx - 1) / nx;
+  const int beg = min(total, ((int)blockIdx.x % nx) * chunk);
+  const int end = min(total, beg + chunk);
+  int item = beg + (int)blockIdx.x / nx;
+  if (item >= end) return;  // uniform over the workgroup
 
   constexpr int kWv = kFp8 ? 2 : 4;  // 16-byte weight loads per lane per chunk
   constexpr size_t welt = kFp8 ? 1 : 2;
@@ -192,7 +205,7 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(ExpertGemmArgs a) {
   // priority the oldest waves win the issue slots, so the first workgroup
   // on a CU would finish long before the last and leave the CU short of
   // requests in flight; a workgroup that is ahead now yields to those behind.
-  const int my_items = (total - 1 - (int)blockIdx.x) / (int)gridDim.x + 1;
+  const int my_items = (end - 1 - item) / gx + 1;
   int done = 0;
   auto set_priority = [&]() __attribute__((always_inline)) {
     switch (3 - min(3, (4 * done) / my_items)) {
@@ -211,8 +224,8 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(ExpertGemmArgs a) {
 
   while (true) {
     const int ngr = (cur.nch + kU - 1) / kU;
-    const int next_item = item + gridDim.x;
-    const bool has_next = next_item < total;  // uniform over the workgroup
+    const int next_item = item + gx;
+    const bool has_next = next_item < end;  // uniform over the workgroup
     Item nxt = cur;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -314,8 +327,9 @@ __global__ __launch_bounds__(256) void stream_gemm_kernel(ExpertGemmArgs a) {
 
 // Workgroups of one kernel that fit on a CU at once (registers and LDS
 // decide: the e4m3 kernels fit three, the bf16 ones two); the grid is that
-// many per CU, capped at the item count, so every workgroup is resident from
-// the start and none picks up its first item late.
+// many per CU, capped at the item count and rounded down to a multiple of
+// the XCD count, so every workgroup is resident from the start and none
+// picks up its first item late.
 template <bool kFp8, int kMode>
 static int resident_per_cu() {
   static int n = 0;  // the same on every gfx950 device; a racing first call computes the same value
@@ -331,7 +345,8 @@ static int resident_per_cu() {
 
 template <bool kFp8, int kMode>
 static hipError_t launch_stream(const ExpertGemmArgs& a, int max_items, int num_cus, hipStream_t s) {
-  const int blocks = std::min(max_items, resident_per_cu<kFp8, kMode>() * num_cus);
+  int blocks = std::min(max_items, resident_per_cu<kFp8, kMode>() * num_cus);
+  if (blocks > kXcds) blocks -= blocks % kXcds;  // whole rounds of XCDs: one item stretch per XCD
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((stream_gemm_kernel<kFp8, kMode>), dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
