@@ -56,12 +56,12 @@ GATEUP_COUNTERS = {
 # `bench.py --config v3_decode_fp8`; the same 1 GiB copy calibrates FETCH_SIZE)
 DECODE_GATEUP_COUNTERS = {
     "sources": {"mixture_experts_layer_38_amd/csrc/stream_gemm.hip":
-                "436bdb7bf91f52ede5b7b688aa79451d50c94c5663e94423126d4087dbd8d83d",
+                "d646320d0c203bdc1648a7b193650f720e6f99e7c13b942fcfaf152206d49473",
                 "mixture_experts_layer_38_amd/csrc/moe_internal.hpp":
                 "d8bec0ef68504479c6f90c9ed087ca29354afba77a4f08124880edeb162eec8d"},
     "workload": "v3_decode_fp8",
-    "fetch_kib": 1886165.5, "write_kib": 2333.9,
-    "fetch_scale": 1048576.0 / 524316.8, "write_scale": 1.0,
+    "fetch_kib": 1829744.4, "write_kib": 2562.7,
+    "fetch_scale": 1048576.0 / 524314.8, "write_scale": 1.0,
 }
 
 
