@@ -234,9 +234,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + (size_t)t * a.D + d0) =
           make_uint4(w[0], w[1], w[2], w[3]);
     } else {
-      float4* p = reinterpret_cast<float4*>(static_cast<float*>(a.out) + (size_t)t * a.D + d0);
-      p[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      p[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+      // the output is written once and not read back here: streaming stores
+      f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + (size_t)t * a.D + d0);
+      __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]}, p);
+      __builtin_nontemporal_store(f32x4{acc[4], acc[5], acc[6], acc[7]}, p + 1);
     }
   }
 }
